@@ -1,0 +1,104 @@
+"""CPU oracle for the index-only TopK selector.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product library
+(``sparse_attention_topk_fp32_amd``) never imports it, and this package never
+imports the product library: the two share no code.
+
+Contents
+--------
+* ``topk`` / ``kth_largest`` - the plain definition (``topk_oracle.c``): sort
+  the valid positions of each row by (value descending, index ascending) with
+  IEEE float comparisons and keep the first k.  Compiled with gcc, no
+  fast-math.
+* ``pages_radix`` - the article's radix-select method restated in Python
+  (mapping, digit histograms, threshold bucket, collection), a second route
+  used to pin the first.
+
+Parity pins (tests/test_oracle_pins.py): brute force over all k-subsets of tiny
+rows, the article's method (``pages_radix``), numpy's stable argsort, closed
+forms, the worked value the article prints (839 -> 100), and the selection
+invariants.  No oracle function is left unpinned.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "topk_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+ORACLE_OK, ORACLE_ERR_ARG, ORACLE_ERR_NAN, ORACLE_ERR_NOMEM = 0, 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile ``topk_oracle.c`` into ``liboracle.so`` with gcc (-O2, no
+    fast-math, so subnormals compare as themselves)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-Wall", "-Werror",
+             _SRC, "-o", tmp],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I = ctypes.c_int32
+            lib.oracle_topk.argtypes = [P, I, I, P, I, P]
+            lib.oracle_topk.restype = ctypes.c_int
+            lib.oracle_kth_largest.argtypes = [P, I, I, I, P]
+            lib.oracle_kth_largest.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def topk(x: np.ndarray, k: int, lengths: Optional[np.ndarray] = None) -> np.ndarray:
+    """Oracle selection: int32 [rows, k], each row in (value desc, index asc)
+    order, padded with -1 when the valid length is below k."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, n = x.shape
+    out = np.empty((rows, k), dtype=np.int32)
+    lp = None
+    if lengths is not None:
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        assert lengths.shape == (rows,)
+        lp = lengths.ctypes.data
+    rc = lib.oracle_topk(x.ctypes.data, rows, n, lp, int(k), out.ctypes.data)
+    if rc == ORACLE_ERR_NAN:
+        raise ValueError("NaN among the valid logits (outside the selector's contract)")
+    if rc != ORACLE_OK:
+        raise ValueError("oracle_topk failed with code %d" % rc)
+    return out
+
+
+def kth_largest(row: np.ndarray, k: int, length: Optional[int] = None) -> float:
+    """The k-th largest valid value of one row, with multiplicity."""
+    lib = _load()
+    row = np.ascontiguousarray(row, dtype=np.float32).ravel()
+    L = row.shape[0] if length is None else int(length)
+    v = ctypes.c_float()
+    rc = lib.oracle_kth_largest(row.ctypes.data, row.shape[0], L, int(k), ctypes.addressof(v))
+    if rc != ORACLE_OK:
+        raise ValueError("oracle_kth_largest failed with code %d" % rc)
+    return float(np.float32(v.value))

@@ -1,0 +1,122 @@
+/*
+ * CPU oracle for the index-only TopK selector.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the package smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header or table
+ * with the GPU library.
+ *
+ * Source: the web article "How to Use FlagOS's New Triton-TLE Language to
+ * Build a TopK Selector Faster Than FlashInfer" (below: the TopK article).
+ *
+ *  - Section 01: the selector returns, per query row of indexer logits, the
+ *    indices of the k largest logits; values are not returned and the output
+ *    need not be sorted.
+ *  - Section 02, the radix_topk pseudocode: first every element strictly above
+ *    the k-th largest value T is taken, then elements equal to T are taken in
+ *    scan order until k are held, i.e. ties at T go to the lowest index.
+ *  - Section 5 (output flush): -1 is the value written for an output slot that
+ *    holds no index.
+ *
+ * This oracle is the plain definition, not the radix method: for each row it
+ * sorts the valid positions by (value descending, index ascending) with IEEE
+ * float comparisons and keeps the first min(k, L) of them.  Readings where
+ * the article is silent:
+ *  - valid length L = lengths[r] clamped to [0, n] (all n when lengths is
+ *    NULL); positions >= L are never returned;
+ *  - when L < k the row holds all of 0..L-1 followed by k-L entries of -1;
+ *  - -0.0 and +0.0 compare equal, so they tie (lowest index first);
+ *    infinities and subnormals are ordinary values (build without fast-math,
+ *    so subnormals are not flushed);
+ *  - NaN is outside the contract: a NaN among the valid positions makes the
+ *    oracle return ORACLE_ERR_NAN.
+ * Each output row is written in (value desc, index asc) order; callers that
+ * compare against the GPU path compare sorted index sets.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NAN 2
+#define ORACLE_ERR_NOMEM 3
+
+/* Each element carries its value and index, so the comparator needs no
+ * outside state and several threads may run the oracle at once. */
+typedef struct {
+    float v;
+    int32_t i;
+} oracle_elem;
+
+/* Total order: larger value first; equal values (including -0 vs +0) by
+ * smaller index first. */
+static int oracle_cmp(const void* pa, const void* pb) {
+    const oracle_elem* a = (const oracle_elem*)pa;
+    const oracle_elem* b = (const oracle_elem*)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    /* a->v == b->v here (NaN was rejected before sorting) */
+    if (a->i < b->i) return -1;
+    if (a->i > b->i) return 1;
+    return 0;
+}
+
+static int oracle_row(const float* x, int32_t n, int32_t L, int32_t k, int32_t* out, oracle_elem* buf) {
+    if (L < 0) L = 0;
+    if (L > n) L = n;
+    /* Elements enter the sort in descending index order, so the result does
+     * not lean on the sort being stable: the index tie-break must come from
+     * the comparator. */
+    for (int32_t i = 0; i < L; ++i) {
+        int32_t j = L - 1 - i;
+        if (x[j] != x[j]) return ORACLE_ERR_NAN;
+        buf[i].v = x[j];
+        buf[i].i = j;
+    }
+    qsort(buf, (size_t)L, sizeof(oracle_elem), oracle_cmp);
+    int32_t take = L < k ? L : k;
+    for (int32_t j = 0; j < take; ++j) out[j] = buf[j].i;
+    for (int32_t j = take; j < k; ++j) out[j] = -1;
+    return ORACLE_OK;
+}
+
+/* logits: [rows, n] row-major float32 (host memory); lengths: [rows] or NULL;
+ * out: [rows, k] int32 (host memory).  Returns ORACLE_OK or an error code. */
+int oracle_topk(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                int32_t* out) {
+    if (rows < 0 || n < 1 || k < 1 || k > n) return ORACLE_ERR_ARG;
+    if (rows == 0) return ORACLE_OK;
+    if (!logits || !out) return ORACLE_ERR_ARG;
+    oracle_elem* buf = (oracle_elem*)malloc(sizeof(oracle_elem) * (size_t)n);
+    if (!buf) return ORACLE_ERR_NOMEM;
+    int rc = ORACLE_OK;
+    for (int32_t r = 0; r < rows && rc == ORACLE_OK; ++r) {
+        int32_t L = lengths ? lengths[r] : n;
+        rc = oracle_row(logits + (size_t)r * (size_t)n, n, L, k, out + (size_t)r * (size_t)k, buf);
+    }
+    free(buf);
+    return rc;
+}
+
+/* The k-th largest valid value of one row (counted with multiplicity), i.e.
+ * the threshold T of the article's radix_topk.  Requires 1 <= k <= L. */
+int oracle_kth_largest(const float* x, int32_t n, int32_t L, int32_t k, float* kth) {
+    if (L > n) L = n;
+    if (n < 1 || k < 1 || L < k || !x || !kth) return ORACLE_ERR_ARG;
+    oracle_elem* buf = (oracle_elem*)malloc(sizeof(oracle_elem) * (size_t)L);
+    if (!buf) return ORACLE_ERR_NOMEM;
+    for (int32_t i = 0; i < L; ++i) {
+        int32_t j = L - 1 - i;
+        if (x[j] != x[j]) {
+            free(buf);
+            return ORACLE_ERR_NAN;
+        }
+        buf[i].v = x[j];
+        buf[i].i = j;
+    }
+    qsort(buf, (size_t)L, sizeof(oracle_elem), oracle_cmp);
+    *kth = buf[k - 1].v;
+    free(buf);
+    return ORACLE_OK;
+}

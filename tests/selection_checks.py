@@ -1,0 +1,51 @@
+"""Checks on a selected index row that hold whatever produced it.
+
+The selector's contract (TopK article, sections 01 and 02): per row, the
+indices of the k largest valid values, each index once, ties at the
+threshold value going to the lowest indices, -1 in slots that hold no index
+(section 5's output flush).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def valid_length(n: int, lengths, r: int) -> int:
+    if lengths is None:
+        return n
+    return int(min(max(int(lengths[r]), 0), n))
+
+
+def check_row_invariants(x_row: np.ndarray, L: int, k: int, sel: np.ndarray) -> None:
+    """Raise AssertionError unless ``sel`` is the unique correct selection for
+    the valid prefix ``x_row[:L]``: k entries, min(k, L) distinct indices in
+    [0, L), -1 in the rest, every selected value >= every unselected valid
+    value, and among values equal to the smallest selected value the selected
+    indices all lie below the unselected ones."""
+    sel = np.asarray(sel)
+    assert sel.shape == (k,), sel.shape
+    take = min(k, L)
+    valid = sel[sel >= 0]
+    assert int((sel == -1).sum()) == k - take, "wrong number of -1 slots"
+    assert valid.size == take, "wrong number of indices"
+    assert np.all(valid < L), "index past the valid length"
+    assert np.unique(valid).size == take, "duplicate index"
+    if take == 0 or take == L:
+        return
+    xv = x_row[:L].astype(np.float64)
+    chosen = np.zeros(L, dtype=bool)
+    chosen[valid] = True
+    lo = xv[chosen].min()
+    hi = xv[~chosen].max()
+    assert lo >= hi, "an unselected value exceeds a selected one"
+    if lo == hi:
+        tied = np.nonzero(xv == lo)[0]
+        tsel = tied[chosen[tied]]
+        tun = tied[~chosen[tied]]
+        assert tsel.max() < tun.min(), "ties at the threshold not taken lowest index first"
+
+
+def same_sets(a: np.ndarray, b: np.ndarray) -> bool:
+    """Row-wise equality of two [rows, k] index arrays as sorted multisets."""
+    return np.array_equal(np.sort(a, axis=-1), np.sort(b, axis=-1))

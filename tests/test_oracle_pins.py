@@ -1,0 +1,287 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+The oracle (``oracle/topk_oracle.c``) is the plain definition of the TopK
+article's selector: sort valid positions by (value desc, index asc), keep k.
+Each test below checks it against an independent source:
+
+* brute force over every k-subset of tiny rows, kept by the defining property;
+* the article's radix-select method restated step by step (``oracle.pages_radix``);
+* numpy's stable sort (a library routine for the same order);
+* closed forms of rows whose answer is known;
+* hand-worked cases and the one value the article prints (``tests/golden``);
+* the invariants every correct selection satisfies.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import pages_radix
+from tests.selection_checks import check_row_invariants, same_sets
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SUB = np.float32(1e-45)  # smallest positive subnormal float32
+ALPHABET = np.array([-np.inf, -1.0, -0.0, 0.0, SUB, -SUB, 1.0, np.inf], dtype=np.float32)
+
+
+def _parse_floats(s):
+    return np.array([float(t) for t in s.split()], dtype=np.float32)
+
+
+def _golden_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "hand_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            vals, k, length, expect = [p.strip() for p in line.split("|")]
+            L = None if length == "all" else int(length)
+            cases.append((_parse_floats(vals), int(k), L, [int(t) for t in expect.split()]))
+    return cases
+
+
+# ---------------------------------------------------------------- golden
+
+@pytest.mark.parametrize("vals,k,L,expect", _golden_cases())
+def test_hand_cases(vals, k, L, expect):
+    lengths = None if L is None else np.array([L], dtype=np.int32)
+    got = oracle.topk(vals[None, :], k, lengths)[0]
+    assert sorted(got.tolist()) == expect
+    # the article's method reaches the same set
+    assert sorted(pages_radix.radix_topk_row(vals.tolist(), k, L)) == expect
+
+
+def test_place_value_printed_by_article():
+    with open(os.path.join(GOLDEN, "pages_place_value.txt")) as f:
+        rows = [l.split("|") for l in f if l.strip() and not l.startswith("#")]
+    assert rows, "empty fixture"
+    for a, b in rows:
+        assert pages_radix.highest_power_of_10(int(a)) == int(b)
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute_force_sets(x, L, k):
+    """Every k-subset S of [0, L) such that each chosen element beats each
+    unchosen one (larger value, or equal value and smaller index)."""
+    found = []
+    for S in itertools.combinations(range(L), k):
+        s = set(S)
+        ok = True
+        for i in S:
+            for j in range(L):
+                if j in s:
+                    continue
+                if not (x[i] > x[j] or (x[i] == x[j] and i < j)):
+                    ok = False
+                    break
+            if not ok:
+                break
+        if ok:
+            found.append(list(S))
+    return found
+
+
+def test_brute_force_tiny_rows():
+    rng = np.random.default_rng(20261202)
+    checked = 0
+    for n in range(1, 9):
+        for _ in range(40):
+            x = rng.choice(ALPHABET, size=n)
+            L = int(rng.integers(0, n + 1)) if rng.random() < 0.3 else n
+            for k in range(1, n + 1):
+                got = oracle.topk(x[None, :], k, np.array([L], np.int32))[0]
+                if L < k:
+                    assert sorted(got.tolist()) == [-1] * (k - L) + list(range(L))
+                    continue
+                sets = _brute_force_sets(x.astype(np.float64), L, k)
+                assert len(sets) == 1, (x, L, k, sets)  # the selection is unique
+                assert sorted(got.tolist()) == sets[0], (x, L, k)
+                checked += 1
+    assert checked > 500
+
+
+# ---------------------------------------------------------------- the article's method
+
+def test_article_method_matches_oracle_random_ties():
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        n = int(rng.integers(1, 400))
+        kind = trial % 3
+        if kind == 0:
+            x = rng.choice(ALPHABET, size=n)
+        elif kind == 1:
+            x = rng.integers(-3, 4, size=n).astype(np.float32)  # heavy ties
+        else:
+            x = rng.standard_normal(n).astype(np.float32)
+        k = int(rng.integers(1, n + 1))
+        got = oracle.topk(x[None, :], k)[0]
+        ref, tkey = pages_radix.radix_topk_indices(x.tolist(), k)
+        assert sorted(got.tolist()) == sorted(ref)
+        # both routes agree on the threshold T (the k-th largest value)
+        assert pages_radix.float_to_ordered_u32(oracle.kth_largest(x, k)) == tkey
+
+
+def test_article_method_on_workload_prefix():
+    import workloads as W
+
+    for name in ("c1", "c2", "c3"):
+        w = W.generate(name)
+        x = w.x[0, :3000]
+        got = oracle.topk(x[None, :], 300)[0]
+        ref = pages_radix.radix_topk_row(x.tolist(), 300)
+        assert sorted(got.tolist()) == sorted(ref), name
+
+
+# ---------------------------------------------------------------- numpy stable sort
+
+def _numpy_select(x, L, k):
+    xv = x[:L]
+    order = np.lexsort((np.arange(L), -xv.astype(np.float64)))
+    sel = order[:k].astype(np.int32)
+    return np.concatenate([sel, -np.ones(k - len(sel), np.int32)])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_numpy_stable_sort_on_workloads(name):
+    import workloads as W
+
+    w = W.generate(name)
+    got = oracle.topk(w.x, w.k, w.lengths)
+    for r in range(w.x.shape[0]):
+        L = w.x.shape[1] if w.lengths is None else int(w.lengths[r])
+        assert sorted(got[r].tolist()) == sorted(_numpy_select(w.x[r], L, w.k).tolist())
+
+
+def test_numpy_stable_sort_on_sampled_causal_rows():
+    import workloads as W
+
+    w = W.generate("c5", rows=[0, 1, 2047, 4095])
+    got = oracle.topk(w.x, w.k, w.lengths)
+    for r in range(4):
+        L = int(w.lengths[r])
+        assert sorted(got[r].tolist()) == sorted(_numpy_select(w.x[r], L, w.k).tolist())
+        check_row_invariants(w.x[r], L, w.k, got[r])
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("L,k", [(1, 1), (5, 3), (100, 100), (4096, 2048), (10000, 2048), (3, 2048)])
+def test_closed_forms(L, k):
+    n = max(L, k)
+    idx = np.arange(n)
+    want_low = list(range(min(k, L))) + [-1] * max(0, k - L)
+    lengths = np.array([L], np.int32)
+    # constant row: lowest indices
+    x = np.full(n, 0.25, np.float32)
+    assert sorted(oracle.topk(x[None], k, lengths)[0].tolist()) == sorted(want_low)
+    # descending ramp: the first k
+    x = (-idx).astype(np.float32)
+    assert sorted(oracle.topk(x[None], k, lengths)[0].tolist()) == sorted(want_low)
+    # all -inf: lowest indices
+    x = np.full(n, -np.inf, np.float32)
+    assert sorted(oracle.topk(x[None], k, lengths)[0].tolist()) == sorted(want_low)
+    # ascending ramp: the last k valid positions
+    x = idx.astype(np.float32)
+    got = sorted(oracle.topk(x[None], k, lengths)[0].tolist())
+    if L >= k:
+        assert got == list(range(L - k, L))
+    else:
+        assert got == sorted(want_low)
+
+
+def test_k_equal_one_is_first_argmax():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(rng.integers(1, 300))
+        x = rng.integers(-5, 5, size=n).astype(np.float32)
+        assert oracle.topk(x[None], 1)[0, 0] == int(np.argmax(x))
+
+
+def test_k_equal_length_is_everything():
+    x = np.random.default_rng(4).standard_normal(777).astype(np.float32)
+    assert sorted(oracle.topk(x[None], 777)[0].tolist()) == list(range(777))
+
+
+def test_zero_length_rows_are_all_padding():
+    x = np.ones((3, 10), np.float32)
+    got = oracle.topk(x, 4, np.array([0, -5, 2], np.int32))
+    assert got[0].tolist() == [-1] * 4 and got[1].tolist() == [-1] * 4
+    assert sorted(got[2].tolist()) == [-1, -1, 0, 1]
+
+
+def test_lengths_beyond_n_are_clamped():
+    x = np.arange(8, dtype=np.float32)[None]
+    assert sorted(oracle.topk(x, 2, np.array([100], np.int32))[0].tolist()) == [6, 7]
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_invariants_hold_on_oracle_outputs():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        n = int(rng.integers(1, 600))
+        x = rng.choice(ALPHABET, size=n) if rng.random() < 0.5 else rng.standard_normal(n).astype(np.float32)
+        k = int(rng.integers(1, n + 1))
+        L = int(rng.integers(0, n + 1))
+        got = oracle.topk(x[None], k, np.array([L], np.int32))[0]
+        check_row_invariants(x, L, k, got)
+
+
+def test_invariant_checker_rejects_planted_mistakes():
+    """A wrong selection (highest-index ties, a dropped element, a value swap)
+    must be caught by the checker the GPU tests rely on."""
+    x = np.array([3, 5, 5, 5, 1, 7], np.float32)
+    good = oracle.topk(x[None], 3)[0]
+    check_row_invariants(x, 6, 3, good)
+    for bad in ([5, 3, 2], [5, 1, 1], [5, 1, 0], [5, 1, -1], [5, 4, 1]):
+        with pytest.raises(AssertionError):
+            check_row_invariants(x, 6, 3, np.array(bad, np.int32))
+
+
+# ---------------------------------------------------------------- key map of the article's method
+
+def test_mapping_step_orders_like_floats():
+    rng = np.random.default_rng(5)
+    specials = np.array(
+        [-np.inf, -np.finfo(np.float32).max, -1.0, -np.finfo(np.float32).tiny, -SUB, -0.0, 0.0, SUB,
+         np.finfo(np.float32).tiny, 1.0, np.finfo(np.float32).max, np.inf], dtype=np.float32)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[~np.isnan(vals)]
+    allv = np.concatenate([specials, vals, rng.standard_normal(2000).astype(np.float32)])
+    keys = np.array([pages_radix.float_to_ordered_u32(float(v)) for v in allv], dtype=np.uint64)
+    order = np.argsort(allv.astype(np.float64), kind="stable")
+    sv, sk = allv[order].astype(np.float64), keys[order]
+    for a in range(len(sv) - 1):
+        if sv[a] < sv[a + 1]:
+            assert sk[a] < sk[a + 1]
+        else:
+            assert sk[a] == sk[a + 1]
+    assert pages_radix.float_to_ordered_u32(-0.0) == pages_radix.float_to_ordered_u32(0.0)
+    # every non-NaN key fits in 32 bits and is non-negative
+    assert all(0 <= int(kk) < 2**32 for kk in keys)
+
+
+def test_oracle_rejects_nan_and_bad_arguments():
+    x = np.array([[1.0, math.nan, 2.0]], np.float32)
+    with pytest.raises(ValueError):
+        oracle.topk(x, 1)
+    # a NaN past the valid length is never read
+    assert oracle.topk(x, 1, np.array([1], np.int32))[0].tolist() == [0]
+    with pytest.raises(ValueError):
+        oracle.topk(np.ones((1, 3), np.float32), 4)
+    with pytest.raises(ValueError):
+        oracle.topk(np.ones((1, 3), np.float32), 0)
+
+
+def test_same_sets_helper():
+    assert same_sets(np.array([[1, 2, 3]]), np.array([[3, 1, 2]]))
+    assert not same_sets(np.array([[1, 2, 3]]), np.array([[3, 1, 4]]))
