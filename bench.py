@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X TopK selector; prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1_n128k_bf16]
+
+A step is one call of the whole selection (every kernel of the path; here a
+single launch) over one batch of seeded synthetic logits already resident in
+device memory.  The headline workload is one row of 131,072 bf16-valued fp32
+logits with k = 2048 (the batch-1 decode case); the batch-64 case (64 rows of
+131,072 with ragged valid lengths) is timed the same way and reported beside it.
+
+Timing: the K timed launches are captured into a HIP graph (torch.cuda.CUDAGraph)
+and replayed, so the per-step time is the GPU time of back-to-back launches, not
+Python's call overhead; HIP events on the launch stream bracket the timed
+region.  The per-call time of plain eager calls from Python is reported too.
+The oracle (CPU) is timed on a bounded sample for the `cpu_baseline` field.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "TopK µs/row @N=128K,k=2048,batch1; rows/s @batch64; % HBM roofline"
+
+
+def algorithmic_bytes(n_rows: int, n: int, k: int, lengths) -> int:
+    """One read of every valid logit, the k int32 indices written per row, and
+    the int32 length per row when lengths are given."""
+    if lengths is None:
+        valid = n_rows * n
+        lbytes = 0
+    else:
+        valid = int(np.clip(np.asarray(lengths, np.int64), 0, n).sum())
+        lbytes = 4 * n_rows
+    return 4 * valid + 4 * k * n_rows + lbytes
+
+
+def time_graph(torch, fn_list, steps: int, warmup: int, stream):
+    """Capture the callables (one launch each) into a graph, replay it
+    until `steps` launches are timed; returns seconds per launch."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for f in fn_list:  # warm: allocates the library workspace outside the capture
+            f()
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for f in fn_list:
+                f()
+    reps = max(1, (steps + len(fn_list) - 1) // len(fn_list))
+    for _ in range(max(1, warmup // len(fn_list))):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * len(fn_list)), reps * len(fn_list)
+
+
+def time_eager(torch, fn, steps: int, warmup: int, stream):
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int):
+    """Per-launch seconds (graph, warm), (graph, cold: rotating copies), eager."""
+    w = W.generate(name)
+    rows, n = w.x.shape
+    stream = torch.cuda.Stream()
+    xs = [torch.from_numpy(w.x).cuda()]
+    for _ in range(copies - 1):
+        xs.append(xs[0].clone())
+    L = None if w.lengths is None else torch.from_numpy(w.lengths).cuda()
+    outs = [torch.empty((rows, w.k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    warm_fns = [lambda: tks.select(xs[0], w.k, lengths=L, out=outs[0])]
+    cold_fns = [(lambda i: (lambda: tks.select(xs[i], w.k, lengths=L, out=outs[i % 2])))(i) for i in range(copies)]
+    t_warm, n_warm = time_graph(torch, warm_fns * 32, steps, warmup, stream)
+    t_cold, n_cold = time_graph(torch, cold_fns, steps, warmup, stream) if copies > 1 else (t_warm, n_warm)
+    t_eager = time_eager(torch, warm_fns[0], max(20, steps // 4), warmup, stream)
+    flags = tks.device_status(stream)
+    if flags:
+        raise RuntimeError("device-side error flags raised during the benchmark: %d" % flags)
+    return {
+        "workload": w.config.name, "rows": rows, "n": n, "k": w.k,
+        "lengths": None if w.lengths is None else "per-row",
+        "bytes": algorithmic_bytes(rows, n, w.k, w.lengths),
+        "t_warm": t_warm, "t_cold": t_cold, "t_eager": t_eager, "launches_timed": n_warm,
+        "plan": tks.plan(rows, n, w.k), "x": w.x, "lengths_arr": w.lengths,
+    }
+
+
+def cpu_baseline(w_x, k, budget_s: float = 10.0):
+    """The oracle as it stands on one host core, on the headline row, repeated
+    for about `budget_s` seconds; returns the median seconds per row."""
+    import oracle
+
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        oracle.topk(w_x, k)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 2000:
+            break
+    return float(np.median(times)) / w_x.shape[0], len(times)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="b1_n128k_bf16")
+    ap.add_argument("--batch-workload", default="b64_n128k_ragged")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cold-copies", type=int, default=0,
+                    help="input copies rotated for the cold-cache timing (0: enough to exceed 512 MiB)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build's selector runs on a single GPU "
+              "(rows shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_attention_topk_fp32_amd as tks
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+
+    def copies_for(name):
+        c = W.config(name)
+        if args.cold_copies:
+            return args.cold_copies
+        return int(max(2, min(1024, (512 << 20) // (c.rows * c.n * 4) + 1)))
+
+    head = bench_workload(torch, tks, W, args.workload, args.steps, args.warmup, copies_for(args.workload))
+    batch = bench_workload(torch, tks, W, args.batch_workload, max(200, args.steps // 10), args.warmup,
+                           copies_for(args.batch_workload))
+
+    t = head["t_warm"]
+    us_per_row = t * 1e6 / head["rows"]
+    achieved = head["bytes"] / t / 1e9
+    bt = batch["t_warm"]
+    res = {
+        "metric": METRIC,
+        "value": round(us_per_row, 4),
+        "unit": "us/row",
+        "n_gpus": 1,
+        "steps": head["launches_timed"],
+        "warmup": args.warmup,
+        "ms_per_step": round(t * 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic (seeded; fp32 logits, order-preserving u32 keys)",
+        "config": {
+            "workload": head["workload"], "rows": head["rows"], "n": head["n"], "k": head["k"],
+            "batch": head["rows"], "plan": head["plan"],
+            "timing": "HIP-graph replay of back-to-back launches on one stream, same input (warm)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 6),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": head["bytes"],
+        },
+        "batch64": {
+            "workload": batch["workload"], "rows": batch["rows"], "n": batch["n"], "k": batch["k"],
+            "rows_per_s": round(batch["rows"] / bt, 1),
+            "us_per_launch": round(bt * 1e6, 3),
+            "us_per_launch_cold": round(batch["t_cold"] * 1e6, 3),
+            "achieved_GBps": round(batch["bytes"] / bt / 1e9, 3),
+            "hbm_frac": round(batch["bytes"] / bt / 1e9 / HBM_PEAK_GBPS, 6),
+            "algorithmic_bytes_per_launch": batch["bytes"],
+            "plan": batch["plan"],
+        },
+        "latency_detail": {
+            "us_per_launch_warm": round(head["t_warm"] * 1e6, 3),
+            "us_per_launch_cold": round(head["t_cold"] * 1e6, 3),
+            "us_per_call_eager_python": round(head["t_eager"] * 1e6, 3),
+        },
+    }
+    if not args.no_cpu:
+        sec_per_row, reps = cpu_baseline(head["x"], head["k"])
+        res["cpu_baseline"] = {
+            "value": round(sec_per_row * 1e6, 2),
+            "unit": "us/row",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": "the headline row (1 x %d, k=%d), %d repeated oracle calls, median; "
+                      "single-threaded C oracle (stable sort by value desc, index asc)"
+                      % (head["n"], head["k"], reps),
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,141 @@
+/*
+ * topk_select.h - C ABI of the MI355X (gfx950) index-only TopK selector.
+ *
+ * What is computed.  The web article "How to Use FlagOS's New Triton-TLE
+ * Language to Build a TopK Selector Faster Than FlashInfer" (below: the TopK
+ * article) describes the selector of DeepSeek-Sparse-Attention-style
+ * decoding: in section 01, per query row of indexer logits over the
+ * historical tokens, return the indices of the k largest logits, indices
+ * only, without a full sort; in section 02, a radix select that maps floats to
+ * order-preserving unsigned integers, histograms their digits from the most
+ * significant end, keeps the bucket holding the k-th element, and finally
+ * collects every element above the threshold value T followed by elements
+ * equal to T in scan order (so ties at T go to the lowest index); in section
+ * 5, -1 as the value of an output slot that holds no index.
+ *
+ * Readings of points the article leaves open (fixed by this ABI):
+ *  - logits are fp32, row-major [rows, n], row stride n;
+ *  - the valid length of row r is lengths[r] clamped to [0, n] (n for every
+ *    row when lengths is NULL); positions at or past it are never returned;
+ *  - when a row's valid length L is below k, the row's output holds every
+ *    index 0..L-1 followed by k-L entries of -1;
+ *  - -0.0 and +0.0 are equal (they tie); infinities and subnormals are
+ *    ordinary values; NaN logits are outside the contract (no error is
+ *    raised, the result for such a row is unspecified but memory-safe);
+ *  - the output order within a row is unspecified (the selected set is
+ *    exact and unique).
+ *
+ * All pointers named "device" point to memory on the calling thread's current
+ * HIP device.  The library never takes ownership of caller memory.
+ * No C++ exception crosses this interface.
+ */
+#ifndef TOPK_SELECT_H_
+#define TOPK_SELECT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TOPK_SELECT_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+    TOPK_SELECT_SUCCESS = 0,
+    TOPK_SELECT_ERROR_INVALID_VALUE = 1, /* bad argument; nothing was enqueued */
+    TOPK_SELECT_ERROR_OUT_OF_MEMORY = 2, /* workspace allocation failed; nothing was enqueued */
+    TOPK_SELECT_ERROR_LAUNCH = 3,        /* a HIP call or the kernel launch failed */
+    TOPK_SELECT_ERROR_NO_DEVICE = 4,     /* no usable HIP device is current */
+    TOPK_SELECT_ERROR_DEVICE_FLAG = 5    /* a kernel raised a device-side error flag */
+};
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers.
+ * NULL is the default (null) stream of the current device. */
+typedef void* topk_select_stream_t;
+
+/*
+ * topk_select - per row, the indices of the k largest valid logits (the TopK
+ * article, sections 01, 02 and 5; readings above).
+ *
+ *   logits   device, const float[rows * n], row-major, row stride n, at least
+ *            4-byte aligned (16-byte alignment of rows is used when present,
+ *            but not required).  Read only.
+ *   rows     number of rows, >= 0.  rows == 0 is a successful no-op.
+ *   n        row length, >= 1.
+ *   lengths  device, const int32_t[rows], or NULL.  Valid length per row; read
+ *            on the device and clamped to [0, n].
+ *   k        number of indices per row, 1 <= k <= n.
+ *   out_idx  device, int32_t[rows * k], row-major.  Written only by the
+ *            enqueued work; must not overlap logits or lengths.
+ *   stream   stream the work is enqueued on.  The call returns without
+ *            waiting; results are ready when the stream reaches this point.
+ *
+ * Returns TOPK_SELECT_SUCCESS when the work was enqueued.  Host-checkable
+ * arguments are checked before any HIP call; on INVALID_VALUE nothing is
+ * enqueued and out_idx is untouched.  The library keeps a scratch workspace
+ * per (device, stream), allocated on first use and grown as needed (the first
+ * call for a new (device, stream) or a larger shape allocates and clears it
+ * with hipMalloc/hipMemsetAsync; later calls of that size allocate nothing).
+ * Thread-safe; calls on different streams use different workspaces.
+ */
+int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                int32_t* out_idx, topk_select_stream_t stream);
+
+/*
+ * Launch-shape description, filled by topk_select_plan and accepted by
+ * topk_select_ex.  Performance only: every plan yields the same selected sets.
+ *   variant       kernel variant id (0 .. topk_select_num_variants()-1)
+ *   wgs_per_row   workgroups cooperating on one row (>= 1)
+ *   block         threads per workgroup of the variant (output only)
+ *   items         logits per thread per tile of the variant (output only)
+ *   resident      1 when each workgroup keeps its whole slice on chip across
+ *                 passes, 0 when it re-reads its slice every pass (output only)
+ */
+typedef struct {
+    int32_t variant;
+    int32_t wgs_per_row;
+    int32_t block;
+    int32_t items;
+    int32_t resident;
+} topk_select_plan_t;
+
+/* The launch shape topk_select would use for (rows, n, k) on the current
+ * device.  Returns INVALID_VALUE for arguments topk_select would reject. */
+int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* plan);
+
+/* topk_select with an explicit launch shape (plan->variant, plan->wgs_per_row).
+ * Used by tests to drive every kernel path and by tuning sweeps.  Returns
+ * INVALID_VALUE when the shape cannot cover n or cannot be co-resident. */
+int topk_select_ex(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                   int32_t* out_idx, topk_select_stream_t stream, const topk_select_plan_t* plan);
+
+/* Number of kernel variants compiled into the library; fills the shape of
+ * variant v (block, items, resident) into plan when v is in range. */
+int topk_select_num_variants(void);
+int topk_select_variant_info(int32_t v, topk_select_plan_t* plan);
+
+/*
+ * Waits for `stream`, then reads and clears the device-side error flags of
+ * the workspace of (current device, stream) and stores them in *flags (0 when
+ * none were raised or no workspace exists).  Flags: 1 = a cross-workgroup
+ * wait exceeded its time bound, 2 = an internal capacity check failed.
+ * Returns DEVICE_FLAG when any flag was set, SUCCESS otherwise.
+ */
+int topk_select_device_status(topk_select_stream_t stream, int32_t* flags);
+
+/* Frees every cached workspace (all devices and streams).  The caller must
+ * make sure no enqueued selection is still running. */
+int topk_select_release_workspace(void);
+
+/* Static, human-readable description of a status code. */
+const char* topk_select_error_string(int status);
+
+/* TOPK_SELECT_VERSION of the built library. */
+int topk_select_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_SELECT_H_ */

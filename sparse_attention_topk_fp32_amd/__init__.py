@@ -1,0 +1,145 @@
+"""MI355X-native index-only TopK selector (radix select, HIP for gfx950).
+
+Python binding over the C ABI of ``libtopk_select.so`` (``include/topk_select.h``).
+PyTorch is used only to allocate device memory and to name the current HIP
+stream; the selection itself runs entirely in the library's kernels.
+
+    import torch, sparse_attention_topk_fp32_amd as tks
+    idx = tks.select(logits, k=2048)              # int32 [rows, k], unsorted
+    idx = tks.select(logits, k=2048, lengths=L)   # per-row valid lengths
+
+Semantics (the TopK article "How to Use FlagOS's New Triton-TLE Language to
+Build a TopK Selector Faster Than FlashInfer", sections 01, 02 and 5): per row,
+the indices of the k largest valid logits, ties at the threshold value going
+to the lowest index, -1 in slots past the valid length, order unspecified.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _native
+from ._native import TopkSelectError  # noqa: F401
+
+__all__ = [
+    "select",
+    "topk_select",
+    "topk_select_ex",
+    "plan",
+    "num_variants",
+    "variant_info",
+    "device_status",
+    "release_workspace",
+    "version",
+    "TopkSelectError",
+]
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != _native.SUCCESS:
+        raise TopkSelectError(rc, what)
+
+
+def topk_select(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                stream: int = 0) -> int:
+    """Raw C-ABI call with device pointers; returns the status code."""
+    return _native.load().topk_select(logits_ptr or None, rows, n, lengths_ptr or None, k, out_ptr or None,
+                                      stream or None)
+
+
+def topk_select_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                   stream: int, variant: int, wgs_per_row: int) -> int:
+    """Raw C-ABI call with an explicit launch shape; returns the status code."""
+    p = _native.PlanT(variant, wgs_per_row, 0, 0, 0)
+    return _native.load().topk_select_ex(logits_ptr or None, rows, n, lengths_ptr or None, k, out_ptr or None,
+                                         stream or None, ctypes.byref(p))
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream) or 0)
+
+
+def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optional[int] = None,
+           wgs_per_row: Optional[int] = None):
+    """Indices of the k largest valid logits of each row.
+
+    logits   float32 tensor on the GPU, [rows, n] (or [n]), contiguous rows.
+    k        1 <= k <= n.
+    lengths  optional int32 GPU tensor [rows] of valid lengths.
+    out      optional preallocated int32 GPU tensor [rows, k].
+    stream   torch stream (default: the current stream).
+    variant, wgs_per_row: optional explicit launch shape (tests, tuning).
+    Returns the int32 [rows, k] tensor (``out`` when given)."""
+    import torch
+
+    if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
+        raise TypeError("logits must be a GPU tensor")
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    squeeze = logits.dim() == 1
+    x = logits.unsqueeze(0) if squeeze else logits
+    if x.dim() != 2:
+        raise ValueError("logits must be [rows, n]")
+    rows, n = x.shape
+    if not x.is_contiguous():
+        raise ValueError("logits must be contiguous (row-major, row stride n)")
+    lp = None
+    if lengths is not None:
+        if lengths.dtype != torch.int32 or lengths.device != x.device or lengths.shape != (rows,):
+            raise ValueError("lengths must be an int32 [rows] tensor on the logits' device")
+        if not lengths.is_contiguous():
+            raise ValueError("lengths must be contiguous")
+        lp = lengths.data_ptr()
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=x.device)
+    elif out.dtype != torch.int32 or out.shape != (rows, k) or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous int32 [rows, k] tensor on the logits' device")
+    sh = _stream_handle(stream)
+    with torch.cuda.device(x.device):
+        if variant is None and wgs_per_row is None:
+            rc = topk_select(x.data_ptr(), rows, n, lp, k, out.data_ptr(), sh)
+        else:
+            if variant is None or wgs_per_row is None:
+                raise ValueError("give both variant and wgs_per_row")
+            rc = topk_select_ex(x.data_ptr(), rows, n, lp, k, out.data_ptr(), sh, variant, wgs_per_row)
+    _check(rc, "topk_select")
+    return out[0] if squeeze else out
+
+
+def plan(rows: int, n: int, k: int) -> dict:
+    """The launch shape the library picks for (rows, n, k) on the current device."""
+    p = _native.PlanT()
+    _check(_native.load().topk_select_plan(rows, n, k, ctypes.byref(p)), "topk_select_plan")
+    return {f: getattr(p, f) for f, _ in _native.PlanT._fields_}
+
+
+def num_variants() -> int:
+    return int(_native.load().topk_select_num_variants())
+
+
+def variant_info(v: int) -> dict:
+    p = _native.PlanT()
+    _check(_native.load().topk_select_variant_info(v, ctypes.byref(p)), "topk_select_variant_info")
+    return {f: getattr(p, f) for f, _ in _native.PlanT._fields_}
+
+
+def device_status(stream=None) -> int:
+    """Synchronise the stream and return (and clear) the device-side error flags."""
+    flags = ctypes.c_int32(0)
+    rc = _native.load().topk_select_device_status(_stream_handle(stream) or None, ctypes.byref(flags))
+    if rc not in (_native.SUCCESS, _native.ERROR_DEVICE_FLAG):
+        raise TopkSelectError(rc, "topk_select_device_status")
+    return int(flags.value)
+
+
+def release_workspace() -> None:
+    _check(_native.load().topk_select_release_workspace(), "topk_select_release_workspace")
+
+
+def version() -> int:
+    return int(_native.load().topk_select_version())

@@ -49,3 +49,37 @@ def check_row_invariants(x_row: np.ndarray, L: int, k: int, sel: np.ndarray) -> 
 def same_sets(a: np.ndarray, b: np.ndarray) -> bool:
     """Row-wise equality of two [rows, k] index arrays as sorted multisets."""
     return np.array_equal(np.sort(a, axis=-1), np.sort(b, axis=-1))
+
+
+def check_rows_vectorized(x: np.ndarray, lengths, k: int, sel: np.ndarray, block: int = 256) -> None:
+    """check_row_invariants for many rows at once (numpy, row blocks)."""
+    rows, n = x.shape
+    col = np.arange(n)
+    for r0 in range(0, rows, block):
+        r1 = min(rows, r0 + block)
+        xb = x[r0:r1]
+        sb = np.asarray(sel[r0:r1])
+        R = r1 - r0
+        L = np.full(R, n) if lengths is None else np.clip(np.asarray(lengths[r0:r1]).astype(np.int64), 0, n)
+        take = np.minimum(k, L)
+        assert np.array_equal((sb == -1).sum(1), k - take), "wrong number of -1 slots"
+        valid_sel = sb >= 0
+        assert np.array_equal(valid_sel.sum(1), take), "wrong number of indices"
+        assert np.all(np.where(valid_sel, sb, 0) < L[:, None]), "index past the valid length"
+        ss = np.sort(np.where(valid_sel, sb, -1), axis=1)
+        dup = (np.diff(ss, axis=1) == 0) & (ss[:, 1:] >= 0)
+        assert not dup.any(), "duplicate index"
+        chosen = np.zeros((R, n), dtype=bool)
+        rr = np.repeat(np.arange(R), k)
+        flat = sb.reshape(-1)
+        m = flat >= 0
+        chosen[rr[m], flat[m]] = True
+        valid = col[None, :] < L[:, None]
+        xf = xb.astype(np.float64)
+        lo = np.where(chosen, xf, np.inf).min(1)
+        hi = np.where(valid & ~chosen, xf, -np.inf).max(1)
+        assert np.all(lo >= hi), "an unselected value exceeds a selected one"
+        tie = valid & (xf == lo[:, None])
+        max_sel_tie = np.where(tie & chosen, col[None, :], -1).max(1)
+        min_uns_tie = np.where(tie & ~chosen, col[None, :], n).min(1)
+        assert np.all(max_sel_tie < min_uns_tie), "ties at the threshold not taken lowest index first"

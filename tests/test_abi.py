@@ -1,0 +1,104 @@
+"""The C-ABI library loads and exports what include/topk_select.h declares;
+host-side argument checks answer before any HIP call (CPU only)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topk_select.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_topk_fp32_amd import _native
+
+    if not os.path.exists(_native.LIB_PATH):
+        pytest.fail("libtopk_select.so is not built: run __graft_entry__.build() or "
+                    "python -m sparse_attention_topk_fp32_amd.build")
+    return _native.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(topk_select\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_exports():
+    from sparse_attention_topk_fp32_amd import _native
+
+    assert _declared_functions() == sorted(_native.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_error_strings(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    assert lib.topk_select_version() == 1
+    for code in range(6):
+        s = _native.error_string(code)
+        assert s and s != "unknown status"
+    assert _native.error_string(99) == "unknown status"
+
+
+def _call(lib, logits, rows, n, lengths, k, out):
+    return lib.topk_select(logits, rows, n, lengths, k, out, None)
+
+
+def test_argument_checks_answer_before_any_hip_call(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    INV = _native.ERROR_INVALID_VALUE
+    a = 0x10000000  # stand-in addresses: never dereferenced, validation is host-only
+    o = 0x20000000
+    assert _call(lib, a, 0, 16, None, 4, o) == _native.SUCCESS  # rows == 0: no-op
+    assert _call(lib, a, -1, 16, None, 4, o) == INV
+    assert _call(lib, a, 1, 0, None, 1, o) == INV
+    assert _call(lib, a, 1, 16, None, 0, o) == INV
+    assert _call(lib, a, 1, 16, None, 17, o) == INV
+    assert _call(lib, None, 1, 16, None, 4, o) == INV
+    assert _call(lib, a, 1, 16, None, 4, None) == INV
+    assert _call(lib, a + 2, 1, 16, None, 4, o) == INV  # logits not 4-byte aligned
+    assert _call(lib, a, 1, 16, None, 4, o + 1) == INV
+    assert _call(lib, a, 2, 16, None, 4, a + 64) == INV  # out overlaps logits
+    assert _call(lib, a, 2, 16, o, 4, o + 4) == INV  # out overlaps lengths
+
+
+def test_variant_table(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    nv = lib.topk_select_num_variants()
+    assert nv >= 2
+    seen_resident = set()
+    for v in range(nv):
+        p = _native.PlanT()
+        assert lib.topk_select_variant_info(v, ctypes.byref(p)) == 0
+        assert p.block % 64 == 0 and p.block >= 256
+        assert p.items % 4 == 0
+        seen_resident.add(p.resident)
+    assert seen_resident == {0, 1}
+    p = _native.PlanT()
+    assert lib.topk_select_variant_info(nv, ctypes.byref(p)) == _native.ERROR_INVALID_VALUE
+    assert lib.topk_select_plan(1, 16, 17, ctypes.byref(p)) == _native.ERROR_INVALID_VALUE
+
+
+def test_select_rejects_non_gpu_tensors():
+    import torch
+
+    import sparse_attention_topk_fp32_amd as tks
+
+    with pytest.raises(TypeError):
+        tks.select(torch.zeros(4, 8), 2)
+    with pytest.raises(TypeError):
+        tks.select(np.zeros((4, 8), np.float32), 2)
