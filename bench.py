@@ -58,15 +58,16 @@ def time_graph(torch, fn_list, steps: int, warmup: int, stream):
             for f in fn_list:
                 f()
     reps = max(1, (steps + len(fn_list) - 1) // len(fn_list))
-    for _ in range(max(1, warmup // len(fn_list))):
-        g.replay()
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e1.record(stream)
+    with torch.cuda.stream(stream):  # replay() launches on the current stream
+        for _ in range(max(1, warmup // len(fn_list))):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / (reps * len(fn_list)), reps * len(fn_list)
 

@@ -90,7 +90,8 @@ int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* len
  *   block         threads per workgroup of the variant (output only)
  *   items         logits per thread per tile of the variant (output only)
  *   resident      1 when each workgroup keeps its whole slice on chip across
- *                 passes, 0 when it re-reads its slice every pass (output only)
+ *                 rounds, 0 when it re-reads its slice every round (output only)
+ *   first_bits    width in bits of the first radix digit (8 or 12) (output only)
  */
 typedef struct {
     int32_t variant;
@@ -98,6 +99,7 @@ typedef struct {
     int32_t block;
     int32_t items;
     int32_t resident;
+    int32_t first_bits;
 } topk_select_plan_t;
 
 /* The launch shape topk_select would use for (rows, n, k) on the current

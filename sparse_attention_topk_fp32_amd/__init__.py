@@ -51,7 +51,7 @@ def topk_select(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], 
 def topk_select_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
                    stream: int, variant: int, wgs_per_row: int) -> int:
     """Raw C-ABI call with an explicit launch shape; returns the status code."""
-    p = _native.PlanT(variant, wgs_per_row, 0, 0, 0)
+    p = _native.PlanT(variant, wgs_per_row, 0, 0, 0, 0)
     return _native.load().topk_select_ex(logits_ptr or None, rows, n, lengths_ptr or None, k, out_ptr or None,
                                          stream or None, ctypes.byref(p))
 

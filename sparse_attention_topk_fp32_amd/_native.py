@@ -42,6 +42,7 @@ class PlanT(ctypes.Structure):
         ("block", ctypes.c_int32),
         ("items", ctypes.c_int32),
         ("resident", ctypes.c_int32),
+        ("first_bits", ctypes.c_int32),
     ]
 
 

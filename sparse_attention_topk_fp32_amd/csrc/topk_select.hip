@@ -57,10 +57,13 @@
 
 namespace tks {
 
-constexpr int kBins = 256;       // 8-bit digits
-constexpr int kCap = 4096;       // candidate buffer capacity (elements)
-constexpr int kSmall = 256;      // bucket size ranked directly by the finisher
-constexpr int kMaxPasses = 8;    // 4 key digits + up to 4 index digits
+constexpr int kCap = 4096;          // candidate buffer capacity (elements)
+constexpr int kSmall = 256;         // bucket size ranked directly by the finisher
+constexpr int kMaxPasses = 8;       // rounds after the first digit (8-bit digits)
+constexpr int kStageLds = 8192;     // staged (key, index) entries a one-WG row may keep in LDS
+constexpr int kFinCopies = 8;       // LDS histogram copies for the finisher's rounds
+constexpr int kMergeCopies = 8;     // global copies of a row's 256-bin histogram (WG w adds into copy w mod 8)
+constexpr int kLineWords = 32;      // one 128-byte line
 constexpr uint32_t kFlagTimeout = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
 // Bound on a cross-workgroup wait, in ticks of the 100 MHz constant clock
@@ -69,99 +72,78 @@ constexpr uint64_t kSpinLimitTicks = 200000000ull;
 
 // Per-row scratch for rows spread over several workgroups.  Every field is
 // zero between calls (the finishing WG of each row clears what it used).
+// All cross-workgroup traffic goes through device-scope atomic operations
+// (read-modify-writes, loads and stores), which are performed at the
+// device's coherence point; their order within a wave is enforced with
+// s_waitcnt vmcnt(0).  No L2 write-back or invalidate fence is needed.
 struct alignas(256) RowWorkspace {
-    uint32_t hist[kMaxPasses][kBins];
-    uint32_t arrive;      // barrier arrivals, G per round
-    uint32_t done;        // WGs finished with the row
-    uint32_t out_count;   // outputs reserved by WGs (elements above the bucket)
-    uint32_t cand_count;  // candidates appended
-    uint32_t pad[60];
-    uint64_t cand[kCap];  // (key << 32) | ~index of the bucket's elements
+    uint32_t hist0[4096];                            // first-digit counts (4096 bins, or 8 copies of 256)
+    uint32_t hist[kMaxPasses][kMergeCopies][256];    // later rounds (8-bit digits)
+    uint32_t arrive[kMergeCopies * kLineWords];      // barrier arrivals, one counter per line
+    uint32_t done;                                   // WGs finished with the row
+    uint32_t reserve;                                // staged entries reserved in the row's stage
+    uint32_t pad[62];
 };
 
 struct KParams {
     const float* logits;
     const int32_t* lengths;
     int32_t* out;
-    RowWorkspace* ws;
+    RowWorkspace* ws;       // per row, when G > 1
+    uint64_t* stage;        // per row, stage_cap entries: (key << 32) | ~index, or null
     uint32_t* status;
     int32_t rows, n, k;
     int32_t G;              // workgroups per row
     int32_t chunks_per_wg;  // 16-byte chunks in one WG's slice
-    int32_t idx_digits;     // 8-bit index digits that follow the 4 key digits
+    int32_t idx_bits;       // bits of the index that vary (multiple of 8, <= 32)
+    int32_t stage_cap;      // entries per row in `stage`
 };
 
 // ----------------------------------------------------------------- device helpers
 
-// Mapping step: float bits -> unsigned key, order-preserving for non-NaN
-// values, with -0.0 folded onto +0.0 so they tie.  Valid keys are >= 1; key 0
-// marks "no element" (out-of-range lanes).  Only the NaN pattern 0xFFFFFFFF
-// would map to 0 and is moved to 1 (NaN is outside the contract).
-__device__ __forceinline__ uint32_t key_of_bits(uint32_t u) {
-    u = (u == 0x80000000u) ? 0u : u;
-    const uint32_t flip = (uint32_t)((int32_t)u >> 31) | 0x80000000u;
-    const uint32_t key = u ^ flip;
-    return key == 0u ? 1u : key;
-}
-
-__device__ __forceinline__ int pass_shift(int pass, int idx_digits) {
-    return pass < 4 ? 56 - 8 * pass : 8 * (idx_digits - 1 - (pass - 4));
+// Mapping step: float -> unsigned key with key(a) < key(b) iff a < b for
+// non-NaN values.  Adding +0.0 turns -0.0 into +0.0 (IEEE round to nearest)
+// and leaves every other value, subnormals included, unchanged, so -0.0 and
+// +0.0 get the same key and tie.  Negative values have all bits flipped,
+// non-negative ones only the sign bit.  Key 0 marks "no element": only the
+// NaN pattern 0xFFFFFFFF also maps there (NaN is outside the contract).
+__device__ __forceinline__ uint32_t key_of(float x) {
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ uint32_t lane_id() {
     return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
+// A value every lane holds identically (read from LDS after a barrier):
+// make it scalar so the loop state and its branches stay in SGPRs.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ void raise_flag(uint32_t* status, uint32_t f) {
     __hip_atomic_fetch_or(status, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thresholding step, run by wave 0: find the bin b holding the element of
-// rank `need` (1-based, counted from the top) in a 256-bin histogram.
-// Writes b, the count of elements in bins above b, and the count in b.
-__device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* s_sel, uint32_t* status) {
-    const uint32_t lane = lane_id();
-    const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
-    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t incl = s;  // sum over this lane's bins and all higher lanes' bins
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(incl, o);
-        if (lane + o < 64) incl += t;
-    }
-    const uint32_t excl = incl - s;
-    const bool hit = excl < need && need <= incl;
-    const uint64_t any = __ballot(hit);
-    if (hit) {
-        uint32_t above = excl, b, hb;
-        if (above + h3 >= need) {
-            b = 4 * lane + 3; hb = h3;
-        } else {
-            above += h3;
-            if (above + h2 >= need) {
-                b = 4 * lane + 2; hb = h2;
-            } else {
-                above += h2;
-                if (above + h1 >= need) {
-                    b = 4 * lane + 1; hb = h1;
-                } else {
-                    above += h1; b = 4 * lane; hb = h0;
-                }
-            }
-        }
-        s_sel[0] = b; s_sel[1] = above; s_sel[2] = hb;
-    }
-    if (any == 0 && lane == 0) {  // fewer elements than `need`: cannot happen for valid input
-        s_sel[0] = 0; s_sel[1] = 0; s_sel[2] = 0;
-        raise_flag(status, kFlagCapacity);
-    }
+// Device-scope atomic accessors (relaxed): performed at the coherence point.
+template <typename T>
+__device__ __forceinline__ T ld_dev(T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T add_dev(T* p, T v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Bounded wait until *ctr >= target (device scope), by one thread.
 __device__ void spin_until(uint32_t* ctr, uint32_t target, uint32_t* status) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (ld_dev(ctr) < target) {
         __builtin_amdgcn_s_sleep(1);
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
             raise_flag(status, kFlagTimeout);
@@ -170,7 +152,18 @@ __device__ void spin_until(uint32_t* ctr, uint32_t target, uint32_t* status) {
     }
 }
 
-// ----------------------------------------------------------------- the kernel
+// Row barrier for the G WGs of a row: WG w counts on line w mod 8, and
+// threads 0..7 each wait for their line to reach its round's total.  The
+// caller has made its own preceding device-scope operations complete.
+__device__ void row_barrier(RowWorkspace* ws, int G, int w, int round, uint32_t* status) {
+    if (threadIdx.x == 0) add_dev(&ws->arrive[(w % kMergeCopies) * kLineWords], 1u);
+    const int t = threadIdx.x;
+    if (t < kMergeCopies && t < G) {
+        const uint32_t per_line = (uint32_t)((G - t + kMergeCopies - 1) / kMergeCopies);
+        spin_until(&ws->arrive[t * kLineWords], per_line * (uint32_t)(round + 1), status);
+    }
+    __syncthreads();
+}
 
 // Block-wide exclusive scan of two counters at once.  Every thread of the
 // block calls it; returns this thread's exclusive prefixes and the totals.
@@ -198,25 +191,172 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* s_
     }
     ea = pa + ia - a;
     eb = pb + ib - b;
+    ta = uniform(ta);
+    tb = uniform(tb);
     __syncthreads();  // s_w may be reused right after
 }
 
-template <int BLOCK, int ITEMS, bool RESIDENT>
+// Digit schedule over the 64-bit composite (key << 32) | ~index, by the
+// number r of top bits already resolved: the key's 32 bits in digits of up
+// to 8 bits (the first digit may be wider), then the index bits that vary.
+// ~index has its top (32 - idx_bits) bits set for every valid index, so they
+// are skipped.
+__device__ __forceinline__ int digit_width(int r) { return r < 32 ? min(8, 32 - r) : min(8, 64 - r); }
+
+struct Prefix {
+    uint32_t kpfx, kmask;  // resolved key bits
+    uint32_t ipfx, imask;  // resolved ~index bits
+    int r;                 // resolved bits of the composite
+    // Value selects only (no branch that picks a field to update), so the
+    // struct stays in registers.
+    __device__ void add_digit(uint32_t b, int width, int idx_bits) {
+        const int sh = 64 - r - width;
+        const bool in_key = sh >= 32;
+        const int s = in_key ? sh - 32 : sh;
+        const uint32_t bb = b << s, mm = ((1u << width) - 1u) << s;  // width <= 12
+        kpfx |= in_key ? bb : 0u;
+        kmask |= in_key ? mm : 0u;
+        ipfx |= in_key ? 0u : bb;
+        imask |= in_key ? 0u : mm;
+        r += width;
+        // past the key: the top (32 - idx_bits) bits of ~index are constant ones
+        const bool jump = r == 32;
+        const uint32_t ones = idx_bits < 32 ? ~((1u << idx_bits) - 1u) : 0u;
+        ipfx |= jump ? ones : 0u;
+        imask |= jump ? ones : 0u;
+        r = jump ? 64 - idx_bits : r;
+    }
+    __device__ uint64_t pfx64() const { return ((uint64_t)kpfx << 32) | ipfx; }
+    __device__ uint64_t mask64() const { return ((uint64_t)kmask << 32) | imask; }
+};
+
+// Thresholding step over an NB-bin histogram held as NC LDS copies (stride
+// NB + 1 words).  Finds the bin b holding the element of rank `need`
+// (1-based, from the top): the caller gets b, the count above b and the
+// count in b through s_sel.  Each owning thread sums the copies of its bins,
+// optionally merges them across the row's WGs (G > 1: add into a global
+// histogram, barrier, read back the sums), then one block scan over the
+// owners' sums, taken from the top bin down, locates b.
+template <int BLOCK, int NB, int NC>
+__device__ void select_bin(const uint32_t* h, uint32_t bin0_sub, uint32_t need, int G, RowWorkspace* ws,
+                           uint32_t* gm, int gcopies, int w, int round, uint32_t* s_sel, uint32_t* s_scan,
+                           uint32_t* status) {
+    constexpr int OWN = (NB + BLOCK - 1) / BLOCK;      // bins per owning thread
+    constexpr int OWNERS = (NB + OWN - 1) / OWN;       // the last group may be partial
+    const int t = threadIdx.x;
+    const bool owner = t < OWNERS;
+    const int g = OWNERS - 1 - t;  // thread 0 owns the top bins
+    uint32_t tot[OWN];
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) tot[i] = 0;
+    if (owner) {
+        // copy by copy, with a few LDS reads in flight at a time (the
+        // caller's resident keys are live here)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int i = 0; i < OWN; ++i) {
+                const int bin = g * OWN + i;
+                if (bin < NB) tot[i] += h[c * (NB + 1) + bin];
+            }
+            if (OWN * (c + 1) % 8 == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < OWN; ++i)
+            if (g * OWN + i == 0) tot[i] -= bin0_sub;
+    }
+    if (G > 1) {
+        if (owner) {
+            uint32_t* dst = gm + (gcopies > 1 ? (w % gcopies) * NB : 0);
+#pragma unroll
+            for (int i = 0; i < OWN; ++i)
+                if (tot[i]) add_dev(&dst[g * OWN + i], tot[i]);
+        }
+        wait_memory();
+        __syncthreads();
+        row_barrier(ws, G, w, round, status);
+        if (owner) {
+            const int nc = G < gcopies ? G : gcopies;
+#pragma unroll
+            for (int i = 0; i < OWN; ++i) {
+                const int bin = g * OWN + i;
+                uint32_t v = 0;
+                if (bin < NB)
+                    for (int c = 0; c < nc; ++c) v += ld_dev(&gm[c * NB + bin]);
+                tot[i] = v;
+            }
+        }
+    }
+    uint32_t gsum = 0;
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) gsum += tot[i];
+    if (t == 0) s_sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
+    uint32_t excl, unused, total, unused2;
+    block_scan2<BLOCK>(gsum, 0u, s_scan, excl, unused, total, unused2);
+    if (owner && excl < need && need <= excl + gsum) {
+        uint32_t above = excl;
+#pragma unroll
+        for (int i = OWN - 1; i >= 0; --i) {
+            if (above + tot[i] >= need) {
+                s_sel[0] = (uint32_t)(g * OWN + i);
+                s_sel[1] = above;
+                s_sel[2] = tot[i];
+                break;
+            }
+            above += tot[i];
+        }
+    }
+    __syncthreads();
+    if (uniform(s_sel[2]) == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
+        __syncthreads();
+        if (t == 0) {
+            s_sel[0] = 0; s_sel[1] = 0; s_sel[2] = 0;
+            raise_flag(status, kFlagCapacity);
+        }
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------- the kernel
+//
+// BLOCK threads per WG; ITEMS logits per thread per tile; FIRST_BITS = width
+// of the first digit (8: 256 bins in 32 LDS copies; 12: 4096 bins in 4
+// copies); RESIDENT: the slice is one tile kept in VGPRs across rounds;
+// MULTI: rows may be spread over several WGs (G > 1).  Variants without
+// MULTI carry none of the cross-workgroup code, which keeps their register
+// budget for the resident keys.
+
+template <int BLOCK, int ITEMS, int FIRST_BITS, bool RESIDENT, bool MULTI>
 __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
-    static_assert(BLOCK % 64 == 0 && BLOCK >= kBins, "one bin per thread in the merge");
+    static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "one bin per thread in the 256-bin rounds");
+    static_assert(FIRST_BITS == 8 || FIRST_BITS == 12, "first digit of 8 or 12 bits");
     constexpr int CHUNKS = ITEMS / 4;              // chunks per thread per tile
     constexpr int TILE_CHUNKS = BLOCK * CHUNKS;    // chunks per tile
+    constexpr int NB0 = 1 << FIRST_BITS;           // first-digit bins
+    constexpr int NC0 = FIRST_BITS == 8 ? 32 : 4;  // LDS copies of the first-digit histogram
+    constexpr int NC8 = 32;                        // LDS copies in the later 8-bit rounds
+    constexpr int STAGE = (RESIDENT && BLOCK * ITEMS < kStageLds) ? BLOCK * ITEMS : kStageLds;
+    constexpr int H0_WORDS = NC0 * (NB0 + 1);
+    constexpr int H8_WORDS = NC8 * 257;
 
-    __shared__ uint32_t s_hist[kBins];
+    // The rounds' histograms and the staged selection are never live at the
+    // same time, so they share LDS.
+    union BigLds {
+        uint32_t h0[H0_WORDS];
+        uint32_t h8[H8_WORDS];
+        uint64_t stage[STAGE];
+    };
+    __shared__ BigLds s_big;
     __shared__ uint64_t s_cand[kCap];
+    __shared__ uint32_t s_fin_hist[kFinCopies * 257];
     __shared__ uint64_t s_small[kSmall];
     __shared__ uint32_t s_scan[2 * (BLOCK / 64)];
     __shared__ uint32_t s_sel[3];   // threshold bin, count above it, count in it
-    __shared__ uint32_t s_bc[3];    // broadcast: global output base, candidate base, last-WG flag
+    __shared__ uint32_t s_bc[2];    // broadcast: stage base, last-WG flag
 
     const int tid = threadIdx.x;
-    const int G = P.G;
+    const int G = MULTI ? P.G : 1;
     const int row = blockIdx.x / G;
     const int w = blockIdx.x - row * G;
     const int n = P.n;
@@ -235,52 +375,71 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         return;
     }
 
-    RowWorkspace* ws = P.ws ? P.ws + row : nullptr;
+    RowWorkspace* ws = (MULTI && P.ws) ? P.ws + row : nullptr;
     const int off = (int)(((uintptr_t)p >> 2) & 3);  // elements before the first 16-byte boundary
     const int nchunks = (off + L + 3) >> 2;
     const int c_begin = w * P.chunks_per_wg;
     const int c_end = min(nchunks, c_begin + P.chunks_per_wg);
+    // chunks whose four elements are all valid
+    const int cf_lo = max(c_begin, off ? 1 : 0);
+    const int cf_hi = min(c_end, (L + off) >> 2);
+    // slots of the slice's chunks that hold no element (key 0): at most the
+    // three before element 0 and the three past L; the first-digit
+    // histogram counts them in bin 0 and subtracts them after
+    const int valid = c_end > c_begin ? max(0, min(L, 4 * c_end - off) - max(0, 4 * c_begin - off)) : 0;
+    const uint32_t n_empty = c_end > c_begin ? (uint32_t)(4 * (c_end - c_begin) - valid) : 0u;
 
     uint32_t keys[ITEMS];
+    const float* __restrict__ pa = p - off;  // 16-byte aligned
 
-    // Load one tile of the slice.  Chunk c of the row is the 16-byte aligned
-    // block holding elements [4c - off, 4c - off + 4).  A chunk with at least
-    // one valid element lies inside the allocation's page, so it is always
-    // read whole; lanes past the slice re-read chunk 0 (valid: L > k >= 1).
-    // All loads are issued before any is used; elements outside [0, L) get
-    // key 0 ("no element").
-    const float* __restrict__ pa = p - off;
+    // Load one tile: chunk c of the row is the aligned 16-byte block holding
+    // elements [4c - off, 4c - off + 4).  A chunk with at least one valid
+    // element lies in the page of that element, so it is read whole; lanes
+    // past the slice re-read chunk 0 (valid: L > k >= 1).  All loads are
+    // issued before any is used.
     auto load_tile = [&](int c_tile) {
-        float4 v[CHUNKS];
+        const char* const base = reinterpret_cast<const char*>(pa);  // uniform base, 32-bit offsets
 #pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {
+        for (int j = 0; j < CHUNKS; ++j) {  // raw bits straight into the key registers
             const int c = c_tile + j * BLOCK + tid;
-            v[j] = *reinterpret_cast<const float4*>(pa + 4 * (c < c_end ? c : 0));
+            const uint32_t byte_off = (uint32_t)(c < c_end ? c : 0) * 16u;
+            const uint4 v = *reinterpret_cast<const uint4*>(base + byte_off);
+            keys[4 * j + 0] = v.x;
+            keys[4 * j + 1] = v.y;
+            keys[4 * j + 2] = v.z;
+            keys[4 * j + 3] = v.w;
         }
 #pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {
+        for (int j = 0; j < CHUNKS; ++j) {  // then mapped in place
             const int c = c_tile + j * BLOCK + tid;
-            const int e0 = 4 * c - off;
-            const uint32_t u[4] = {__float_as_uint(v[j].x), __float_as_uint(v[j].y),
-                                   __float_as_uint(v[j].z), __float_as_uint(v[j].w)};
+            if (c >= cf_lo && c < cf_hi) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {  // bitwise tests: no branches
-                const bool ok = (c < c_end) & ((uint32_t)(e0 + e) < (uint32_t)L);
-                keys[4 * j + e] = ok ? key_of_bits(u[e]) : 0u;
+                for (int e = 0; e < 4; ++e) keys[4 * j + e] = key_of(__uint_as_float(keys[4 * j + e]));
+            } else {
+                const int e0 = 4 * c - off;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = (c < c_end) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                    keys[4 * j + e] = ok ? key_of(__uint_as_float(keys[4 * j + e])) : 0u;
+                }
             }
         }
     };
-    // f(key, index) for every element of one tile; index of element e of
-    // chunk j is ibase + 4 * BLOCK * j + e.
+    // f(key, index) for every element of one tile; element e of chunk j has
+    // index ibase + 4 * BLOCK * j + e.
     auto visit_tile = [&](int c_tile, auto&& f) {
-        const int ibase = 4 * (c_tile + tid) - off;
+        int ibase = 4 * (c_tile + tid) - off;
+        __asm__ volatile("" : "+v"(ibase));  // indices are recomputed per visit, never kept live
 #pragma unroll
         for (int j = 0; j < CHUNKS; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) f(keys[4 * j + e], ibase + 4 * BLOCK * j + e);
+            // keep each chunk's temporaries local: without this the scheduler
+            // hoists every element's address ahead of the LDS operations
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Visit every element of the slice (uniform trip count across the WG).
+    // Visit every slot of the slice (uniform trip count across the WG).
     auto visit = [&](auto&& f) {
         if constexpr (RESIDENT) {
             visit_tile(c_begin, f);
@@ -292,15 +451,35 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         }
     };
 
+    // f(key) for every slot of the chunks in [c_begin, c_end): chunks past
+    // the slice are skipped (one test per chunk, not per element)
+    auto visit_chunks = [&](auto&& f) {
+        auto tile = [&](int c_tile) {
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                if (c_tile + j * BLOCK + tid < c_end) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f(keys[4 * j + e]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if constexpr (RESIDENT) {
+            tile(c_begin);
+        } else {
+            for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
+                load_tile(ct);
+                tile(ct);
+            }
+        }
+    };
+
     if constexpr (RESIDENT) load_tile(c_begin);
 
     // ---------------- screening rounds over the whole row
-    // Resolved prefix of the composite (key, ~index): kpfx/kmask over the key,
-    // ipfx/imask over ~index (only non-zero after all four key digits).
-    const int npasses = 4 + P.idx_digits;
-    uint32_t kpfx = 0, kmask = 0, ipfx = 0, imask = 0;
+    Prefix pf{0u, 0u, 0u, 0u, 0};
     uint32_t need = (uint32_t)k;
-    int pass = 0;
+    int round = 0;
     bool all_sel = false;
     for (;;) {
         if constexpr (RESIDENT) {
@@ -309,225 +488,220 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
         }
-        for (int i = tid; i < kBins; i += BLOCK) s_hist[i] = 0;
-        __syncthreads();
-        if (pass < 4) {
-            const int sh = 24 - 8 * pass;
-            visit([&](uint32_t key, int) {
-                if ((key != 0u) & ((key & kmask) == kpfx)) atomicAdd(&s_hist[(key >> sh) & 0xFFu], 1u);
-            });
+        int width;
+        if (pf.r == 0) {
+            // first digit: every slot adds into bin (key >> (32 - FIRST_BITS));
+            // empty slots (key 0) land in bin 0 and are subtracted after
+            width = FIRST_BITS;
+            for (int i = tid; i < H0_WORDS; i += BLOCK) s_big.h0[i] = 0u;
+            __syncthreads();
+            uint32_t* const hc = s_big.h0 + (tid % NC0) * (NB0 + 1);
+            visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> (32 - FIRST_BITS)], 1u); });
+            __syncthreads();
+            select_bin<BLOCK, NB0, NC0>(s_big.h0, n_empty, need, G, ws, ws ? ws->hist0 : nullptr,
+                                        FIRST_BITS == 8 ? kMergeCopies : 1, w, round, s_sel, s_scan, P.status);
         } else {
-            const int sh = 8 * (P.idx_digits - 1 - (pass - 4));
-            visit([&](uint32_t key, int idx) {
-                const uint32_t ni = ~(uint32_t)idx;
-                if ((key != 0u) & (key == kpfx) & ((ni & imask) == ipfx)) atomicAdd(&s_hist[(ni >> sh) & 0xFFu], 1u);
-            });
-        }
-        __syncthreads();
-        if (G > 1) {
-            // merge into the row's global histogram, then wait for all G WGs
-            if (tid < kBins) {
-                const uint32_t v = s_hist[tid];
-                if (v) __hip_atomic_fetch_add(&ws->hist[pass][tid], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            width = digit_width(pf.r);
+            const int sh = 64 - pf.r - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int i = tid; i < H8_WORDS; i += BLOCK) s_big.h8[i] = 0u;
+            __syncthreads();
+            uint32_t* const hc = s_big.h8 + (tid % NC8) * 257;
+            if (sh >= 32) {
+                const int ks = sh - 32;
+                const uint32_t km = pf.kmask, kp = pf.kpfx;
+                visit([&](uint32_t key, int) {
+                    if ((key != 0u) & ((key & km) == kp)) atomicAdd(&hc[(key >> ks) & dmask], 1u);
+                });
+            } else {
+                const uint32_t kp = pf.kpfx, im = pf.imask, ip = pf.ipfx;
+                visit([&](uint32_t key, int idx) {
+                    const uint32_t ni = ~(uint32_t)idx;
+                    if ((key != 0u) & (key == kp) & ((ni & im) == ip)) atomicAdd(&hc[(ni >> sh) & dmask], 1u);
+                });
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             __syncthreads();
-            if (tid == 0) {
-                __hip_atomic_fetch_add(&ws->arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                spin_until(&ws->arrive, (uint32_t)(pass + 1) * (uint32_t)G, P.status);
-            }
-            __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (tid < kBins)
-                s_hist[tid] = __hip_atomic_load(&ws->hist[pass][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
+            select_bin<BLOCK, 256, NC8>(s_big.h8, 0u, need, G, ws, ws ? &ws->hist[round - 1][0][0] : nullptr,
+                                        kMergeCopies, w, round, s_sel, s_scan, P.status);
         }
-        if (tid < 64) select_bin(s_hist, need, s_sel, P.status);
+        const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
         __syncthreads();
-        const uint32_t b = s_sel[0], above = s_sel[1], hb = s_sel[2];
         need -= above;
-        if (pass < 4) {
-            kpfx |= b << (24 - 8 * pass);
-            kmask |= 0xFFu << (24 - 8 * pass);
-        } else {
-            const int sh = 8 * (P.idx_digits - 1 - (pass - 4));
-            ipfx |= b << sh;
-            imask |= 0xFFu << sh;
-        }
-        ++pass;
+        pf.add_digit(b, width, P.idx_bits);
+        ++round;
         if (hb == need) { all_sel = true; break; }
-        if (hb <= (uint32_t)kCap || pass >= npasses) break;
+        if (hb <= (uint32_t)kCap || pf.r >= 64 || round > kMaxPasses) break;
     }
 
     // ---------------- collection over the row
-    // Composite prefix above the bucket -> output now ("win"); in the bucket
-    // -> candidate for the on-chip finish, unless the whole bucket is taken.
-    auto classify = [&](uint32_t key, int idx, bool& win, bool& cand) {
-        const uint32_t pk = key & kmask;
-        const uint32_t pi = ~(uint32_t)idx & imask;
-        const bool eq = (pk == kpfx) & (pi == ipfx);
-        const bool gt = (pk > kpfx) | ((pk == kpfx) & (pi > ipfx));
-        win = (key != 0u) & (gt | (all_sel & eq));
-        cand = (key != 0u) & (!all_sel) & eq;
+    // Selected = composite prefix at or above the threshold prefix: every
+    // element above the bucket plus the bucket itself.  They are staged as
+    // (key << 32) | ~index; the finisher splits them.
+    const bool key_only = pf.imask == 0u;
+    const uint32_t lo = pf.kpfx > 1u ? pf.kpfx : 1u;
+    auto selected = [&](uint32_t key, int idx) -> bool {
+        if (key_only) return key >= lo;
+        return (key != 0u) & ((key > pf.kpfx) | ((key == pf.kpfx) & ((~(uint32_t)idx & pf.imask) >= pf.ipfx)));
     };
-    // Resident slices record the classification as two per-thread bit masks
-    // (bit 4j+e = element e of chunk j), so the write pass below touches only
-    // selected elements; streaming slices classify again tile by tile.
-    uint32_t nw = 0, nc = 0;
-    uint64_t wmask = 0, cmask = 0;
+    uint32_t nsel = 0;
     if constexpr (RESIDENT) {
-        static_assert(ITEMS <= 64, "one 64-bit mask per thread");
-        visit_tile(c_begin, [&](uint32_t key, int idx) {
-            bool win, cand;
-            classify(key, idx, win, cand);
-            wmask = (wmask >> 1) | ((uint64_t)win << 63);
-            cmask = (cmask >> 1) | ((uint64_t)cand << 63);
-        });
-        wmask >>= 64 - ITEMS;
-        cmask >>= 64 - ITEMS;
-        nw = (uint32_t)__popcll(wmask);
-        nc = (uint32_t)__popcll(cmask);
-    } else {
-        visit([&](uint32_t key, int idx) {
-            bool win, cand;
-            classify(key, idx, win, cand);
-            nw += win;
-            nc += cand;
-        });
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
     }
-    uint32_t ow, oc, tw, tc;
-    block_scan2<BLOCK>(nw, nc, s_scan, ow, oc, tw, tc);
+    if (key_only) visit([&](uint32_t key, int) { nsel += key >= lo; });
+    else visit([&](uint32_t key, int idx) { nsel += selected(key, idx); });
+    uint32_t off_sel, unused, tot_sel, unused2;
+    block_scan2<BLOCK>(nsel, 0u, s_scan, off_sel, unused, tot_sel, unused2);
+    const bool in_lds = (G == 1) && tot_sel <= (uint32_t)STAGE;
+    uint64_t* const gstage = P.stage ? P.stage + (size_t)row * (size_t)P.stage_cap : nullptr;
+    uint32_t cap = in_lds ? (uint32_t)STAGE : (uint32_t)P.stage_cap;
+    if (!in_lds && !gstage) cap = 0;
     if (G > 1) {
-        if (tid == 0) {
-            s_bc[0] = tw ? __hip_atomic_fetch_add(&ws->out_count, tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-            s_bc[1] = tc ? __hip_atomic_fetch_add(&ws->cand_count, tc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-        }
+        if (tid == 0) s_bc[0] = tot_sel ? add_dev(&ws->reserve, tot_sel) : 0u;
         __syncthreads();
-        ow += s_bc[0];
-        oc += s_bc[1];
+        off_sel += uniform(s_bc[0]);
     }
-    const uint32_t nwin_total = (uint32_t)k - (all_sel ? 0u : need);
-    uint64_t* cand_dst = G > 1 ? ws->cand : s_cand;
-    auto emit_win = [&](int idx) {
-        if (ow < nwin_total) out[ow] = idx;
-        else raise_flag(P.status, kFlagCapacity);
-        ++ow;
-    };
-    auto emit_cand = [&](uint32_t key, int idx) {
-        if (oc < (uint32_t)kCap) cand_dst[oc] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)idx);
-        else raise_flag(P.status, kFlagCapacity);
-        ++oc;
-    };
-    // per-thread loops: no barrier or wave operation inside
-    if constexpr (RESIDENT) {
-        const int ibase = 4 * (c_begin + tid) - off;
-        while (wmask) {
-            const int i = __builtin_ctzll(wmask);
-            wmask &= wmask - 1;
-            emit_win(ibase + 4 * BLOCK * (i >> 2) + (i & 3));
+    auto put = [&](uint32_t key, int idx) {
+        // a copy, so the resident key is not pinned to the high half of a
+        // register pair (which would cost one extra VGPR per key)
+        uint32_t kc = key;
+        __asm__ volatile("" : "+v"(kc));
+        const uint64_t ck = ((uint64_t)kc << 32) | (uint64_t)(~(uint32_t)idx);
+        if (off_sel < cap) {
+            if (in_lds) s_big.stage[off_sel] = ck;
+            else st_dev(&gstage[off_sel], ck);  // device scope: may be read by another WG
+        } else {
+            raise_flag(P.status, kFlagCapacity);
         }
-        while (cmask) {
-            const int i = __builtin_ctzll(cmask);
-            cmask &= cmask - 1;
-            const int idx = ibase + 4 * BLOCK * (i >> 2) + (i & 3);
-            emit_cand(key_of_bits(__float_as_uint(p[idx])), idx);  // re-read: candidates are few
-        }
-    } else if (nw | nc) {
-        visit([&](uint32_t key, int idx) {
-            bool win, cand;
-            classify(key, idx, win, cand);
-            if (win) emit_win(idx);
-            if (cand) emit_cand(key, idx);
-        });
+        ++off_sel;
+    };
+    if constexpr (RESIDENT) {  // no per-element result of the count pass stays live
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
     }
-    __syncthreads();
+    if (nsel) {  // per-thread loops: no barrier or wave operation inside
+        if (key_only) {
+            visit([&](uint32_t key, int idx) {
+                if (key >= lo) put(key, idx);
+            });
+        } else {
+            visit([&](uint32_t key, int idx) {
+                if (selected(key, idx)) put(key, idx);
+            });
+        }
+    }
 
-    uint32_t m = 0;
+    uint32_t m_sel = tot_sel;  // staged entries of the row
     if (G > 1) {
         // the last WG of the row to get here finishes it and clears the workspace
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        wait_memory();
         __syncthreads();
-        if (tid == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&ws->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            s_bc[2] = (old == (uint32_t)G - 1u) ? 1u : 0u;
-        }
+        if (tid == 0) s_bc[1] = (add_dev(&ws->done, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
         __syncthreads();
-        if (s_bc[2] == 0u) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (!all_sel) {
-            m = __hip_atomic_load(&ws->cand_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            m = m > (uint32_t)kCap ? (uint32_t)kCap : m;
-            for (uint32_t i = tid; i < m; i += BLOCK)
-                s_cand[i] = __hip_atomic_load(&ws->cand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (uniform(s_bc[1]) == 0u) return;
+        m_sel = uniform(ld_dev(&ws->reserve));
     } else {
-        m = tc > (uint32_t)kCap ? (uint32_t)kCap : tc;
+        __syncthreads();
     }
-    __syncthreads();
+    if (m_sel > cap) m_sel = cap;
 
-    // ---------------- on-chip finish over the candidate buffer
-    if (!all_sel) {
-        uint64_t pfx = ((uint64_t)kpfx << 32) | ipfx;
-        uint64_t pmask = ((uint64_t)kmask << 32) | imask;
-        int32_t* __restrict__ fout = out + nwin_total;  // `need` slots remain
-        const uint32_t need0 = need;
-        bool fin_all = false;
-        uint32_t mb = m;
-        while (mb > (uint32_t)kSmall && pass < npasses) {
-            const int sh = pass_shift(pass, P.idx_digits);
-            for (int i = tid; i < kBins; i += BLOCK) s_hist[i] = 0;
-            __syncthreads();
+    // ---------------- on-chip finish
+    // Split the staged entries: above the threshold prefix (or the whole
+    // bucket when it is taken entirely) -> output; in the bucket -> LDS
+    // candidates.  Positions come from a block scan, so the order is
+    // reproducible for a given staging order.
+    const uint64_t pfx0 = pf.pfx64(), pmask0 = pf.mask64();
+    const uint32_t nwin_total = (uint32_t)k - (all_sel ? 0u : need);
+    auto staged = [&](uint32_t i) -> uint64_t { return in_lds ? s_big.stage[i] : ld_dev(&gstage[i]); };
+    {
+        uint32_t cw = 0, cb = 0;
+        for (uint32_t i = tid; i < m_sel; i += BLOCK) {
+            const uint64_t pm = staged(i) & pmask0;
+            cw += (pm > pfx0) | (all_sel & (pm == pfx0));
+            cb += (!all_sel) & (pm == pfx0);
+        }
+        uint32_t ow, ob, tw, tb;
+        block_scan2<BLOCK>(cw, cb, s_scan, ow, ob, tw, tb);
+        if (tw != nwin_total || tb > (uint32_t)kCap) raise_flag(P.status, kFlagCapacity);
+        for (uint32_t i = tid; i < m_sel; i += BLOCK) {
+            const uint64_t ck = staged(i);
+            const uint64_t pm = ck & pmask0;
+            if ((pm > pfx0) | (all_sel & (pm == pfx0))) {
+                if (ow < nwin_total) out[ow] = (int32_t)~(uint32_t)ck;
+                ++ow;
+            } else if ((!all_sel) & (pm == pfx0)) {
+                if (ob < (uint32_t)kCap) s_cand[ob] = ck;
+                ++ob;
+            }
+        }
+        __syncthreads();
+        if (!all_sel) {
+            uint32_t m = tb > (uint32_t)kCap ? (uint32_t)kCap : tb;
+            int32_t* __restrict__ fout = out + nwin_total;  // `need` slots remain
+            const uint32_t need0 = need;
+            uint64_t pfx = pfx0, pmask = pmask0;
+            bool fin_all = false;
+            uint32_t mb = m;
+            int fround = 0;
+            while (mb > (uint32_t)kSmall && pf.r < 64) {
+                const int width = digit_width(pf.r);
+                const int sh = 64 - pf.r - width;
+                const uint32_t dmask = (1u << width) - 1u;
+                for (int i = tid; i < kFinCopies * 257; i += BLOCK) s_fin_hist[i] = 0u;
+                __syncthreads();
+                uint32_t* const fc = s_fin_hist + (tid % kFinCopies) * 257;
+                for (uint32_t i = tid; i < m; i += BLOCK) {
+                    const uint64_t ck = s_cand[i];
+                    if ((ck & pmask) == pfx) atomicAdd(&fc[(uint32_t)(ck >> sh) & dmask], 1u);
+                }
+                __syncthreads();
+                select_bin<BLOCK, 256, kFinCopies>(s_fin_hist, 0u, need, 1, nullptr, nullptr, 1, 0, fround,
+                                                   s_sel, s_scan, P.status);
+                const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
+                __syncthreads();
+                need -= above;
+                pf.add_digit(b, width, P.idx_bits);
+                pfx = pf.pfx64();
+                pmask = pf.mask64();
+                ++fround;
+                mb = hb;
+                if (hb == need) { fin_all = true; break; }
+            }
+            // winners among the candidates, and the small bucket to rank exactly
+            uint32_t fw = 0, fb = 0;
+            for (uint32_t i = tid; i < m; i += BLOCK) {
+                const uint64_t pm = s_cand[i] & pmask;
+                fw += (pm > pfx) | (fin_all & (pm == pfx));
+                fb += (!fin_all) & (pm == pfx);
+            }
+            uint32_t ofw, ofb, tfw, tfb;
+            block_scan2<BLOCK>(fw, fb, s_scan, ofw, ofb, tfw, tfb);
             for (uint32_t i = tid; i < m; i += BLOCK) {
                 const uint64_t ck = s_cand[i];
-                if ((ck & pmask) == pfx) atomicAdd(&s_hist[(uint32_t)(ck >> sh) & 0xFFu], 1u);
-            }
-            __syncthreads();
-            if (tid < 64) select_bin(s_hist, need, s_sel, P.status);
-            __syncthreads();
-            const uint32_t b = s_sel[0], above = s_sel[1], hb = s_sel[2];
-            __syncthreads();
-            need -= above;
-            pfx |= (uint64_t)b << sh;
-            pmask |= (uint64_t)0xFFu << sh;
-            ++pass;
-            mb = hb;
-            if (hb == need) { fin_all = true; break; }
-        }
-        // winners among the candidates, and the small bucket to rank exactly;
-        // positions come from a block scan, so the order is reproducible
-        uint32_t fw = 0, fb = 0;
-        for (uint32_t i = tid; i < m; i += BLOCK) {
-            const uint64_t pm = s_cand[i] & pmask;
-            fw += (pm > pfx) | (fin_all & (pm == pfx));
-            fb += (!fin_all) & (pm == pfx);
-        }
-        uint32_t ofw, ofb, tfw, tfb;
-        block_scan2<BLOCK>(fw, fb, s_scan, ofw, ofb, tfw, tfb);
-        for (uint32_t i = tid; i < m; i += BLOCK) {
-            const uint64_t ck = s_cand[i];
-            const uint64_t pm = ck & pmask;
-            if ((pm > pfx) | (fin_all & (pm == pfx))) {
-                if (ofw < need0) fout[ofw] = (int32_t)~(uint32_t)ck;
-                else raise_flag(P.status, kFlagCapacity);
-                ++ofw;
-            } else if ((!fin_all) & (pm == pfx)) {
-                if (ofb < (uint32_t)kSmall) s_small[ofb] = ck;
-                else raise_flag(P.status, kFlagCapacity);
-                ++ofb;
-            }
-        }
-        __syncthreads();
-        if (!fin_all) {
-            const uint32_t ms = tfb > (uint32_t)kSmall ? (uint32_t)kSmall : tfb;
-            const uint32_t base = tfw;
-            for (uint32_t i = tid; i < ms; i += BLOCK) {
-                const uint64_t c = s_small[i];
-                uint32_t rank = 0;
-                for (uint32_t j = 0; j < ms; ++j) rank += s_small[j] > c;
-                if (rank < need) {
-                    const uint32_t pos = base + rank;
-                    if (pos < need0) fout[pos] = (int32_t)~(uint32_t)c;
+                const uint64_t pm = ck & pmask;
+                if ((pm > pfx) | (fin_all & (pm == pfx))) {
+                    if (ofw < need0) fout[ofw] = (int32_t)~(uint32_t)ck;
                     else raise_flag(P.status, kFlagCapacity);
+                    ++ofw;
+                } else if ((!fin_all) & (pm == pfx)) {
+                    if (ofb < (uint32_t)kSmall) s_small[ofb] = ck;
+                    else raise_flag(P.status, kFlagCapacity);
+                    ++ofb;
+                }
+            }
+            __syncthreads();
+            if (!fin_all) {
+                const uint32_t ms = tfb > (uint32_t)kSmall ? (uint32_t)kSmall : tfb;
+                const uint32_t base = tfw;
+                for (uint32_t i = tid; i < ms; i += BLOCK) {
+                    const uint64_t c = s_small[i];
+                    uint32_t rank = 0;
+                    for (uint32_t j = 0; j < ms; ++j) rank += s_small[j] > c;
+                    if (rank < need) {
+                        const uint32_t pos = base + rank;
+                        if (pos < need0) fout[pos] = (int32_t)~(uint32_t)c;
+                        else raise_flag(P.status, kFlagCapacity);
+                    }
                 }
             }
         }
@@ -535,12 +709,16 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 
     if (G > 1) {
         // leave the row's workspace zeroed for the next call
-        for (int i = tid; i < pass * kBins; i += BLOCK) ws->hist[i / kBins][i % kBins] = 0u;
+        for (int i = tid; i < 4096; i += BLOCK) st_dev(&ws->hist0[i], 0u);
+        const int ncopy = G < kMergeCopies ? G : kMergeCopies;
+        for (int i = tid; i < (round - 1) * kMergeCopies * 256; i += BLOCK) {
+            const int c = (i / 256) % kMergeCopies;
+            if (c < ncopy) st_dev(&ws->hist[i / (kMergeCopies * 256)][c][i % 256], 0u);
+        }
+        if (tid < kMergeCopies) st_dev(&ws->arrive[tid * kLineWords], 0u);
         if (tid == 0) {
-            ws->arrive = 0u;
-            ws->done = 0u;
-            ws->out_count = 0u;
-            ws->cand_count = 0u;
+            st_dev(&ws->done, 0u);
+            st_dev(&ws->reserve, 0u);
         }
     }
 }
@@ -550,45 +728,60 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
 using OccFn = int (*)(int*, int);
 
-template <int B, int I, bool R>
+template <int B, int I, int F, bool R, bool M>
 void launch_variant(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    hipLaunchKernelGGL((topk_select_kernel<B, I, R>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((topk_select_kernel<B, I, F, R, M>), grid, block, 0, s, p);
 }
 
-template <int B, int I, bool R>
+template <int B, int I, int F, bool R, bool M>
 int occupancy_variant(int* nb, int block) {
-    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, R>, block, 0);
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, F, R, M>, block, 0);
 }
 
 struct Variant {
-    int block, items, resident;
+    int block, items, first_bits, resident, multi;
+    int stage_lds;  // staged entries a one-WG row keeps in LDS
     LaunchFn launch;
     OccFn occupancy;
 };
 
-#define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
+constexpr int stage_lds_of(int b, int i, bool r) { return (r && b * i < kStageLds) ? b * i : kStageLds; }
+
+#define TKS_VARIANT(B, I, F, R, M)                                                               \
+    {B, I, F, R ? 1 : 0, M ? 1 : 0, stage_lds_of(B, I, R), &launch_variant<B, I, F, R, M>, \
+     &occupancy_variant<B, I, F, R, M>}
 const Variant kVariants[] = {
-    TKS_VARIANT(256, 4, true),    // 0: 1024 logits per WG
-    TKS_VARIANT(256, 8, true),    // 1: 2048
-    TKS_VARIANT(256, 16, true),   // 2: 4096
-    TKS_VARIANT(512, 32, true),   // 3: 16384
-    TKS_VARIANT(512, 64, true),   // 4: 32768
-    TKS_VARIANT(1024, 64, true),  // 5: 65536
-    TKS_VARIANT(256, 16, false),  // 6: streaming, 4096 per tile
-    TKS_VARIANT(1024, 16, false), // 7: streaming, 16384 per tile
+    TKS_VARIANT(256, 4, 8, true, true),      // 0: 1024 logits per WG, 8-bit first digit (many WGs per row)
+    TKS_VARIANT(256, 8, 8, true, true),      // 1: 2048
+    TKS_VARIANT(256, 16, 8, true, true),     // 2: 4096
+    TKS_VARIANT(512, 32, 8, true, true),     // 3: 16384
+    TKS_VARIANT(512, 64, 8, true, true),     // 4: 32768
+    TKS_VARIANT(256, 16, 12, true, false),   // 5: 4096, 12-bit first digit, one WG per row
+    TKS_VARIANT(512, 32, 12, true, false),   // 6: 16384
+    TKS_VARIANT(512, 64, 12, true, true),    // 7: 32768 (also several WGs per row)
+    TKS_VARIANT(1024, 32, 12, true, false),  // 8: 32768
+    TKS_VARIANT(1024, 16, 12, false, true),  // 9: streaming, 16384 per tile
+    TKS_VARIANT(256, 16, 8, false, true),    // 10: streaming, 4096 per tile
 };
 #undef TKS_VARIANT
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
-constexpr int kFirstStreaming = 6;
 
 struct DeviceInfo {
     int cus = 0;
     int capacity[kNumVariants] = {};  // co-resident WGs per variant on the whole device
 };
 
+// Scratch of one (device, stream).  `base` holds the status word and the
+// per-row workspaces at fixed offsets (row r always at the same address,
+// whatever the row count of a call); it is zeroed when allocated and left
+// zeroed by every kernel.  `stage` holds staged entries; it needs no
+// initial value and lives in its own allocation so that it never overlaps
+// a row workspace of a later call.
 struct Workspace {
     void* base = nullptr;
     size_t bytes = 0;
+    void* stage = nullptr;
+    size_t stage_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -624,11 +817,11 @@ int64_t max_row_chunks(const float* logits, int32_t n) {
     return (3 + (int64_t)n + 3) / 4;
 }
 
-int idx_digits_for(int32_t n) {
+int idx_bits_for(int32_t n) {
     uint32_t top = (uint32_t)(n - 1);
     int bits = 0;
     while (top) { ++bits; top >>= 1; }
-    return (bits + 7) / 8;
+    return (bits + 7) / 8 * 8;
 }
 
 struct Launch {
@@ -649,6 +842,7 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
         cpw = tile_chunks;
     }
     if (cpw < 1) cpw = 1;
+    if (G > 1 && !var.multi) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (G > 1 && rows * (int64_t)G > (int64_t)d.capacity[v]) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows * (int64_t)G > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
     L->variant = v;
@@ -657,27 +851,39 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
     return TOPK_SELECT_SUCCESS;
 }
 
-// Default shape: the smallest resident tile whose grid stays within one WG
-// per CU (batch-1 rows spread over many WGs, long batches one WG per row);
-// otherwise the largest resident tile that fits; otherwise streaming.
+// Default shape.  Many rows: one WG per row with the 12-bit first digit
+// when the row fits one resident tile.  Few rows: spread each row over
+// enough 8-bit-digit WGs to cover about one WG per CU.  Otherwise the
+// largest resident tile that fits, else streaming.
 int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
     const int target = d.cus;
-    int best = -1, bestG = 0;
-    for (int v = 0; v < kFirstStreaming; ++v) {
-        const int64_t tile_chunks = (int64_t)kVariants[v].block * (kVariants[v].items / 4);
-        const int64_t G = (maxc + tile_chunks - 1) / tile_chunks;
-        const bool fits = G == 1 || rows * G <= (int64_t)d.capacity[v];
-        if (!fits) continue;
-        if (rows * G <= target) return check_shape(d, rows, maxc, v, (int)G, L);
-        best = v;
-        bestG = (int)G;
+    auto tile_chunks = [](int v) { return (int64_t)kVariants[v].block * (kVariants[v].items / 4); };
+    if (rows >= target / 2) {
+        const int one_wg[] = {5, 6, 7, 8};
+        for (int v : one_wg)
+            if (maxc <= tile_chunks(v)) return check_shape(d, rows, maxc, v, 1, L);
+        const int split[] = {7};
+        for (int v : split) {
+            const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
+            if (rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
+        }
+    } else {
+        int best = -1, bestG = 0;
+        const int few[] = {0, 1, 2, 3, 4};
+        for (int v : few) {
+            const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
+            const bool fits = G == 1 || rows * G <= (int64_t)d.capacity[v];
+            if (!fits) continue;
+            if (rows * G <= target) return check_shape(d, rows, maxc, v, (int)G, L);
+            best = v;
+            bestG = (int)G;
+        }
+        if (best >= 0) return check_shape(d, rows, maxc, best, bestG, L);
     }
-    if (best >= 0) return check_shape(d, rows, maxc, best, bestG, L);
     // streaming: as many WGs per row as can be co-resident, at least one
-    const int v = (maxc >= 16384) ? 7 : 6;
+    const int v = (maxc >= 16384) ? 9 : 10;
     int64_t G = d.capacity[v] / (rows > 0 ? rows : 1);
-    const int64_t tile_chunks = (int64_t)kVariants[v].block * (kVariants[v].items / 4);
-    const int64_t gmax = (maxc + tile_chunks - 1) / tile_chunks;
+    const int64_t gmax = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
     if (G > gmax) G = gmax;
     if (G < 1) G = 1;
     return check_shape(d, rows, maxc, v, (int)G, L);
@@ -699,27 +905,33 @@ int validate(const float* logits, int32_t rows, int32_t n, const int32_t* length
     return TOPK_SELECT_SUCCESS;
 }
 
-int get_workspace(int dev, hipStream_t stream, size_t need, Workspace** out) {
-    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
-    if (w.bytes < need) {
-        if (w.base) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            (void)hipFree(w.base);
-            w.base = nullptr;
-            w.bytes = 0;
-        }
-        void* p = nullptr;
-        if (hipMalloc(&p, need) != hipSuccess) {
-            (void)hipGetLastError();
-            return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
-        }
-        if (hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
-            (void)hipFree(p);
-            return TOPK_SELECT_ERROR_LAUNCH;
-        }
-        w.base = p;
-        w.bytes = need;
+int grow(void** ptr, size_t* have, size_t need, bool zero, hipStream_t stream) {
+    if (*have >= need) return TOPK_SELECT_SUCCESS;
+    if (*ptr) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        (void)hipFree(*ptr);
+        *ptr = nullptr;
+        *have = 0;
     }
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess) {
+        (void)hipGetLastError();
+        return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
+    }
+    if (zero && hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
+        (void)hipFree(p);
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+    *ptr = p;
+    *have = need;
+    return TOPK_SELECT_SUCCESS;
+}
+
+int get_workspace(int dev, hipStream_t stream, size_t need, size_t stage_need, Workspace** out) {
+    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+    int rc = grow(&w.base, &w.bytes, need, true, stream);
+    if (rc == TOPK_SELECT_SUCCESS && stage_need) rc = grow(&w.stage, &w.stage_bytes, stage_need, false, stream);
+    if (rc != TOPK_SELECT_SUCCESS) return rc;
     *out = &w;
     return TOPK_SELECT_SUCCESS;
 }
@@ -739,23 +951,31 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     rc = forced ? check_shape(*d, rows, maxc, forced->variant, forced->wgs_per_row, &L)
                 : choose_shape(*d, rows, maxc, &L);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
-    const size_t ws_bytes = kStatusBytes + (L.G > 1 ? (size_t)rows * sizeof(RowWorkspace) : 0);
+    const Variant& var0 = kVariants[L.variant];
+    const bool need_stage = L.G > 1 || (int64_t)k + kCap > (int64_t)var0.stage_lds;
+    const int64_t stage_cap = need_stage ? (int64_t)k + kCap : 0;
+    const size_t rows_bytes = L.G > 1 ? (size_t)rows * sizeof(RowWorkspace) : 0;
+    const size_t stage_bytes = (size_t)rows * (size_t)stage_cap * sizeof(uint64_t);
+    const size_t ws_bytes = kStatusBytes + rows_bytes;
     Workspace* w = nullptr;
-    rc = get_workspace(dev, stream, ws_bytes, &w);
+    rc = get_workspace(dev, stream, ws_bytes, stage_bytes, &w);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
+    char* base = reinterpret_cast<char*>(w->base);
     KParams P;
     P.logits = logits;
     P.lengths = lengths;
     P.out = out;
-    P.status = reinterpret_cast<uint32_t*>(w->base);
-    P.ws = L.G > 1 ? reinterpret_cast<RowWorkspace*>(reinterpret_cast<char*>(w->base) + kStatusBytes) : nullptr;
+    P.status = reinterpret_cast<uint32_t*>(base);
+    P.ws = L.G > 1 ? reinterpret_cast<RowWorkspace*>(base + kStatusBytes) : nullptr;
+    P.stage = need_stage ? reinterpret_cast<uint64_t*>(w->stage) : nullptr;
     P.rows = rows;
     P.n = n;
     P.k = k;
     P.G = L.G;
     P.chunks_per_wg = L.chunks_per_wg;
-    P.idx_digits = idx_digits_for(n);
-    const Variant& var = kVariants[L.variant];
+    P.idx_bits = idx_bits_for(n);
+    P.stage_cap = (int32_t)stage_cap;
+    const Variant& var = var0;
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
@@ -803,6 +1023,7 @@ int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* pla
         plan->block = tks::kVariants[L.variant].block;
         plan->items = tks::kVariants[L.variant].items;
         plan->resident = tks::kVariants[L.variant].resident;
+        plan->first_bits = tks::kVariants[L.variant].first_bits;
         return TOPK_SELECT_SUCCESS;
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
@@ -818,6 +1039,7 @@ int topk_select_variant_info(int32_t v, topk_select_plan_t* plan) {
     plan->block = tks::kVariants[v].block;
     plan->items = tks::kVariants[v].items;
     plan->resident = tks::kVariants[v].resident;
+    plan->first_bits = tks::kVariants[v].first_bits;
     return TOPK_SELECT_SUCCESS;
 }
 
@@ -851,12 +1073,13 @@ int topk_select_release_workspace(void) {
         std::lock_guard<std::mutex> lock(tks::g_mu);
         int rc = TOPK_SELECT_SUCCESS;
         for (auto& kv : tks::g_ws) {
-            if (kv.second.base) {
+            if (kv.second.base || kv.second.stage) {
                 int cur = 0;
                 (void)hipGetDevice(&cur);
                 (void)hipSetDevice(kv.first.first);
                 if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                if (hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+                if (kv.second.base && hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+                if (kv.second.stage && hipFree(kv.second.stage) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
                 (void)hipSetDevice(cur);
             }
         }

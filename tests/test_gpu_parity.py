@@ -235,9 +235,11 @@ def test_single_workgroup_rows_repeat_in_identical_order(torch_gpu):
     _say("identical order x5, one WG per row")
     x = torch_gpu.from_numpy(w.x).cuda()
     L = torch_gpu.from_numpy(w.lengths).cuda()
-    first = tks.select(x, w.k, lengths=L, variant=5, wgs_per_row=1)
+    v = next(v for v in range(tks.num_variants())
+             if not tks.variant_info(v)["resident"])  # one streaming WG covers any row
+    first = tks.select(x, w.k, lengths=L, variant=v, wgs_per_row=1)
     for _ in range(5):
-        again = tks.select(x, w.k, lengths=L, variant=5, wgs_per_row=1)
+        again = tks.select(x, w.k, lengths=L, variant=v, wgs_per_row=1)
         assert torch_gpu.equal(again, first)
     assert_parity(w.x, w.k, w.lengths, first.cpu().numpy())
 
@@ -318,3 +320,19 @@ def test_graph_replay_matches_eager(torch_gpu):
             torch.cuda.synchronize()
         assert tks.device_status(s) == 0
         assert_parity(w.x, w.k, w.lengths, out.cpu().numpy())
+
+
+def test_workspace_reuse_across_row_counts(torch_gpu):
+    """Calls with different row counts reuse one workspace: per-row scratch
+    must never be overlapped by another call's staging area (a one-row split
+    call followed by a many-row split call once left row 1 dirty)."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    _say("workspace reuse: 1 row, 8 rows, 1 row (big k), 8 rows")
+    tks.release_workspace()
+    rng = np.random.default_rng(77)
+    one = rng.standard_normal((1, 131072)).astype(np.float32)
+    eight = rng.integers(-2, 3, (8, 9000)).astype(np.float32)
+    for x, k in ((one, 2048), (eight, 1000), (one, 9000), (eight, 1000), (eight[:3], 16)):
+        got = run_gpu(torch_gpu, x, k)
+        assert_parity(x, k, None, got)
