@@ -87,7 +87,7 @@ def time_eager(torch, fn, steps: int, warmup: int, stream):
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
-def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int):
+def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int, eager_only: bool = False):
     """Per-launch seconds (graph, warm), (graph, cold: rotating copies), eager."""
     w = W.generate(name)
     rows, n = w.x.shape
@@ -100,9 +100,13 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
     torch.cuda.synchronize()
     warm_fns = [lambda: tks.select(xs[0], w.k, lengths=L, out=outs[0])]
     cold_fns = [(lambda i: (lambda: tks.select(xs[i], w.k, lengths=L, out=outs[i % 2])))(i) for i in range(copies)]
-    t_warm, n_warm = time_graph(torch, warm_fns * 32, steps, warmup, stream)
-    t_cold, n_cold = time_graph(torch, cold_fns, steps, warmup, stream) if copies > 1 else (t_warm, n_warm)
-    t_eager = time_eager(torch, warm_fns[0], max(20, steps // 4), warmup, stream)
+    if eager_only:
+        t_eager = time_eager(torch, warm_fns[0], steps, warmup, stream)
+        t_warm, n_warm, t_cold = t_eager, steps, t_eager
+    else:
+        t_warm, n_warm = time_graph(torch, warm_fns * 32, steps, warmup, stream)
+        t_cold, n_cold = time_graph(torch, cold_fns, steps, warmup, stream) if copies > 1 else (t_warm, n_warm)
+        t_eager = time_eager(torch, warm_fns[0], max(20, steps // 4), warmup, stream)
     flags = tks.device_status(stream)
     if flags:
         raise RuntimeError("device-side error flags raised during the benchmark: %d" % flags)
@@ -113,6 +117,39 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
         "t_warm": t_warm, "t_cold": t_cold, "t_eager": t_eager, "launches_timed": n_warm,
         "plan": tks.plan(rows, n, w.k), "x": w.x, "lengths_arr": w.lengths,
     }
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+
+    src = os.path.join(ROOT, "sparse_attention_topk_fp32_amd", "csrc", "topk_select.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the selection kernel on `workload`, from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, when that summary
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel_source_sha256") == kernel_source_sha256():
+                return rec
+    return None
+
+
+def calibrate_copy(torch, mib: int):
+    """Copies of a known size, so that the same profiled run holds the
+    counter values of a plain copy kernel (for scaling FETCH/WRITE_SIZE)."""
+    n = mib << 18  # float32 elements
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(w_x, k, budget_s: float = 10.0):
@@ -141,6 +178,10 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-copies", type=int, default=0,
                     help="input copies rotated for the cold-cache timing (0: enough to exceed 512 MiB)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time plain eager launches only (no graph capture; for counter collection)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build's selector runs on a single GPU "
@@ -163,12 +204,17 @@ def main() -> int:
             return args.cold_copies
         return int(max(2, min(1024, (512 << 20) // (c.rows * c.n * 4) + 1)))
 
-    head = bench_workload(torch, tks, W, args.workload, args.steps, args.warmup, copies_for(args.workload))
+    head = bench_workload(torch, tks, W, args.workload, args.steps, args.warmup,
+                          1 if args.eager_only else copies_for(args.workload), args.eager_only)
     batch = bench_workload(torch, tks, W, args.batch_workload, max(200, args.steps // 10), args.warmup,
-                           copies_for(args.batch_workload))
+                           1 if args.eager_only else copies_for(args.batch_workload), args.eager_only)
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(torch, args.calibrate_copy_mib)
 
     t = head["t_warm"]
     us_per_row = t * 1e6 / head["rows"]
+    traffic = measured_traffic(head["workload"])
     achieved = head["bytes"] / t / 1e9
     bt = batch["t_warm"]
     res = {
@@ -195,7 +241,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 6),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
             "algorithmic_bytes_per_launch": head["bytes"],
         },
         "batch64": {

@@ -140,6 +140,13 @@ __device__ __forceinline__ T add_dev(T* p, T v) {
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_memory() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also makes the
+// compiler wait for this wave's outstanding global stores (vmcnt), which
+// puts a memory round trip after every phase that writes output; here the
+// global data crossing a barrier is published explicitly with wait_memory()
+// and read with device-scope loads, so LDS ordering is all a barrier needs.
+__device__ __forceinline__ void lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Bounded wait until *ctr >= target (device scope), by one thread.
 __device__ void spin_until(uint32_t* ctr, uint32_t target, uint32_t* status) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -162,7 +169,21 @@ __device__ void row_barrier(RowWorkspace* ws, int G, int w, int round, uint32_t*
         const uint32_t per_line = (uint32_t)((G - t + kMergeCopies - 1) / kMergeCopies);
         spin_until(&ws->arrive[t * kLineWords], per_line * (uint32_t)(round + 1), status);
     }
-    __syncthreads();
+    lds_sync();
+}
+
+// Inclusive scan across the 64 lanes of a wave with DPP lane moves (no LDS
+// round trip): shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the
+// last lane of a row is broadcast into the rows above it.  Lanes with no
+// source lane read 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
 }
 
 // Block-wide exclusive scan of two counters at once.  Every thread of the
@@ -173,14 +194,9 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* s_
     constexpr int NW = BLOCK / 64;
     const uint32_t lane = lane_id();
     const uint32_t wid = threadIdx.x / 64;
-    uint32_t ia = a, ib = b;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t xa = __shfl_up(ia, o), xb = __shfl_up(ib, o);
-        if (lane >= (uint32_t)o) { ia += xa; ib += xb; }
-    }
+    const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
     if (lane == 63) { s_w[wid] = ia; s_w[NW + wid] = ib; }
-    __syncthreads();
+    lds_sync();
     uint32_t pa = 0, pb = 0;
     ta = 0; tb = 0;
 #pragma unroll
@@ -193,7 +209,7 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* s_
     eb = pb + ib - b;
     ta = uniform(ta);
     tb = uniform(tb);
-    __syncthreads();  // s_w may be reused right after
+    lds_sync();  // s_w may be reused right after
 }
 
 // Digit schedule over the 64-bit composite (key << 32) | ~index, by the
@@ -273,7 +289,7 @@ __device__ void select_bin(const uint32_t* h, uint32_t bin0_sub, uint32_t need, 
                 if (tot[i]) add_dev(&dst[g * OWN + i], tot[i]);
         }
         wait_memory();
-        __syncthreads();
+        lds_sync();
         row_barrier(ws, G, w, round, status);
         if (owner) {
             const int nc = G < gcopies ? G : gcopies;
@@ -306,14 +322,14 @@ __device__ void select_bin(const uint32_t* h, uint32_t bin0_sub, uint32_t need, 
             above += tot[i];
         }
     }
-    __syncthreads();
+    lds_sync();
     if (uniform(s_sel[2]) == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
-        __syncthreads();
+        lds_sync();
         if (t == 0) {
             s_sel[0] = 0; s_sel[1] = 0; s_sel[2] = 0;
             raise_flag(status, kFlagCapacity);
         }
-        __syncthreads();
+        lds_sync();
     }
 }
 
@@ -336,7 +352,9 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     constexpr int NB0 = 1 << FIRST_BITS;           // first-digit bins
     constexpr int NC0 = FIRST_BITS == 8 ? 32 : 4;  // LDS copies of the first-digit histogram
     constexpr int NC8 = 32;                        // LDS copies in the later 8-bit rounds
-    constexpr int STAGE = (RESIDENT && BLOCK * ITEMS < kStageLds) ? BLOCK * ITEMS : kStageLds;
+    // LDS stage: a one-WG row stages at most its own tile; the finisher of
+    // a split row pulls the row's whole staging area (up to kStageLds).
+    constexpr int STAGE = (RESIDENT && !MULTI && BLOCK * ITEMS < kStageLds) ? BLOCK * ITEMS : kStageLds;
     constexpr int H0_WORDS = NC0 * (NB0 + 1);
     constexpr int H8_WORDS = NC8 * 257;
 
@@ -493,19 +511,21 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             // first digit: every slot adds into bin (key >> (32 - FIRST_BITS));
             // empty slots (key 0) land in bin 0 and are subtracted after
             width = FIRST_BITS;
-            for (int i = tid; i < H0_WORDS; i += BLOCK) s_big.h0[i] = 0u;
-            __syncthreads();
+            for (int i = tid; i < H0_WORDS / 4; i += BLOCK) reinterpret_cast<uint4*>(s_big.h0)[i] = uint4{0u, 0u, 0u, 0u};
+            for (int i = H0_WORDS / 4 * 4 + tid; i < H0_WORDS; i += BLOCK) s_big.h0[i] = 0u;
+            lds_sync();
             uint32_t* const hc = s_big.h0 + (tid % NC0) * (NB0 + 1);
             visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> (32 - FIRST_BITS)], 1u); });
-            __syncthreads();
+            lds_sync();
             select_bin<BLOCK, NB0, NC0>(s_big.h0, n_empty, need, G, ws, ws ? ws->hist0 : nullptr,
                                         FIRST_BITS == 8 ? kMergeCopies : 1, w, round, s_sel, s_scan, P.status);
         } else {
             width = digit_width(pf.r);
             const int sh = 64 - pf.r - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < H8_WORDS; i += BLOCK) s_big.h8[i] = 0u;
-            __syncthreads();
+            for (int i = tid; i < H8_WORDS / 4; i += BLOCK) reinterpret_cast<uint4*>(s_big.h8)[i] = uint4{0u, 0u, 0u, 0u};
+            for (int i = H8_WORDS / 4 * 4 + tid; i < H8_WORDS; i += BLOCK) s_big.h8[i] = 0u;
+            lds_sync();
             uint32_t* const hc = s_big.h8 + (tid % NC8) * 257;
             if (sh >= 32) {
                 const int ks = sh - 32;
@@ -520,12 +540,12 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
                     if ((key != 0u) & (key == kp) & ((ni & im) == ip)) atomicAdd(&hc[(ni >> sh) & dmask], 1u);
                 });
             }
-            __syncthreads();
+            lds_sync();
             select_bin<BLOCK, 256, NC8>(s_big.h8, 0u, need, G, ws, ws ? &ws->hist[round - 1][0][0] : nullptr,
                                         kMergeCopies, w, round, s_sel, s_scan, P.status);
         }
         const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
-        __syncthreads();
+        lds_sync();
         need -= above;
         pf.add_digit(b, width, P.idx_bits);
         ++round;
@@ -552,157 +572,222 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     else visit([&](uint32_t key, int idx) { nsel += selected(key, idx); });
     uint32_t off_sel, unused, tot_sel, unused2;
     block_scan2<BLOCK>(nsel, 0u, s_scan, off_sel, unused, tot_sel, unused2);
-    const bool in_lds = (G == 1) && tot_sel <= (uint32_t)STAGE;
+    bool in_lds = (G == 1) && tot_sel <= (uint32_t)STAGE;
     uint64_t* const gstage = P.stage ? P.stage + (size_t)row * (size_t)P.stage_cap : nullptr;
     uint32_t cap = in_lds ? (uint32_t)STAGE : (uint32_t)P.stage_cap;
     if (!in_lds && !gstage) cap = 0;
     if (G > 1) {
         if (tid == 0) s_bc[0] = tot_sel ? add_dev(&ws->reserve, tot_sel) : 0u;
-        __syncthreads();
+        lds_sync();
         off_sel += uniform(s_bc[0]);
     }
-    auto put = [&](uint32_t key, int idx) {
-        // a copy, so the resident key is not pinned to the high half of a
-        // register pair (which would cost one extra VGPR per key)
-        uint32_t kc = key;
-        __asm__ volatile("" : "+v"(kc));
-        const uint64_t ck = ((uint64_t)kc << 32) | (uint64_t)(~(uint32_t)idx);
-        if (off_sel < cap) {
-            if (in_lds) s_big.stage[off_sel] = ck;
-            else st_dev(&gstage[off_sel], ck);  // device scope: may be read by another WG
-        } else {
-            raise_flag(P.status, kFlagCapacity);
-        }
-        ++off_sel;
-    };
+    // Capacity holds by construction (the rounds end with the bucket at most
+    // kCap, so at most k + kCap entries); checked once, never per element.
+    const bool fits = tot_sel <= cap;
+    if (!fits && tid == 0) raise_flag(P.status, kFlagCapacity);
     if constexpr (RESIDENT) {  // no per-element result of the count pass stays live
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
     }
-    if (nsel) {  // per-thread loops: no barrier or wave operation inside
-        if (key_only) {
+    // one write loop per destination; per-thread loops: no barrier or wave
+    // operation inside.  The key is copied before it is paired with the
+    // index, so resident keys are not pinned to the high half of a register
+    // pair (one extra VGPR per key).
+    auto entry = [](uint32_t key, int idx) -> uint64_t {
+        uint32_t kc = key;
+        __asm__ volatile("" : "+v"(kc));
+        return ((uint64_t)kc << 32) | (uint64_t)(~(uint32_t)idx);
+    };
+    if (fits && nsel) {
+        if (!key_only) {
             visit([&](uint32_t key, int idx) {
-                if (key >= lo) put(key, idx);
+                if (selected(key, idx)) {
+                    const uint64_t ck = entry(key, idx);
+                    if (in_lds) s_big.stage[off_sel] = ck;
+                    else st_dev(&gstage[off_sel], ck);
+                    ++off_sel;
+                }
+            });
+        } else if (in_lds) {
+            visit([&](uint32_t key, int idx) {
+                if (key >= lo) s_big.stage[off_sel++] = entry(key, idx);
+            });
+        } else if (G > 1) {  // read by another WG: device-scope stores
+            visit([&](uint32_t key, int idx) {
+                if (key >= lo) st_dev(&gstage[off_sel++], entry(key, idx));
             });
         } else {
             visit([&](uint32_t key, int idx) {
-                if (selected(key, idx)) put(key, idx);
+                if (key >= lo) st_dev(&gstage[off_sel++], entry(key, idx));
             });
         }
     }
 
+    if (!in_lds) wait_memory();  // the staging area is read by other threads (or WGs) next
     uint32_t m_sel = tot_sel;  // staged entries of the row
     if (G > 1) {
         // the last WG of the row to get here finishes it and clears the workspace
         wait_memory();
-        __syncthreads();
+        lds_sync();
         if (tid == 0) s_bc[1] = (add_dev(&ws->done, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
-        __syncthreads();
+        lds_sync();
         if (uniform(s_bc[1]) == 0u) return;
         m_sel = uniform(ld_dev(&ws->reserve));
-    } else {
-        __syncthreads();
+        if (m_sel > cap) m_sel = cap;
+        if (m_sel <= (uint32_t)STAGE) {
+            // the whole staging area on chip: eight independent loads in
+            // flight per thread per step instead of one dependent chain
+            for (uint32_t i0 = 0; i0 < m_sel; i0 += 8u * BLOCK) {
+                uint64_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + u * BLOCK + tid;
+                    v[u] = i < m_sel ? ld_dev(&gstage[i]) : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + u * BLOCK + tid;
+                    if (i < m_sel) s_big.stage[i] = v[u];
+                }
+            }
+            in_lds = true;
+        }
     }
+    lds_sync();
     if (m_sel > cap) m_sel = cap;
 
     // ---------------- on-chip finish
+    // Two-way partition of n entries (get(i) supplies entry i): cls(v) is 1
+    // (-> putA), 2 (-> putB) or 0 (dropped).  Positions follow entry order
+    // through a block scan, so the order is reproducible.  Loads are taken
+    // eight per thread at a time before any store, so they overlap instead
+    // of waiting behind the previous entry's LDS store.  When a total would
+    // exceed its bound, a flag is raised and nothing is written.
+    constexpr int U = 8;
+    auto partition = [&](uint32_t n, auto&& get, auto&& cls, auto&& putA, auto&& putB, uint32_t capA,
+                         uint32_t capB, uint32_t& tA, uint32_t& tB) {
+        uint32_t ca = 0, cb = 0;
+        for (uint32_t i0 = 0; i0 < n; i0 += U * BLOCK) {
+            uint64_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + u * BLOCK + tid;
+                v[u] = i < n ? get(i) : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t c = (i0 + u * BLOCK + tid < n) ? cls(v[u]) : 0u;
+                ca += c == 1u;
+                cb += c == 2u;
+            }
+        }
+        uint32_t oa, ob;
+        block_scan2<BLOCK>(ca, cb, s_scan, oa, ob, tA, tB);
+        const bool ok = tA <= capA && tB <= capB;
+        if (!ok && tid == 0) raise_flag(P.status, kFlagCapacity);
+        if (ok && (ca | cb)) {
+            for (uint32_t i0 = 0; i0 < n; i0 += U * BLOCK) {
+                uint64_t v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t i = i0 + u * BLOCK + tid;
+                    v[u] = i < n ? get(i) : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t c = (i0 + u * BLOCK + tid < n) ? cls(v[u]) : 0u;
+                    if (c == 1u) putA(oa++, v[u]);
+                    else if (c == 2u) putB(ob++, v[u]);
+                }
+            }
+        }
+        lds_sync();
+    };
+
     // Split the staged entries: above the threshold prefix (or the whole
     // bucket when it is taken entirely) -> output; in the bucket -> LDS
-    // candidates.  Positions come from a block scan, so the order is
-    // reproducible for a given staging order.
+    // candidates.
     const uint64_t pfx0 = pf.pfx64(), pmask0 = pf.mask64();
     const uint32_t nwin_total = (uint32_t)k - (all_sel ? 0u : need);
-    auto staged = [&](uint32_t i) -> uint64_t { return in_lds ? s_big.stage[i] : ld_dev(&gstage[i]); };
-    {
-        uint32_t cw = 0, cb = 0;
-        for (uint32_t i = tid; i < m_sel; i += BLOCK) {
-            const uint64_t pm = staged(i) & pmask0;
-            cw += (pm > pfx0) | (all_sel & (pm == pfx0));
-            cb += (!all_sel) & (pm == pfx0);
+    uint32_t tw = 0, tb = 0;
+    auto put_out = [&](uint32_t pos, uint64_t v) { out[pos] = (int32_t)~(uint32_t)v; };
+    auto put_cand = [&](uint32_t pos, uint64_t v) { s_cand[pos] = v; };
+    auto cls0 = [&](uint64_t v) -> uint32_t {
+        const uint64_t pm = v & pmask0;
+        if ((pm > pfx0) | (all_sel & (pm == pfx0))) return 1u;
+        return ((!all_sel) & (pm == pfx0)) ? 2u : 0u;
+    };
+    if (in_lds) {
+        partition(m_sel, [&](uint32_t i) { return s_big.stage[i]; }, cls0, put_out, put_cand, nwin_total,
+                  (uint32_t)kCap, tw, tb);
+    } else {
+        partition(m_sel, [&](uint32_t i) { return ld_dev(&gstage[i]); }, cls0, put_out, put_cand, nwin_total,
+                  (uint32_t)kCap, tw, tb);
+    }
+    if (tw != nwin_total && tid == 0) raise_flag(P.status, kFlagCapacity);
+
+    if (!all_sel && tb <= (uint32_t)kCap) {
+        const uint32_t m = tb;
+        int32_t* __restrict__ fout = out + nwin_total;  // `need` slots remain
+        const uint32_t need0 = need;
+        uint64_t pfx = pfx0, pmask = pmask0;
+        bool fin_all = false;
+        uint32_t mb = m;
+        int fround = 0;
+        while (mb > (uint32_t)kSmall && pf.r < 64) {
+            const int width = digit_width(pf.r);
+            const int sh = 64 - pf.r - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int i = tid; i < kFinCopies * 257; i += BLOCK) s_fin_hist[i] = 0u;
+            lds_sync();
+            uint32_t* const fc = s_fin_hist + (tid % kFinCopies) * 257;
+            for (uint32_t i0 = 0; i0 < m; i0 += U * BLOCK) {
+                uint64_t v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t i = i0 + u * BLOCK + tid;
+                    v[u] = i < m ? s_cand[i] : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if ((i0 + u * BLOCK + tid < m) & ((v[u] & pmask) == pfx))
+                        atomicAdd(&fc[(uint32_t)(v[u] >> sh) & dmask], 1u);
+                }
+            }
+            lds_sync();
+            select_bin<BLOCK, 256, kFinCopies>(s_fin_hist, 0u, need, 1, nullptr, nullptr, 1, 0, fround,
+                                               s_sel, s_scan, P.status);
+            const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
+            lds_sync();
+            need -= above;
+            pf.add_digit(b, width, P.idx_bits);
+            pfx = pf.pfx64();
+            pmask = pf.mask64();
+            ++fround;
+            mb = hb;
+            if (hb == need) { fin_all = true; break; }
         }
-        uint32_t ow, ob, tw, tb;
-        block_scan2<BLOCK>(cw, cb, s_scan, ow, ob, tw, tb);
-        if (tw != nwin_total || tb > (uint32_t)kCap) raise_flag(P.status, kFlagCapacity);
-        for (uint32_t i = tid; i < m_sel; i += BLOCK) {
-            const uint64_t ck = staged(i);
-            const uint64_t pm = ck & pmask0;
-            if ((pm > pfx0) | (all_sel & (pm == pfx0))) {
-                if (ow < nwin_total) out[ow] = (int32_t)~(uint32_t)ck;
-                ++ow;
-            } else if ((!all_sel) & (pm == pfx0)) {
-                if (ob < (uint32_t)kCap) s_cand[ob] = ck;
-                ++ob;
-            }
-        }
-        __syncthreads();
-        if (!all_sel) {
-            uint32_t m = tb > (uint32_t)kCap ? (uint32_t)kCap : tb;
-            int32_t* __restrict__ fout = out + nwin_total;  // `need` slots remain
-            const uint32_t need0 = need;
-            uint64_t pfx = pfx0, pmask = pmask0;
-            bool fin_all = false;
-            uint32_t mb = m;
-            int fround = 0;
-            while (mb > (uint32_t)kSmall && pf.r < 64) {
-                const int width = digit_width(pf.r);
-                const int sh = 64 - pf.r - width;
-                const uint32_t dmask = (1u << width) - 1u;
-                for (int i = tid; i < kFinCopies * 257; i += BLOCK) s_fin_hist[i] = 0u;
-                __syncthreads();
-                uint32_t* const fc = s_fin_hist + (tid % kFinCopies) * 257;
-                for (uint32_t i = tid; i < m; i += BLOCK) {
-                    const uint64_t ck = s_cand[i];
-                    if ((ck & pmask) == pfx) atomicAdd(&fc[(uint32_t)(ck >> sh) & dmask], 1u);
-                }
-                __syncthreads();
-                select_bin<BLOCK, 256, kFinCopies>(s_fin_hist, 0u, need, 1, nullptr, nullptr, 1, 0, fround,
-                                                   s_sel, s_scan, P.status);
-                const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
-                __syncthreads();
-                need -= above;
-                pf.add_digit(b, width, P.idx_bits);
-                pfx = pf.pfx64();
-                pmask = pf.mask64();
-                ++fround;
-                mb = hb;
-                if (hb == need) { fin_all = true; break; }
-            }
-            // winners among the candidates, and the small bucket to rank exactly
-            uint32_t fw = 0, fb = 0;
-            for (uint32_t i = tid; i < m; i += BLOCK) {
-                const uint64_t pm = s_cand[i] & pmask;
-                fw += (pm > pfx) | (fin_all & (pm == pfx));
-                fb += (!fin_all) & (pm == pfx);
-            }
-            uint32_t ofw, ofb, tfw, tfb;
-            block_scan2<BLOCK>(fw, fb, s_scan, ofw, ofb, tfw, tfb);
-            for (uint32_t i = tid; i < m; i += BLOCK) {
-                const uint64_t ck = s_cand[i];
-                const uint64_t pm = ck & pmask;
-                if ((pm > pfx) | (fin_all & (pm == pfx))) {
-                    if (ofw < need0) fout[ofw] = (int32_t)~(uint32_t)ck;
-                    else raise_flag(P.status, kFlagCapacity);
-                    ++ofw;
-                } else if ((!fin_all) & (pm == pfx)) {
-                    if (ofb < (uint32_t)kSmall) s_small[ofb] = ck;
-                    else raise_flag(P.status, kFlagCapacity);
-                    ++ofb;
-                }
-            }
-            __syncthreads();
-            if (!fin_all) {
-                const uint32_t ms = tfb > (uint32_t)kSmall ? (uint32_t)kSmall : tfb;
-                const uint32_t base = tfw;
-                for (uint32_t i = tid; i < ms; i += BLOCK) {
-                    const uint64_t c = s_small[i];
-                    uint32_t rank = 0;
-                    for (uint32_t j = 0; j < ms; ++j) rank += s_small[j] > c;
-                    if (rank < need) {
-                        const uint32_t pos = base + rank;
-                        if (pos < need0) fout[pos] = (int32_t)~(uint32_t)c;
-                        else raise_flag(P.status, kFlagCapacity);
-                    }
-                }
+        // winners among the candidates, and the small bucket to rank exactly
+        uint32_t tfw = 0, tfb = 0;
+        partition(
+            m, [&](uint32_t i) { return s_cand[i]; },
+            [&](uint64_t v) -> uint32_t {
+                const uint64_t pm = v & pmask;
+                if ((pm > pfx) | (fin_all & (pm == pfx))) return 1u;
+                return ((!fin_all) & (pm == pfx)) ? 2u : 0u;
+            },
+            [&](uint32_t pos, uint64_t v) { fout[pos] = (int32_t)~(uint32_t)v; },
+            [&](uint32_t pos, uint64_t v) { s_small[pos] = v; }, need0, (uint32_t)kSmall, tfw, tfb);
+        if (!fin_all && tfb <= (uint32_t)kSmall) {
+            const uint32_t ms = tfb;
+            const uint32_t base = tfw;
+            for (uint32_t i = tid; i < ms; i += BLOCK) {
+                const uint64_t c = s_small[i];
+                uint32_t rank = 0;
+#pragma unroll 8
+                for (uint32_t j = 0; j < ms; ++j) rank += s_small[j] > c;
+                const uint32_t pos = base + rank;
+                if ((rank < need) & (pos < need0)) fout[pos] = (int32_t)~(uint32_t)c;
             }
         }
     }
@@ -851,15 +936,17 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
     return TOPK_SELECT_SUCCESS;
 }
 
-// Default shape.  Many rows: one WG per row with the 12-bit first digit
-// when the row fits one resident tile.  Few rows: spread each row over
-// enough 8-bit-digit WGs to cover about one WG per CU.  Otherwise the
-// largest resident tile that fits, else streaming.
+// Default shape (measured on MI355X: a cross-workgroup round costs a few
+// microseconds whatever the split, so few rows use few, large workgroups).
+// Many rows: one WG per row with the 12-bit first digit when the row fits
+// one resident tile, else several 12-bit WGs per row when they can all be
+// resident, else streaming.  Few rows: 512-thread WGs holding 16K (then
+// 32K, then smaller) logits each, as many per row as the row needs.
 int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
     const int target = d.cus;
     auto tile_chunks = [](int v) { return (int64_t)kVariants[v].block * (kVariants[v].items / 4); };
     if (rows >= target / 2) {
-        const int one_wg[] = {5, 6, 7, 8};
+        const int one_wg[] = {5, 6, 8};
         for (int v : one_wg)
             if (maxc <= tile_chunks(v)) return check_shape(d, rows, maxc, v, 1, L);
         const int split[] = {7};
@@ -868,17 +955,11 @@ int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
             if (rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
         }
     } else {
-        int best = -1, bestG = 0;
-        const int few[] = {0, 1, 2, 3, 4};
+        const int few[] = {3, 4, 2, 1, 0};
         for (int v : few) {
             const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
-            const bool fits = G == 1 || rows * G <= (int64_t)d.capacity[v];
-            if (!fits) continue;
-            if (rows * G <= target) return check_shape(d, rows, maxc, v, (int)G, L);
-            best = v;
-            bestG = (int)G;
+            if (G == 1 || rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
         }
-        if (best >= 0) return check_shape(d, rows, maxc, best, bestG, L);
     }
     // streaming: as many WGs per row as can be co-resident, at least one
     const int v = (maxc >= 16384) ? 9 : 10;
