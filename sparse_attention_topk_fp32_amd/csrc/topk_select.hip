@@ -10,38 +10,40 @@
 //    the bin holding the k-th element (thresholding) and finally collects the
 //    elements above the threshold, then ties at the threshold in index order
 //    (collection).
-//  * Section 03: two refinements - keep the surviving candidates on chip once
-//    the bucket is small after the first screening, and stop the screening
-//    over global memory once the bucket holds at most 4096 elements; wide
-//    vector loads.
+//  * Section 03: keep the surviving candidates on chip once the bucket is
+//    small, and stop the screening over global memory once the bucket holds
+//    at most 4096 elements; wide vector loads.
 //  * Section 5: one row split over several blocks that merge their
-//    histograms and continue together after a barrier; -1 for empty slots.
+//    histograms and continue together; -1 for empty output slots.
 //
 // MI355X design (not a translation of the article's Triton/CUDA kernels):
-//  * Each row is cut into slices of 16-byte chunks; one workgroup (WG) owns
-//    one slice.  "Resident" variants load their slice once with 16-byte
-//    loads, fuse the key map into the load and keep the keys in VGPRs for
-//    every later round; "streaming" variants re-read their slice each round
-//    (only used when a row is too long to stay on chip).
+//  * A row is cut into slices of 16-byte chunks, one workgroup (WG) per
+//    slice, G WGs per row.  Resident variants load their slice once, fuse the
+//    key map into the load and keep the keys in VGPRs for every later pass;
+//    streaming variants re-read their slice in each pass (rows too long to
+//    keep on chip).
 //  * Ties are made unique by ranking the 64-bit composite
 //    (key << 32 | ~index): larger composite = larger value, or equal value and
-//    smaller index.  Rounds run over 8-bit digits of the key (4 rounds) and,
-//    only when the threshold value is tied past capacity, of the index.  The
-//    k largest composites are exactly the selection with lowest-index ties.
-//  * A row spread over G > 1 WGs (the batch-1 case) merges its 256-bin LDS
-//    histograms through device-scope atomics into a per-row global histogram
-//    and waits at a bounded spin barrier; every WG then picks the same
-//    threshold bin from the merged counts, so no broadcast round trip is
-//    needed.  The host only uses G > 1 when all WGs of the launch fit on the
-//    GPU at once (occupancy query), so the barrier always completes.
-//  * Once the threshold bucket holds <= 4096 elements, its (key, index) pairs
-//    go to a candidate buffer (LDS for G == 1, global for G > 1) and one WG
-//    (the last to arrive, for G > 1) finishes the selection on chip: more
-//    digit rounds in LDS while the bucket exceeds 256, then an exact rank of
-//    the remaining composites.
-//  * Elements above the threshold bucket are written straight to the output
-//    by the WG that holds them.  The per-row workspace is left zeroed by the
-//    finishing WG, so no clearing launch is needed between calls.
+//    smaller index.  Rounds run over 8-bit digits of the key and, only when a
+//    value is tied past capacity, of the index.
+//  * Merge of a round across the G WGs of a row: each WG adds
+//    (1 << 32 | count) for each of the 256 bins into the row's global
+//    histogram with one 64-bit device-scope atomic per bin, and polls the bin
+//    until its arrival field reaches G; no separate barrier, no cache fence.
+//    The value the atomic returns is the count of the WGs that added before
+//    this one, which gives every WG a private, disjoint range of output
+//    positions inside each bin.  Every WG selects the threshold bin itself
+//    from the merged counts.
+//  * Elements above the threshold bin are written straight to the output by
+//    the WG holding them, at (start of their bin) + (the WG's range) + (rank
+//    inside the WG, from a wave-aggregated LDS counter).  Once the threshold
+//    bucket holds at most 4096 elements, its (key, index) composites go to a
+//    candidate buffer (LDS for G == 1, the row's global stage for G > 1) and
+//    one WG finishes on chip: more digit rounds in LDS while more than 256
+//    remain, then an exact rank.
+//  * The per-row workspace is double-buffered by launch parity: a launch
+//    uses one half, and its finishing WG clears the half the previous launch
+//    used, so no clearing launch or end-of-kernel barrier is needed.
 
 #include <hip/hip_runtime.h>
 
@@ -57,32 +59,28 @@
 
 namespace tks {
 
-constexpr int kCap = 4096;          // candidate buffer capacity (elements)
-constexpr int kSmall = 256;         // bucket size ranked directly by the finisher
-constexpr int kMaxPasses = 8;       // rounds after the first digit (8-bit digits)
-constexpr int kStageLds = 8192;     // staged (key, index) entries a one-WG row may keep in LDS
-constexpr int kFinCopies = 8;       // LDS histogram copies for the finisher's rounds
-constexpr int kMergeCopies = 8;     // global copies of a row's 256-bin histogram (WG w adds into copy w mod 8)
-constexpr int kLineWords = 32;      // one 128-byte line
+constexpr int kCap = 4096;        // final bucket size handed to one WG (entries)
+constexpr int kSmall = 256;       // bucket ranked exactly by comparisons
+constexpr int kRounds = 8;        // digit rounds: 4 key bytes + up to 4 index bytes
+constexpr int kCopies = 16;       // LDS copies of the 256-bin histogram (against atomic conflicts)
+constexpr int kMergeCopies = 4;   // global copies of a row's histogram per round (WG w -> copy w mod C)
 constexpr uint32_t kFlagTimeout = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
 // Bound on a cross-workgroup wait, in ticks of the 100 MHz constant clock
 // (s_memrealtime): 2 s, far beyond any legitimate wait.
 constexpr uint64_t kSpinLimitTicks = 200000000ull;
 
-// Per-row scratch for rows spread over several workgroups.  Every field is
-// zero between calls (the finishing WG of each row clears what it used).
-// All cross-workgroup traffic goes through device-scope atomic operations
-// (read-modify-writes, loads and stores), which are performed at the
-// device's coherence point; their order within a wave is enforced with
-// s_waitcnt vmcnt(0).  No L2 write-back or invalidate fence is needed.
+// Per-row scratch for rows spread over several workgroups, in two halves
+// selected by the parity of the launch.  All cross-workgroup traffic uses
+// device-scope atomic operations, performed at the device's coherence point.
 struct alignas(256) RowWorkspace {
-    uint32_t hist0[4096];                            // first-digit counts (4096 bins, or 8 copies of 256)
-    uint32_t hist[kMaxPasses][kMergeCopies][256];    // later rounds (8-bit digits)
-    uint32_t arrive[kMergeCopies * kLineWords];      // barrier arrivals, one counter per line
-    uint32_t done;                                   // WGs finished with the row
-    uint32_t reserve;                                // staged entries reserved in the row's stage
-    uint32_t pad[62];
+    uint64_t hist[2][kRounds][kMergeCopies][256];  // (arrivals << 32) | count
+    uint64_t stage[2][kCap];                       // final-bucket composites; 0 = not written yet
+    uint32_t parity;                               // half used by the next launch
+    uint32_t used_rounds[2];                       // what each half holds (cleared by the next launch)
+    uint32_t used_copies[2];
+    uint32_t used_stage[2];
+    uint32_t pad[57];
 };
 
 struct KParams {
@@ -90,13 +88,12 @@ struct KParams {
     const int32_t* lengths;
     int32_t* out;
     RowWorkspace* ws;       // per row, when G > 1
-    uint64_t* stage;        // per row, stage_cap entries: (key << 32) | ~index, or null
     uint32_t* status;
     int32_t rows, n, k;
     int32_t G;              // workgroups per row
     int32_t chunks_per_wg;  // 16-byte chunks in one WG's slice
-    int32_t idx_bits;       // bits of the index that vary (multiple of 8, <= 32)
-    int32_t stage_cap;      // entries per row in `stage`
+    int32_t idx_bits;       // bits of the index that vary (multiple of 8, 8..32)
+    int32_t mcopies;        // global histogram copies used (1..kMergeCopies)
 };
 
 // ----------------------------------------------------------------- device helpers
@@ -116,8 +113,7 @@ __device__ __forceinline__ uint32_t lane_id() {
     return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
-// A value every lane holds identically (read from LDS after a barrier):
-// make it scalar so the loop state and its branches stay in SGPRs.
+// A value every lane holds identically: make it scalar.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ void raise_flag(uint32_t* status, uint32_t f) {
@@ -137,45 +133,14 @@ template <typename T>
 __device__ __forceinline__ T add_dev(T* p, T v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until every memory operation this wave issued has completed.
-__device__ __forceinline__ void wait_memory() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also makes the
-// compiler wait for this wave's outstanding global stores (vmcnt), which
-// puts a memory round trip after every phase that writes output; here the
-// global data crossing a barrier is published explicitly with wait_memory()
-// and read with device-scope loads, so LDS ordering is all a barrier needs.
+// Workgroup barrier that orders LDS only (global data crossing WGs goes
+// through device-scope atomics, global data inside a WG is never re-read).
 __device__ __forceinline__ void lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Bounded wait until *ctr >= target (device scope), by one thread.
-__device__ void spin_until(uint32_t* ctr, uint32_t target, uint32_t* status) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (ld_dev(ctr) < target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-            raise_flag(status, kFlagTimeout);
-            break;
-        }
-    }
-}
-
-// Row barrier for the G WGs of a row: WG w counts on line w mod 8, and
-// threads 0..7 each wait for their line to reach its round's total.  The
-// caller has made its own preceding device-scope operations complete.
-__device__ void row_barrier(RowWorkspace* ws, int G, int w, int round, uint32_t* status) {
-    if (threadIdx.x == 0) add_dev(&ws->arrive[(w % kMergeCopies) * kLineWords], 1u);
-    const int t = threadIdx.x;
-    if (t < kMergeCopies && t < G) {
-        const uint32_t per_line = (uint32_t)((G - t + kMergeCopies - 1) / kMergeCopies);
-        spin_until(&ws->arrive[t * kLineWords], per_line * (uint32_t)(round + 1), status);
-    }
-    lds_sync();
-}
-
-// Inclusive scan across the 64 lanes of a wave with DPP lane moves (no LDS
-// round trip): shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the
-// last lane of a row is broadcast into the rows above it.  Lanes with no
-// source lane read 0.
+// Inclusive scan across the 64 lanes of a wave with DPP lane moves: shifts
+// by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of a row is
+// broadcast into the rows above it.  Lanes with no source lane read 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
     x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
@@ -186,239 +151,229 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// Block-wide exclusive scan of two counters at once.  Every thread of the
-// block calls it; returns this thread's exclusive prefixes and the totals.
-template <int BLOCK>
-__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* s_w /* [2 * BLOCK / 64] */,
-                                            uint32_t& ea, uint32_t& eb, uint32_t& ta, uint32_t& tb) {
-    constexpr int NW = BLOCK / 64;
-    const uint32_t lane = lane_id();
+// Block-wide exclusive scan (thread order) of one counter over the first NT
+// threads (NT a multiple of 64, <= BLOCK); every thread of the block calls
+// it.  Returns this thread's exclusive prefix.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, uint32_t* s_w /* [NT / 64] */) {
+    constexpr int NW = NT / 64;
     const uint32_t wid = threadIdx.x / 64;
-    const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
-    if (lane == 63) { s_w[wid] = ia; s_w[NW + wid] = ib; }
+    const uint32_t ia = wave_inclusive_scan(a);
+    if (wid < NW && lane_id() == 63) s_w[wid] = ia;
     lds_sync();
-    uint32_t pa = 0, pb = 0;
-    ta = 0; tb = 0;
+    uint32_t pa = 0;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const uint32_t wa = s_w[i], wb = s_w[NW + i];
-        if ((uint32_t)i < wid) { pa += wa; pb += wb; }
-        ta += wa; tb += wb;
-    }
-    ea = pa + ia - a;
-    eb = pb + ib - b;
-    ta = uniform(ta);
-    tb = uniform(tb);
+    for (int i = 0; i < NW; ++i)
+        if ((uint32_t)i < wid) pa += s_w[i];
     lds_sync();  // s_w may be reused right after
+    return pa + ia - a;
 }
 
-// Digit schedule over the 64-bit composite (key << 32) | ~index, by the
-// number r of top bits already resolved: the key's 32 bits in digits of up
-// to 8 bits (the first digit may be wider), then the index bits that vary.
-// ~index has its top (32 - idx_bits) bits set for every valid index, so they
-// are skipped.
-__device__ __forceinline__ int digit_width(int r) { return r < 32 ? min(8, 32 - r) : min(8, 64 - r); }
+// Bit position of round r's digit inside its 32-bit word: rounds 0..3 cut
+// the key from the top, later rounds the varying low idx_bits of ~index
+// (its top 32 - idx_bits bits are ones for every valid index).
+__device__ __forceinline__ int digit_shift(int r, int idx_bits) { return r < 4 ? 24 - 8 * r : idx_bits - 8 - 8 * (r - 4); }
+__device__ __forceinline__ int num_rounds(int idx_bits) { return 4 + idx_bits / 8; }
 
+// The composite prefix resolved so far: key bits (kpfx under kmask) and
+// ~index bits (ipfx under imask).
 struct Prefix {
-    uint32_t kpfx, kmask;  // resolved key bits
-    uint32_t ipfx, imask;  // resolved ~index bits
-    int r;                 // resolved bits of the composite
-    // Value selects only (no branch that picks a field to update), so the
-    // struct stays in registers.
-    __device__ void add_digit(uint32_t b, int width, int idx_bits) {
-        const int sh = 64 - r - width;
-        const bool in_key = sh >= 32;
-        const int s = in_key ? sh - 32 : sh;
-        const uint32_t bb = b << s, mm = ((1u << width) - 1u) << s;  // width <= 12
+    uint32_t kpfx, kmask, ipfx, imask;
+    // value selects only (a branch that picks the field to update would
+    // put the struct in scratch memory)
+    __device__ void add(int r, uint32_t b, int idx_bits) {
+        const int s = digit_shift(r, idx_bits);
+        const bool in_key = r < 4;
+        const uint32_t bb = b << s, mm = 0xFFu << s;
         kpfx |= in_key ? bb : 0u;
         kmask |= in_key ? mm : 0u;
         ipfx |= in_key ? 0u : bb;
         imask |= in_key ? 0u : mm;
-        r += width;
-        // past the key: the top (32 - idx_bits) bits of ~index are constant ones
-        const bool jump = r == 32;
-        const uint32_t ones = idx_bits < 32 ? ~((1u << idx_bits) - 1u) : 0u;
-        ipfx |= jump ? ones : 0u;
-        imask |= jump ? ones : 0u;
-        r = jump ? 64 - idx_bits : r;
     }
-    __device__ uint64_t pfx64() const { return ((uint64_t)kpfx << 32) | ipfx; }
-    __device__ uint64_t mask64() const { return ((uint64_t)kmask << 32) | imask; }
+    // Does the element (key, ~index) match the prefix?
+    __device__ __forceinline__ bool match(uint32_t key, uint32_t ni) const {
+        return (key != 0u) & ((key & kmask) == kpfx) & ((ni & imask) == ipfx);
+    }
 };
 
-// Thresholding step over an NB-bin histogram held as NC LDS copies (stride
-// NB + 1 words).  Finds the bin b holding the element of rank `need`
-// (1-based, from the top): the caller gets b, the count above b and the
-// count in b through s_sel.  Each owning thread sums the copies of its bins,
-// optionally merges them across the row's WGs (G > 1: add into a global
-// histogram, barrier, read back the sums), then one block scan over the
-// owners' sums, taken from the top bin down, locates b.
-template <int BLOCK, int NB, int NC>
-__device__ void select_bin(const uint32_t* h, uint32_t bin0_sub, uint32_t need, int G, RowWorkspace* ws,
-                           uint32_t* gm, int gcopies, int w, int round, uint32_t* s_sel, uint32_t* s_scan,
-                           uint32_t* status) {
-    constexpr int OWN = (NB + BLOCK - 1) / BLOCK;      // bins per owning thread
-    constexpr int OWNERS = (NB + OWN - 1) / OWN;       // the last group may be partial
+// Relation of an element to the prefix after rounds 0..R: returns 1 when it
+// is above it (a winner; *slot = 256 * deciding round + its digit there),
+// 2 when it matches it (in the bucket), 0 otherwise.  Composites compare as
+// (key, ~index) pairs.
+__device__ __forceinline__ uint32_t classify(uint32_t key, uint32_t ni, const Prefix& pf, bool idx_rounds,
+                                             int idx_bits, uint32_t* slot) {
+    if (key == 0u) return 0u;
+    if (!idx_rounds) {
+        const uint32_t s = key & pf.kmask;
+        if (s == pf.kpfx) return 2u;
+        if (s < pf.kpfx) return 0u;
+        const uint32_t r = (uint32_t)__builtin_clz(s ^ pf.kpfx) >> 3;
+        *slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
+        return 1u;
+    }
+    if (key != pf.kpfx) {
+        if (key < pf.kpfx) return 0u;
+        const uint32_t r = (uint32_t)__builtin_clz(key ^ pf.kpfx) >> 3;
+        *slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
+        return 1u;
+    }
+    const uint32_t s = ni & pf.imask;
+    if (s == pf.ipfx) return 2u;
+    if (s < pf.ipfx) return 0u;
+    const int lead = __builtin_clz(s ^ pf.ipfx) - (32 - idx_bits);  // leading bit inside the index digits
+    const int r = 4 + lead / 8;
+    *slot = (uint32_t)r * 256u + ((ni >> digit_shift(r, idx_bits)) & 0xFFu);
+    return 1u;
+}
+
+// Shared state of one WG.
+template <int BLOCK>
+struct Smem {
+    alignas(16) uint32_t hist[kCopies * 257];  // histogram copies (stride 257 words)
+    uint32_t pos[kRounds * 256];        // output / stage position counters per (round, bin)
+    uint64_t cand[kCap];                // final bucket, on chip
+    uint64_t small[kSmall];             // last few candidates, ranked exactly
+    uint32_t scan[BLOCK / 64];
+    uint32_t sel[4];                    // threshold bin, count above it, count in it, small count
+};
+
+// Thresholding step for round r from the LDS histogram copies (the first
+// 256 threads own one bin each, thread t the bin 255 - t, so thread order is
+// descending bin order).  With G > 1 the counts are merged across the row's
+// WGs first.  Finds the bin b holding the element of rank `need` (1-based,
+// from the top) and sets the position counters of the bins at and above b:
+// winners of bin j > b go to W + (count above j) + (this WG's range in j);
+// the bucket bin b goes to the output the same way when it is taken whole
+// (`need` == count in b after the elements above), else to positions
+// (this WG's range in b) of the candidate buffer.
+template <int BLOCK>
+__device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, uint32_t bin0_sub, uint32_t need, uint32_t W, RowWorkspace* ws,
+                          int p, int C, int w, int G, uint32_t* status, uint32_t& b_out, uint32_t& above_out,
+                          uint32_t& hb_out) {
     const int t = threadIdx.x;
-    const bool owner = t < OWNERS;
-    const int g = OWNERS - 1 - t;  // thread 0 owns the top bins
-    uint32_t tot[OWN];
-#pragma unroll
-    for (int i = 0; i < OWN; ++i) tot[i] = 0;
+    const bool owner = t < 256;
+    const int j = 255 - t;
+    uint32_t tot = 0, pre = 0;
     if (owner) {
-        // copy by copy, with a few LDS reads in flight at a time (the
-        // caller's resident keys are live here)
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int i = 0; i < OWN; ++i) {
-                const int bin = g * OWN + i;
-                if (bin < NB) tot[i] += h[c * (NB + 1) + bin];
+        for (int c = 0; c < kCopies; ++c) cnt += sm.hist[c * 257 + j];
+        if (j == 0) cnt -= bin0_sub;
+        if (G > 1) {
+            uint64_t* h = &ws->hist[p][r][0][0];
+            const int mc = w % C;
+            const uint64_t old = add_dev(&h[mc * 256 + j], (uint64_t)((1ull << 32) | cnt));
+            // poll the copies (all loads in flight together) until every
+            // WG of the row has added
+            uint64_t v0, v1, v2, v3;
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
+                v0 = ld_dev(&h[j]);
+                v1 = C > 1 ? ld_dev(&h[256 + j]) : 0ull;
+                v2 = C > 2 ? ld_dev(&h[512 + j]) : 0ull;
+                v3 = C > 3 ? ld_dev(&h[768 + j]) : 0ull;
+                const uint32_t arr = (uint32_t)(v0 >> 32) + (uint32_t)(v1 >> 32) + (uint32_t)(v2 >> 32) +
+                                     (uint32_t)(v3 >> 32);
+                if (arr >= (uint32_t)G) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+                    raise_flag(status, kFlagTimeout);
+                    break;
+                }
             }
-            if (OWN * (c + 1) % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int i = 0; i < OWN; ++i)
-            if (g * OWN + i == 0) tot[i] -= bin0_sub;
-    }
-    if (G > 1) {
-        if (owner) {
-            uint32_t* dst = gm + (gcopies > 1 ? (w % gcopies) * NB : 0);
-#pragma unroll
-            for (int i = 0; i < OWN; ++i)
-                if (tot[i]) add_dev(&dst[g * OWN + i], tot[i]);
-        }
-        wait_memory();
-        lds_sync();
-        row_barrier(ws, G, w, round, status);
-        if (owner) {
-            const int nc = G < gcopies ? G : gcopies;
-#pragma unroll
-            for (int i = 0; i < OWN; ++i) {
-                const int bin = g * OWN + i;
-                uint32_t v = 0;
-                if (bin < NB)
-                    for (int c = 0; c < nc; ++c) v += ld_dev(&gm[c * NB + bin]);
-                tot[i] = v;
-            }
+            tot = (uint32_t)v0 + (uint32_t)v1 + (uint32_t)v2 + (uint32_t)v3;
+            pre = (uint32_t)old + (mc > 0 ? (uint32_t)v0 : 0u) + (mc > 1 ? (uint32_t)v1 : 0u) +
+                  (mc > 2 ? (uint32_t)v2 : 0u);
+        } else {
+            tot = cnt;
         }
     }
-    uint32_t gsum = 0;
-#pragma unroll
-    for (int i = 0; i < OWN; ++i) gsum += tot[i];
-    if (t == 0) s_sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
-    uint32_t excl, unused, total, unused2;
-    block_scan2<BLOCK>(gsum, 0u, s_scan, excl, unused, total, unused2);
-    if (owner && excl < need && need <= excl + gsum) {
-        uint32_t above = excl;
-#pragma unroll
-        for (int i = OWN - 1; i >= 0; --i) {
-            if (above + tot[i] >= need) {
-                s_sel[0] = (uint32_t)(g * OWN + i);
-                s_sel[1] = above;
-                s_sel[2] = tot[i];
-                break;
-            }
-            above += tot[i];
-        }
+    if (t == 0) sm.sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
+    const uint32_t excl = block_exclusive_scan<256>(owner ? tot : 0u, sm.scan);
+    if (owner && excl < need && need <= excl + tot) {
+        sm.sel[0] = (uint32_t)j;
+        sm.sel[1] = excl;
+        sm.sel[2] = tot;
     }
     lds_sync();
-    if (uniform(s_sel[2]) == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
-        lds_sync();
-        if (t == 0) {
-            s_sel[0] = 0; s_sel[1] = 0; s_sel[2] = 0;
-            raise_flag(status, kFlagCapacity);
-        }
-        lds_sync();
+    uint32_t b = uniform(sm.sel[0]), above = uniform(sm.sel[1]), hb = uniform(sm.sel[2]);
+    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
+        if (t == 0) raise_flag(status, kFlagCapacity);
+        b = 0; above = 0; hb = 0;
     }
+    if (owner && (uint32_t)j >= b) {
+        const bool whole = (uint32_t)j > b || hb == need - above;
+        sm.pos[r * 256 + j] = whole ? W + excl + pre : pre;
+    }
+    lds_sync();
+    b_out = b;
+    above_out = above;
+    hb_out = hb;
 }
 
 // ----------------------------------------------------------------- the kernel
 //
-// BLOCK threads per WG; ITEMS logits per thread per tile; FIRST_BITS = width
-// of the first digit (8: 256 bins in 32 LDS copies; 12: 4096 bins in 4
-// copies); RESIDENT: the slice is one tile kept in VGPRs across rounds;
-// MULTI: rows may be spread over several WGs (G > 1).  Variants without
-// MULTI carry none of the cross-workgroup code, which keeps their register
-// budget for the resident keys.
+// BLOCK threads per WG; ITEMS logits per thread per tile; RESIDENT: the
+// slice is one tile kept in VGPRs across passes (else re-read every pass).
 
-template <int BLOCK, int ITEMS, int FIRST_BITS, bool RESIDENT, bool MULTI>
+template <int BLOCK, int ITEMS, bool RESIDENT>
 __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "one bin per thread in the 256-bin rounds");
-    static_assert(FIRST_BITS == 8 || FIRST_BITS == 12, "first digit of 8 or 12 bits");
-    constexpr int CHUNKS = ITEMS / 4;              // chunks per thread per tile
-    constexpr int TILE_CHUNKS = BLOCK * CHUNKS;    // chunks per tile
-    constexpr int NB0 = 1 << FIRST_BITS;           // first-digit bins
-    constexpr int NC0 = FIRST_BITS == 8 ? 32 : 4;  // LDS copies of the first-digit histogram
-    constexpr int NC8 = 32;                        // LDS copies in the later 8-bit rounds
-    // LDS stage: a one-WG row stages at most its own tile; the finisher of
-    // a split row pulls the row's whole staging area (up to kStageLds).
-    constexpr int STAGE = (RESIDENT && !MULTI && BLOCK * ITEMS < kStageLds) ? BLOCK * ITEMS : kStageLds;
-    constexpr int H0_WORDS = NC0 * (NB0 + 1);
-    constexpr int H8_WORDS = NC8 * 257;
-
-    // The rounds' histograms and the staged selection are never live at the
-    // same time, so they share LDS.
-    union BigLds {
-        uint32_t h0[H0_WORDS];
-        uint32_t h8[H8_WORDS];
-        uint64_t stage[STAGE];
-    };
-    __shared__ BigLds s_big;
-    __shared__ uint64_t s_cand[kCap];
-    __shared__ uint32_t s_fin_hist[kFinCopies * 257];
-    __shared__ uint64_t s_small[kSmall];
-    __shared__ uint32_t s_scan[2 * (BLOCK / 64)];
-    __shared__ uint32_t s_sel[3];   // threshold bin, count above it, count in it
-    __shared__ uint32_t s_bc[2];    // broadcast: stage base, last-WG flag
+    constexpr int CHUNKS = ITEMS / 4;            // chunks per thread per tile
+    constexpr int TILE_CHUNKS = BLOCK * CHUNKS;  // chunks per tile
+    __shared__ Smem<BLOCK> sm;
 
     const int tid = threadIdx.x;
-    const int G = MULTI ? P.G : 1;
+    const int G = P.G;
     const int row = blockIdx.x / G;
     const int w = blockIdx.x - row * G;
     const int n = P.n;
     const int k = P.k;
-    const float* __restrict__ p = P.logits + (size_t)row * (size_t)n;
+    const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
     int L = n;
     if (P.lengths) {
         L = P.lengths[row];
         L = L < 0 ? 0 : (L > n ? n : L);
     }
-
     if (L <= k) {  // everything valid is selected; pad with -1
         if (w == 0)
             for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
         return;
     }
 
-    RowWorkspace* ws = (MULTI && P.ws) ? P.ws + row : nullptr;
-    const int off = (int)(((uintptr_t)p >> 2) & 3);  // elements before the first 16-byte boundary
+    const int off = (int)(((uintptr_t)prow >> 2) & 3);  // elements before the first 16-byte boundary
     const int nchunks = (off + L + 3) >> 2;
+    const int Geff = min(G, (nchunks + P.chunks_per_wg - 1) / P.chunks_per_wg);  // WGs with a non-empty slice
+    if (w >= Geff) return;
+    const bool multi = Geff > 1;
+    RowWorkspace* const ws = multi ? P.ws + row : nullptr;
+    const int p = multi ? (int)(ld_dev(&ws->parity) & 1u) : 0;
+    const int C = P.mcopies;
+    const int idx_bits = P.idx_bits;
+    const int nrounds = num_rounds(idx_bits);
+
     const int c_begin = w * P.chunks_per_wg;
     const int c_end = min(nchunks, c_begin + P.chunks_per_wg);
     // chunks whose four elements are all valid
     const int cf_lo = max(c_begin, off ? 1 : 0);
     const int cf_hi = min(c_end, (L + off) >> 2);
-    // slots of the slice's chunks that hold no element (key 0): at most the
-    // three before element 0 and the three past L; the first-digit
+    // slots of the slice that hold no element (key 0): the first-round
     // histogram counts them in bin 0 and subtracts them after
-    const int valid = c_end > c_begin ? max(0, min(L, 4 * c_end - off) - max(0, 4 * c_begin - off)) : 0;
-    const uint32_t n_empty = c_end > c_begin ? (uint32_t)(4 * (c_end - c_begin) - valid) : 0u;
+    const int valid = max(0, min(L, 4 * c_end - off) - max(0, 4 * c_begin - off));
+    const uint32_t n_empty = (uint32_t)(4 * (c_end - c_begin) - valid);
 
     uint32_t keys[ITEMS];
-    const float* __restrict__ pa = p - off;  // 16-byte aligned
+    const char* const base = reinterpret_cast<const char*>(prow - off);  // 16-byte aligned
 
     // Load one tile: chunk c of the row is the aligned 16-byte block holding
     // elements [4c - off, 4c - off + 4).  A chunk with at least one valid
-    // element lies in the page of that element, so it is read whole; lanes
-    // past the slice re-read chunk 0 (valid: L > k >= 1).  All loads are
-    // issued before any is used.
+    // element is read whole; lanes past the slice re-read chunk 0 (valid:
+    // L > k >= 1) and hold empty slots.  All loads are issued before any is
+    // used.
     auto load_tile = [&](int c_tile) {
-        const char* const base = reinterpret_cast<const char*>(pa);  // uniform base, 32-bit offsets
 #pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {  // raw bits straight into the key registers
+        for (int j = 0; j < CHUNKS; ++j) {
             const int c = c_tile + j * BLOCK + tid;
             const uint32_t byte_off = (uint32_t)(c < c_end ? c : 0) * 16u;
             const uint4 v = *reinterpret_cast<const uint4*>(base + byte_off);
@@ -428,7 +383,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             keys[4 * j + 3] = v.w;
         }
 #pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {  // then mapped in place
+        for (int j = 0; j < CHUNKS; ++j) {
             const int c = c_tile + j * BLOCK + tid;
             if (c >= cf_lo && c < cf_hi) {
 #pragma unroll
@@ -443,43 +398,16 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
     };
-    // f(key, index) for every element of one tile; element e of chunk j has
-    // index ibase + 4 * BLOCK * j + e.
-    auto visit_tile = [&](int c_tile, auto&& f) {
-        int ibase = 4 * (c_tile + tid) - off;
-        __asm__ volatile("" : "+v"(ibase));  // indices are recomputed per visit, never kept live
-#pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f(keys[4 * j + e], ibase + 4 * BLOCK * j + e);
-            // keep each chunk's temporaries local: without this the scheduler
-            // hoists every element's address ahead of the LDS operations
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // Visit every slot of the slice (uniform trip count across the WG).
+    // f(key, ~index) for every slot of the slice, tile by tile; element e of
+    // chunk j of a tile has index ibase + 4 * BLOCK * j + e.
     auto visit = [&](auto&& f) {
-        if constexpr (RESIDENT) {
-            visit_tile(c_begin, f);
-        } else {
-            for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
-                load_tile(ct);
-                visit_tile(ct, f);
-            }
-        }
-    };
-
-    // f(key) for every slot of the chunks in [c_begin, c_end): chunks past
-    // the slice are skipped (one test per chunk, not per element)
-    auto visit_chunks = [&](auto&& f) {
         auto tile = [&](int c_tile) {
+            int ibase = 4 * (c_tile + tid) - off;
+            __asm__ volatile("" : "+v"(ibase));  // indices are recomputed per visit, never kept live
 #pragma unroll
             for (int j = 0; j < CHUNKS; ++j) {
-                if (c_tile + j * BLOCK + tid < c_end) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) f(keys[4 * j + e]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int e = 0; e < 4; ++e) f(keys[4 * j + e], ~(uint32_t)(ibase + 4 * BLOCK * j + e));
             }
         };
         if constexpr (RESIDENT) {
@@ -491,319 +419,247 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
     };
-
-    if constexpr (RESIDENT) load_tile(c_begin);
-
-    // ---------------- screening rounds over the whole row
-    Prefix pf{0u, 0u, 0u, 0u, 0};
-    uint32_t need = (uint32_t)k;
-    int round = 0;
-    bool all_sel = false;
-    for (;;) {
+    // f(key) for every slot of the chunks in [c_begin, c_end)
+    auto visit_chunks = [&](auto&& f) {
+        auto tile = [&](int c_tile) {
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                if (c_tile + j * BLOCK + tid < c_end) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f(keys[4 * j + e]);
+                }
+            }
+        };
         if constexpr (RESIDENT) {
-            // Opaque to the optimiser: stops it from hoisting per-element
-            // values (one lane mask or VGPR per element) out of the rounds.
+            tile(c_begin);
+        } else {
+            for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
+                load_tile(ct);
+                tile(ct);
+            }
+        }
+    };
+    auto opaque_keys = [&]() {
+        if constexpr (RESIDENT) {
+            // stops the optimiser from hoisting per-element values out of
+            // the passes (one VGPR per element and pass)
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
         }
-        int width;
-        if (pf.r == 0) {
-            // first digit: every slot adds into bin (key >> (32 - FIRST_BITS));
-            // empty slots (key 0) land in bin 0 and are subtracted after
-            width = FIRST_BITS;
-            for (int i = tid; i < H0_WORDS / 4; i += BLOCK) reinterpret_cast<uint4*>(s_big.h0)[i] = uint4{0u, 0u, 0u, 0u};
-            for (int i = H0_WORDS / 4 * 4 + tid; i < H0_WORDS; i += BLOCK) s_big.h0[i] = 0u;
-            lds_sync();
-            uint32_t* const hc = s_big.h0 + (tid % NC0) * (NB0 + 1);
-            visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> (32 - FIRST_BITS)], 1u); });
-            lds_sync();
-            select_bin<BLOCK, NB0, NC0>(s_big.h0, n_empty, need, G, ws, ws ? ws->hist0 : nullptr,
-                                        FIRST_BITS == 8 ? kMergeCopies : 1, w, round, s_sel, s_scan, P.status);
-        } else {
-            width = digit_width(pf.r);
-            const int sh = 64 - pf.r - width;
-            const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < H8_WORDS / 4; i += BLOCK) reinterpret_cast<uint4*>(s_big.h8)[i] = uint4{0u, 0u, 0u, 0u};
-            for (int i = H8_WORDS / 4 * 4 + tid; i < H8_WORDS; i += BLOCK) s_big.h8[i] = 0u;
-            lds_sync();
-            uint32_t* const hc = s_big.h8 + (tid % NC8) * 257;
-            if (sh >= 32) {
-                const int ks = sh - 32;
-                const uint32_t km = pf.kmask, kp = pf.kpfx;
-                visit([&](uint32_t key, int) {
-                    if ((key != 0u) & ((key & km) == kp)) atomicAdd(&hc[(key >> ks) & dmask], 1u);
-                });
-            } else {
-                const uint32_t kp = pf.kpfx, im = pf.imask, ip = pf.ipfx;
-                visit([&](uint32_t key, int idx) {
-                    const uint32_t ni = ~(uint32_t)idx;
-                    if ((key != 0u) & (key == kp) & ((ni & im) == ip)) atomicAdd(&hc[(ni >> sh) & dmask], 1u);
-                });
-            }
-            lds_sync();
-            select_bin<BLOCK, 256, NC8>(s_big.h8, 0u, need, G, ws, ws ? &ws->hist[round - 1][0][0] : nullptr,
-                                        kMergeCopies, w, round, s_sel, s_scan, P.status);
-        }
-        const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
+    };
+
+    auto clear_hist = [&]() {  // 16-byte LDS stores
+        uint4* const h4 = reinterpret_cast<uint4*>(sm.hist);
+        for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        if (tid < (kCopies * 257) % 4) sm.hist[kCopies * 257 / 4 * 4 + tid] = 0u;
+    };
+
+    if constexpr (RESIDENT) load_tile(c_begin);
+
+    // ---------------- screening rounds over the row
+    Prefix pf{0u, 0u, 0u, 0u};
+    uint32_t need = (uint32_t)k;  // rank still to place, counted inside the current bucket
+    uint32_t W = 0;               // winners placed so far (output positions [0, W))
+    uint32_t hb = 0;              // size of the current bucket
+    int R = 0;                    // last round done
+    bool whole = false;           // the last bucket is taken whole
+    for (int r = 0;; ++r) {
+        opaque_keys();
+        clear_hist();
         lds_sync();
+        uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
+        if (r == 0) {
+            // every slot of the slice's chunks adds into its top byte's bin;
+            // the few empty ones (key 0) land in bin 0 and are subtracted
+            // after.  Chunks past the slice are skipped (one test per chunk).
+            visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> 24], 1u); });
+        } else if (r < 4) {
+            const int sh = digit_shift(r, idx_bits);
+            visit([&](uint32_t key, uint32_t) {
+                if ((key != 0u) & ((key & pf.kmask) == pf.kpfx)) atomicAdd(&hc[(key >> sh) & 0xFFu], 1u);
+            });
+        } else {
+            const int sh = digit_shift(r, idx_bits);
+            visit([&](uint32_t key, uint32_t ni) {
+                if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
+            });
+        }
+        lds_sync();
+        uint32_t b, above;
+        threshold<BLOCK>(sm, r, r == 0 ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status, b, above, hb);
         need -= above;
-        pf.add_digit(b, width, P.idx_bits);
-        ++round;
-        if (hb == need) { all_sel = true; break; }
-        if (hb <= (uint32_t)kCap || pf.r >= 64 || round > kMaxPasses) break;
+        W += above;
+        pf.add(r, b, idx_bits);
+        R = r;
+        if (hb == need) { whole = true; break; }
+        if (hb <= (uint32_t)kCap || r + 1 >= nrounds) break;
     }
 
     // ---------------- collection over the row
-    // Selected = composite prefix at or above the threshold prefix: every
-    // element above the bucket plus the bucket itself.  They are staged as
-    // (key << 32) | ~index; the finisher splits them.
-    const bool key_only = pf.imask == 0u;
-    const uint32_t lo = pf.kpfx > 1u ? pf.kpfx : 1u;
-    auto selected = [&](uint32_t key, int idx) -> bool {
-        if (key_only) return key >= lo;
-        return (key != 0u) & ((key > pf.kpfx) | ((key == pf.kpfx) & ((~(uint32_t)idx & pf.imask) >= pf.ipfx)));
-    };
-    uint32_t nsel = 0;
-    if constexpr (RESIDENT) {
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
+    // Winners go to the output; the bucket goes to the output when taken
+    // whole, else to the candidate buffer (LDS) or the row's stage (G > 1).
+    const bool idx_rounds = R >= 4;
+    uint32_t bslot;  // position counter of the bucket: its bin in round R
+    {
+        const int s = digit_shift(R, idx_bits);
+        bslot = (uint32_t)R * 256u + ((R < 4 ? (pf.kpfx >> s) : (pf.ipfx >> s)) & 0xFFu);
     }
-    if (key_only) visit([&](uint32_t key, int) { nsel += key >= lo; });
-    else visit([&](uint32_t key, int idx) { nsel += selected(key, idx); });
-    uint32_t off_sel, unused, tot_sel, unused2;
-    block_scan2<BLOCK>(nsel, 0u, s_scan, off_sel, unused, tot_sel, unused2);
-    bool in_lds = (G == 1) && tot_sel <= (uint32_t)STAGE;
-    uint64_t* const gstage = P.stage ? P.stage + (size_t)row * (size_t)P.stage_cap : nullptr;
-    uint32_t cap = in_lds ? (uint32_t)STAGE : (uint32_t)P.stage_cap;
-    if (!in_lds && !gstage) cap = 0;
-    if (G > 1) {
-        if (tid == 0) s_bc[0] = tot_sel ? add_dev(&ws->reserve, tot_sel) : 0u;
-        lds_sync();
-        off_sel += uniform(s_bc[0]);
-    }
-    // Capacity holds by construction (the rounds end with the bucket at most
-    // kCap, so at most k + kCap entries); checked once, never per element.
-    const bool fits = tot_sel <= cap;
-    if (!fits && tid == 0) raise_flag(P.status, kFlagCapacity);
-    if constexpr (RESIDENT) {  // no per-element result of the count pass stays live
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
-    }
-    // one write loop per destination; per-thread loops: no barrier or wave
-    // operation inside.  The key is copied before it is paired with the
-    // index, so resident keys are not pinned to the high half of a register
-    // pair (one extra VGPR per key).
-    auto entry = [](uint32_t key, int idx) -> uint64_t {
-        uint32_t kc = key;
-        __asm__ volatile("" : "+v"(kc));
-        return ((uint64_t)kc << 32) | (uint64_t)(~(uint32_t)idx);
-    };
-    if (fits && nsel) {
-        if (!key_only) {
-            visit([&](uint32_t key, int idx) {
-                if (selected(key, idx)) {
-                    const uint64_t ck = entry(key, idx);
-                    if (in_lds) s_big.stage[off_sel] = ck;
-                    else st_dev(&gstage[off_sel], ck);
-                    ++off_sel;
-                }
-            });
-        } else if (in_lds) {
-            visit([&](uint32_t key, int idx) {
-                if (key >= lo) s_big.stage[off_sel++] = entry(key, idx);
-            });
-        } else if (G > 1) {  // read by another WG: device-scope stores
-            visit([&](uint32_t key, int idx) {
-                if (key >= lo) st_dev(&gstage[off_sel++], entry(key, idx));
-            });
+    uint64_t* const gstage = multi ? &ws->stage[p][0] : nullptr;
+    bool overflow = false;
+    opaque_keys();
+    visit([&](uint32_t key, uint32_t ni) {
+        uint32_t slot = bslot;
+        const uint32_t cls = classify(key, ni, pf, idx_rounds, idx_bits, &slot);
+        if (cls == 0u) return;
+        // rank inside the WG's range of the slot: one LDS atomic per element
+        // (lanes of a wave on different slots do not wait for each other)
+        const uint32_t pos = atomicAdd(&sm.pos[slot], 1u);
+        if (cls == 1u || whole) {
+            if (pos < (uint32_t)k) out[pos] = (int32_t)~ni;
+            else overflow = true;
         } else {
-            visit([&](uint32_t key, int idx) {
-                if (key >= lo) st_dev(&gstage[off_sel++], entry(key, idx));
-            });
+            const uint64_t comp = ((uint64_t)key << 32) | (uint64_t)ni;
+            if (pos < (uint32_t)kCap) {
+                if (multi) st_dev(&gstage[pos], comp);
+                else sm.cand[pos] = comp;
+            } else {
+                overflow = true;
+            }
         }
-    }
+    });
+    if (overflow) raise_flag(P.status, kFlagCapacity);
 
-    if (!in_lds) wait_memory();  // the staging area is read by other threads (or WGs) next
-    uint32_t m_sel = tot_sel;  // staged entries of the row
-    if (G > 1) {
-        // the last WG of the row to get here finishes it and clears the workspace
-        wait_memory();
-        lds_sync();
-        if (tid == 0) s_bc[1] = (add_dev(&ws->done, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
-        lds_sync();
-        if (uniform(s_bc[1]) == 0u) return;
-        m_sel = uniform(ld_dev(&ws->reserve));
-        if (m_sel > cap) m_sel = cap;
-        if (m_sel <= (uint32_t)STAGE) {
-            // the whole staging area on chip: eight independent loads in
-            // flight per thread per step instead of one dependent chain
-            for (uint32_t i0 = 0; i0 < m_sel; i0 += 8u * BLOCK) {
+    if (multi && w != 0) return;  // WG 0 finishes the row
+
+    // ---------------- on-chip finish of the last bucket
+    if (!whole) {
+        uint32_t m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
+        if (multi) {
+            // pull the staged bucket: every entry is non-zero once written;
+            // one load per entry in flight, then a bounded re-poll of the
+            // few entries not written yet
+            for (uint32_t i0 = 0; i0 < m; i0 += 8u * BLOCK) {
                 uint64_t v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + u * BLOCK + tid;
-                    v[u] = i < m_sel ? ld_dev(&gstage[i]) : 0ull;
+                for (int u = 0; u < 8; ++u) {  // eight loads in flight per thread
+                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                    v[u] = i < m ? ld_dev(&gstage[i]) : 0ull;
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + u * BLOCK + tid;
-                    if (i < m_sel) s_big.stage[i] = v[u];
+                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                    if (i < m) sm.cand[i] = v[u];
                 }
             }
-            in_lds = true;
-        }
-    }
-    lds_sync();
-    if (m_sel > cap) m_sel = cap;
-
-    // ---------------- on-chip finish
-    // Two-way partition of n entries (get(i) supplies entry i): cls(v) is 1
-    // (-> putA), 2 (-> putB) or 0 (dropped).  Positions follow entry order
-    // through a block scan, so the order is reproducible.  Loads are taken
-    // eight per thread at a time before any store, so they overlap instead
-    // of waiting behind the previous entry's LDS store.  When a total would
-    // exceed its bound, a flag is raised and nothing is written.
-    constexpr int U = 8;
-    auto partition = [&](uint32_t n, auto&& get, auto&& cls, auto&& putA, auto&& putB, uint32_t capA,
-                         uint32_t capB, uint32_t& tA, uint32_t& tB) {
-        uint32_t ca = 0, cb = 0;
-        for (uint32_t i0 = 0; i0 < n; i0 += U * BLOCK) {
-            uint64_t v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t i = i0 + u * BLOCK + tid;
-                v[u] = i < n ? get(i) : 0ull;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t c = (i0 + u * BLOCK + tid < n) ? cls(v[u]) : 0u;
-                ca += c == 1u;
-                cb += c == 2u;
-            }
-        }
-        uint32_t oa, ob;
-        block_scan2<BLOCK>(ca, cb, s_scan, oa, ob, tA, tB);
-        const bool ok = tA <= capA && tB <= capB;
-        if (!ok && tid == 0) raise_flag(P.status, kFlagCapacity);
-        if (ok && (ca | cb)) {
-            for (uint32_t i0 = 0; i0 < n; i0 += U * BLOCK) {
-                uint64_t v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t i = i0 + u * BLOCK + tid;
-                    v[u] = i < n ? get(i) : 0ull;
+            lds_sync();
+            for (uint32_t i = tid; i < m; i += BLOCK) {
+                if (sm.cand[i] != 0ull) continue;
+                uint64_t x;
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                while ((x = ld_dev(&gstage[i])) == 0ull) {
+                    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+                        raise_flag(P.status, kFlagTimeout);
+                        break;
+                    }
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t c = (i0 + u * BLOCK + tid < n) ? cls(v[u]) : 0u;
-                    if (c == 1u) putA(oa++, v[u]);
-                    else if (c == 2u) putB(ob++, v[u]);
-                }
+                sm.cand[i] = x;
             }
         }
         lds_sync();
-    };
-
-    // Split the staged entries: above the threshold prefix (or the whole
-    // bucket when it is taken entirely) -> output; in the bucket -> LDS
-    // candidates.
-    const uint64_t pfx0 = pf.pfx64(), pmask0 = pf.mask64();
-    const uint32_t nwin_total = (uint32_t)k - (all_sel ? 0u : need);
-    uint32_t tw = 0, tb = 0;
-    auto put_out = [&](uint32_t pos, uint64_t v) { out[pos] = (int32_t)~(uint32_t)v; };
-    auto put_cand = [&](uint32_t pos, uint64_t v) { s_cand[pos] = v; };
-    auto cls0 = [&](uint64_t v) -> uint32_t {
-        const uint64_t pm = v & pmask0;
-        if ((pm > pfx0) | (all_sel & (pm == pfx0))) return 1u;
-        return ((!all_sel) & (pm == pfx0)) ? 2u : 0u;
-    };
-    if (in_lds) {
-        partition(m_sel, [&](uint32_t i) { return s_big.stage[i]; }, cls0, put_out, put_cand, nwin_total,
-                  (uint32_t)kCap, tw, tb);
-    } else {
-        partition(m_sel, [&](uint32_t i) { return ld_dev(&gstage[i]); }, cls0, put_out, put_cand, nwin_total,
-                  (uint32_t)kCap, tw, tb);
-    }
-    if (tw != nwin_total && tid == 0) raise_flag(P.status, kFlagCapacity);
-
-    if (!all_sel && tb <= (uint32_t)kCap) {
-        const uint32_t m = tb;
-        int32_t* __restrict__ fout = out + nwin_total;  // `need` slots remain
-        const uint32_t need0 = need;
-        uint64_t pfx = pfx0, pmask = pmask0;
-        bool fin_all = false;
-        uint32_t mb = m;
-        int fround = 0;
-        while (mb > (uint32_t)kSmall && pf.r < 64) {
-            const int width = digit_width(pf.r);
-            const int sh = 64 - pf.r - width;
-            const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < kFinCopies * 257; i += BLOCK) s_fin_hist[i] = 0u;
-            lds_sync();
-            uint32_t* const fc = s_fin_hist + (tid % kFinCopies) * 257;
-            for (uint32_t i0 = 0; i0 < m; i0 += U * BLOCK) {
-                uint64_t v[U];
+        const int idxb = idx_bits;
+        auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
+        auto c_digit = [&](uint64_t c, int r) -> uint32_t {
+            const int s = digit_shift(r, idxb);
+            return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & 0xFFu;
+        };
+        // f(entry) for every candidate, four LDS loads in flight per thread
+        // (entries past m read as 0, which matches no prefix)
+        auto for_each_cand = [&](auto&& f) {
+            for (uint32_t i0 = 0; i0 < m; i0 += 4u * BLOCK) {
+                uint64_t c[4];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t i = i0 + u * BLOCK + tid;
-                    v[u] = i < m ? s_cand[i] : 0ull;
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                    c[u] = i < m ? sm.cand[i] : 0ull;
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if ((i0 + u * BLOCK + tid < m) & ((v[u] & pmask) == pfx))
-                        atomicAdd(&fc[(uint32_t)(v[u] >> sh) & dmask], 1u);
-                }
+                for (int u = 0; u < 4; ++u) f(c[u]);
             }
+        };
+        int r = R + 1;
+        bool done = false;
+        uint32_t mb = hb;  // entries still matching the prefix
+        while (mb > (uint32_t)kSmall && r < nrounds) {
+            clear_hist();
             lds_sync();
-            select_bin<BLOCK, 256, kFinCopies>(s_fin_hist, 0u, need, 1, nullptr, nullptr, 1, 0, fround,
-                                               s_sel, s_scan, P.status);
-            const uint32_t b = uniform(s_sel[0]), above = uniform(s_sel[1]), hb = uniform(s_sel[2]);
+            uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
+            for_each_cand([&](uint64_t c) {
+                if (c_match(c)) atomicAdd(&hc[c_digit(c, r)], 1u);
+            });
             lds_sync();
-            need -= above;
-            pf.add_digit(b, width, P.idx_bits);
-            pfx = pf.pfx64();
-            pmask = pf.mask64();
-            ++fround;
-            mb = hb;
-            if (hb == need) { fin_all = true; break; }
+            uint32_t b, above, nb;
+            threshold<BLOCK>(sm, r, 0u, need, W, nullptr, 0, 1, 0, 1, P.status, b, above, nb);
+            const uint32_t need2 = need - above;
+            const bool all = nb == need2;
+            // winners of this round (digit above b), and the bin itself when taken whole
+            for_each_cand([&](uint64_t c) {
+                const uint32_t d = c_digit(c, r);
+                if (c_match(c) && (d > b || (all && d == b))) {
+                    const uint32_t pos = atomicAdd(&sm.pos[r * 256 + (int)d], 1u);
+                    if (pos < (uint32_t)k) out[pos] = (int32_t)~(uint32_t)c;
+                    else raise_flag(P.status, kFlagCapacity);
+                }
+            });
+            need = need2;
+            W += above;
+            pf.add(r, b, idxb);
+            mb = nb;
+            ++r;
+            lds_sync();
+            if (all) { done = true; break; }
         }
-        // winners among the candidates, and the small bucket to rank exactly
-        uint32_t tfw = 0, tfb = 0;
-        partition(
-            m, [&](uint32_t i) { return s_cand[i]; },
-            [&](uint64_t v) -> uint32_t {
-                const uint64_t pm = v & pmask;
-                if ((pm > pfx) | (fin_all & (pm == pfx))) return 1u;
-                return ((!fin_all) & (pm == pfx)) ? 2u : 0u;
-            },
-            [&](uint32_t pos, uint64_t v) { fout[pos] = (int32_t)~(uint32_t)v; },
-            [&](uint32_t pos, uint64_t v) { s_small[pos] = v; }, need0, (uint32_t)kSmall, tfw, tfb);
-        if (!fin_all && tfb <= (uint32_t)kSmall) {
-            const uint32_t ms = tfb;
-            const uint32_t base = tfw;
+        if (!done) {
+            // the few candidates still matching: exact rank by comparison
+            if (tid == 0) sm.sel[3] = 0u;
+            lds_sync();
+            for_each_cand([&](uint64_t c) {
+                if (c_match(c)) {
+                    const uint32_t pos = atomicAdd(&sm.sel[3], 1u);
+                    if (pos < (uint32_t)kSmall) sm.small[pos] = c;
+                }
+            });
+            lds_sync();
+            uint32_t ms = sm.sel[3];
+            if (ms > (uint32_t)kSmall) {
+                if (tid == 0) raise_flag(P.status, kFlagCapacity);
+                ms = kSmall;
+            }
             for (uint32_t i = tid; i < ms; i += BLOCK) {
-                const uint64_t c = s_small[i];
+                const uint64_t c = sm.small[i];
                 uint32_t rank = 0;
 #pragma unroll 8
-                for (uint32_t j = 0; j < ms; ++j) rank += s_small[j] > c;
-                const uint32_t pos = base + rank;
-                if ((rank < need) & (pos < need0)) fout[pos] = (int32_t)~(uint32_t)c;
+                for (uint32_t q = 0; q < ms; ++q) rank += sm.small[q] > c;
+                if (rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
             }
         }
     }
 
-    if (G > 1) {
-        // leave the row's workspace zeroed for the next call
-        for (int i = tid; i < 4096; i += BLOCK) st_dev(&ws->hist0[i], 0u);
-        const int ncopy = G < kMergeCopies ? G : kMergeCopies;
-        for (int i = tid; i < (round - 1) * kMergeCopies * 256; i += BLOCK) {
-            const int c = (i / 256) % kMergeCopies;
-            if (c < ncopy) st_dev(&ws->hist[i / (kMergeCopies * 256)][c][i % 256], 0u);
-        }
-        if (tid < kMergeCopies) st_dev(&ws->arrive[tid * kLineWords], 0u);
+    if (multi) {
+        // clear the half the previous launch used, record this launch's use
+        // and hand the other half to the next launch
+        const int op = p ^ 1;
+        const uint32_t ur = min(ld_dev(&ws->used_rounds[op]), (uint32_t)kRounds);
+        const uint32_t uc = min(ld_dev(&ws->used_copies[op]), (uint32_t)kMergeCopies);
+        const uint32_t us = min(ld_dev(&ws->used_stage[op]), (uint32_t)kCap);
+        uint64_t* const h = &ws->hist[op][0][0][0];
+        for (uint32_t i = tid; i < ur * kMergeCopies * 256u; i += BLOCK)
+            if ((i / 256u) % kMergeCopies < uc) st_dev(&h[i], (uint64_t)0);
+        for (uint32_t i = tid; i < us; i += BLOCK) st_dev(&ws->stage[op][i], (uint64_t)0);
         if (tid == 0) {
-            st_dev(&ws->done, 0u);
-            st_dev(&ws->reserve, 0u);
+            st_dev(&ws->used_rounds[p], (uint32_t)(R + 1));
+            st_dev(&ws->used_copies[p], (uint32_t)C);
+            st_dev(&ws->used_stage[p], whole ? 0u : (hb > (uint32_t)kCap ? (uint32_t)kCap : hb));
+            st_dev(&ws->parity, (uint32_t)op);
         }
     }
 }
@@ -813,40 +669,34 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
 using OccFn = int (*)(int*, int);
 
-template <int B, int I, int F, bool R, bool M>
+template <int B, int I, bool R>
 void launch_variant(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    hipLaunchKernelGGL((topk_select_kernel<B, I, F, R, M>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((topk_select_kernel<B, I, R>), grid, block, 0, s, p);
 }
 
-template <int B, int I, int F, bool R, bool M>
+template <int B, int I, bool R>
 int occupancy_variant(int* nb, int block) {
-    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, F, R, M>, block, 0);
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, R>, block, 0);
 }
 
 struct Variant {
-    int block, items, first_bits, resident, multi;
-    int stage_lds;  // staged entries a one-WG row keeps in LDS
+    int block, items, resident;
     LaunchFn launch;
     OccFn occupancy;
 };
 
-constexpr int stage_lds_of(int b, int i, bool r) { return (r && b * i < kStageLds) ? b * i : kStageLds; }
-
-#define TKS_VARIANT(B, I, F, R, M)                                                               \
-    {B, I, F, R ? 1 : 0, M ? 1 : 0, stage_lds_of(B, I, R), &launch_variant<B, I, F, R, M>, \
-     &occupancy_variant<B, I, F, R, M>}
+#define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
 const Variant kVariants[] = {
-    TKS_VARIANT(256, 4, 8, true, true),      // 0: 1024 logits per WG, 8-bit first digit (many WGs per row)
-    TKS_VARIANT(256, 8, 8, true, true),      // 1: 2048
-    TKS_VARIANT(256, 16, 8, true, true),     // 2: 4096
-    TKS_VARIANT(512, 32, 8, true, true),     // 3: 16384
-    TKS_VARIANT(512, 64, 8, true, true),     // 4: 32768
-    TKS_VARIANT(256, 16, 12, true, false),   // 5: 4096, 12-bit first digit, one WG per row
-    TKS_VARIANT(512, 32, 12, true, false),   // 6: 16384
-    TKS_VARIANT(512, 64, 12, true, true),    // 7: 32768 (also several WGs per row)
-    TKS_VARIANT(1024, 32, 12, true, false),  // 8: 32768
-    TKS_VARIANT(1024, 16, 12, false, true),  // 9: streaming, 16384 per tile
-    TKS_VARIANT(256, 16, 8, false, true),    // 10: streaming, 4096 per tile
+    TKS_VARIANT(512, 4, true),     // 0: 2048 logits per WG
+    TKS_VARIANT(512, 8, true),     // 1: 4096
+    TKS_VARIANT(1024, 4, true),    // 2: 4096
+    TKS_VARIANT(1024, 8, true),    // 3: 8192
+    TKS_VARIANT(512, 16, true),    // 4: 8192
+    TKS_VARIANT(1024, 16, true),   // 5: 16384
+    TKS_VARIANT(512, 32, true),    // 6: 16384
+    TKS_VARIANT(1024, 32, true),   // 7: 32768
+    TKS_VARIANT(1024, 16, false),  // 8: streaming, 16384 per tile
+    TKS_VARIANT(256, 16, false),   // 9: streaming, 4096 per tile
 };
 #undef TKS_VARIANT
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
@@ -856,17 +706,12 @@ struct DeviceInfo {
     int capacity[kNumVariants] = {};  // co-resident WGs per variant on the whole device
 };
 
-// Scratch of one (device, stream).  `base` holds the status word and the
-// per-row workspaces at fixed offsets (row r always at the same address,
-// whatever the row count of a call); it is zeroed when allocated and left
-// zeroed by every kernel.  `stage` holds staged entries; it needs no
-// initial value and lives in its own allocation so that it never overlaps
-// a row workspace of a later call.
+// Scratch of one (device, stream): the status word, then one RowWorkspace
+// per row (row r always at the same address, whatever the row count of a
+// call).  Zeroed when allocated; kernels keep it consistent across calls.
 struct Workspace {
     void* base = nullptr;
     size_t bytes = 0;
-    void* stage = nullptr;
-    size_t stage_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -884,7 +729,10 @@ int device_info(int dev, DeviceInfo** out) {
         for (int v = 0; v < kNumVariants; ++v) {
             int nb = 0;
             if (kVariants[v].occupancy(&nb, kVariants[v].block) != (int)hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            d.capacity[v] = nb * d.cus;
+            // WGs that are certainly co-resident: what the occupancy query
+            // allows, but never more than one per CU (full occupancy is not
+            // always reached for large WGs in practice)
+            d.capacity[v] = nb < 1 ? 0 : d.cus;
         }
         it = g_dev.emplace(dev, d).first;
     }
@@ -906,7 +754,8 @@ int idx_bits_for(int32_t n) {
     uint32_t top = (uint32_t)(n - 1);
     int bits = 0;
     while (top) { ++bits; top >>= 1; }
-    return (bits + 7) / 8 * 8;
+    bits = (bits + 7) / 8 * 8;
+    return bits < 8 ? 8 : bits;
 }
 
 struct Launch {
@@ -922,12 +771,8 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
     const Variant& var = kVariants[v];
     const int64_t tile_chunks = (int64_t)var.block * (var.items / 4);
     int64_t cpw = (maxc + G - 1) / G;
-    if (var.resident) {
-        if (cpw > tile_chunks) return TOPK_SELECT_ERROR_INVALID_VALUE;
-        cpw = tile_chunks;
-    }
+    if (var.resident && cpw > tile_chunks) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (cpw < 1) cpw = 1;
-    if (G > 1 && !var.multi) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (G > 1 && rows * (int64_t)G > (int64_t)d.capacity[v]) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows * (int64_t)G > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
     L->variant = v;
@@ -936,33 +781,35 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
     return TOPK_SELECT_SUCCESS;
 }
 
-// Default shape (measured on MI355X: a cross-workgroup round costs a few
-// microseconds whatever the split, so few rows use few, large workgroups).
-// Many rows: one WG per row with the 12-bit first digit when the row fits
-// one resident tile, else several 12-bit WGs per row when they can all be
-// resident, else streaming.  Few rows: 512-thread WGs holding 16K (then
-// 32K, then smaller) logits each, as many per row as the row needs.
+// Default shape (measured on MI355X).  A cross-workgroup merge round costs
+// about the same for any split, while the per-pass time falls with the
+// slice, so few rows are spread over many WGs of about 2K-8K logits each
+// (1024 threads once a row uses more than 16 WGs).  Many rows: the fewest
+// resident WGs per row that can all be co-resident, else streaming WGs.
 int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
-    const int target = d.cus;
     auto tile_chunks = [](int v) { return (int64_t)kVariants[v].block * (kVariants[v].items / 4); };
-    if (rows >= target / 2) {
-        const int one_wg[] = {5, 6, 8};
-        for (int v : one_wg)
-            if (maxc <= tile_chunks(v)) return check_shape(d, rows, maxc, v, 1, L);
-        const int split[] = {7};
-        for (int v : split) {
-            const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
-            if (rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
-        }
-    } else {
-        const int few[] = {3, 4, 2, 1, 0};
-        for (int v : few) {
-            const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
-            if (G == 1 || rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
+    if (rows * 8 <= d.cus) {
+        int64_t G = (maxc + 511) / 512;  // about 2K logits per WG
+        if (G > 128) G = 128;
+        if (G > d.cus / rows) G = d.cus / rows;
+        if (G < 1) G = 1;
+        const int64_t per = (maxc + G - 1) / G;
+        const int v512[] = {0, 1, 4, 6, 7}, v1024[] = {2, 3, 5, 7};
+        if (G <= 16) {
+            for (int v : v512)
+                if (per <= tile_chunks(v)) return check_shape(d, rows, maxc, v, (int)G, L);
+        } else {
+            for (int v : v1024)
+                if (per <= tile_chunks(v)) return check_shape(d, rows, maxc, v, (int)G, L);
         }
     }
+    const int order_many[] = {7, 5, 3, 1, 0};
+    for (int v : order_many) {
+        const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
+        if (G == 1 || rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
+    }
     // streaming: as many WGs per row as can be co-resident, at least one
-    const int v = (maxc >= 16384) ? 9 : 10;
+    const int v = (maxc >= 16384) ? 8 : 9;
     int64_t G = d.capacity[v] / (rows > 0 ? rows : 1);
     const int64_t gmax = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
     if (G > gmax) G = gmax;
@@ -986,33 +833,28 @@ int validate(const float* logits, int32_t rows, int32_t n, const int32_t* length
     return TOPK_SELECT_SUCCESS;
 }
 
-int grow(void** ptr, size_t* have, size_t need, bool zero, hipStream_t stream) {
-    if (*have >= need) return TOPK_SELECT_SUCCESS;
-    if (*ptr) {
-        if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-        (void)hipFree(*ptr);
-        *ptr = nullptr;
-        *have = 0;
-    }
-    void* p = nullptr;
-    if (hipMalloc(&p, need) != hipSuccess) {
-        (void)hipGetLastError();
-        return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
-    }
-    if (zero && hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
-        (void)hipFree(p);
-        return TOPK_SELECT_ERROR_LAUNCH;
-    }
-    *ptr = p;
-    *have = need;
-    return TOPK_SELECT_SUCCESS;
-}
-
-int get_workspace(int dev, hipStream_t stream, size_t need, size_t stage_need, Workspace** out) {
+int get_workspace(int dev, hipStream_t stream, size_t need, Workspace** out) {
     Workspace& w = g_ws[{dev, (uintptr_t)stream}];
-    int rc = grow(&w.base, &w.bytes, need, true, stream);
-    if (rc == TOPK_SELECT_SUCCESS && stage_need) rc = grow(&w.stage, &w.stage_bytes, stage_need, false, stream);
-    if (rc != TOPK_SELECT_SUCCESS) return rc;
+    if (w.bytes < need) {
+        if (w.base) {
+            // the old workspace may still be in use by enqueued work
+            if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+            (void)hipFree(w.base);
+            w.base = nullptr;
+            w.bytes = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, need) != hipSuccess) {
+            (void)hipGetLastError();
+            return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
+        }
+        if (hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
+            (void)hipFree(p);
+            return TOPK_SELECT_ERROR_LAUNCH;
+        }
+        w.base = p;
+        w.bytes = need;
+    }
     *out = &w;
     return TOPK_SELECT_SUCCESS;
 }
@@ -1032,14 +874,10 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     rc = forced ? check_shape(*d, rows, maxc, forced->variant, forced->wgs_per_row, &L)
                 : choose_shape(*d, rows, maxc, &L);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
-    const Variant& var0 = kVariants[L.variant];
-    const bool need_stage = L.G > 1 || (int64_t)k + kCap > (int64_t)var0.stage_lds;
-    const int64_t stage_cap = need_stage ? (int64_t)k + kCap : 0;
+    const Variant& var = kVariants[L.variant];
     const size_t rows_bytes = L.G > 1 ? (size_t)rows * sizeof(RowWorkspace) : 0;
-    const size_t stage_bytes = (size_t)rows * (size_t)stage_cap * sizeof(uint64_t);
-    const size_t ws_bytes = kStatusBytes + rows_bytes;
     Workspace* w = nullptr;
-    rc = get_workspace(dev, stream, ws_bytes, stage_bytes, &w);
+    rc = get_workspace(dev, stream, kStatusBytes + rows_bytes, &w);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     char* base = reinterpret_cast<char*>(w->base);
     KParams P;
@@ -1048,15 +886,13 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.out = out;
     P.status = reinterpret_cast<uint32_t*>(base);
     P.ws = L.G > 1 ? reinterpret_cast<RowWorkspace*>(base + kStatusBytes) : nullptr;
-    P.stage = need_stage ? reinterpret_cast<uint64_t*>(w->stage) : nullptr;
     P.rows = rows;
     P.n = n;
     P.k = k;
     P.G = L.G;
     P.chunks_per_wg = L.chunks_per_wg;
     P.idx_bits = idx_bits_for(n);
-    P.stage_cap = (int32_t)stage_cap;
-    const Variant& var = var0;
+    P.mcopies = L.G <= 16 ? 1 : (L.G <= 32 ? 2 : kMergeCopies);
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
@@ -1104,7 +940,7 @@ int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* pla
         plan->block = tks::kVariants[L.variant].block;
         plan->items = tks::kVariants[L.variant].items;
         plan->resident = tks::kVariants[L.variant].resident;
-        plan->first_bits = tks::kVariants[L.variant].first_bits;
+        plan->first_bits = 8;
         return TOPK_SELECT_SUCCESS;
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
@@ -1120,7 +956,7 @@ int topk_select_variant_info(int32_t v, topk_select_plan_t* plan) {
     plan->block = tks::kVariants[v].block;
     plan->items = tks::kVariants[v].items;
     plan->resident = tks::kVariants[v].resident;
-    plan->first_bits = tks::kVariants[v].first_bits;
+    plan->first_bits = 8;
     return TOPK_SELECT_SUCCESS;
 }
 
@@ -1154,13 +990,12 @@ int topk_select_release_workspace(void) {
         std::lock_guard<std::mutex> lock(tks::g_mu);
         int rc = TOPK_SELECT_SUCCESS;
         for (auto& kv : tks::g_ws) {
-            if (kv.second.base || kv.second.stage) {
+            if (kv.second.base) {
                 int cur = 0;
                 (void)hipGetDevice(&cur);
                 (void)hipSetDevice(kv.first.first);
                 if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                if (kv.second.base && hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                if (kv.second.stage && hipFree(kv.second.stage) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+                if (hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
                 (void)hipSetDevice(cur);
             }
         }
