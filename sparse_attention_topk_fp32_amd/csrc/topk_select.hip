@@ -169,10 +169,25 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, uint32_t* s
     return pa + ia - a;
 }
 
-// Bit position of round r's digit inside its 32-bit word: rounds 0..3 cut
-// the key from the top, later rounds the varying low idx_bits of ~index
-// (its top 32 - idx_bits bits are ones for every valid index).
-__device__ __forceinline__ int digit_shift(int r, int idx_bits) { return r < 4 ? 24 - 8 * r : idx_bits - 8 - 8 * (r - 4); }
+// Digit schedule: rounds 0..3 cut the key from the top, the first digit
+// F bits wide (8 or 12) and the others 8 bits (the last key digit keeps what
+// is left); later rounds cut the varying low idx_bits of ~index (its top
+// 32 - idx_bits bits are ones for every valid index).  shift: bit position
+// of round r's digit inside its 32-bit word; width: its bits.
+template <int F>
+__device__ __forceinline__ int digit_shift(int r, int idx_bits) {
+    if (r < 4) {
+        const int s = 32 - F - 8 * r;
+        return s < 0 ? 0 : s;
+    }
+    return idx_bits - 8 - 8 * (r - 4);
+}
+template <int F>
+__device__ __forceinline__ int digit_width(int r) {
+    if (r == 0) return F;
+    if (r < 4) return min(8, 32 - F - 8 * (r - 1));
+    return 8;
+}
 __device__ __forceinline__ int num_rounds(int idx_bits) { return 4 + idx_bits / 8; }
 
 // The composite prefix resolved so far: key bits (kpfx under kmask) and
@@ -181,10 +196,11 @@ struct Prefix {
     uint32_t kpfx, kmask, ipfx, imask;
     // value selects only (a branch that picks the field to update would
     // put the struct in scratch memory)
+    template <int F>
     __device__ void add(int r, uint32_t b, int idx_bits) {
-        const int s = digit_shift(r, idx_bits);
+        const int s = digit_shift<F>(r, idx_bits);
         const bool in_key = r < 4;
-        const uint32_t bb = b << s, mm = 0xFFu << s;
+        const uint32_t bb = b << s, mm = ((1u << digit_width<F>(r)) - 1u) << s;
         kpfx |= in_key ? bb : 0u;
         kmask |= in_key ? mm : 0u;
         ipfx |= in_key ? 0u : bb;
@@ -194,9 +210,15 @@ struct Prefix {
     __device__ __forceinline__ bool match(uint32_t key, uint32_t ni) const {
         return (key != 0u) & ((key & kmask) == kpfx) & ((ni & imask) == ipfx);
     }
+    // Is the element above the prefix (a winner of some round done)?
+    __device__ __forceinline__ bool above(uint32_t key, uint32_t ni) const {
+        const uint32_t s = key & kmask;
+        return (s > kpfx) | ((s == kpfx) & ((ni & imask) > ipfx));
+    }
 };
 
-// Relation of an element to the prefix after rounds 0..R: returns 1 when it
+// Relation of an element to the prefix after rounds 0..R of the 8-bit
+// schedule: returns 1 when it
 // is above it (a winner; *slot = 256 * deciding round + its digit there),
 // 2 when it matches it (in the bucket), 0 otherwise.  Composites compare as
 // (key, ~index) pairs.
@@ -222,7 +244,7 @@ __device__ __forceinline__ uint32_t classify(uint32_t key, uint32_t ni, const Pr
     if (s < pf.ipfx) return 0u;
     const int lead = __builtin_clz(s ^ pf.ipfx) - (32 - idx_bits);  // leading bit inside the index digits
     const int r = 4 + lead / 8;
-    *slot = (uint32_t)r * 256u + ((ni >> digit_shift(r, idx_bits)) & 0xFFu);
+    *slot = (uint32_t)r * 256u + ((ni >> digit_shift<8>(r, idx_bits)) & 0xFFu);
     return 1u;
 }
 
@@ -234,8 +256,152 @@ struct Smem {
     uint64_t cand[kCap];                // final bucket, on chip
     uint64_t small[kSmall];             // last few candidates, ranked exactly
     uint32_t scan[BLOCK / 64];
-    uint32_t sel[4];                    // threshold bin, count above it, count in it, small count
+    uint32_t sel[4];                    // threshold bin, count above it, count in it
+    uint32_t ctr;                       // finisher position counter
 };
+
+// Thresholding step on one WG's own histogram: NB bins held as NC LDS
+// copies of stride STRIDE words.  Owner threads take NB / OWNERS bins each,
+// in descending bin order across threads, so one block scan over the
+// owners' sums locates the bin b that holds the element of rank `need`
+// (1-based, from the top).  Returns b, the count above b and the count in b.
+template <int BLOCK, int NB, int NC, int STRIDE>
+__device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_sub, uint32_t need, uint32_t* scan,
+                                             uint32_t* sel, uint32_t* status, uint32_t& b_out, uint32_t& above_out,
+                                             uint32_t& hb_out) {
+    constexpr int OWNERS = NB < BLOCK ? NB : BLOCK;
+    constexpr int OWN = NB / OWNERS;
+    static_assert(OWNERS % 64 == 0, "whole waves of owners");
+    const int t = threadIdx.x;
+    const bool owner = t < OWNERS;
+    uint32_t cnt[OWN];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) {
+        const int bin = NB - 1 - (t * OWN + i);
+        uint32_t c = 0;
+        if (owner) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q) c += h[q * STRIDE + bin];
+            if (bin == 0) c -= bin0_sub;
+        }
+        cnt[i] = c;
+        tot += c;
+    }
+    if (t == 0) sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
+    uint32_t above = block_exclusive_scan<OWNERS>(tot, scan);
+    if (owner && above < need && need <= above + tot) {
+#pragma unroll
+        for (int i = 0; i < OWN; ++i) {
+            if (above < need && need <= above + cnt[i]) {
+                sel[0] = (uint32_t)(NB - 1 - (t * OWN + i));
+                sel[1] = above;
+                sel[2] = cnt[i];
+            }
+            above += cnt[i];
+        }
+    }
+    lds_sync();
+    uint32_t b = uniform(sel[0]), ab = uniform(sel[1]), hb = uniform(sel[2]);
+    lds_sync();
+    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
+        if (t == 0) raise_flag(status, kFlagCapacity);
+        b = 0; ab = 0; hb = 0;
+    }
+    b_out = b;
+    above_out = ab;
+    hb_out = hb;
+}
+
+// On-chip finish of the final bucket: the m composites in cand all match
+// the prefix pf (rounds done: < r0); `need` of them remain to be selected,
+// at output positions W..W+need-1.  More digit rounds in LDS while more
+// than kSmall match, then an exact rank of the rest.  Uses the scratch
+// `hist` (kCopies x 257 words), `small`, `scan`, `sel` and the counter
+// `ctr`.  Every thread of the WG calls it.
+template <int BLOCK, int F>
+__device__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
+                              int idx_bits, uint32_t* hist, uint64_t* small, uint32_t* scan, uint32_t* sel,
+                              uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
+    const int tid = threadIdx.x;
+    const int nrounds = num_rounds(idx_bits);
+    auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
+    auto c_digit = [&](uint64_t c, int r) -> uint32_t {
+        const int s = digit_shift<F>(r, idx_bits);
+        return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & ((1u << digit_width<F>(r)) - 1u);
+    };
+    // f(entry) for every candidate, four LDS loads in flight per thread
+    // (entries past m read as 0, which matches no prefix)
+    auto for_each_cand = [&](auto&& f) {
+        for (uint32_t i0 = 0; i0 < m; i0 += 4u * BLOCK) {
+            uint64_t c[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                c[u] = i < m ? cand[i] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f(c[u]);
+        }
+    };
+    int r = r0;
+    uint32_t mb = m;  // entries still matching the prefix
+    while (mb > (uint32_t)kSmall && r < nrounds) {
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(hist);
+            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+            if (tid == 0) *ctr = 0u;
+        }
+        lds_sync();
+        uint32_t* const hc = hist + (tid % kCopies) * 257;
+        for_each_cand([&](uint64_t c) {
+            if (c_match(c)) atomicAdd(&hc[c_digit(c, r)], 1u);
+        });
+        lds_sync();
+        uint32_t b, above, nb;
+        local_select<BLOCK, 256, kCopies, 257>(hist, 0u, need, scan, sel, status, b, above, nb);
+        const uint32_t need2 = need - above;
+        const bool all = nb == need2;
+        // winners of this round (digit above b), and the bin itself when taken whole
+        for_each_cand([&](uint64_t c) {
+            const uint32_t d = c_digit(c, r);
+            if (c_match(c) && (d > b || (all && d == b))) {
+                const uint32_t pos = W + atomicAdd(ctr, 1u);
+                if (pos < (uint32_t)k) out[pos] = (int32_t)~(uint32_t)c;
+                else raise_flag(status, kFlagCapacity);
+            }
+        });
+        need = need2;
+        W += above;
+        pf.add<F>(r, b, idx_bits);
+        mb = nb;
+        ++r;
+        lds_sync();
+        if (all) return;
+    }
+    // the few candidates still matching: exact rank by comparison
+    if (tid == 0) *ctr = 0u;
+    lds_sync();
+    for_each_cand([&](uint64_t c) {
+        if (c_match(c)) {
+            const uint32_t pos = atomicAdd(ctr, 1u);
+            if (pos < (uint32_t)kSmall) small[pos] = c;
+        }
+    });
+    lds_sync();
+    uint32_t ms = *ctr;
+    if (ms > (uint32_t)kSmall) {
+        if (tid == 0) raise_flag(status, kFlagCapacity);
+        ms = kSmall;
+    }
+    for (uint32_t i = tid; i < ms; i += BLOCK) {
+        const uint64_t c = small[i];
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (uint32_t q = 0; q < ms; ++q) rank += small[q] > c;
+        if (rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
+    }
+}
 
 // Thresholding step for round r from the LDS histogram copies (the first
 // 256 threads own one bin each, thread t the bin 255 - t, so thread order is
@@ -474,12 +640,12 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             // after.  Chunks past the slice are skipped (one test per chunk).
             visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> 24], 1u); });
         } else if (r < 4) {
-            const int sh = digit_shift(r, idx_bits);
+            const int sh = digit_shift<8>(r, idx_bits);
             visit([&](uint32_t key, uint32_t) {
                 if ((key != 0u) & ((key & pf.kmask) == pf.kpfx)) atomicAdd(&hc[(key >> sh) & 0xFFu], 1u);
             });
         } else {
-            const int sh = digit_shift(r, idx_bits);
+            const int sh = digit_shift<8>(r, idx_bits);
             visit([&](uint32_t key, uint32_t ni) {
                 if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
             });
@@ -489,7 +655,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         threshold<BLOCK>(sm, r, r == 0 ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status, b, above, hb);
         need -= above;
         W += above;
-        pf.add(r, b, idx_bits);
+        pf.add<8>(r, b, idx_bits);
         R = r;
         if (hb == need) { whole = true; break; }
         if (hb <= (uint32_t)kCap || r + 1 >= nrounds) break;
@@ -501,7 +667,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     const bool idx_rounds = R >= 4;
     uint32_t bslot;  // position counter of the bucket: its bin in round R
     {
-        const int s = digit_shift(R, idx_bits);
+        const int s = digit_shift<8>(R, idx_bits);
         bslot = (uint32_t)R * 256u + ((R < 4 ? (pf.kpfx >> s) : (pf.ipfx >> s)) & 0xFFu);
     }
     uint64_t* const gstage = multi ? &ws->stage[p][0] : nullptr;
@@ -566,82 +732,8 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
         lds_sync();
-        const int idxb = idx_bits;
-        auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
-        auto c_digit = [&](uint64_t c, int r) -> uint32_t {
-            const int s = digit_shift(r, idxb);
-            return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & 0xFFu;
-        };
-        // f(entry) for every candidate, four LDS loads in flight per thread
-        // (entries past m read as 0, which matches no prefix)
-        auto for_each_cand = [&](auto&& f) {
-            for (uint32_t i0 = 0; i0 < m; i0 += 4u * BLOCK) {
-                uint64_t c[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                    c[u] = i < m ? sm.cand[i] : 0ull;
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) f(c[u]);
-            }
-        };
-        int r = R + 1;
-        bool done = false;
-        uint32_t mb = hb;  // entries still matching the prefix
-        while (mb > (uint32_t)kSmall && r < nrounds) {
-            clear_hist();
-            lds_sync();
-            uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
-            for_each_cand([&](uint64_t c) {
-                if (c_match(c)) atomicAdd(&hc[c_digit(c, r)], 1u);
-            });
-            lds_sync();
-            uint32_t b, above, nb;
-            threshold<BLOCK>(sm, r, 0u, need, W, nullptr, 0, 1, 0, 1, P.status, b, above, nb);
-            const uint32_t need2 = need - above;
-            const bool all = nb == need2;
-            // winners of this round (digit above b), and the bin itself when taken whole
-            for_each_cand([&](uint64_t c) {
-                const uint32_t d = c_digit(c, r);
-                if (c_match(c) && (d > b || (all && d == b))) {
-                    const uint32_t pos = atomicAdd(&sm.pos[r * 256 + (int)d], 1u);
-                    if (pos < (uint32_t)k) out[pos] = (int32_t)~(uint32_t)c;
-                    else raise_flag(P.status, kFlagCapacity);
-                }
-            });
-            need = need2;
-            W += above;
-            pf.add(r, b, idxb);
-            mb = nb;
-            ++r;
-            lds_sync();
-            if (all) { done = true; break; }
-        }
-        if (!done) {
-            // the few candidates still matching: exact rank by comparison
-            if (tid == 0) sm.sel[3] = 0u;
-            lds_sync();
-            for_each_cand([&](uint64_t c) {
-                if (c_match(c)) {
-                    const uint32_t pos = atomicAdd(&sm.sel[3], 1u);
-                    if (pos < (uint32_t)kSmall) sm.small[pos] = c;
-                }
-            });
-            lds_sync();
-            uint32_t ms = sm.sel[3];
-            if (ms > (uint32_t)kSmall) {
-                if (tid == 0) raise_flag(P.status, kFlagCapacity);
-                ms = kSmall;
-            }
-            for (uint32_t i = tid; i < ms; i += BLOCK) {
-                const uint64_t c = sm.small[i];
-                uint32_t rank = 0;
-#pragma unroll 8
-                for (uint32_t q = 0; q < ms; ++q) rank += sm.small[q] > c;
-                if (rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
-            }
-        }
+        finish_bucket<BLOCK, 8>(sm.cand, m, need, W, pf, R + 1, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, &sm.ctr,
+                                out, k, P.status);
     }
 
     if (multi) {
@@ -664,6 +756,199 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     }
 }
 
+// ----------------------------------------------------------------- one WG per row
+//
+// Batches of many rows: one WG owns a whole row and streams it in tiles of
+// BLOCK x ITEMS logits, the next tile's loads in flight while the current
+// one is processed.  The first digit is 12 bits wide (4096 bins), which for
+// typical rows leaves a bucket of at most 4096 after one pass; a second pass
+// (re-reading the row, by then in the device's caches) writes the winners
+// and gathers the bucket into LDS; the on-chip finish does the rest.
+// Positions come from two wave-aggregated LDS counters (winners, bucket).
+
+template <int BLOCK>
+struct RowsSmem {
+    union {
+        uint32_t h12[2 * 4097];                  // first digit: 2 copies of 4096 bins (stride 4097)
+        alignas(16) uint32_t h8[kCopies * 257];  // later 8-bit rounds and the finisher
+    } h;
+    uint64_t cand[kCap];
+    uint64_t small[kSmall];
+    uint32_t scan[BLOCK / 64];
+    uint32_t sel[4];
+    uint32_t ctr[3];  // winners, bucket, finisher
+};
+
+template <int BLOCK, int ITEMS>
+__global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
+    static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
+    constexpr int F = 12;
+    constexpr int NB0 = 1 << F;
+    constexpr int CHUNKS = ITEMS / 4;
+    constexpr int TILE_CHUNKS = BLOCK * CHUNKS;
+    __shared__ RowsSmem<BLOCK> sm;
+
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int n = P.n;
+    const int k = P.k;
+    const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
+    int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
+    int L = n;
+    if (P.lengths) {
+        L = P.lengths[row];
+        L = L < 0 ? 0 : (L > n ? n : L);
+    }
+    if (L <= k) {  // everything valid is selected; pad with -1
+        for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
+        return;
+    }
+    const int off = (int)(((uintptr_t)prow >> 2) & 3);
+    const int nchunks = (off + L + 3) >> 2;
+    const int cf_lo = off ? 1 : 0;         // chunks whose four elements are all valid
+    const int cf_hi = (L + off) >> 2;
+    const uint32_t n_empty = (uint32_t)(4 * nchunks - L);  // empty slots inside the row's chunks
+    const int idx_bits = P.idx_bits;
+    const int nrounds = num_rounds(idx_bits);
+    const char* const base = reinterpret_cast<const char*>(prow - off);
+
+    // f(keys, c_tile) for every tile of the row; slot 4j+e of a thread is
+    // element 4(c_tile + j*BLOCK + tid) - off + e, key 0 when empty.  The
+    // next tile is loaded while f runs on the current one.
+    auto stream = [&](auto&& f) {
+        uint4 buf[CHUNKS];
+        auto issue = [&](int ct) {
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                const int c = ct + j * BLOCK + tid;
+                buf[j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
+            }
+        };
+        issue(0);
+        for (int ct = 0; ct < nchunks; ct += TILE_CHUNKS) {
+            uint32_t keys[ITEMS];
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                const int c = ct + j * BLOCK + tid;
+                const uint32_t v[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
+                if (c >= cf_lo && c < cf_hi) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) keys[4 * j + e] = key_of(__uint_as_float(v[e]));
+                } else {
+                    const int e0 = 4 * c - off;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                        keys[4 * j + e] = ok ? key_of(__uint_as_float(v[e])) : 0u;
+                    }
+                }
+            }
+            if (ct + TILE_CHUNKS < nchunks) issue(ct + TILE_CHUNKS);
+            f(keys, ct);
+        }
+    };
+
+    // ---------------- first digit: 12-bit histogram over the whole row
+    {
+        uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
+        for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
+        if (tid < 3) sm.ctr[tid] = 0u;
+    }
+    lds_sync();
+    {
+        uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
+        stream([&](const uint32_t* keys, int ct) {
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                if (ct + j * BLOCK + tid < nchunks) {  // chunks past the row are skipped
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicAdd(&hc[keys[4 * j + e] >> (32 - F)], 1u);
+                }
+            }
+        });
+    }
+    lds_sync();
+    Prefix pf{0u, 0u, 0u, 0u};
+    uint32_t need = (uint32_t)k, W = 0, hb = 0;
+    int R = 0;
+    bool whole = false;
+    {
+        uint32_t b, above;
+        local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, n_empty, need, sm.scan, sm.sel, P.status, b, above, hb);
+        need -= above;
+        W += above;
+        pf.add<F>(0, b, idx_bits);
+        whole = hb == need;
+    }
+    // ---------------- further rounds (only when the bucket is still large)
+    for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
+            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        }
+        lds_sync();
+        uint32_t* const hc = sm.h.h8 + (tid % kCopies) * 257;
+        const int sh = digit_shift<F>(r, idx_bits);
+        const uint32_t dm = (1u << digit_width<F>(r)) - 1u;
+        stream([&](const uint32_t* keys, int ct) {
+            const int ibase = 4 * (ct + tid) - off;
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = keys[4 * j + e];
+                    const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
+                    if (pf.match(key, ni)) atomicAdd(&hc[((r < 4 ? key : ni) >> sh) & dm], 1u);
+                }
+            }
+        });
+        lds_sync();
+        uint32_t b, above;
+        local_select<BLOCK, 256, kCopies, 257>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, b, above, hb);
+        need -= above;
+        W += above;
+        pf.add<F>(r, b, idx_bits);
+        R = r;
+        whole = hb == need;
+    }
+    // ---------------- collection: winners to the output, the bucket to LDS
+    // (or to the output when it is taken whole)
+    bool overflow = false;
+    stream([&](const uint32_t* keys, int ct) {
+        const int ibase = 4 * (ct + tid) - off;
+#pragma unroll
+        for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = keys[4 * j + e];
+                const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
+                if (key == 0u) continue;
+                if (pf.above(key, ni)) {
+                    const uint32_t pos = atomicAdd(&sm.ctr[0], 1u);
+                    if (pos < W) out[pos] = (int32_t)~ni;
+                    else overflow = true;
+                } else if (pf.match(key, ni)) {
+                    const uint32_t pos = atomicAdd(&sm.ctr[1], 1u);
+                    if (whole) {
+                        if (W + pos < (uint32_t)k) out[W + pos] = (int32_t)~ni;
+                        else overflow = true;
+                    } else if (pos < (uint32_t)kCap) {
+                        sm.cand[pos] = ((uint64_t)key << 32) | (uint64_t)ni;
+                    } else {
+                        overflow = true;
+                    }
+                }
+            }
+        }
+    });
+    if (overflow) raise_flag(P.status, kFlagCapacity);
+    if (whole) return;
+    lds_sync();
+    finish_bucket<BLOCK, F>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, idx_bits,
+                            sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, k, P.status);
+}
+
 // ----------------------------------------------------------------- host side
 
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
@@ -679,13 +964,25 @@ int occupancy_variant(int* nb, int block) {
     return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, R>, block, 0);
 }
 
+template <int B, int I>
+void launch_rows(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
+    hipLaunchKernelGGL((topk_rows_kernel<B, I>), grid, block, 0, s, p);
+}
+
+template <int B, int I>
+int occupancy_rows(int* nb, int block) {
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_rows_kernel<B, I>, block, 0);
+}
+
 struct Variant {
     int block, items, resident;
+    int rows_kernel;  // 1: one WG per row, 12-bit first digit (wgs_per_row must be 1)
     LaunchFn launch;
     OccFn occupancy;
 };
 
-#define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
+#define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
+#define TKS_ROWS(B, I) {B, I, 0, 1, &launch_rows<B, I>, &occupancy_rows<B, I>}
 const Variant kVariants[] = {
     TKS_VARIANT(512, 4, true),     // 0: 2048 logits per WG
     TKS_VARIANT(512, 8, true),     // 1: 4096
@@ -697,8 +994,12 @@ const Variant kVariants[] = {
     TKS_VARIANT(1024, 32, true),   // 7: 32768
     TKS_VARIANT(1024, 16, false),  // 8: streaming, 16384 per tile
     TKS_VARIANT(256, 16, false),   // 9: streaming, 4096 per tile
+    TKS_ROWS(512, 16),             // 10: one WG per row, 8192 per tile
+    TKS_ROWS(1024, 16),            // 11: one WG per row, 16384 per tile
+    TKS_ROWS(512, 32),             // 12: one WG per row, 16384 per tile
 };
 #undef TKS_VARIANT
+#undef TKS_ROWS
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 struct DeviceInfo {
@@ -772,6 +1073,7 @@ int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, L
     const int64_t tile_chunks = (int64_t)var.block * (var.items / 4);
     int64_t cpw = (maxc + G - 1) / G;
     if (var.resident && cpw > tile_chunks) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (var.rows_kernel && G != 1) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (cpw < 1) cpw = 1;
     if (G > 1 && rows * (int64_t)G > (int64_t)d.capacity[v]) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows * (int64_t)G > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
@@ -808,7 +1110,9 @@ int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
         const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
         if (G == 1 || rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
     }
-    // streaming: as many WGs per row as can be co-resident, at least one
+    // many rows: one streaming WG per row
+    if (rows >= d.cus) return check_shape(d, rows, maxc, 10, 1, L);
+    // few long rows: as many streaming WGs per row as can be co-resident
     const int v = (maxc >= 16384) ? 8 : 9;
     int64_t G = d.capacity[v] / (rows > 0 ? rows : 1);
     const int64_t gmax = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
@@ -940,7 +1244,7 @@ int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* pla
         plan->block = tks::kVariants[L.variant].block;
         plan->items = tks::kVariants[L.variant].items;
         plan->resident = tks::kVariants[L.variant].resident;
-        plan->first_bits = 8;
+        plan->first_bits = tks::kVariants[L.variant].rows_kernel ? 12 : 8;
         return TOPK_SELECT_SUCCESS;
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
@@ -956,7 +1260,7 @@ int topk_select_variant_info(int32_t v, topk_select_plan_t* plan) {
     plan->block = tks::kVariants[v].block;
     plan->items = tks::kVariants[v].items;
     plan->resident = tks::kVariants[v].resident;
-    plan->first_bits = 8;
+    plan->first_bits = tks::kVariants[v].rows_kernel ? 12 : 8;
     return TOPK_SELECT_SUCCESS;
 }
 

@@ -151,6 +151,34 @@ def test_edge_case(torch_gpu, request, x, k, lengths):
         check_row_invariants(x2[r], L, k, got[r])
 
 
+def _one_wg_per_row_variants():
+    import sparse_attention_topk_fp32_amd as tks
+
+    return [v for v in range(tks.num_variants()) if tks.variant_info(v)["first_bits"] == 12]
+
+
+@pytest.mark.parametrize("x,k,lengths", _edge_cases())
+def test_edge_case_one_wg_per_row(torch_gpu, request, x, k, lengths):
+    """The same edge cases through the one-WG-per-row kernels (12-bit first
+    digit, streamed tiles)."""
+    x2 = x if x.ndim == 2 else x[None]
+    for v in _one_wg_per_row_variants():
+        _say("edge %s variant %d" % (request.node.callspec.id, v))
+        got = run_gpu(torch_gpu, x2, k, lengths, variant=v, wgs=1)
+        assert_parity(x2, k, lengths, got)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_unaligned_rows_one_wg_per_row(torch_gpu, offset):
+    rng = np.random.default_rng(10 + offset)
+    for rows, n in ((2, 70001), (3, 10001), (5, 4097)):
+        x = rng.standard_normal((rows, n)).astype(np.float32)
+        for v in _one_wg_per_row_variants():
+            _say("unaligned offset=%d rows=%d n=%d variant %d" % (offset, rows, n, v))
+            got = run_gpu(torch_gpu, x, 1024, offset=offset, variant=v, wgs=1)
+            assert_parity(x, 1024, None, got)
+
+
 @pytest.mark.parametrize("offset", [1, 2, 3])
 def test_unaligned_rows(torch_gpu, offset):
     rng = np.random.default_rng(offset)
