@@ -169,6 +169,27 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, uint32_t* s
     return pa + ia - a;
 }
 
+// Block-wide exclusive scan over all BLOCK threads that also returns the
+// total (uniform).
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_scan_total(uint32_t a, uint32_t* s_w /* [BLOCK / 64] */, uint32_t& total) {
+    constexpr int NW = BLOCK / 64;
+    const uint32_t wid = threadIdx.x / 64;
+    const uint32_t ia = wave_inclusive_scan(a);
+    if (lane_id() == 63) s_w[wid] = ia;
+    lds_sync();
+    uint32_t pa = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t v = s_w[i];
+        if ((uint32_t)i < wid) pa += v;
+        tot += v;
+    }
+    lds_sync();
+    total = uniform(tot);
+    return pa + ia - a;
+}
+
 // Digit schedule: rounds 0..3 cut the key from the top, the first digit
 // F bits wide (8 or 12) and the others 8 bits (the last key digit keeps what
 // is left); later rounds cut the varying low idx_bits of ~index (its top
@@ -265,7 +286,7 @@ struct Smem {
 // in descending bin order across threads, so one block scan over the
 // owners' sums locates the bin b that holds the element of rank `need`
 // (1-based, from the top).  Returns b, the count above b and the count in b.
-template <int BLOCK, int NB, int NC, int STRIDE>
+template <int BLOCK, int NB, int NC, int STRIDE, bool STRICT = true>
 __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_sub, uint32_t need, uint32_t* scan,
                                              uint32_t* sel, uint32_t* status, uint32_t& b_out, uint32_t& above_out,
                                              uint32_t& hb_out) {
@@ -304,8 +325,8 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
     lds_sync();
     uint32_t b = uniform(sel[0]), ab = uniform(sel[1]), hb = uniform(sel[2]);
     lds_sync();
-    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
-        if (t == 0) raise_flag(status, kFlagCapacity);
+    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need` (an error unless !STRICT)
+        if (STRICT && t == 0) raise_flag(status, kFlagCapacity);
         b = 0; ab = 0; hb = 0;
     }
     b_out = b;
@@ -320,7 +341,7 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
 // `hist` (kCopies x 257 words), `small`, `scan`, `sel` and the counter
 // `ctr`.  Every thread of the WG calls it.
 template <int BLOCK, int F>
-__device__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
+__device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
                               int idx_bits, uint32_t* hist, uint64_t* small, uint32_t* scan, uint32_t* sel,
                               uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
     const int tid = threadIdx.x;
@@ -759,12 +780,14 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 // ----------------------------------------------------------------- one WG per row
 //
 // Batches of many rows: one WG owns a whole row and streams it in tiles of
-// BLOCK x ITEMS logits, the next tile's loads in flight while the current
-// one is processed.  The first digit is 12 bits wide (4096 bins), which for
+// BLOCK x ITEMS logits, the next PD tiles' loads in flight while the
+// current one is processed.  The first digit is 12 bits wide (4096 bins), which for
 // typical rows leaves a bucket of at most 4096 after one pass; a second pass
 // (re-reading the row, by then in the device's caches) writes the winners
 // and gathers the bucket into LDS; the on-chip finish does the rest.
 // Positions come from two wave-aggregated LDS counters (winners, bucket).
+
+constexpr int kRowsCap = 4608;  // candidate buffer of the one-WG-per-row kernel (entries)
 
 template <int BLOCK>
 struct RowsSmem {
@@ -772,15 +795,15 @@ struct RowsSmem {
         uint32_t h12[2 * 4097];                  // first digit: 2 copies of 4096 bins (stride 4097)
         alignas(16) uint32_t h8[kCopies * 257];  // later 8-bit rounds and the finisher
     } h;
-    uint64_t cand[kCap];
+    uint64_t cand[kRowsCap];  // candidates at or above the running bound; later the final bucket
     uint64_t small[kSmall];
     uint32_t scan[BLOCK / 64];
     uint32_t sel[4];
-    uint32_t ctr[3];  // winners, bucket, finisher
+    uint32_t ctr[4];  // winners, bucket, finisher, buffered entries
 };
 
-template <int BLOCK, int ITEMS>
-__global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
+template <int BLOCK, int ITEMS, int PD>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void topk_rows_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     constexpr int F = 12;
     constexpr int NB0 = 1 << F;
@@ -807,7 +830,6 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
     const int nchunks = (off + L + 3) >> 2;
     const int cf_lo = off ? 1 : 0;         // chunks whose four elements are all valid
     const int cf_hi = (L + off) >> 2;
-    const uint32_t n_empty = (uint32_t)(4 * nchunks - L);  // empty slots inside the row's chunks
     const int idx_bits = P.idx_bits;
     const int nrounds = num_rounds(idx_bits);
     const char* const base = reinterpret_cast<const char*>(prow - off);
@@ -816,55 +838,191 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
     // element 4(c_tile + j*BLOCK + tid) - off + e, key 0 when empty.  The
     // next tile is loaded while f runs on the current one.
     auto stream = [&](auto&& f) {
-        uint4 buf[CHUNKS];
-        auto issue = [&](int ct) {
+        uint4 buf[PD][CHUNKS];  // PD tiles in flight
 #pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-                const int c = ct + j * BLOCK + tid;
-                buf[j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
-            }
-        };
-        issue(0);
-        for (int ct = 0; ct < nchunks; ct += TILE_CHUNKS) {
-            uint32_t keys[ITEMS];
+        for (int d = 0; d < PD; ++d) {
+            if (d * TILE_CHUNKS < nchunks) {
 #pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-                const int c = ct + j * BLOCK + tid;
-                const uint32_t v[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
-                if (c >= cf_lo && c < cf_hi) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) keys[4 * j + e] = key_of(__uint_as_float(v[e]));
-                } else {
-                    const int e0 = 4 * c - off;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
-                        keys[4 * j + e] = ok ? key_of(__uint_as_float(v[e])) : 0u;
-                    }
+                for (int j = 0; j < CHUNKS; ++j) {
+                    const int c = d * TILE_CHUNKS + j * BLOCK + tid;
+                    buf[d][j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
                 }
             }
-            if (ct + TILE_CHUNKS < nchunks) issue(ct + TILE_CHUNKS);
-            f(keys, ct);
+        }
+        for (int ct0 = 0; ct0 < nchunks; ct0 += PD * TILE_CHUNKS) {
+#pragma unroll
+            for (int d = 0; d < PD; ++d) {
+                const int ct = ct0 + d * TILE_CHUNKS;
+                if (ct < nchunks) {
+                    uint32_t keys[ITEMS];
+#pragma unroll
+                    for (int j = 0; j < CHUNKS; ++j) {
+                        const int c = ct + j * BLOCK + tid;
+                        const uint32_t v[4] = {buf[d][j].x, buf[d][j].y, buf[d][j].z, buf[d][j].w};
+                        if (c >= cf_lo && c < cf_hi) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) keys[4 * j + e] = key_of(__uint_as_float(v[e]));
+                        } else {
+                            const int e0 = 4 * c - off;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                                keys[4 * j + e] = ok ? key_of(__uint_as_float(v[e])) : 0u;
+                            }
+                        }
+                    }
+                    const int cn = ct + PD * TILE_CHUNKS;  // the tile PD ahead reuses this buffer
+                    if (cn < nchunks) {
+#pragma unroll
+                        for (int j = 0; j < CHUNKS; ++j) {
+                            const int c = cn + j * BLOCK + tid;
+                            buf[d][j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
+                        }
+                    }
+                    f(keys, ct);
+                }
+            }
         }
     };
 
-    // ---------------- first digit: 12-bit histogram over the whole row
+    // ---------------- first pass: 12-bit histogram of the row, and every
+    // element at or above a lower bound `lo` (a first-digit bin) kept in LDS.
+    // The bound is an estimate: the bin of the element of rank
+    // 1.25 * k * seen / L + 64 among the `seen` elements read so far, where
+    // the k-th largest of the row is expected near rank k * seen / L.  It is
+    // taken after the first tile and raised (with the buffer compacted)
+    // whenever the buffer fills up.  The buffer then holds every element at
+    // or above `lo`; when the exact threshold bin b0 of the row turns out to
+    // be at least `lo` (checked below), everything selected is in it.
+    // Otherwise, or when the buffer overflowed, the row is finished with
+    // re-reads.
     {
         uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
         for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
         if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-        if (tid < 3) sm.ctr[tid] = 0u;
+        if (tid < 4) sm.ctr[tid] = 0u;
     }
     lds_sync();
+    bool keep = true;   // candidates are being buffered
+    uint32_t used = 0;  // buffered entries
+    uint32_t lo = 0;    // running lower bound (first-digit bin)
+    bool partial = false;  // the histogram skipped elements below the bound
+    // Walk the buffer in slices of RC * BLOCK entries: every thread reads its
+    // RC entries, a block scan numbers the chosen ones, and f(entry, kind,
+    // rank) places them.  Kinds: pred returns 0 (drop), 1 or 2, counted
+    // separately (ranks are per kind, across slices).  A chosen entry of
+    // kind 2 may be moved to the front of the buffer: its new index is never
+    // above its old one, and each slice is read before any of it is written.
+    constexpr int RC = 3;
+    auto walk = [&](auto&& pred, auto&& f, uint32_t& n1, uint32_t& n2) {
+        n1 = 0;
+        n2 = 0;
+        for (uint32_t i0 = 0; i0 < used; i0 += RC * BLOCK) {
+            uint64_t e[RC];
+            uint32_t kinds = 0, cnt = 0;
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                e[u] = i < used ? sm.cand[i] : 0ull;
+                const uint32_t kd = i < used ? pred(e[u]) : 0u;
+                kinds |= kd << (2 * u);
+                cnt += kd == 1u ? (1u << 16) : (kd == 2u ? 1u : 0u);
+            }
+            uint32_t tot;
+            const uint32_t pos = block_scan_total<BLOCK>(cnt, sm.scan, tot);
+            uint32_t p1 = n1 + (pos >> 16), p2 = n2 + (pos & 0xFFFFu);
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const uint32_t kd = (kinds >> (2 * u)) & 3u;
+                if (kd == 1u) f(e[u], 1u, p1++);
+                else if (kd == 2u) f(e[u], 2u, p2++);
+            }
+            n1 += tot >> 16;
+            n2 += tot & 0xFFFFu;
+        }
+    };
+    // rank of the bound after `seen` valid elements
+    auto bound_rank = [&](uint32_t seen) -> uint32_t {
+        const uint64_t est = ((uint64_t)k * seen * 5u) / (4u * (uint64_t)L) + 64u;
+        return (uint32_t)(est < seen ? est : seen);
+    };
+    // raise the bound from the histogram of the first `seen` elements
+    auto raise_bound = [&](uint32_t seen) {
+        uint32_t b, ab, hbx;
+        local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, bound_rank(seen), sm.scan, sm.sel, P.status, b, ab,
+                                                 hbx);
+        lo = b > lo ? b : lo;
+    };
     {
         uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
+        const uint32_t lane = lane_id();
         stream([&](const uint32_t* keys, int ct) {
+            // histogram: the first tile counts every element, later tiles
+            // only those at or above the bound (the counts of the bins at or
+            // above the bound stay exact, which is all the final threshold
+            // needs once it is found at or above the bound)
+            if (ct == 0) {
 #pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-                if (ct + j * BLOCK + tid < nchunks) {  // chunks past the row are skipped
+                for (int i = 0; i < ITEMS; ++i)
+                    if (keys[i] != 0u) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
+            } else {
+                partial |= lo != 0u;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicAdd(&hc[keys[4 * j + e] >> (32 - F)], 1u);
+                for (int i = 0; i < ITEMS; ++i)
+                    if ((keys[i] != 0u) & ((keys[i] >> (32 - F)) >= lo)) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
+            }
+            if (!keep) {
+                lo = 0;  // count everything from here on
+                return;
+            }
+            // valid elements read once this tile is done
+            const uint32_t seen = (uint32_t)min(L, 4 * min(nchunks, ct + TILE_CHUNKS) - off);
+            if (ct == 0) {
+                lds_sync();  // the first tile's histogram is complete
+                raise_bound(seen);
+            }
+            // append: lanes count their candidates, a wave prefix ranks
+            // them, one LDS atomic per wave reserves the wave's range
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) c += (keys[i] != 0u) & ((keys[i] >> (32 - F)) >= lo);
+            const uint32_t ic = wave_inclusive_scan(c);
+            const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
+            if (tw) {
+                uint32_t wb = 0;
+                if (lane == 0) wb = atomicAdd(&sm.ctr[3], tw);
+                uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + ic - c;
+                const int ibase = 4 * (ct + tid) - off;
+#pragma unroll
+                for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t key = keys[4 * j + e];
+                        if ((key != 0u) & ((key >> (32 - F)) >= lo)) {
+                            if (pos < (uint32_t)kRowsCap)
+                                sm.cand[pos] = ((uint64_t)key << 32) |
+                                               (uint64_t)~(uint32_t)(ibase + 4 * BLOCK * j + e);
+                            ++pos;
+                        }
+                    }
                 }
+            }
+            lds_sync();
+            used = uniform(sm.ctr[3]);
+            if (used > (uint32_t)kRowsCap) {  // entries were lost
+                keep = false;
+                return;
+            }
+            if (used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks) {
+                // tighter bound from more data, and drop what fell below it
+                raise_bound(seen);
+                const uint32_t lob = lo;
+                uint32_t n1, n2;
+                walk([&](uint64_t e) { return (uint32_t)(e >> (64 - F)) >= lob ? 2u : 0u; },
+                     [&](uint64_t e, uint32_t, uint32_t r) { sm.cand[r] = e; }, n1, n2);
+                used = n2;
+                if (tid == 0) sm.ctr[3] = n2;
+                lds_sync();
             }
         });
     }
@@ -873,14 +1031,64 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
     uint32_t need = (uint32_t)k, W = 0, hb = 0;
     int R = 0;
     bool whole = false;
-    {
-        uint32_t b, above;
-        local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, n_empty, need, sm.scan, sm.sel, P.status, b, above, hb);
+    uint32_t b0, above;
+    local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+    if (keep && hb > 0u && b0 >= lo) {
         need -= above;
         W += above;
-        pf.add<F>(0, b, idx_bits);
+        pf.add<F>(0, b0, idx_bits);
         whole = hb == need;
+        // every element at or above bin b0 is buffered: winners (above b0)
+        // to the output, the bucket (bin b0) to the front of the buffer, or
+        // to the output when it is taken whole
+        uint32_t nw, nbk;
+        const uint32_t bsel = b0;
+        const bool wh = whole;
+        const uint32_t Wv = W;
+        walk([&](uint64_t e) {
+                 const uint32_t bin = (uint32_t)(e >> (64 - F));
+                 return bin > bsel ? 1u : (bin == bsel ? 2u : 0u);
+             },
+             [&](uint64_t e, uint32_t kind, uint32_t r) {
+                 if (kind == 1u) {
+                     if (r < Wv) out[r] = (int32_t)~(uint32_t)e;
+                 } else if (wh) {
+                     if (Wv + r < (uint32_t)k) out[Wv + r] = (int32_t)~(uint32_t)e;
+                 } else {
+                     sm.cand[r] = e;
+                 }
+             },
+             nw, nbk);
+        const bool bad = nw != W || nbk != hb;
+        if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
+        if (whole) return;
+        lds_sync();
+        finish_bucket<BLOCK, F>(sm.cand, hb, need, W, pf, 1, idx_bits, sm.h.h8, sm.small, sm.scan, sm.sel,
+                                &sm.ctr[2], out, k, P.status);
+        return;
     }
+    // ---------------- fallback: the full first-digit histogram by a second
+    // read, then rounds and collection by further reads
+    if (partial) {
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
+            for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+            if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
+        }
+        lds_sync();
+        uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
+        stream([&](const uint32_t* keys, int) {
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                if (keys[i] != 0u) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
+        });
+        lds_sync();
+    }
+    local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+    need -= above;
+    W += above;
+    pf.add<F>(0, b0, idx_bits);
+    whole = hb == need;
     // ---------------- further rounds (only when the bucket is still large)
     for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
         {
@@ -913,30 +1121,61 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_kernel(const KParams P) {
         whole = hb == need;
     }
     // ---------------- collection: winners to the output, the bucket to LDS
-    // (or to the output when it is taken whole)
+    // (or to the output when it is taken whole).  Positions per tile: each
+    // lane counts its winners and bucket elements, a wave prefix (DPP) ranks
+    // the lanes, and one LDS atomic per wave and kind reserves the wave's
+    // range.
+    static_assert(ITEMS <= 32, "per-lane selection masks are 32 bits");
     bool overflow = false;
+    const uint32_t lane = lane_id();
     stream([&](const uint32_t* keys, int ct) {
         const int ibase = 4 * (ct + tid) - off;
+        uint32_t mw = 0, mbk = 0;  // this lane's winners / bucket elements, one bit per slot
 #pragma unroll
         for (int j = 0; j < CHUNKS; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t key = keys[4 * j + e];
                 const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                if (key == 0u) continue;
-                if (pf.above(key, ni)) {
-                    const uint32_t pos = atomicAdd(&sm.ctr[0], 1u);
-                    if (pos < W) out[pos] = (int32_t)~ni;
-                    else overflow = true;
-                } else if (pf.match(key, ni)) {
-                    const uint32_t pos = atomicAdd(&sm.ctr[1], 1u);
-                    if (whole) {
-                        if (W + pos < (uint32_t)k) out[W + pos] = (int32_t)~ni;
+                const bool a = (key != 0u) & pf.above(key, ni);
+                const bool m = pf.match(key, ni);
+                mw |= (uint32_t)a << (4 * j + e);
+                mbk |= (uint32_t)m << (4 * j + e);
+            }
+        }
+        const uint32_t nw = (uint32_t)__builtin_popcount(mw), nb = (uint32_t)__builtin_popcount(mbk);
+        const uint32_t iw = wave_inclusive_scan(nw), ib = wave_inclusive_scan(nb);
+        const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)iw, 63);
+        const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, 63);
+        if (tw | tb) {
+            uint32_t bw = 0, bb = 0;
+            if (lane == 0) {
+                if (tw) bw = atomicAdd(&sm.ctr[0], tw);
+                if (tb) bb = atomicAdd(&sm.ctr[1], tb);
+            }
+            uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)bw, 0) + iw - nw;
+            uint32_t pb = (uint32_t)__builtin_amdgcn_readlane((int)bb, 0) + ib - nb;
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int slot = 4 * j + e;
+                    const uint32_t key = keys[slot];
+                    const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
+                    if ((mw >> slot) & 1u) {
+                        if (pw < W) out[pw] = (int32_t)~ni;
                         else overflow = true;
-                    } else if (pos < (uint32_t)kCap) {
-                        sm.cand[pos] = ((uint64_t)key << 32) | (uint64_t)ni;
-                    } else {
-                        overflow = true;
+                        ++pw;
+                    } else if ((mbk >> slot) & 1u) {
+                        if (whole) {
+                            if (W + pb < (uint32_t)k) out[W + pb] = (int32_t)~ni;
+                            else overflow = true;
+                        } else if (pb < (uint32_t)kCap) {
+                            sm.cand[pb] = ((uint64_t)key << 32) | (uint64_t)ni;
+                        } else {
+                            overflow = true;
+                        }
+                        ++pb;
                     }
                 }
             }
@@ -964,14 +1203,14 @@ int occupancy_variant(int* nb, int block) {
     return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, R>, block, 0);
 }
 
-template <int B, int I>
+template <int B, int I, int D>
 void launch_rows(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    hipLaunchKernelGGL((topk_rows_kernel<B, I>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((topk_rows_kernel<B, I, D>), grid, block, 0, s, p);
 }
 
-template <int B, int I>
+template <int B, int I, int D>
 int occupancy_rows(int* nb, int block) {
-    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_rows_kernel<B, I>, block, 0);
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_rows_kernel<B, I, D>, block, 0);
 }
 
 struct Variant {
@@ -982,7 +1221,7 @@ struct Variant {
 };
 
 #define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
-#define TKS_ROWS(B, I) {B, I, 0, 1, &launch_rows<B, I>, &occupancy_rows<B, I>}
+#define TKS_ROWS(B, I, D) {B, I, 0, 1, &launch_rows<B, I, D>, &occupancy_rows<B, I, D>}
 const Variant kVariants[] = {
     TKS_VARIANT(512, 4, true),     // 0: 2048 logits per WG
     TKS_VARIANT(512, 8, true),     // 1: 4096
@@ -994,9 +1233,8 @@ const Variant kVariants[] = {
     TKS_VARIANT(1024, 32, true),   // 7: 32768
     TKS_VARIANT(1024, 16, false),  // 8: streaming, 16384 per tile
     TKS_VARIANT(256, 16, false),   // 9: streaming, 4096 per tile
-    TKS_ROWS(512, 16),             // 10: one WG per row, 8192 per tile
-    TKS_ROWS(1024, 16),            // 11: one WG per row, 16384 per tile
-    TKS_ROWS(512, 32),             // 12: one WG per row, 16384 per tile
+    TKS_ROWS(512, 16, 1),          // 10: one WG per row, 8192 per tile
+    TKS_ROWS(1024, 16, 1),         // 11: one WG per row, 16384 per tile
 };
 #undef TKS_VARIANT
 #undef TKS_ROWS
