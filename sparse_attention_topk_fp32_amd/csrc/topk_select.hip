@@ -278,7 +278,7 @@ struct Smem {
     uint64_t small[kSmall];             // last few candidates, ranked exactly
     uint32_t scan[BLOCK / 64];
     uint32_t sel[4];                    // threshold bin, count above it, count in it
-    uint32_t ctr;                       // finisher position counter
+    uint32_t ctr[2];                    // finisher position counters
 };
 
 // Thresholding step on one WG's own histogram: NB bins held as NC LDS
@@ -366,12 +366,13 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
         }
     };
     int r = r0;
-    uint32_t mb = m;  // entries still matching the prefix
+    uint32_t mb = m;        // entries still matching the prefix
+    bool in_small = false;  // they are already gathered in small[0 .. ctr[1])
     while (mb > (uint32_t)kSmall && r < nrounds) {
         {
             uint4* const h4 = reinterpret_cast<uint4*>(hist);
             for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-            if (tid == 0) *ctr = 0u;
+            if (tid < 2) ctr[tid] = 0u;
         }
         lds_sync();
         uint32_t* const hc = hist + (tid % kCopies) * 257;
@@ -383,13 +384,19 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
         local_select<BLOCK, 256, kCopies, 257>(hist, 0u, need, scan, sel, status, b, above, nb);
         const uint32_t need2 = need - above;
         const bool all = nb == need2;
-        // winners of this round (digit above b), and the bin itself when taken whole
+        const bool gather = !all && nb <= (uint32_t)kSmall;
+        // winners of this round (digit above b), and the bin itself when
+        // taken whole; a small enough bin is gathered for the exact rank
         for_each_cand([&](uint64_t c) {
             const uint32_t d = c_digit(c, r);
-            if (c_match(c) && (d > b || (all && d == b))) {
-                const uint32_t pos = W + atomicAdd(ctr, 1u);
+            if (!c_match(c)) return;
+            if (d > b || (all && d == b)) {
+                const uint32_t pos = W + atomicAdd(&ctr[0], 1u);
                 if (pos < (uint32_t)k) out[pos] = (int32_t)~(uint32_t)c;
                 else raise_flag(status, kFlagCapacity);
+            } else if (gather && d == b) {
+                const uint32_t pos = atomicAdd(&ctr[1], 1u);
+                if (pos < (uint32_t)kSmall) small[pos] = c;
             }
         });
         need = need2;
@@ -399,29 +406,39 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
         ++r;
         lds_sync();
         if (all) return;
+        in_small = gather;
     }
-    // the few candidates still matching: exact rank by comparison
-    if (tid == 0) *ctr = 0u;
-    lds_sync();
-    for_each_cand([&](uint64_t c) {
-        if (c_match(c)) {
-            const uint32_t pos = atomicAdd(ctr, 1u);
-            if (pos < (uint32_t)kSmall) small[pos] = c;
-        }
-    });
-    lds_sync();
-    uint32_t ms = *ctr;
+    if (!in_small) {
+        // the few candidates still matching, gathered
+        if (tid == 1) ctr[1] = 0u;
+        lds_sync();
+        for_each_cand([&](uint64_t c) {
+            if (c_match(c)) {
+                const uint32_t pos = atomicAdd(&ctr[1], 1u);
+                if (pos < (uint32_t)kSmall) small[pos] = c;
+            }
+        });
+        lds_sync();
+    }
+    uint32_t ms = uniform(ctr[1]);
     if (ms > (uint32_t)kSmall) {
         if (tid == 0) raise_flag(status, kFlagCapacity);
         ms = kSmall;
     }
-    for (uint32_t i = tid; i < ms; i += BLOCK) {
-        const uint64_t c = small[i];
-        uint32_t rank = 0;
-#pragma unroll 8
-        for (uint32_t q = 0; q < ms; ++q) rank += small[q] > c;
-        if (rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
+    // exact rank by comparison, P lanes per candidate (each compares a
+    // strided share, then the lanes add up their counts)
+    uint32_t P = 1;
+    while (P < 64u && 2u * P * ms <= (uint32_t)BLOCK) P *= 2u;
+    const uint32_t i = (uint32_t)tid / P, q = (uint32_t)tid % P;
+    const uint64_t c = i < ms ? small[i] : 0ull;
+    uint32_t rank = 0;
+    if (i < ms) {
+        for (uint32_t j = q; j < ms; j += P) rank += small[j] > c;
     }
+    for (uint32_t sft = 32u; sft >= 1u; sft >>= 1) {
+        if (sft < P) rank += (uint32_t)__shfl_xor((int)rank, (int)sft);
+    }
+    if (i < ms && q == 0u && rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
 }
 
 // Thresholding step for round r from the LDS histogram copies (the first
@@ -722,15 +739,29 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     if (!whole) {
         uint32_t m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
         if (multi) {
-            // pull the staged bucket: every entry is non-zero once written;
-            // one load per entry in flight, then a bounded re-poll of the
-            // few entries not written yet
+            // pull the staged bucket: every entry is non-zero once written.
+            // Eight loads in flight per thread; entries not written yet are
+            // re-polled together (bounded wait).
             for (uint32_t i0 = 0; i0 < m; i0 += 8u * BLOCK) {
                 uint64_t v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {  // eight loads in flight per thread
+                for (int u = 0; u < 8; ++u) {
                     const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                    v[u] = i < m ? ld_dev(&gstage[i]) : 0ull;
+                    v[u] = i < m ? ld_dev(&gstage[i]) : 1ull;
+                }
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                for (;;) {
+                    bool miss = false;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) miss |= v[u] == 0ull;
+                    if (!miss) break;
+                    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+                        raise_flag(P.status, kFlagTimeout);
+                        break;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (v[u] == 0ull) v[u] = ld_dev(&gstage[i0 + (uint32_t)(u * BLOCK + tid)]);
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -738,22 +769,9 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
                     if (i < m) sm.cand[i] = v[u];
                 }
             }
-            lds_sync();
-            for (uint32_t i = tid; i < m; i += BLOCK) {
-                if (sm.cand[i] != 0ull) continue;
-                uint64_t x;
-                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                while ((x = ld_dev(&gstage[i])) == 0ull) {
-                    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-                        raise_flag(P.status, kFlagTimeout);
-                        break;
-                    }
-                }
-                sm.cand[i] = x;
-            }
         }
         lds_sync();
-        finish_bucket<BLOCK, 8>(sm.cand, m, need, W, pf, R + 1, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, &sm.ctr,
+        finish_bucket<BLOCK, 8>(sm.cand, m, need, W, pf, R + 1, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, sm.ctr,
                                 out, k, P.status);
     }
 
@@ -799,7 +817,7 @@ struct RowsSmem {
     uint64_t small[kSmall];
     uint32_t scan[BLOCK / 64];
     uint32_t sel[4];
-    uint32_t ctr[4];  // winners, bucket, finisher, buffered entries
+    uint32_t ctr[5];  // winners, bucket, finisher (2), buffered entries
 };
 
 template <int BLOCK, int ITEMS, int PD>
@@ -900,7 +918,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
         for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
         if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-        if (tid < 4) sm.ctr[tid] = 0u;
+        if (tid < 5) sm.ctr[tid] = 0u;
     }
     lds_sync();
     bool keep = true;   // candidates are being buffered
@@ -990,7 +1008,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
             if (tw) {
                 uint32_t wb = 0;
-                if (lane == 0) wb = atomicAdd(&sm.ctr[3], tw);
+                if (lane == 0) wb = atomicAdd(&sm.ctr[4], tw);
                 uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + ic - c;
                 const int ibase = 4 * (ct + tid) - off;
 #pragma unroll
@@ -1008,7 +1026,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 }
             }
             lds_sync();
-            used = uniform(sm.ctr[3]);
+            used = uniform(sm.ctr[4]);
             if (used > (uint32_t)kRowsCap) {  // entries were lost
                 keep = false;
                 return;
@@ -1021,7 +1039,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 walk([&](uint64_t e) { return (uint32_t)(e >> (64 - F)) >= lob ? 2u : 0u; },
                      [&](uint64_t e, uint32_t, uint32_t r) { sm.cand[r] = e; }, n1, n2);
                 used = n2;
-                if (tid == 0) sm.ctr[3] = n2;
+                if (tid == 0) sm.ctr[4] = n2;
                 lds_sync();
             }
         });
@@ -1269,9 +1287,10 @@ int device_info(int dev, DeviceInfo** out) {
             int nb = 0;
             if (kVariants[v].occupancy(&nb, kVariants[v].block) != (int)hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
             // WGs that are certainly co-resident: what the occupancy query
-            // allows, but never more than one per CU (full occupancy is not
-            // always reached for large WGs in practice)
-            d.capacity[v] = nb < 1 ? 0 : d.cus;
+            // allows, but at most two per CU, and one for 1024-thread WGs
+            // (measured with a bounded-wait probe on MI355X)
+            const int cap = kVariants[v].block >= 1024 ? 1 : 2;
+            d.capacity[v] = (nb < cap ? nb : cap) * d.cus;
         }
         it = g_dev.emplace(dev, d).first;
     }
