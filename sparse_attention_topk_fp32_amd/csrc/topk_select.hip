@@ -711,26 +711,71 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     uint64_t* const gstage = multi ? &ws->stage[p][0] : nullptr;
     bool overflow = false;
     opaque_keys();
-    visit([&](uint32_t key, uint32_t ni) {
+    // With many elements per thread, three steps, so that the per-element
+    // work stays a compare: count the
+    // selected elements (winners and bucket) per thread; copy them, in rank
+    // order from a block scan, into a compact LDS list (the histogram
+    // space, in chunks); place the list's entries with all lanes busy.
+    const uint32_t kp = pf.kpfx, km = pf.kmask;
+    auto selected = [&](uint32_t key, uint32_t ni) -> bool {
+        if (!idx_rounds) return ((key & km) >= kp) & (key != 0u);
+        uint32_t slot;
+        return classify(key, ni, pf, true, idx_bits, &slot) != 0u;
+    };
+    // place one selected element (a winner or a bucket element)
+    auto place = [&](uint32_t key, uint32_t ni) {
         uint32_t slot = bslot;
-        const uint32_t cls = classify(key, ni, pf, idx_rounds, idx_bits, &slot);
-        if (cls == 0u) return;
-        // rank inside the WG's range of the slot: one LDS atomic per element
-        // (lanes of a wave on different slots do not wait for each other)
+        bool ab;
+        if (!idx_rounds) {
+            const uint32_t s = key & km;
+            ab = s > kp;
+            const uint32_t r = (uint32_t)__builtin_clz((s ^ kp) | 1u) >> 3;
+            if (ab) slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
+        } else {
+            ab = classify(key, ni, pf, true, idx_bits, &slot) == 1u;
+        }
         const uint32_t pos = atomicAdd(&sm.pos[slot], 1u);
-        if (cls == 1u || whole) {
+        if (ab || whole) {
             if (pos < (uint32_t)k) out[pos] = (int32_t)~ni;
             else overflow = true;
+        } else if (pos < (uint32_t)kCap) {
+            const uint64_t e = ((uint64_t)key << 32) | (uint64_t)ni;
+            if (multi) st_dev(&gstage[pos], e);
+            else sm.cand[pos] = e;
         } else {
-            const uint64_t comp = ((uint64_t)key << 32) | (uint64_t)ni;
-            if (pos < (uint32_t)kCap) {
-                if (multi) st_dev(&gstage[pos], comp);
-                else sm.cand[pos] = comp;
-            } else {
-                overflow = true;
-            }
+            overflow = true;
         }
-    });
+    };
+    if constexpr (ITEMS <= 8) {
+        // few elements per thread: place them directly
+        visit([&](uint32_t key, uint32_t ni) {
+            if (selected(key, ni)) place(key, ni);
+        });
+    } else {
+    uint32_t nsel = 0;
+    visit([&](uint32_t key, uint32_t ni) { nsel += selected(key, ni); });
+    uint32_t tot_sel;
+    const uint32_t my_first = block_scan_total<BLOCK>(nsel, sm.scan, tot_sel);
+    uint64_t* const list = reinterpret_cast<uint64_t*>(sm.hist);
+    constexpr uint32_t LISTN = kCopies * 257 / 2;
+    for (uint32_t c0 = 0; c0 < tot_sel; c0 += LISTN) {
+        uint32_t rk = my_first - c0;  // wraps for ranks before the chunk: never < LISTN then
+        opaque_keys();
+        visit([&](uint32_t key, uint32_t ni) {
+            if (selected(key, ni)) {
+                if (rk < LISTN) list[rk] = ((uint64_t)key << 32) | (uint64_t)ni;
+                ++rk;
+            }
+        });
+        lds_sync();
+        const uint32_t nl = min(LISTN, tot_sel - c0);
+        for (uint32_t i = tid; i < nl; i += BLOCK) {
+            const uint64_t e = list[i];
+            place((uint32_t)(e >> 32), (uint32_t)e);
+        }
+        lds_sync();
+    }
+    }
     if (overflow) raise_flag(P.status, kFlagCapacity);
 
     if (multi && w != 0) return;  // WG 0 finishes the row
