@@ -61,7 +61,7 @@ namespace tks {
 
 constexpr int kCap = 4096;        // final bucket size handed to one WG (entries)
 constexpr int kSmall = 256;       // bucket ranked exactly by comparisons
-constexpr int kRounds = 8;        // digit rounds: 4 key bytes + up to 4 index bytes
+constexpr int kRounds = 9;        // merge rounds: a window round, then up to 4 key + 4 index digits
 constexpr int kCopies = 16;       // LDS copies of the 256-bin histogram (against atomic conflicts)
 constexpr int kMergeCopies = 4;   // global copies of a row's histogram per round (WG w -> copy w mod C)
 constexpr uint32_t kFlagTimeout = 1u;
@@ -195,20 +195,19 @@ __device__ __forceinline__ uint32_t block_scan_total(uint32_t a, uint32_t* s_w /
 // is left); later rounds cut the varying low idx_bits of ~index (its top
 // 32 - idx_bits bits are ones for every valid index).  shift: bit position
 // of round r's digit inside its 32-bit word; width: its bits.
-template <int F>
-__device__ __forceinline__ int digit_shift(int r, int idx_bits) {
+__device__ __forceinline__ int digit_shift(int F, int r, int idx_bits) {
     if (r < 4) {
         const int s = 32 - F - 8 * r;
         return s < 0 ? 0 : s;
     }
     return idx_bits - 8 - 8 * (r - 4);
 }
-template <int F>
-__device__ __forceinline__ int digit_width(int r) {
+__device__ __forceinline__ int digit_width(int F, int r) {
     if (r == 0) return F;
     if (r < 4) return min(8, 32 - F - 8 * (r - 1));
     return 8;
 }
+__device__ __forceinline__ uint32_t digit_mask(int F, int r) { return (1u << digit_width(F, r)) - 1u; }
 __device__ __forceinline__ int num_rounds(int idx_bits) { return 4 + idx_bits / 8; }
 
 // The composite prefix resolved so far: key bits (kpfx under kmask) and
@@ -217,11 +216,10 @@ struct Prefix {
     uint32_t kpfx, kmask, ipfx, imask;
     // value selects only (a branch that picks the field to update would
     // put the struct in scratch memory)
-    template <int F>
-    __device__ void add(int r, uint32_t b, int idx_bits) {
-        const int s = digit_shift<F>(r, idx_bits);
+    __device__ void add(int F, int r, uint32_t b, int idx_bits) {
+        const int s = digit_shift(F, r, idx_bits);
         const bool in_key = r < 4;
-        const uint32_t bb = b << s, mm = ((1u << digit_width<F>(r)) - 1u) << s;
+        const uint32_t bb = b << s, mm = digit_mask(F, r) << s;
         kpfx |= in_key ? bb : 0u;
         kmask |= in_key ? mm : 0u;
         ipfx |= in_key ? 0u : bb;
@@ -238,34 +236,47 @@ struct Prefix {
     }
 };
 
-// Relation of an element to the prefix after rounds 0..R of the 8-bit
-// schedule: returns 1 when it
-// is above it (a winner; *slot = 256 * deciding round + its digit there),
-// 2 when it matches it (in the bucket), 0 otherwise.  Composites compare as
+// Where the first round's digit comes from: the top F bits of the key, or
+// (win) the 12-bit first digit seen through a window of 256 bins starting
+// at bin LO (bins above the window fold into its top bin).
+struct FirstDigit {
+    int F;
+    bool win;
+    uint32_t LO;
+    __device__ __forceinline__ uint32_t of(uint32_t key) const {
+        return win ? min((key >> 20) - LO, 255u) : key >> (32 - F);
+    }
+};
+
+// Position-counter slot (256 * round + digit) of a winner whose key differs
+// from the prefix, x = the differing key bits (non-zero): the round is the
+// one whose digit holds the top differing bit.
+__device__ __forceinline__ uint32_t key_slot(uint32_t key, uint32_t x, const FirstDigit& fd, int idx_bits) {
+    const int p = 31 - __builtin_clz(x);
+    if (p >= 32 - fd.F) return fd.of(key);
+    const int r = 1 + (31 - fd.F - p) / 8;
+    return 256u * (uint32_t)r + ((key >> digit_shift(fd.F, r, idx_bits)) & digit_mask(fd.F, r));
+}
+
+// Relation of an element to the prefix after the rounds done: returns 1 when
+// it is above it (a winner; *slot = its position-counter slot), 2 when it
+// matches it (in the bucket), 0 otherwise.  Composites compare as
 // (key, ~index) pairs.
-__device__ __forceinline__ uint32_t classify(uint32_t key, uint32_t ni, const Prefix& pf, bool idx_rounds,
+__device__ __forceinline__ uint32_t classify(uint32_t key, uint32_t ni, const Prefix& pf, const FirstDigit& fd,
                                              int idx_bits, uint32_t* slot) {
     if (key == 0u) return 0u;
-    if (!idx_rounds) {
-        const uint32_t s = key & pf.kmask;
-        if (s == pf.kpfx) return 2u;
+    const uint32_t s = key & pf.kmask;
+    if (s != pf.kpfx) {
         if (s < pf.kpfx) return 0u;
-        const uint32_t r = (uint32_t)__builtin_clz(s ^ pf.kpfx) >> 3;
-        *slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
+        *slot = key_slot(key, s ^ pf.kpfx, fd, idx_bits);
         return 1u;
     }
-    if (key != pf.kpfx) {
-        if (key < pf.kpfx) return 0u;
-        const uint32_t r = (uint32_t)__builtin_clz(key ^ pf.kpfx) >> 3;
-        *slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
-        return 1u;
-    }
-    const uint32_t s = ni & pf.imask;
-    if (s == pf.ipfx) return 2u;
-    if (s < pf.ipfx) return 0u;
-    const int lead = __builtin_clz(s ^ pf.ipfx) - (32 - idx_bits);  // leading bit inside the index digits
+    const uint32_t t = ni & pf.imask;
+    if (t == pf.ipfx) return 2u;
+    if (t < pf.ipfx) return 0u;
+    const int lead = __builtin_clz(t ^ pf.ipfx) - (32 - idx_bits);  // leading bit inside the index digits
     const int r = 4 + lead / 8;
-    *slot = (uint32_t)r * 256u + ((ni >> digit_shift<8>(r, idx_bits)) & 0xFFu);
+    *slot = (uint32_t)r * 256u + ((ni >> digit_shift(fd.F, r, idx_bits)) & 0xFFu);
     return 1u;
 }
 
@@ -340,16 +351,16 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
 // than kSmall match, then an exact rank of the rest.  Uses the scratch
 // `hist` (kCopies x 257 words), `small`, `scan`, `sel` and the counter
 // `ctr`.  Every thread of the WG calls it.
-template <int BLOCK, int F>
+template <int BLOCK>
 __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
-                              int idx_bits, uint32_t* hist, uint64_t* small, uint32_t* scan, uint32_t* sel,
+                              int F, int idx_bits, uint32_t* hist, uint64_t* small, uint32_t* scan, uint32_t* sel,
                               uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
     const int tid = threadIdx.x;
     const int nrounds = num_rounds(idx_bits);
     auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
     auto c_digit = [&](uint64_t c, int r) -> uint32_t {
-        const int s = digit_shift<F>(r, idx_bits);
-        return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & ((1u << digit_width<F>(r)) - 1u);
+        const int s = digit_shift(F, r, idx_bits);
+        return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & digit_mask(F, r);
     };
     // f(entry) for every candidate, four LDS loads in flight per thread
     // (entries past m read as 0, which matches no prefix)
@@ -401,7 +412,7 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
         });
         need = need2;
         W += above;
-        pf.add<F>(r, b, idx_bits);
+        pf.add(F, r, b, idx_bits);
         mb = nb;
         ++r;
         lds_sync();
@@ -451,9 +462,9 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
 // (`need` == count in b after the elements above), else to positions
 // (this WG's range in b) of the candidate buffer.
 template <int BLOCK>
-__device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, uint32_t bin0_sub, uint32_t need, uint32_t W, RowWorkspace* ws,
-                          int p, int C, int w, int G, uint32_t* status, uint32_t& b_out, uint32_t& above_out,
-                          uint32_t& hb_out) {
+__device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, int mslot, bool strict, uint32_t bin0_sub,
+                                          uint32_t need, uint32_t W, RowWorkspace* ws, int p, int C, int w, int G,
+                                          uint32_t* status, uint32_t& b_out, uint32_t& above_out, uint32_t& hb_out) {
     const int t = threadIdx.x;
     const bool owner = t < 256;
     const int j = 255 - t;
@@ -464,7 +475,7 @@ __device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, uint32_t bin0_
         for (int c = 0; c < kCopies; ++c) cnt += sm.hist[c * 257 + j];
         if (j == 0) cnt -= bin0_sub;
         if (G > 1) {
-            uint64_t* h = &ws->hist[p][r][0][0];
+            uint64_t* h = &ws->hist[p][mslot][0][0];
             const int mc = w % C;
             const uint64_t old = add_dev(&h[mc * 256 + j], (uint64_t)((1ull << 32) | cnt));
             // poll the copies (all loads in flight together) until every
@@ -500,9 +511,13 @@ __device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, uint32_t bin0_
     }
     lds_sync();
     uint32_t b = uniform(sm.sel[0]), above = uniform(sm.sel[1]), hb = uniform(sm.sel[2]);
-    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: cannot happen for valid input
-        if (t == 0) raise_flag(status, kFlagCapacity);
-        b = 0; above = 0; hb = 0;
+    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: an error unless !strict
+        if (strict && t == 0) raise_flag(status, kFlagCapacity);
+        b_out = 0;
+        above_out = 0;
+        hb_out = strict ? 0u : 0xFFFFFFFFu;
+        lds_sync();
+        return;
     }
     if (owner && (uint32_t)j >= b) {
         const bool whole = (uint32_t)j > b || hb == need - above;
@@ -658,6 +673,14 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         if (tid < (kCopies * 257) % 4) sm.hist[kCopies * 257 / 4 * 4 + tid] = 0u;
     };
 
+    // the window round's sample (the row's first chunks, one per thread) is
+    // loaded together with the slice.  Only long rows (split over many WGs,
+    // where a second merge round is expensive) take the window round: for
+    // shorter rows its extra steps cost more than they save (measured).
+    const bool try_win = L >= 524288;
+    const int nsc = min(nchunks, BLOCK);
+    uint4 sraw = uint4{0u, 0u, 0u, 0u};
+    if (try_win && tid < nsc) sraw = *reinterpret_cast<const uint4*>(base + (uint32_t)tid * 16u);
     if constexpr (RESIDENT) load_tile(c_begin);
 
     // ---------------- screening rounds over the row
@@ -667,46 +690,115 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     uint32_t hb = 0;              // size of the current bucket
     int R = 0;                    // last round done
     bool whole = false;           // the last bucket is taken whole
-    for (int r = 0;; ++r) {
+    FirstDigit fd{8, false, 0u};  // first-round digit (set by the window round when it succeeds)
+    uint32_t bwin = 0;            // the window round's threshold bin
+    int slot_base = 0;            // merge slot of round 0 of the 8-bit schedule
+
+    // -- window round.  A sample (the row's first chunks, one per thread)
+    // estimates the threshold: the first-digit bin b8 (8 bits) of its
+    // element of rank 1.25 * k * S / L + 64 (the k-th largest of the row is
+    // expected near rank k * S / L).  Then every WG histograms the 12-bit
+    // first digit of its elements at or above LO = b8 << 4 only, in a window
+    // of 256 bins from LO (the top bin also takes all bins above the
+    // window), merged like any round.  When the threshold falls inside the
+    // window below its top bin, the counts it needs are exact and the first
+    // round is done at 12-bit resolution; otherwise the row starts over with
+    // the 8-bit schedule.
+    if (try_win) {
+        uint32_t sk[4];
+        {
+            const uint32_t raw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ix = 4 * tid - off + e;
+                sk[e] = (tid < nsc && ix >= 0 && ix < L) ? key_of(__uint_as_float(raw[e])) : 0u;
+            }
+        }
+        const uint32_t s_valid = (uint32_t)min(L, 4 * nsc - off);
+        const uint64_t est64 = ((uint64_t)k * s_valid * 5u) / (4u * (uint64_t)L) + 64u;
+        const uint32_t est = (uint32_t)(est64 < s_valid ? est64 : s_valid);
+        uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
+        clear_hist();
+        lds_sync();
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (sk[e] != 0u) atomicAdd(&hc[sk[e] >> 24], 1u);
+        lds_sync();
+        uint32_t b8, ab8, hb8;
+        local_select<BLOCK, 256, kCopies, 257, false>(sm.hist, 0u, est, sm.scan, sm.sel, P.status, b8, ab8, hb8);
+        const uint32_t LO = hb8 ? b8 << 4 : 0u;
         opaque_keys();
         clear_hist();
         lds_sync();
-        uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
-        if (r == 0) {
-            // every slot of the slice's chunks adds into its top byte's bin;
-            // the few empty ones (key 0) land in bin 0 and are subtracted
-            // after.  Chunks past the slice are skipped (one test per chunk).
-            visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> 24], 1u); });
-        } else if (r < 4) {
-            const int sh = digit_shift<8>(r, idx_bits);
-            visit([&](uint32_t key, uint32_t) {
-                if ((key != 0u) & ((key & pf.kmask) == pf.kpfx)) atomicAdd(&hc[(key >> sh) & 0xFFu], 1u);
-            });
-        } else {
-            const int sh = digit_shift<8>(r, idx_bits);
-            visit([&](uint32_t key, uint32_t ni) {
-                if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
-            });
-        }
+        visit_chunks([&](uint32_t key) {
+            const uint32_t b12 = key >> 20;
+            if (b12 >= LO) atomicAdd(&hc[min(b12 - LO, 255u)], 1u);
+        });
         lds_sync();
-        uint32_t b, above;
-        threshold<BLOCK>(sm, r, r == 0 ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status, b, above, hb);
-        need -= above;
-        W += above;
-        pf.add<8>(r, b, idx_bits);
-        R = r;
-        if (hb == need) { whole = true; break; }
-        if (hb <= (uint32_t)kCap || r + 1 >= nrounds) break;
+        uint32_t b, above, hw;
+        threshold<BLOCK>(sm, 0, 0, false, LO == 0u ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status, b, above,
+                         hw);
+        if (hw != 0xFFFFFFFFu && b < 255u) {
+            fd = FirstDigit{12, true, LO};
+            bwin = b;
+            hb = hw;
+            need -= above;
+            W += above;
+            pf.kpfx = (LO + b) << 20;
+            pf.kmask = 0xFFFu << 20;
+            whole = hb == need;
+        } else {
+            slot_base = 1;
+        }
     }
+    const int F = fd.F;
+    if (!fd.win || (!whole && hb > (uint32_t)kCap)) {
+        for (int r = fd.win ? 1 : 0;; ++r) {
+            opaque_keys();
+            clear_hist();
+            lds_sync();
+            uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
+            if (r == 0) {
+                // every slot of the slice's chunks adds into its top byte's
+                // bin; the few empty ones (key 0) land in bin 0 and are
+                // subtracted after.  Chunks past the slice are skipped.
+                visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> 24], 1u); });
+            } else if (r < 4) {
+                const int sh = digit_shift(F, r, idx_bits);
+                const uint32_t dm = digit_mask(F, r);
+                visit([&](uint32_t key, uint32_t) {
+                    if ((key != 0u) & ((key & pf.kmask) == pf.kpfx)) atomicAdd(&hc[(key >> sh) & dm], 1u);
+                });
+            } else {
+                const int sh = digit_shift(F, r, idx_bits);
+                visit([&](uint32_t key, uint32_t ni) {
+                    if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
+                });
+            }
+            lds_sync();
+            uint32_t b, above;
+            threshold<BLOCK>(sm, r, r + slot_base, true, r == 0 ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status,
+                             b, above, hb);
+            need -= above;
+            W += above;
+            pf.add(F, r, b, idx_bits);
+            R = r;
+            if (hb == need) { whole = true; break; }
+            if (hb <= (uint32_t)kCap || r + 1 >= nrounds) break;
+        }
+    }
+    const int last_slot = R + (fd.win ? 0 : slot_base);  // merge slots used: 0 .. last_slot
 
     // ---------------- collection over the row
     // Winners go to the output; the bucket goes to the output when taken
     // whole, else to the candidate buffer (LDS) or the row's stage (G > 1).
     const bool idx_rounds = R >= 4;
     uint32_t bslot;  // position counter of the bucket: its bin in round R
-    {
-        const int s = digit_shift<8>(R, idx_bits);
-        bslot = (uint32_t)R * 256u + ((R < 4 ? (pf.kpfx >> s) : (pf.ipfx >> s)) & 0xFFu);
+    if (R == 0) {
+        bslot = fd.win ? bwin : pf.kpfx >> 24;
+    } else {
+        const int sft = digit_shift(F, R, idx_bits);
+        bslot = (uint32_t)R * 256u + (((R < 4 ? pf.kpfx : pf.ipfx) >> sft) & digit_mask(F, R));
     }
     uint64_t* const gstage = multi ? &ws->stage[p][0] : nullptr;
     bool overflow = false;
@@ -720,7 +812,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     auto selected = [&](uint32_t key, uint32_t ni) -> bool {
         if (!idx_rounds) return ((key & km) >= kp) & (key != 0u);
         uint32_t slot;
-        return classify(key, ni, pf, true, idx_bits, &slot) != 0u;
+        return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
     };
     // place one selected element (a winner or a bucket element)
     auto place = [&](uint32_t key, uint32_t ni) {
@@ -729,10 +821,9 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         if (!idx_rounds) {
             const uint32_t s = key & km;
             ab = s > kp;
-            const uint32_t r = (uint32_t)__builtin_clz((s ^ kp) | 1u) >> 3;
-            if (ab) slot = r * 256u + ((key >> (24u - 8u * r)) & 0xFFu);
+            if (ab) slot = key_slot(key, s ^ kp, fd, idx_bits);
         } else {
-            ab = classify(key, ni, pf, true, idx_bits, &slot) == 1u;
+            ab = classify(key, ni, pf, fd, idx_bits, &slot) == 1u;
         }
         const uint32_t pos = atomicAdd(&sm.pos[slot], 1u);
         if (ab || whole) {
@@ -816,7 +907,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
         lds_sync();
-        finish_bucket<BLOCK, 8>(sm.cand, m, need, W, pf, R + 1, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, sm.ctr,
+        finish_bucket<BLOCK>(sm.cand, m, need, W, pf, R + 1, F, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, sm.ctr,
                                 out, k, P.status);
     }
 
@@ -832,7 +923,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             if ((i / 256u) % kMergeCopies < uc) st_dev(&h[i], (uint64_t)0);
         for (uint32_t i = tid; i < us; i += BLOCK) st_dev(&ws->stage[op][i], (uint64_t)0);
         if (tid == 0) {
-            st_dev(&ws->used_rounds[p], (uint32_t)(R + 1));
+            st_dev(&ws->used_rounds[p], (uint32_t)(last_slot + 1));
             st_dev(&ws->used_copies[p], (uint32_t)C);
             st_dev(&ws->used_stage[p], whole ? 0u : (hb > (uint32_t)kCap ? (uint32_t)kCap : hb));
             st_dev(&ws->parity, (uint32_t)op);
@@ -1099,7 +1190,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     if (keep && hb > 0u && b0 >= lo) {
         need -= above;
         W += above;
-        pf.add<F>(0, b0, idx_bits);
+        pf.add(F, 0, b0, idx_bits);
         whole = hb == need;
         // every element at or above bin b0 is buffered: winners (above b0)
         // to the output, the bucket (bin b0) to the front of the buffer, or
@@ -1126,7 +1217,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
         if (whole) return;
         lds_sync();
-        finish_bucket<BLOCK, F>(sm.cand, hb, need, W, pf, 1, idx_bits, sm.h.h8, sm.small, sm.scan, sm.sel,
+        finish_bucket<BLOCK>(sm.cand, hb, need, W, pf, 1, F, idx_bits, sm.h.h8, sm.small, sm.scan, sm.sel,
                                 &sm.ctr[2], out, k, P.status);
         return;
     }
@@ -1150,7 +1241,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
     need -= above;
     W += above;
-    pf.add<F>(0, b0, idx_bits);
+    pf.add(F, 0, b0, idx_bits);
     whole = hb == need;
     // ---------------- further rounds (only when the bucket is still large)
     for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
@@ -1160,8 +1251,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
         lds_sync();
         uint32_t* const hc = sm.h.h8 + (tid % kCopies) * 257;
-        const int sh = digit_shift<F>(r, idx_bits);
-        const uint32_t dm = (1u << digit_width<F>(r)) - 1u;
+        const int sh = digit_shift(F, r, idx_bits);
+        const uint32_t dm = digit_mask(F, r);
         stream([&](const uint32_t* keys, int ct) {
             const int ibase = 4 * (ct + tid) - off;
 #pragma unroll
@@ -1179,7 +1270,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         local_select<BLOCK, 256, kCopies, 257>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, b, above, hb);
         need -= above;
         W += above;
-        pf.add<F>(r, b, idx_bits);
+        pf.add(F, r, b, idx_bits);
         R = r;
         whole = hb == need;
     }
@@ -1247,7 +1338,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     if (overflow) raise_flag(P.status, kFlagCapacity);
     if (whole) return;
     lds_sync();
-    finish_bucket<BLOCK, F>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, idx_bits,
+    finish_bucket<BLOCK>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, F, idx_bits,
                             sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, k, P.status);
 }
 

@@ -131,6 +131,21 @@ def _edge_cases():
     add("subnormals_at_threshold", d, 3000)
     add("ascending_ramp", np.arange(70000), 2048)
     add("descending_ramp", -np.arange(70000), 2048)
+    # rows whose first chunks misrepresent the rest (a sampled estimate of
+    # the threshold is far off): the exact fallback must take over
+    add("descending_values_k30000", np.arange(70000, 0, -1), 30000)
+    hi_head = rng.standard_normal(40000)
+    hi_head[:6000] += 50.0
+    add("large_values_first", hi_head, 2048)
+    lo_head = rng.standard_normal(40000)
+    lo_head[:6000] -= 50.0
+    add("small_values_first", lo_head, 2048)
+    # long rows (the ones that take the sampled window round)
+    long_hi = rng.standard_normal(600000)
+    long_hi[:1000] += 50.0  # fewer than k large values, all in the sample
+    add("long_row_large_values_first", long_hi, 2048)
+    add("long_row_descending_k300000", np.arange(600000, 0, -1), 300000)
+    add("long_row_normal", rng.standard_normal(600000), 2048)
     # 256 distinct values, each 256 times: keys agree on their top 24 bits
     base = np.float32(1.0).view(np.uint32)
     add("top24_bits_shared", (base + (np.arange(65536) % 256).astype(np.uint32)).view(np.float32), 2048)
