@@ -353,8 +353,8 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
 // `ctr`.  Every thread of the WG calls it.
 template <int BLOCK>
 __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
-                              int F, int idx_bits, uint32_t* hist, uint64_t* small, uint32_t* scan, uint32_t* sel,
-                              uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
+                              int F, int idx_bits, bool cleared, uint32_t* hist, uint64_t* small, uint32_t* scan,
+                              uint32_t* sel, uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
     const int tid = threadIdx.x;
     const int nrounds = num_rounds(idx_bits);
     auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
@@ -380,12 +380,13 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
     uint32_t mb = m;        // entries still matching the prefix
     bool in_small = false;  // they are already gathered in small[0 .. ctr[1])
     while (mb > (uint32_t)kSmall && r < nrounds) {
-        {
+        if (!cleared) {
             uint4* const h4 = reinterpret_cast<uint4*>(hist);
             for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
             if (tid < 2) ctr[tid] = 0u;
+            lds_sync();
         }
-        lds_sync();
+        cleared = false;
         uint32_t* const hc = hist + (tid % kCopies) * 257;
         for_each_cand([&](uint64_t c) {
             if (c_match(c)) atomicAdd(&hc[c_digit(c, r)], 1u);
@@ -874,6 +875,10 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     // ---------------- on-chip finish of the last bucket
     if (!whole) {
         uint32_t m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
+        // the finisher's first histogram is cleared while the pull's loads
+        // are in flight
+        clear_hist();
+        if (tid < 2) sm.ctr[tid] = 0u;
         if (multi) {
             // pull the staged bucket: every entry is non-zero once written.
             // Eight loads in flight per thread; entries not written yet are
@@ -907,8 +912,8 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
         lds_sync();
-        finish_bucket<BLOCK>(sm.cand, m, need, W, pf, R + 1, F, idx_bits, sm.hist, sm.small, sm.scan, sm.sel, sm.ctr,
-                                out, k, P.status);
+        finish_bucket<BLOCK>(sm.cand, m, need, W, pf, R + 1, F, idx_bits, true, sm.hist, sm.small, sm.scan, sm.sel,
+                                sm.ctr, out, k, P.status);
     }
 
     if (multi) {
@@ -1217,7 +1222,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
         if (whole) return;
         lds_sync();
-        finish_bucket<BLOCK>(sm.cand, hb, need, W, pf, 1, F, idx_bits, sm.h.h8, sm.small, sm.scan, sm.sel,
+        finish_bucket<BLOCK>(sm.cand, hb, need, W, pf, 1, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
                                 &sm.ctr[2], out, k, P.status);
         return;
     }
@@ -1339,7 +1344,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     if (whole) return;
     lds_sync();
     finish_bucket<BLOCK>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, F, idx_bits,
-                            sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, k, P.status);
+                            false, sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, k, P.status);
 }
 
 // ----------------------------------------------------------------- host side
