@@ -11,6 +11,8 @@ Contents
   the valid positions of each row by (value descending, index ascending) with
   IEEE float comparisons and keep the first k.  Compiled with gcc, no
   fast-math.
+* ``topk_sorted`` - the same selection in that order, with the selected
+  values (the ordered output of the article's radix_topk, section 02).
 * ``pages_radix`` - the article's radix-select method restated in Python
   (mapping, digit histograms, threshold bucket, collection), a second route
   used to pin the first.
@@ -64,6 +66,8 @@ def _load():
             I = ctypes.c_int32
             lib.oracle_topk.argtypes = [P, I, I, P, I, P]
             lib.oracle_topk.restype = ctypes.c_int
+            lib.oracle_topk_sorted.argtypes = [P, I, I, P, I, P, P]
+            lib.oracle_topk_sorted.restype = ctypes.c_int
             lib.oracle_kth_largest.argtypes = [P, I, I, I, P]
             lib.oracle_kth_largest.restype = ctypes.c_int
             _lib = lib
@@ -90,6 +94,30 @@ def topk(x: np.ndarray, k: int, lengths: Optional[np.ndarray] = None) -> np.ndar
     if rc != ORACLE_OK:
         raise ValueError("oracle_topk failed with code %d" % rc)
     return out
+
+
+def topk_sorted(x: np.ndarray, k: int, lengths: Optional[np.ndarray] = None):
+    """Ordered oracle selection: (int32 [rows, k] indices in (value desc,
+    index asc) order, float32 [rows, k] values at those indices, -inf beside
+    each -1)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, n = x.shape
+    out = np.empty((rows, k), dtype=np.int32)
+    val = np.empty((rows, k), dtype=np.float32)
+    lp = None
+    if lengths is not None:
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        assert lengths.shape == (rows,)
+        lp = lengths.ctypes.data
+    rc = lib.oracle_topk_sorted(x.ctypes.data, rows, n, lp, int(k), out.ctypes.data, val.ctypes.data)
+    if rc == ORACLE_ERR_NAN:
+        raise ValueError("NaN among the valid logits (outside the selector's contract)")
+    if rc != ORACLE_OK:
+        raise ValueError("oracle_topk_sorted failed with code %d" % rc)
+    return out, val
 
 
 def kth_largest(row: np.ndarray, k: int, length: Optional[int] = None) -> float:

@@ -21,6 +21,9 @@ Than FlashInfer"):
                  above T, then elements equal to T in scan (index) order until
                  k are held.
 
+With the pseudocode's need_sorted option the collected output is then sorted
+in descending order (``radix_topk_sorted``).
+
 Pure-Python loops: meant for rows of a few thousand elements at most.
 Readings where the article leaves a step open:
 - the pseudocode works on non-negative integers; it is applied here to the
@@ -28,7 +31,9 @@ Readings where the article leaves a step open:
 - ``highest_power_of_10(0)`` is undefined in the article; it is taken as 1 so a
   row whose largest key is 0 still runs one (trivial) digit round;
 - -0.0 is mapped to the key of +0.0 (the two compare equal as floats, so they
-  must tie); NaN keys are not produced (NaN is outside the contract).
+  must tie); NaN keys are not produced (NaN is outside the contract);
+- the descending sort of need_sorted is taken as stable: equal values keep the
+  order in which the collection took them, which is index order.
 """
 
 from __future__ import annotations
@@ -111,3 +116,11 @@ def radix_topk_row(values: Sequence[float], k: int, length: int = None) -> List[
         return list(range(L)) + [-1] * (k - L)
     out, _ = radix_topk_indices(values[:L], k)
     return out
+
+
+def radix_topk_sorted(values: Sequence[float], k: int) -> List[int]:
+    """need_sorted: the collected indices sorted by value, largest first; a
+    stable sort, so equal values stay in collection (= index) order."""
+    out, _ = radix_topk_indices(values, k)
+    keys = [float_to_ordered_u32(v) for v in values]
+    return sorted(out, key=lambda i: keys[i], reverse=True)

@@ -31,8 +31,16 @@
  *  - NaN is outside the contract: a NaN among the valid positions makes the
  *    oracle return ORACLE_ERR_NAN.
  * Each output row is written in (value desc, index asc) order; callers that
- * compare against the GPU path compare sorted index sets.
+ * compare against the unsorted GPU path compare sorted index sets.
+ *
+ * Ordered output (oracle_topk_sorted): section 02's radix_topk has a
+ * need_sorted option that sorts the collected output in descending order.
+ * The order among equal values is not stated; the reading taken is the
+ * same rule that decides which of them are selected: lowest index first.
+ * The values returned are the logits at the selected positions, bit for bit
+ * (so -0.0 stays -0.0), and -INFINITY beside each -1.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -118,5 +126,22 @@ int oracle_kth_largest(const float* x, int32_t n, int32_t L, int32_t k, float* k
     qsort(buf, (size_t)L, sizeof(oracle_elem), oracle_cmp);
     *kth = buf[k - 1].v;
     free(buf);
+    return ORACLE_OK;
+}
+
+/* oracle_topk, each row in (value desc, index asc) order, plus the selected
+ * values.  out_val: [rows, k] float32 (host memory); out_val[j] is the logit
+ * at out_idx[j], or -INFINITY where out_idx[j] is -1. */
+int oracle_topk_sorted(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                       int32_t* out_idx, float* out_val) {
+    if (!out_val && rows > 0) return ORACLE_ERR_ARG;
+    int rc = oracle_topk(logits, rows, n, lengths, k, out_idx);
+    if (rc != ORACLE_OK) return rc;
+    for (int32_t r = 0; r < rows; ++r) {
+        const float* x = logits + (size_t)r * (size_t)n;
+        const int32_t* o = out_idx + (size_t)r * (size_t)k;
+        float* v = out_val + (size_t)r * (size_t)k;
+        for (int32_t j = 0; j < k; ++j) v[j] = o[j] >= 0 ? x[o[j]] : -INFINITY;
+    }
     return ORACLE_OK;
 }

@@ -46,6 +46,29 @@ def check_row_invariants(x_row: np.ndarray, L: int, k: int, sel: np.ndarray) -> 
         assert tsel.max() < tun.min(), "ties at the threshold not taken lowest index first"
 
 
+def check_row_order(x_row: np.ndarray, L: int, k: int, sel: np.ndarray, vals=None) -> None:
+    """Raise AssertionError unless ``sel`` is the correct selection (as in
+    check_row_invariants) laid out in order: values descending, equal values
+    by index ascending, the -1 slots last; and, when ``vals`` is given, each
+    value is the logit at its index bit for bit, -inf beside each -1."""
+    sel = np.asarray(sel)
+    check_row_invariants(x_row, L, k, sel)
+    take = min(k, L)
+    assert np.all(sel[:take] >= 0) and np.all(sel[take:] == -1), "-1 slots not at the end"
+    s = sel[:take].astype(np.int64)
+    xv = x_row.astype(np.float64)[s]
+    if take > 1:
+        a, b = xv[:-1], xv[1:]
+        ok = (a > b) | ((a == b) & (s[:-1] < s[1:]))
+        assert np.all(ok), "out of order at position %d" % int(np.argmin(ok))
+    if vals is not None:
+        vals = np.asarray(vals, dtype=np.float32)
+        assert vals.shape == (k,)
+        want = x_row[s].astype(np.float32)
+        assert np.array_equal(vals[:take].view(np.uint32), want.view(np.uint32)), "values differ from the logits"
+        assert np.all(vals[take:] == -np.inf), "padding values are not -inf"
+
+
 def same_sets(a: np.ndarray, b: np.ndarray) -> bool:
     """Row-wise equality of two [rows, k] index arrays as sorted multisets."""
     return np.array_equal(np.sort(a, axis=-1), np.sort(b, axis=-1))

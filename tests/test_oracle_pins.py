@@ -23,7 +23,7 @@ import pytest
 
 import oracle
 from oracle import pages_radix
-from tests.selection_checks import check_row_invariants, same_sets
+from tests.selection_checks import check_row_invariants, check_row_order, same_sets
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SUB = np.float32(1e-45)  # smallest positive subnormal float32
@@ -285,3 +285,124 @@ def test_oracle_rejects_nan_and_bad_arguments():
 def test_same_sets_helper():
     assert same_sets(np.array([[1, 2, 3]]), np.array([[3, 1, 2]]))
     assert not same_sets(np.array([[1, 2, 3]]), np.array([[3, 1, 4]]))
+
+
+# ---------------------------------------------------------------- ordered output (need_sorted)
+
+def _ordered_ok(x, seq):
+    """Defining property of the ordered output: values never increase, equal
+    values have increasing indices."""
+    return all(x[a] > x[b] or (x[a] == x[b] and a < b) for a, b in zip(seq, seq[1:]))
+
+
+def test_sorted_brute_force_tiny_rows():
+    """Every ordered k-sequence of distinct valid positions that is a correct
+    selection and satisfies the order property: exactly one exists, and it is
+    the oracle's ordered output."""
+    rng = np.random.default_rng(99)
+    checked = 0
+    for n in range(1, 7):
+        for _ in range(25):
+            x = rng.choice(ALPHABET, size=n)
+            L = int(rng.integers(0, n + 1)) if rng.random() < 0.3 else n
+            xv = x.astype(np.float64)
+            for k in range(1, n + 1):
+                idx, vals = oracle.topk_sorted(x[None, :], k, np.array([L], np.int32))
+                take = min(k, L)
+                found = []
+                for seq in itertools.permutations(range(L), take):
+                    row = np.array(list(seq) + [-1] * (k - take), np.int32)
+                    try:
+                        check_row_invariants(x, L, k, row)
+                    except AssertionError:
+                        continue
+                    if _ordered_ok(xv, seq):
+                        found.append(list(seq))
+                assert len(found) == 1, (x, L, k, found)
+                assert idx[0, :take].tolist() == found[0] and np.all(idx[0, take:] == -1)
+                check_row_order(x, L, k, idx[0], vals[0])
+                checked += 1
+    assert checked > 200
+
+
+def test_sorted_matches_article_method_with_need_sorted():
+    rng = np.random.default_rng(17)
+    for trial in range(200):
+        n = int(rng.integers(1, 300))
+        kind = trial % 3
+        if kind == 0:
+            x = rng.choice(ALPHABET, size=n)
+        elif kind == 1:
+            x = rng.integers(-3, 4, size=n).astype(np.float32)
+        else:
+            x = rng.standard_normal(n).astype(np.float32)
+        k = int(rng.integers(1, n + 1))
+        idx, _ = oracle.topk_sorted(x[None, :], k)
+        assert idx[0].tolist() == pages_radix.radix_topk_sorted(x.tolist(), k)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_sorted_matches_numpy_lexsort_on_workloads(name):
+    import workloads as W
+
+    w = W.generate(name)
+    rows = range(w.x.shape[0]) if w.x.shape[0] <= 8 else range(0, w.x.shape[0], 9)
+    for r in rows:
+        L = w.x.shape[1] if w.lengths is None else int(w.lengths[r])
+        lr = None if w.lengths is None else w.lengths[r:r + 1]
+        idx, vals = oracle.topk_sorted(w.x[r:r + 1], w.k, lr)
+        assert np.array_equal(idx[0], _numpy_select(w.x[r], L, w.k))
+        check_row_order(w.x[r], L, w.k, idx[0], vals[0])
+
+
+@pytest.mark.parametrize("L,k", [(1, 1), (5, 3), (100, 100), (4096, 2048), (3, 2048)])
+def test_sorted_closed_forms(L, k):
+    n = max(L, k)
+    idx = np.arange(n)
+    lengths = np.array([L], np.int32)
+    take = min(k, L)
+    low = list(range(take)) + [-1] * (k - take)
+    for x in (np.full(n, 0.25, np.float32), (-idx).astype(np.float32), np.full(n, -np.inf, np.float32)):
+        got, vals = oracle.topk_sorted(x[None], k, lengths)
+        assert got[0].tolist() == low
+        assert np.array_equal(vals[0, :take], x[:take]) and np.all(vals[0, take:] == -np.inf)
+    # ascending ramp: the last positions, largest first
+    got, vals = oracle.topk_sorted(idx.astype(np.float32)[None], k, lengths)
+    assert got[0].tolist() == list(range(L - 1, L - 1 - take, -1)) + [-1] * (k - take)
+
+
+def test_sorted_values_keep_the_sign_of_zero():
+    x = np.array([-0.0, 0.0, -1.0, -0.0], np.float32)
+    idx, vals = oracle.topk_sorted(x[None], 3)
+    assert idx[0].tolist() == [0, 1, 3]
+    assert vals[0].view(np.uint32).tolist() == [0x80000000, 0, 0x80000000]
+
+
+def test_order_checker_rejects_planted_mistakes():
+    x = np.array([3, 5, 5, 5, 1, 7, -0.0], np.float32)
+    idx, vals = oracle.topk_sorted(x[None], 4)
+    check_row_order(x, 7, 4, idx[0], vals[0])
+    bad = idx[0].copy()
+    bad[[1, 2]] = bad[[2, 1]]  # equal values, indices descending
+    with pytest.raises(AssertionError):
+        check_row_order(x, 7, 4, bad)
+    bad = idx[0].copy()
+    bad[[0, 1]] = bad[[1, 0]]  # smaller value first
+    with pytest.raises(AssertionError):
+        check_row_order(x, 7, 4, bad)
+    badv = vals[0].copy()
+    badv[0] = 6.0
+    with pytest.raises(AssertionError):
+        check_row_order(x, 7, 4, idx[0], badv)
+    # -0.0 reported as +0.0 is caught
+    i2, v2 = oracle.topk_sorted(x[None], 7)
+    v2 = v2[0].copy()
+    v2[-1] = 0.0
+    with pytest.raises(AssertionError):
+        check_row_order(x, 7, 7, i2[0], v2)
+    # padding not at the end is caught
+    i3, _ = oracle.topk_sorted(x[None], 7, np.array([5], np.int32))
+    row = i3[0].copy()
+    row[[0, 5]] = row[[5, 0]]
+    with pytest.raises(AssertionError):
+        check_row_order(x, 5, 7, row)
