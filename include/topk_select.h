@@ -83,6 +83,30 @@ int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* len
                 int32_t* out_idx, topk_select_stream_t stream);
 
 /*
+ * topk_select_sorted - the same selection, each row in order: values
+ * descending, equal values by index ascending, the -1 slots (rows whose
+ * valid length L is below k) last.  The TopK article, section 02: the
+ * radix_topk pseudocode's need_sorted option sorts the collected output in
+ * descending order; the order among equal values is not stated there, the
+ * one taken is the rule that selects them (lowest index first).
+ *
+ *   out_val  device, float[rows * k], or NULL (indices only).  out_val[j] is
+ *            the logit at out_idx[j] bit for bit (-0.0 stays -0.0), and
+ *            -INFINITY where out_idx[j] is -1.  Must not overlap logits,
+ *            lengths or out_idx.
+ *   other arguments, ownership and errors as for topk_select.
+ *
+ * The order is fully determined, so repeated calls give identical outputs.
+ * Besides the workspace of topk_select, the (device, stream) keeps a second
+ * scratch area (grown as needed with hipMalloc; no clearing): rows*k*4 bytes
+ * of keys, plus 2*rows*kp*8 bytes when k > 8192 (kp = k rounded up to a
+ * multiple of 8192).  The work is the selection kernel followed by one sort
+ * kernel (k <= 8192) or a sort kernel and ceil(log2(kp/8192)) merge passes.
+ */
+int topk_select_sorted(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                       int32_t* out_idx, float* out_val, topk_select_stream_t stream);
+
+/*
  * Launch-shape description, filled by topk_select_plan and accepted by
  * topk_select_ex.  Performance only: every plan yields the same selected sets.
  *   variant       kernel variant id (0 .. topk_select_num_variants()-1)
@@ -111,6 +135,12 @@ int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* pla
  * INVALID_VALUE when the shape cannot cover n or cannot be co-resident. */
 int topk_select_ex(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                    int32_t* out_idx, topk_select_stream_t stream, const topk_select_plan_t* plan);
+
+/* topk_select_sorted with an explicit selection launch shape (as for
+ * topk_select_ex; the sort that follows does not depend on it). */
+int topk_select_sorted_ex(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                          int32_t* out_idx, float* out_val, topk_select_stream_t stream,
+                          const topk_select_plan_t* plan);
 
 /* Number of kernel variants compiled into the library; fills the shape of
  * variant v (block, items, resident) into plan when v is in range. */

@@ -7,11 +7,14 @@ stream; the selection itself runs entirely in the library's kernels.
     import torch, sparse_attention_topk_fp32_amd as tks
     idx = tks.select(logits, k=2048)              # int32 [rows, k], unsorted
     idx = tks.select(logits, k=2048, lengths=L)   # per-row valid lengths
+    idx, val = tks.select_sorted(logits, k=2048, return_values=True)  # ordered
 
 Semantics (the TopK article "How to Use FlagOS's New Triton-TLE Language to
 Build a TopK Selector Faster Than FlashInfer", sections 01, 02 and 5): per row,
 the indices of the k largest valid logits, ties at the threshold value going
 to the lowest index, -1 in slots past the valid length, order unspecified.
+``select_sorted`` gives the same sets in order (value descending, equal values
+by index ascending; section 02's need_sorted option), optionally with values.
 """
 
 from __future__ import annotations
@@ -26,6 +29,9 @@ __all__ = [
     "select",
     "topk_select",
     "topk_select_ex",
+    "select_sorted",
+    "topk_select_sorted",
+    "topk_select_sorted_ex",
     "plan",
     "num_variants",
     "variant_info",
@@ -56,6 +62,21 @@ def topk_select_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int
                                          stream or None, ctypes.byref(p))
 
 
+def topk_select_sorted(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                       val_ptr: Optional[int], stream: int = 0) -> int:
+    """Raw C-ABI call of the ordered selection; returns the status code."""
+    return _native.load().topk_select_sorted(logits_ptr or None, rows, n, lengths_ptr or None, k, out_ptr or None,
+                                             val_ptr or None, stream or None)
+
+
+def topk_select_sorted_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                          val_ptr: Optional[int], stream: int, variant: int, wgs_per_row: int) -> int:
+    """Raw C-ABI call of the ordered selection with an explicit launch shape."""
+    p = _native.PlanT(variant, wgs_per_row, 0, 0, 0, 0)
+    return _native.load().topk_select_sorted_ex(logits_ptr or None, rows, n, lengths_ptr or None, k,
+                                                out_ptr or None, val_ptr or None, stream or None, ctypes.byref(p))
+
+
 def _stream_handle(stream) -> int:
     import torch
 
@@ -64,17 +85,7 @@ def _stream_handle(stream) -> int:
     return int(getattr(stream, "cuda_stream", stream) or 0)
 
 
-def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optional[int] = None,
-           wgs_per_row: Optional[int] = None):
-    """Indices of the k largest valid logits of each row.
-
-    logits   float32 tensor on the GPU, [rows, n] (or [n]), contiguous rows.
-    k        1 <= k <= n.
-    lengths  optional int32 GPU tensor [rows] of valid lengths.
-    out      optional preallocated int32 GPU tensor [rows, k].
-    stream   torch stream (default: the current stream).
-    variant, wgs_per_row: optional explicit launch shape (tests, tuning).
-    Returns the int32 [rows, k] tensor (``out`` when given)."""
+def _prepare(logits, k, lengths):
     import torch
 
     if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
@@ -95,10 +106,66 @@ def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optiona
         if not lengths.is_contiguous():
             raise ValueError("lengths must be contiguous")
         lp = lengths.data_ptr()
+    return x, squeeze, rows, n, lp
+
+
+def _check_out(t, dtype, rows, k, x, name):
+    if t.dtype != dtype or t.shape != (rows, k) or not t.is_contiguous() or t.device != x.device:
+        raise ValueError("%s must be a contiguous %s [rows, k] tensor on the logits' device" % (name, dtype))
+
+
+def select_sorted(logits, k: int, lengths=None, out=None, out_values=None, return_values: bool = False,
+                  stream=None, variant: Optional[int] = None, wgs_per_row: Optional[int] = None):
+    """``select`` with each row in order: values descending, equal values by
+    index ascending, -1 slots last.  With ``return_values`` (or
+    ``out_values`` given) also the selected logits, bit for bit, -inf beside
+    each -1; returns (indices, values) then, else the indices."""
+    import torch
+
+    x, squeeze, rows, n, lp = _prepare(logits, k, lengths)
     if out is None:
         out = torch.empty((rows, k), dtype=torch.int32, device=x.device)
-    elif out.dtype != torch.int32 or out.shape != (rows, k) or not out.is_contiguous() or out.device != x.device:
-        raise ValueError("out must be a contiguous int32 [rows, k] tensor on the logits' device")
+    else:
+        _check_out(out, torch.int32, rows, k, x, "out")
+    want_vals = return_values or out_values is not None
+    if want_vals and out_values is None:
+        out_values = torch.empty((rows, k), dtype=torch.float32, device=x.device)
+    elif want_vals:
+        _check_out(out_values, torch.float32, rows, k, x, "out_values")
+    vp = out_values.data_ptr() if want_vals else None
+    sh = _stream_handle(stream)
+    with torch.cuda.device(x.device):
+        if variant is None and wgs_per_row is None:
+            rc = topk_select_sorted(x.data_ptr(), rows, n, lp, k, out.data_ptr(), vp, sh)
+        else:
+            if variant is None or wgs_per_row is None:
+                raise ValueError("give both variant and wgs_per_row")
+            rc = topk_select_sorted_ex(x.data_ptr(), rows, n, lp, k, out.data_ptr(), vp, sh, variant, wgs_per_row)
+    _check(rc, "topk_select_sorted")
+    if squeeze:
+        out = out[0]
+        out_values = out_values[0] if want_vals else None
+    return (out, out_values) if want_vals else out
+
+
+def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optional[int] = None,
+           wgs_per_row: Optional[int] = None):
+    """Indices of the k largest valid logits of each row.
+
+    logits   float32 tensor on the GPU, [rows, n] (or [n]), contiguous rows.
+    k        1 <= k <= n.
+    lengths  optional int32 GPU tensor [rows] of valid lengths.
+    out      optional preallocated int32 GPU tensor [rows, k].
+    stream   torch stream (default: the current stream).
+    variant, wgs_per_row: optional explicit launch shape (tests, tuning).
+    Returns the int32 [rows, k] tensor (``out`` when given)."""
+    import torch
+
+    x, squeeze, rows, n, lp = _prepare(logits, k, lengths)
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=x.device)
+    else:
+        _check_out(out, torch.int32, rows, k, x, "out")
     sh = _stream_handle(stream)
     with torch.cuda.device(x.device):
         if variant is None and wgs_per_row is None:

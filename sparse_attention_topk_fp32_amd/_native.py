@@ -25,6 +25,8 @@ ERROR_DEVICE_FLAG = 5
 EXPORTS = (
     "topk_select",
     "topk_select_ex",
+    "topk_select_sorted",
+    "topk_select_sorted_ex",
     "topk_select_plan",
     "topk_select_num_variants",
     "topk_select_variant_info",
@@ -72,6 +74,10 @@ def load() -> ctypes.CDLL:
         lib.topk_select.restype = ctypes.c_int
         lib.topk_select_ex.argtypes = [P, I, I, P, I, P, P, ctypes.POINTER(PlanT)]
         lib.topk_select_ex.restype = ctypes.c_int
+        lib.topk_select_sorted.argtypes = [P, I, I, P, I, P, P, P]
+        lib.topk_select_sorted.restype = ctypes.c_int
+        lib.topk_select_sorted_ex.argtypes = [P, I, I, P, I, P, P, P, ctypes.POINTER(PlanT)]
+        lib.topk_select_sorted_ex.restype = ctypes.c_int
         lib.topk_select_plan.argtypes = [I, I, I, ctypes.POINTER(PlanT)]
         lib.topk_select_plan.restype = ctypes.c_int
         lib.topk_select_num_variants.argtypes = []

@@ -87,6 +87,7 @@ struct KParams {
     const float* logits;
     const int32_t* lengths;
     int32_t* out;
+    uint32_t* keys;         // [rows, k]: key of the element at each output slot, or null
     RowWorkspace* ws;       // per row, when G > 1
     uint32_t* status;
     int32_t rows, n, k;
@@ -354,7 +355,8 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
 template <int BLOCK>
 __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
                               int F, int idx_bits, bool cleared, uint32_t* hist, uint64_t* small, uint32_t* scan,
-                              uint32_t* sel, uint32_t* ctr, int32_t* out, int k, uint32_t* status) {
+                              uint32_t* sel, uint32_t* ctr, int32_t* out, uint32_t* okey, int k,
+                              uint32_t* status) {
     const int tid = threadIdx.x;
     const int nrounds = num_rounds(idx_bits);
     auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
@@ -404,8 +406,12 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
             if (!c_match(c)) return;
             if (d > b || (all && d == b)) {
                 const uint32_t pos = W + atomicAdd(&ctr[0], 1u);
-                if (pos < (uint32_t)k) out[pos] = (int32_t)~(uint32_t)c;
-                else raise_flag(status, kFlagCapacity);
+                if (pos < (uint32_t)k) {
+                    out[pos] = (int32_t)~(uint32_t)c;
+                    if (okey) okey[pos] = (uint32_t)(c >> 32);
+                } else {
+                    raise_flag(status, kFlagCapacity);
+                }
             } else if (gather && d == b) {
                 const uint32_t pos = atomicAdd(&ctr[1], 1u);
                 if (pos < (uint32_t)kSmall) small[pos] = c;
@@ -450,7 +456,10 @@ __device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, 
     for (uint32_t sft = 32u; sft >= 1u; sft >>= 1) {
         if (sft < P) rank += (uint32_t)__shfl_xor((int)rank, (int)sft);
     }
-    if (i < ms && q == 0u && rank < need && W + rank < (uint32_t)k) out[W + rank] = (int32_t)~(uint32_t)c;
+    if (i < ms && q == 0u && rank < need && W + rank < (uint32_t)k) {
+        out[W + rank] = (int32_t)~(uint32_t)c;
+        if (okey) okey[W + rank] = (uint32_t)(c >> 32);
+    }
 }
 
 // Thresholding step for round r from the LDS histogram copies (the first
@@ -535,7 +544,7 @@ __device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, int mslot, boo
 // BLOCK threads per WG; ITEMS logits per thread per tile; RESIDENT: the
 // slice is one tile kept in VGPRs across passes (else re-read every pass).
 
-template <int BLOCK, int ITEMS, bool RESIDENT>
+template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS>
 __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "one bin per thread in the 256-bin rounds");
@@ -551,6 +560,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     const int k = P.k;
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
+    uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;  // recorded keys (ordered output)
     int L = n;
     if (P.lengths) {
         L = P.lengths[row];
@@ -828,8 +838,12 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         }
         const uint32_t pos = atomicAdd(&sm.pos[slot], 1u);
         if (ab || whole) {
-            if (pos < (uint32_t)k) out[pos] = (int32_t)~ni;
-            else overflow = true;
+            if (pos < (uint32_t)k) {
+                out[pos] = (int32_t)~ni;
+                if (okey) okey[pos] = key;
+            } else {
+                overflow = true;
+            }
         } else if (pos < (uint32_t)kCap) {
             const uint64_t e = ((uint64_t)key << 32) | (uint64_t)ni;
             if (multi) st_dev(&gstage[pos], e);
@@ -913,7 +927,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         }
         lds_sync();
         finish_bucket<BLOCK>(sm.cand, m, need, W, pf, R + 1, F, idx_bits, true, sm.hist, sm.small, sm.scan, sm.sel,
-                                sm.ctr, out, k, P.status);
+                                sm.ctr, out, okey, k, P.status);
     }
 
     if (multi) {
@@ -961,7 +975,7 @@ struct RowsSmem {
     uint32_t ctr[5];  // winners, bucket, finisher (2), buffered entries
 };
 
-template <int BLOCK, int ITEMS, int PD>
+template <int BLOCK, int ITEMS, int PD, bool KEYS>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void topk_rows_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     constexpr int F = 12;
@@ -976,6 +990,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     const int k = P.k;
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
+    uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;  // recorded keys (ordered output)
     int L = n;
     if (P.lengths) {
         L = P.lengths[row];
@@ -1210,9 +1225,15 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
              },
              [&](uint64_t e, uint32_t kind, uint32_t r) {
                  if (kind == 1u) {
-                     if (r < Wv) out[r] = (int32_t)~(uint32_t)e;
+                     if (r < Wv) {
+                         out[r] = (int32_t)~(uint32_t)e;
+                         if (okey) okey[r] = (uint32_t)(e >> 32);
+                     }
                  } else if (wh) {
-                     if (Wv + r < (uint32_t)k) out[Wv + r] = (int32_t)~(uint32_t)e;
+                     if (Wv + r < (uint32_t)k) {
+                         out[Wv + r] = (int32_t)~(uint32_t)e;
+                         if (okey) okey[Wv + r] = (uint32_t)(e >> 32);
+                     }
                  } else {
                      sm.cand[r] = e;
                  }
@@ -1223,7 +1244,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         if (whole) return;
         lds_sync();
         finish_bucket<BLOCK>(sm.cand, hb, need, W, pf, 1, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
-                                &sm.ctr[2], out, k, P.status);
+                                &sm.ctr[2], out, okey, k, P.status);
         return;
     }
     // ---------------- fallback: the full first-digit histogram by a second
@@ -1322,13 +1343,21 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                     const uint32_t key = keys[slot];
                     const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
                     if ((mw >> slot) & 1u) {
-                        if (pw < W) out[pw] = (int32_t)~ni;
-                        else overflow = true;
+                        if (pw < W) {
+                            out[pw] = (int32_t)~ni;
+                            if (okey) okey[pw] = key;
+                        } else {
+                            overflow = true;
+                        }
                         ++pw;
                     } else if ((mbk >> slot) & 1u) {
                         if (whole) {
-                            if (W + pb < (uint32_t)k) out[W + pb] = (int32_t)~ni;
-                            else overflow = true;
+                            if (W + pb < (uint32_t)k) {
+                                out[W + pb] = (int32_t)~ni;
+                                if (okey) okey[W + pb] = key;
+                            } else {
+                                overflow = true;
+                            }
                         } else if (pb < (uint32_t)kCap) {
                             sm.cand[pb] = ((uint64_t)key << 32) | (uint64_t)ni;
                         } else {
@@ -1344,7 +1373,284 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     if (whole) return;
     lds_sync();
     finish_bucket<BLOCK>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, F, idx_bits,
-                            false, sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, k, P.status);
+                            false, sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, okey, k, P.status);
+}
+
+// ----------------------------------------------------------------- ordered output
+// The ordered form of the selection: section 02 of the TopK article gives
+// radix_topk a need_sorted option that sorts the collected output in
+// descending order; equal values are ordered by index ascending, the same
+// rule that decides which of them are selected.  The selection kernels
+// record, beside each output index, the key of its element; then one WG
+// per row sorts the row's composites (key << 32 | ~index) in descending
+// order with a bitonic network.  Rows longer than kSortRun are cut into
+// runs of kSortRun that are sorted on chip, then merged pairwise in global
+// memory (merge path: each thread finds where its outputs start on both
+// runs by a binary search, then merges a few entries).
+
+constexpr int kSortRun = 8192;  // composites one WG sorts on chip
+constexpr int kMergeBlock = 256, kMergeItems = 8;
+
+struct SortParams {
+    const float* logits;
+    const int32_t* lengths;
+    int32_t* out;
+    float* vals;            // [rows, k] or null
+    const int32_t* idx;     // [rows, k]: the selection's output (unordered)
+    const uint32_t* keys;   // [rows, k]: the key at each slot of idx
+    const uint64_t* src;    // merge input, [rows, kp]
+    uint64_t* dst;          // sorted runs / merge output, [rows, kp] (null: to out/vals)
+    int32_t rows, n, k;
+    int32_t kp;             // padded row length of the runs (multiple of kSortRun)
+    int32_t nruns;          // runs per row (rank kernel: WGs per row)
+    int32_t width;          // merge: length of the runs being merged
+};
+
+// The composite of slot g of a row's unordered selection: from the
+// recorded key and index, or, when the whole valid row is selected (L <= k:
+// the selection then writes 0..L-1 and records no keys), from the logits.
+__device__ __forceinline__ uint64_t sort_input(const SortParams& P, int row, int L, uint32_t g) {
+    uint32_t idx, key;
+    if (L <= P.k) {
+        idx = g;
+        key = key_of(P.logits[(size_t)row * (size_t)P.n + g]);
+    } else {
+        const size_t at = (size_t)row * (size_t)P.k + g;
+        idx = (uint32_t)P.idx[at];
+        key = P.keys[at];
+    }
+    return ((uint64_t)key << 32) | (uint64_t)~idx;
+}
+
+// The logit a key came from; -0.0 and +0.0 share a key, so a zero key reads
+// the logit itself to return its sign.
+__device__ __forceinline__ float value_of(uint32_t key, const float* prow, uint32_t L, uint32_t idx) {
+    if (key == 0x80000000u) return idx < L ? prow[idx] : 0.0f;
+    return __uint_as_float(key & 0x80000000u ? key ^ 0x80000000u : ~key);
+}
+
+// Write output slot j of a row from a composite (0 = no element: -1, -inf).
+__device__ __forceinline__ void put_sorted(uint64_t c, int32_t* orow, float* vrow, const float* prow, uint32_t L,
+                                           uint32_t j) {
+    const uint32_t idx = ~(uint32_t)c;
+    const bool has = c != 0ull;
+    orow[j] = has ? (int32_t)idx : -1;
+    if (vrow) vrow[j] = has ? value_of((uint32_t)(c >> 32), prow, L, idx) : -__builtin_huge_valf();
+}
+
+__device__ __forceinline__ int valid_length(const int32_t* lengths, int row, int n) {
+    if (!lengths) return n;
+    const int L = lengths[row];
+    return L < 0 ? 0 : (L > n ? n : L);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Keep the larger of (mine, other) when keep_max, else the smaller: one
+// 64-bit compare and two selects.
+__device__ __forceinline__ uint64_t bitonic_pick(uint64_t mine, uint64_t other, bool keep_max) {
+    return ((mine > other) == keep_max) ? mine : other;
+}
+
+// One bitonic step whose partner lanes are a DPP quad permutation away
+// (QP 0xB1: lane ^ 1, 0x4E: lane ^ 2).
+template <int E, int QP>
+__device__ __forceinline__ void dpp_step(uint64_t (&c)[E], bool keep_max) {
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)c[u], QP, 0xF, 0xF, false);
+        const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(c[u] >> 32), QP, 0xF, 0xF, false);
+        c[u] = bitonic_pick(c[u], ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo, keep_max);
+    }
+}
+
+// Bitonic sort, descending, of the first Sp (a power of two, 2 <= Sp <=
+// BLOCK*E) of the WG's BLOCK*E composites; entry e = tid*E + u is c[u] of
+// thread tid.  At merge level p, entry e belongs to a descending block when
+// (e & p) == 0; of the pair (e, e ^ j) the lower entry of a descending block
+// keeps the larger value.  For j >= E (partner in another thread) both
+// tests depend on the thread only, so each step costs one compare and two
+// selects per entry.  buf: 2*BLOCK*E composites of LDS (double buffer, so
+// one barrier per cross-wave step).  Every thread of the WG calls it.
+template <int BLOCK, int E>
+__device__ __forceinline__ void bitonic_desc(uint64_t (&c)[E], uint32_t Sp, uint64_t* buf) {
+    const uint32_t e0 = threadIdx.x * (uint32_t)E;
+    int par = 0;
+    for (uint32_t p = 2; p <= Sp; p <<= 1) {
+        const bool desc = (e0 & p) == 0u || p < (uint32_t)E;  // p < E: decided per entry below
+        uint32_t j = p >> 1;
+        for (; j >= 64u * E; j >>= 1) {  // partner in another wave
+            uint64_t* const b = buf + par * (BLOCK * E);
+            par ^= 1;
+#pragma unroll
+            for (int u = 0; u < E; ++u) b[e0 + u] = c[u];
+            __syncthreads();
+            const bool keep_max = ((e0 & j) == 0u) == desc;
+            uint64_t o[E];
+#pragma unroll
+            for (int u = 0; u < E; ++u) o[u] = b[(e0 + (uint32_t)u) ^ j];
+#pragma unroll
+            for (int u = 0; u < E; ++u) c[u] = bitonic_pick(c[u], o[u], keep_max);
+        }
+        for (; j >= 4u * E; j >>= 1) {  // partner in another lane of the wave
+            // every partner value of the step is fetched before any is used,
+            // so the lane exchanges overlap
+            const int lj = (int)(j / (uint32_t)E);
+            const bool keep_max = ((e0 & j) == 0u) == desc;
+            uint64_t o[E];
+#pragma unroll
+            for (int u = 0; u < E; ++u) o[u] = (uint64_t)__shfl_xor((unsigned long long)c[u], lj);
+#pragma unroll
+            for (int u = 0; u < E; ++u) c[u] = bitonic_pick(c[u], o[u], keep_max);
+        }
+        // partners 2 and 1 lanes away: DPP quad permutations, no LDS trip
+        if (j == 2u * E) {
+            dpp_step<E, 0x4E>(c, ((e0 & j) == 0u) == desc);
+            j >>= 1;
+        }
+        if (j == (uint32_t)E) dpp_step<E, 0xB1>(c, ((e0 & j) == 0u) == desc);
+#pragma unroll
+        for (int jj = E / 2; jj >= 1; jj >>= 1) {  // partner in this thread
+            if ((uint32_t)jj < p) {
+#pragma unroll
+                for (int u = 0; u < E; ++u) {
+                    if ((u & jj) == 0) {
+                        const bool d = p < (uint32_t)E ? (((uint32_t)u & p) == 0u) : desc;
+                        const uint64_t a = c[u], b2 = c[u | jj];
+                        const bool sw = (a < b2) == d;
+                        c[u] = sw ? b2 : a;
+                        c[u | jj] = sw ? a : b2;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// One WG per (row, run): load the run's composites (from the recorded keys,
+// or from the logits when the whole valid row is selected), sort them, and
+// write them to the output (one run per row) or to dst.
+template <int BLOCK, int E>
+__global__ void __launch_bounds__(BLOCK) topk_sort_kernel(SortParams P) {
+    __shared__ uint64_t buf[2 * BLOCK * E];
+    const int row = blockIdx.x / P.nruns;
+    const int run = blockIdx.x - row * P.nruns;
+    const int n = P.n, k = P.k;
+    const int L = valid_length(P.lengths, row, n);
+    const uint32_t take = (uint32_t)(L < k ? L : k);
+    const float* const prow = P.logits + (size_t)row * (size_t)n;
+    int32_t* const orow = P.out + (size_t)row * (size_t)k;
+    float* const vrow = P.vals ? P.vals + (size_t)row * (size_t)k : nullptr;
+    const uint32_t r0 = (uint32_t)run * (uint32_t)kSortRun;
+    const uint32_t cnt = take > r0 ? min(take - r0, (uint32_t)(BLOCK * E)) : 0u;
+    const uint32_t e0 = threadIdx.x * (uint32_t)E;
+    uint64_t c[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const uint32_t e = e0 + (uint32_t)u;
+        c[u] = e < cnt ? sort_input(P, row, L, r0 + e) : 0ull;
+    }
+    uint32_t Sp = 2;
+    while (Sp < cnt) Sp <<= 1;
+    bitonic_desc<BLOCK, E>(c, Sp, buf);
+    if (P.dst) {
+        uint64_t* const drow = P.dst + (size_t)row * (size_t)P.kp + r0;
+#pragma unroll
+        for (int u = 0; u < E; ++u) drow[e0 + u] = c[u];
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const uint32_t e = e0 + (uint32_t)u;
+        if (e < take) put_sorted(c[u], orow, vrow, prow, (uint32_t)L, e);
+    }
+    for (uint32_t j = take + threadIdx.x; j < (uint32_t)k; j += BLOCK) put_sorted(0ull, orow, vrow, prow, 0u, j);
+}
+
+// One merge pass: runs of P.width entries, pairwise, descending.  Each
+// thread writes kMergeItems consecutive entries of the merged pair: to dst,
+// or (last pass) to the output.  Equal composites (only the zero padding)
+// come from the first run first.
+__global__ void __launch_bounds__(kMergeBlock) topk_merge_kernel(SortParams P) {
+    const uint32_t per_row = (uint32_t)P.kp / (kMergeBlock * kMergeItems);
+    const uint32_t row = blockIdx.x / per_row;
+    const uint32_t o = ((blockIdx.x - row * per_row) * kMergeBlock + threadIdx.x) * kMergeItems;
+    const uint32_t w = (uint32_t)P.width, kp = (uint32_t)P.kp;
+    const uint32_t base = o / (2u * w) * (2u * w);
+    const uint32_t lenA = min(w, kp - base);
+    const uint32_t lenB = kp - base > w ? min(w, kp - base - w) : 0u;
+    const uint64_t* const A = P.src + (size_t)row * kp + base;
+    const uint64_t* const B = A + w;
+    const uint32_t d = o - base;
+    // co-rank: how many of the first d merged entries come from A
+    uint32_t lo = d > lenB ? d - lenB : 0u, hi = min(d, lenA);
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (A[mid] >= B[d - mid - 1u]) lo = mid + 1u;
+        else hi = mid;
+    }
+    uint32_t i = lo, j = d - lo;
+    const int k = P.k;
+    int32_t* const orow = P.out + (size_t)row * (size_t)k;
+    float* const vrow = P.vals ? P.vals + (size_t)row * (size_t)k : nullptr;
+    const float* const prow = P.logits + (size_t)row * (size_t)P.n;
+    const uint32_t L = P.dst ? 0u : (uint32_t)valid_length(P.lengths, (int)row, P.n);
+#pragma unroll
+    for (int t = 0; t < kMergeItems; ++t) {
+        const uint64_t a = i < lenA ? A[i] : 0ull;
+        const uint64_t b = j < lenB ? B[j] : 0ull;
+        const bool fromA = j >= lenB || (i < lenA && a >= b);
+        const uint64_t v = fromA ? a : b;
+        i += fromA;
+        j += !fromA;
+        const uint32_t pos = o + (uint32_t)t;
+        if (P.dst) P.dst[(size_t)row * kp + pos] = v;
+        else if (pos < (uint32_t)k) put_sorted(v, orow, vrow, prow, L, pos);
+    }
+}
+
+// Few rows: each row's order is spread over RG = P.nruns WGs.  Every WG
+// holds the row's take composites in LDS and places a share of them: the
+// output position of a composite is the number of larger ones, counted by
+// Q lanes per composite over strided parts of the row (then added by lane
+// shuffles).  Rows of at most kRankMax selected entries.
+constexpr int kRankMax = 4096;
+constexpr int kRankBlock = 256;
+
+__global__ void __launch_bounds__(kRankBlock) topk_rank_kernel(SortParams P) {
+    __shared__ uint64_t all[kRankMax];
+    const int RG = P.nruns;
+    const int row = blockIdx.x / RG;
+    const int w = blockIdx.x - row * RG;
+    const int tid = threadIdx.x;
+    const int n = P.n, k = P.k;
+    const int L = valid_length(P.lengths, row, n);
+    const uint32_t take = (uint32_t)(L < k ? L : k);
+    for (uint32_t g = tid; g < take; g += kRankBlock) all[g] = sort_input(P, row, L, g);
+    __syncthreads();
+    const float* const prow = P.logits + (size_t)row * (size_t)n;
+    int32_t* const orow = P.out + (size_t)row * (size_t)k;
+    float* const vrow = P.vals ? P.vals + (size_t)row * (size_t)k : nullptr;
+    if (w == 0)
+        for (uint32_t j = take + tid; j < (uint32_t)k; j += kRankBlock) put_sorted(0ull, orow, vrow, prow, 0u, j);
+    const uint32_t chunk = (take + RG - 1) / RG;
+    const uint32_t first = (uint32_t)w * chunk;
+    if (chunk == 0u || first >= take) return;
+    const uint32_t cnt = min(chunk, take - first);
+    uint32_t Q = 1;
+    while (Q < 64u && 2u * Q * cnt <= (uint32_t)kRankBlock) Q *= 2u;
+    const uint32_t i = (uint32_t)tid / Q, q = (uint32_t)tid % Q;
+    const uint64_t me = i < cnt ? all[first + i] : ~0ull;
+    uint32_t above = 0;
+    uint32_t j = q;
+    for (; j + 3u * Q < take; j += 4u * Q) {
+        const uint64_t a = all[j], b = all[j + Q], c = all[j + 2u * Q], d = all[j + 3u * Q];
+        above += (uint32_t)(a > me) + (uint32_t)(b > me) + (uint32_t)(c > me) + (uint32_t)(d > me);
+    }
+    for (; j < take; j += Q) above += (uint32_t)(all[j] > me);
+    for (uint32_t sft = 1u; sft < Q; sft <<= 1) above += (uint32_t)__shfl_xor((int)above, (int)sft);
+    if (i < cnt && q == 0u) put_sorted(me, orow, vrow, prow, (uint32_t)L, above);
 }
 
 // ----------------------------------------------------------------- host side
@@ -1354,22 +1660,33 @@ using OccFn = int (*)(int*, int);
 
 template <int B, int I, bool R>
 void launch_variant(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    hipLaunchKernelGGL((topk_select_kernel<B, I, R>), grid, block, 0, s, p);
+    if (p.keys) hipLaunchKernelGGL((topk_select_kernel<B, I, R, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((topk_select_kernel<B, I, R, false>), grid, block, 0, s, p);
 }
 
+// co-resident WGs per CU: the smaller figure of the two instantiations
 template <int B, int I, bool R>
 int occupancy_variant(int* nb, int block) {
-    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_select_kernel<B, I, R>, block, 0);
+    int a = 0, b = 0;
+    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_select_kernel<B, I, R, false>, block, 0);
+    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_select_kernel<B, I, R, true>, block, 0);
+    *nb = a < b ? a : b;
+    return r1 != 0 ? r1 : r2;
 }
 
 template <int B, int I, int D>
 void launch_rows(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    hipLaunchKernelGGL((topk_rows_kernel<B, I, D>), grid, block, 0, s, p);
+    if (p.keys) hipLaunchKernelGGL((topk_rows_kernel<B, I, D, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((topk_rows_kernel<B, I, D, false>), grid, block, 0, s, p);
 }
 
 template <int B, int I, int D>
 int occupancy_rows(int* nb, int block) {
-    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, topk_rows_kernel<B, I, D>, block, 0);
+    int a = 0, b = 0;
+    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_rows_kernel<B, I, D, false>, block, 0);
+    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_rows_kernel<B, I, D, true>, block, 0);
+    *nb = a < b ? a : b;
+    return r1 != 0 ? r1 : r2;
 }
 
 struct Variant {
@@ -1410,6 +1727,8 @@ struct DeviceInfo {
 struct Workspace {
     void* base = nullptr;
     size_t bytes = 0;
+    void* aux = nullptr;  // ordered output: recorded keys, merge buffers (no clearing needed)
+    size_t aux_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -1561,10 +1880,72 @@ int get_workspace(int dev, hipStream_t stream, size_t need, Workspace** out) {
     return TOPK_SELECT_SUCCESS;
 }
 
+int get_aux(hipStream_t stream, Workspace* w, size_t need) {
+    if (w->aux_bytes < need) {
+        if (w->aux) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+            (void)hipFree(w->aux);
+            w->aux = nullptr;
+            w->aux_bytes = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, need) != hipSuccess) {
+            (void)hipGetLastError();
+            return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
+        }
+        w->aux = p;
+        w->aux_bytes = need;
+    }
+    return TOPK_SELECT_SUCCESS;
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a && b && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Launches of the ordered output: for a few rows with k <= kRankMax the
+// rank kernel (up to 128 WGs per row); else one sorting WG per row when k
+// fits one on-chip sort, or runs of kSortRun and merge passes.
+struct SortShape {
+    bool rank;
+    int rank_wgs;      // rank kernel: WGs per row
+    int block, items;  // sort kernel variant
+    int nruns;
+    int64_t kp;        // padded row length of the runs
+};
+
+SortShape sort_shape(int32_t rows, int32_t k) {
+    SortShape s;
+    s.rank = k <= kRankMax && (int64_t)rows * (int64_t)k * (int64_t)k <= (int64_t)1 << 25;
+    s.rank_wgs = k / 16 < 1 ? 1 : (k / 16 > 128 ? 128 : k / 16);
+    if (k <= 1024) { s.block = 256; s.items = 4; }
+    else if (k <= 2048) { s.block = 512; s.items = 4; }
+    else if (k <= 4096) { s.block = 1024; s.items = 4; }
+    else { s.block = 1024; s.items = 8; }
+    s.nruns = (int)((k + kSortRun - 1) / kSortRun);
+    s.kp = (int64_t)s.nruns * kSortRun;
+    return s;
+}
+
+void launch_sort(const SortShape& sh, int32_t rows, hipStream_t stream, const SortParams& p) {
+    const dim3 grid((unsigned)((int64_t)rows * sh.nruns));
+    if (sh.block == 256) topk_sort_kernel<256, 4><<<grid, 256, 0, stream>>>(p);
+    else if (sh.block == 512) topk_sort_kernel<512, 4><<<grid, 512, 0, stream>>>(p);
+    else if (sh.items == 4) topk_sort_kernel<1024, 4><<<grid, 1024, 0, stream>>>(p);
+    else topk_sort_kernel<1024, 8><<<grid, 1024, 0, stream>>>(p);
+}
+
 int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k, int32_t* out,
-        hipStream_t stream, const topk_select_plan_t* forced) {
+        bool ordered, float* vals, hipStream_t stream, const topk_select_plan_t* forced) {
     int rc = validate(logits, rows, n, lengths, k, out);
     if (rc != TOPK_SELECT_SUCCESS || rows == 0) return rc;
+    if (ordered && vals) {
+        const size_t vb = (size_t)rows * (size_t)k * 4u;
+        if (((uintptr_t)vals & 3) || overlaps(vals, vb, logits, (size_t)rows * (size_t)n * 4u) ||
+            overlaps(vals, vb, out, vb) || overlaps(vals, vb, lengths, (size_t)rows * 4u))
+            return TOPK_SELECT_ERROR_INVALID_VALUE;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
     std::lock_guard<std::mutex> lock(g_mu);
@@ -1581,11 +1962,27 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     Workspace* w = nullptr;
     rc = get_workspace(dev, stream, kStatusBytes + rows_bytes, &w);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
+    SortShape sh{};
+    size_t keys_bytes = 0;
+    if (ordered) {
+        sh = sort_shape(rows, k);
+        keys_bytes = ((size_t)rows * (size_t)k * 4u + 255u) / 256u * 256u;
+        const size_t run_bytes = (!sh.rank && sh.nruns > 1) ? 2u * (size_t)rows * (size_t)sh.kp * 8u : 0u;
+        if ((int64_t)rows * sh.nruns > 0x7FFFFFFFll || (int64_t)rows * sh.rank_wgs > 0x7FFFFFFFll ||
+            (int64_t)rows * (sh.kp / (kMergeBlock * kMergeItems)) > 0x7FFFFFFFll)
+            return TOPK_SELECT_ERROR_INVALID_VALUE;
+        rc = get_aux(stream, w, 2u * keys_bytes + run_bytes);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+    }
     char* base = reinterpret_cast<char*>(w->base);
     KParams P;
     P.logits = logits;
     P.lengths = lengths;
-    P.out = out;
+    // ordered output: the selection writes its indices and their keys to
+    // scratch, the sort writes out_idx
+    char* const aux = reinterpret_cast<char*>(w->aux);
+    P.out = ordered ? reinterpret_cast<int32_t*>(aux + keys_bytes) : out;
+    P.keys = ordered ? reinterpret_cast<uint32_t*>(aux) : nullptr;
     P.status = reinterpret_cast<uint32_t*>(base);
     P.ws = L.G > 1 ? reinterpret_cast<RowWorkspace*>(base + kStatusBytes) : nullptr;
     P.rows = rows;
@@ -1598,6 +1995,43 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+    if (!ordered) return TOPK_SELECT_SUCCESS;
+
+    SortParams S;
+    S.logits = logits;
+    S.lengths = lengths;
+    S.out = out;
+    S.vals = vals;
+    S.idx = P.out;
+    S.keys = P.keys;
+    S.rows = rows;
+    S.n = n;
+    S.k = k;
+    S.kp = (int32_t)sh.kp;
+    S.nruns = sh.nruns;
+    S.width = 0;
+    if (sh.rank) {
+        S.nruns = sh.rank_wgs;
+        topk_rank_kernel<<<dim3((unsigned)((int64_t)rows * sh.rank_wgs)), kRankBlock, 0, stream>>>(S);
+        return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
+    }
+    uint64_t* const run0 = reinterpret_cast<uint64_t*>(aux + 2u * keys_bytes);
+    uint64_t* const run1 = run0 + (size_t)rows * (size_t)sh.kp;
+    S.src = nullptr;
+    S.dst = sh.nruns > 1 ? run0 : nullptr;
+    launch_sort(sh, rows, stream, S);
+    if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+    uint64_t* bufs[2] = {run0, run1};
+    int cur = 0;
+    for (int64_t width = kSortRun; width < sh.kp; width *= 2) {
+        S.width = (int32_t)width;
+        S.src = bufs[cur];
+        S.dst = 2 * width >= sh.kp ? nullptr : bufs[cur ^ 1];
+        const int64_t wgs = (int64_t)rows * (sh.kp / (kMergeBlock * kMergeItems));
+        topk_merge_kernel<<<dim3((unsigned)wgs), kMergeBlock, 0, stream>>>(S);
+        if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        cur ^= 1;
+    }
     return TOPK_SELECT_SUCCESS;
 }
 
@@ -1608,7 +2042,7 @@ extern "C" {
 int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                 int32_t* out_idx, topk_select_stream_t stream) {
     try {
-        return tks::run(logits, rows, n, lengths, k, out_idx, (hipStream_t)stream, nullptr);
+        return tks::run(logits, rows, n, lengths, k, out_idx, false, nullptr, (hipStream_t)stream, nullptr);
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
     }
@@ -1618,7 +2052,27 @@ int topk_select_ex(const float* logits, int32_t rows, int32_t n, const int32_t* 
                    int32_t* out_idx, topk_select_stream_t stream, const topk_select_plan_t* plan) {
     if (!plan) return TOPK_SELECT_ERROR_INVALID_VALUE;
     try {
-        return tks::run(logits, rows, n, lengths, k, out_idx, (hipStream_t)stream, plan);
+        return tks::run(logits, rows, n, lengths, k, out_idx, false, nullptr, (hipStream_t)stream, plan);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
+int topk_select_sorted(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                       int32_t* out_idx, float* out_val, topk_select_stream_t stream) {
+    try {
+        return tks::run(logits, rows, n, lengths, k, out_idx, true, out_val, (hipStream_t)stream, nullptr);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
+int topk_select_sorted_ex(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                          int32_t* out_idx, float* out_val, topk_select_stream_t stream,
+                          const topk_select_plan_t* plan) {
+    if (!plan) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    try {
+        return tks::run(logits, rows, n, lengths, k, out_idx, true, out_val, (hipStream_t)stream, plan);
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
     }
@@ -1698,6 +2152,7 @@ int topk_select_release_workspace(void) {
                 (void)hipSetDevice(kv.first.first);
                 if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
                 if (hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+                if (kv.second.aux && hipFree(kv.second.aux) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
                 (void)hipSetDevice(cur);
             }
         }

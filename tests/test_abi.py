@@ -75,6 +75,26 @@ def test_argument_checks_answer_before_any_hip_call(lib):
     assert _call(lib, a, 2, 16, o, 4, o + 4) == INV  # out overlaps lengths
 
 
+def test_sorted_argument_checks_answer_before_any_hip_call(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    INV = _native.ERROR_INVALID_VALUE
+    a, o, v = 0x10000000, 0x20000000, 0x30000000  # stand-in addresses, never dereferenced
+
+    def call(logits, rows, n, lengths, k, out, vals):
+        return lib.topk_select_sorted(logits, rows, n, lengths, k, out, vals, None)
+
+    assert call(a, 0, 16, None, 4, o, v) == _native.SUCCESS
+    assert call(a, 1, 16, None, 17, o, v) == INV
+    assert call(a, 1, 16, None, 4, None, v) == INV
+    assert call(a, 1, 16, None, 4, o, v + 2) == INV  # values not 4-byte aligned
+    assert call(a, 2, 16, None, 4, o, a + 64) == INV  # values overlap logits
+    assert call(a, 2, 16, None, 4, o, o + 4) == INV  # values overlap out
+    assert call(a, 2, 16, v, 4, o, v + 4) == INV  # values overlap lengths
+    assert call(a, 2, 16, None, 4, a + 8, v) == INV  # out overlaps logits
+    assert lib.topk_select_sorted_ex(a, 1, 16, None, 4, o, v, None, None) == INV  # no plan
+
+
 def test_variant_table(lib):
     from sparse_attention_topk_fp32_amd import _native
 
@@ -102,3 +122,5 @@ def test_select_rejects_non_gpu_tensors():
         tks.select(torch.zeros(4, 8), 2)
     with pytest.raises(TypeError):
         tks.select(np.zeros((4, 8), np.float32), 2)
+    with pytest.raises(TypeError):
+        tks.select_sorted(torch.zeros(4, 8), 2)
