@@ -87,8 +87,10 @@ def time_eager(torch, fn, steps: int, warmup: int, stream):
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
-def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int, eager_only: bool = False):
-    """Per-launch seconds (graph, warm), (graph, cold: rotating copies), eager."""
+def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int, eager_only: bool = False,
+                   ordered: bool = False):
+    """Per-launch seconds (graph, warm), (graph, cold: rotating copies), eager.
+    With `ordered`, the ordered selection with values (topk_select_sorted)."""
     w = W.generate(name)
     rows, n = w.x.shape
     stream = torch.cuda.Stream()
@@ -97,9 +99,16 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
         xs.append(xs[0].clone())
     L = None if w.lengths is None else torch.from_numpy(w.lengths).cuda()
     outs = [torch.empty((rows, w.k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    vals = [torch.empty((rows, w.k), dtype=torch.float32, device="cuda") for _ in range(2)]
     torch.cuda.synchronize()
-    warm_fns = [lambda: tks.select(xs[0], w.k, lengths=L, out=outs[0])]
-    cold_fns = [(lambda i: (lambda: tks.select(xs[i], w.k, lengths=L, out=outs[i % 2])))(i) for i in range(copies)]
+
+    def call(i, j):
+        if ordered:
+            return tks.select_sorted(xs[i], w.k, lengths=L, out=outs[j], out_values=vals[j])
+        return tks.select(xs[i], w.k, lengths=L, out=outs[j])
+
+    warm_fns = [lambda: call(0, 0)]
+    cold_fns = [(lambda i: (lambda: call(i, i % 2)))(i) for i in range(copies)]
     if eager_only:
         t_eager = time_eager(torch, warm_fns[0], steps, warmup, stream)
         t_warm, n_warm, t_cold = t_eager, steps, t_eager
@@ -177,6 +186,8 @@ def main() -> int:
     ap.add_argument("--batch-workload", default="b64_n128k_ragged")
     ap.add_argument("--other-workloads", default="b1_n16k_normal,b1_n1m_outlier_bf16,b4096_n64k_causal_relu8",
                     help="comma-separated further workloads reported beside the headline ('' for none)")
+    ap.add_argument("--ordered-workloads", default="b1_n128k_bf16,b64_n128k_ragged,b4096_n64k_causal_relu8",
+                    help="workloads also timed with the ordered output (indices and values)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-copies", type=int, default=0,
                     help="input copies rotated for the cold-cache timing (0: enough to exceed 512 MiB)")
@@ -218,6 +229,14 @@ def main() -> int:
         st = int(max(20, min(args.steps, (2 << 30) // (c.rows * c.n * 4))))
         others.append(bench_workload(torch, tks, W, name, st, min(args.warmup, st),
                                      1 if args.eager_only else copies_for(name), args.eager_only))
+
+    ordered = []
+    if not args.eager_only:
+        for name in [x for x in args.ordered_workloads.split(",") if x]:
+            c = W.config(name)
+            st = int(max(20, min(args.steps // 4, (1 << 30) // (c.rows * c.n * 4))))
+            ordered.append(bench_workload(torch, tks, W, name, st, min(args.warmup, st), copies_for(name),
+                                          False, ordered=True))
 
     if args.calibrate_copy_mib:
         calibrate_copy(torch, args.calibrate_copy_mib)
@@ -279,6 +298,16 @@ def main() -> int:
         "achieved_GBps": round(o["bytes"] / o["t_cold"] / 1e9, 3),
         "hbm_frac": round(o["bytes"] / o["t_cold"] / 1e9 / HBM_PEAK_GBPS, 6),
         "algorithmic_bytes_per_launch": o["bytes"], "plan": o["plan"]} for o in others]
+    # ordered output: the selection, then the sort of each row's k entries;
+    # algorithmic bytes add the value output (4 bytes per slot)
+    res["ordered_output"] = [{
+        "workload": o["workload"], "rows": o["rows"], "n": o["n"], "k": o["k"],
+        "outputs": "indices and values, by value descending (index ascending on ties)",
+        "us_per_launch": round(o["t_cold"] * 1e6, 3), "us_per_launch_warm": round(o["t_warm"] * 1e6, 3),
+        "us_per_row": round(o["t_cold"] * 1e6 / o["rows"], 4), "rows_per_s": round(o["rows"] / o["t_cold"], 1),
+        "achieved_GBps": round((o["bytes"] + 4 * o["rows"] * o["k"]) / o["t_cold"] / 1e9, 3),
+        "hbm_frac": round((o["bytes"] + 4 * o["rows"] * o["k"]) / o["t_cold"] / 1e9 / HBM_PEAK_GBPS, 6),
+        "algorithmic_bytes_per_launch": o["bytes"] + 4 * o["rows"] * o["k"]} for o in ordered]
     if not args.no_cpu:
         sec_per_row, reps = cpu_baseline(head["x"], head["k"])
         res["cpu_baseline"] = {

@@ -87,7 +87,6 @@ struct KParams {
     const float* logits;
     const int32_t* lengths;
     int32_t* out;
-    uint32_t* keys;         // [rows, k]: key of the element at each output slot, or null
     RowWorkspace* ws;       // per row, when G > 1
     uint32_t* status;
     int32_t rows, n, k;
@@ -95,6 +94,7 @@ struct KParams {
     int32_t chunks_per_wg;  // 16-byte chunks in one WG's slice
     int32_t idx_bits;       // bits of the index that vary (multiple of 8, 8..32)
     int32_t mcopies;        // global histogram copies used (1..kMergeCopies)
+    uint32_t* keys;         // [rows, k]: key of the element at each output slot (ordered output), or null
 };
 
 // ----------------------------------------------------------------- device helpers
