@@ -1059,17 +1059,17 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
     };
 
-    // ---------------- first pass: 12-bit histogram of the row, and every
-    // element at or above a lower bound `lo` (a first-digit bin) kept in LDS.
-    // The bound is an estimate: the bin of the element of rank
-    // 1.25 * k * seen / L + 64 among the `seen` elements read so far, where
-    // the k-th largest of the row is expected near rank k * seen / L.  It is
-    // taken after the first tile and raised (with the buffer compacted)
-    // whenever the buffer fills up.  The buffer then holds every element at
-    // or above `lo`; when the exact threshold bin b0 of the row turns out to
-    // be at least `lo` (checked below), everything selected is in it.
-    // Otherwise, or when the buffer overflowed, the row is finished with
-    // re-reads.
+    // ---------------- first pass: every element at or above a lower bound
+    // `lo` (a first-digit bin) kept in LDS.  The bound is an estimate: the
+    // bin of the element of rank 1.25 * k * seen / L + 64 among the `seen`
+    // elements read so far, where the k-th largest of the row is expected
+    // near rank k * seen / L.  It is taken from a 12-bit histogram of the
+    // first tile and raised (with the buffer compacted) whenever the buffer
+    // fills up, from a histogram of the buffer.  The buffer then holds every
+    // element at or above `lo`, so the histogram of the buffer is exact for
+    // the bins at or above `lo`; when the row's threshold bin b0 is found
+    // there (checked below), everything selected is in it.  Otherwise, or
+    // when the buffer overflowed, the row is finished with re-reads.
     {
         uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
         for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
@@ -1080,7 +1080,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     bool keep = true;   // candidates are being buffered
     uint32_t used = 0;  // buffered entries
     uint32_t lo = 0;    // running lower bound (first-digit bin)
-    bool partial = false;  // the histogram skipped elements below the bound
     // Walk the buffer in slices of RC * BLOCK entries: every thread reads its
     // RC entries, a block scan numbers the chosen ones, and f(entry, kind,
     // rank) places them.  Kinds: pred returns 0 (drop), 1 or 2, counted
@@ -1120,7 +1119,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         const uint64_t est = ((uint64_t)k * seen * 5u) / (4u * (uint64_t)L) + 64u;
         return (uint32_t)(est < seen ? est : seen);
     };
-    // raise the bound from the histogram of the first `seen` elements
+    // the first-digit histogram of the buffered entries
+    auto hist_from_buffer = [&]() {
+        uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
+        for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
+        lds_sync();
+        uint32_t* const hcb = sm.h.h12 + (tid & 1) * 4097;
+        for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) atomicAdd(&hcb[(uint32_t)(sm.cand[i] >> (64 - F))], 1u);
+        lds_sync();
+    };
+    // raise the bound from the histogram of the first `seen` elements (only
+    // its bins at or above the bound need to be exact)
     auto raise_bound = [&](uint32_t seen) {
         uint32_t b, ab, hbx;
         local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, bound_rank(seen), sm.scan, sm.sel, P.status, b, ab,
@@ -1131,23 +1141,11 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
         const uint32_t lane = lane_id();
         stream([&](const uint32_t* keys, int ct) {
-            // histogram: the first tile counts every element, later tiles
-            // only those at or above the bound (the counts of the bins at or
-            // above the bound stay exact, which is all the final threshold
-            // needs once it is found at or above the bound)
-            if (ct == 0) {
+            if (!keep) return;  // overflowed: the fallback re-reads the row
+            if (ct == 0) {  // the first tile: histogram of every element
 #pragma unroll
                 for (int i = 0; i < ITEMS; ++i)
                     if (keys[i] != 0u) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
-            } else {
-                partial |= lo != 0u;
-#pragma unroll
-                for (int i = 0; i < ITEMS; ++i)
-                    if ((keys[i] != 0u) & ((keys[i] >> (32 - F)) >= lo)) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
-            }
-            if (!keep) {
-                lo = 0;  // count everything from here on
-                return;
             }
             // valid elements read once this tile is done
             const uint32_t seen = (uint32_t)min(L, 4 * min(nchunks, ct + TILE_CHUNKS) - off);
@@ -1189,6 +1187,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             }
             if (used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks) {
                 // tighter bound from more data, and drop what fell below it
+                hist_from_buffer();
                 raise_bound(seen);
                 const uint32_t lob = lo;
                 uint32_t n1, n2;
@@ -1205,8 +1204,11 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     uint32_t need = (uint32_t)k, W = 0, hb = 0;
     int R = 0;
     bool whole = false;
-    uint32_t b0, above;
-    local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+    uint32_t b0 = 0, above = 0;
+    if (keep) {
+        hist_from_buffer();
+        local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+    }
     if (keep && hb > 0u && b0 >= lo) {
         need -= above;
         W += above;
@@ -1249,7 +1251,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     }
     // ---------------- fallback: the full first-digit histogram by a second
     // read, then rounds and collection by further reads
-    if (partial) {
+    {
         {
             uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
             for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
