@@ -1206,8 +1206,31 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     bool whole = false;
     uint32_t b0 = 0, above = 0;
     if (keep) {
-        hist_from_buffer();
-        local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+        // the threshold bin, from the buffer: first over a 256-bin window of
+        // first-digit bins lo .. lo+254 (the last bin takes everything above;
+        // every buffered entry is at or above lo), which normally holds it;
+        // else over all 4096 bins
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
+            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        }
+        lds_sync();
+        {
+            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
+            for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
+                const uint32_t bin = (uint32_t)(sm.cand[i] >> (64 - F));
+                atomicAdd(&hcw[min(bin - lo, 255u)], 1u);
+            }
+        }
+        lds_sync();
+        uint32_t bw;
+        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, bw, above, hb);
+        if (hb > 0u && bw < 255u) {
+            b0 = lo + bw;
+        } else {
+            hist_from_buffer();
+            local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
+        }
     }
     if (keep && hb > 0u && b0 >= lo) {
         need -= above;
