@@ -13,6 +13,9 @@ Contents
   fast-math.
 * ``topk_sorted`` - the same selection in that order, with the selected
   values (the ordered output of the article's radix_topk, section 02).
+* ``indexer_logits`` - the logits the selector is fed (DSA step 1 of the
+  article's section 01), in double precision from bf16 inputs, with the
+  magnitude of the summed terms (the scale of float32 rounding errors).
 * ``pages_radix`` - the article's radix-select method restated in Python
   (mapping, digit histograms, threshold bucket, collection), a second route
   used to pin the first.
@@ -20,7 +23,10 @@ Contents
 Parity pins (tests/test_oracle_pins.py): brute force over all k-subsets of tiny
 rows, the article's method (``pages_radix``), numpy's stable argsort, closed
 forms, the worked value the article prints (839 -> 100), and the selection
-invariants.  No oracle function is left unpinned.
+invariants; for the indexer logits, closed forms (one-hot queries, queries
+opposite to every key), numpy matrix products in float64, linearity in the
+weights and independence of the head order.  No oracle function is left
+unpinned.
 """
 
 from __future__ import annotations
@@ -68,6 +74,8 @@ def _load():
             lib.oracle_topk.restype = ctypes.c_int
             lib.oracle_topk_sorted.argtypes = [P, I, I, P, I, P, P]
             lib.oracle_topk_sorted.restype = ctypes.c_int
+            lib.oracle_indexer_logits.argtypes = [P, P, P, I, I, I, I, ctypes.c_int64, P, P]
+            lib.oracle_indexer_logits.restype = ctypes.c_int
             lib.oracle_kth_largest.argtypes = [P, I, I, I, P]
             lib.oracle_kth_largest.restype = ctypes.c_int
             _lib = lib
@@ -118,6 +126,35 @@ def topk_sorted(x: np.ndarray, k: int, lengths: Optional[np.ndarray] = None):
     if rc != ORACLE_OK:
         raise ValueError("oracle_topk_sorted failed with code %d" % rc)
     return out, val
+
+
+def indexer_logits(q: np.ndarray, kc: np.ndarray, w: np.ndarray):
+    """Indexer logits: q [rows, H, d], kc [n, d] (shared by every row) or
+    [rows, n, d], w [rows, H]; float32 arrays holding bf16 values.  Returns
+    (logits, absterm), both float64 [rows, n]: logits[r, t] = sum_h w[r, h] *
+    max(0, q[r, h] . kc[t]); absterm[r, t] = sum_h |w[r, h]| * sum_i
+    |q[r, h, i] * kc[t, i]|."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    kc = np.ascontiguousarray(kc, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, H, d = q.shape
+    assert w.shape == (rows, H)
+    if kc.ndim == 2:
+        n = kc.shape[0]
+        kstride = 0
+    else:
+        assert kc.shape[0] == rows
+        n = kc.shape[1]
+        kstride = n * d
+    assert kc.shape[-1] == d
+    logits = np.empty((rows, n), dtype=np.float64)
+    absterm = np.empty((rows, n), dtype=np.float64)
+    rc = lib.oracle_indexer_logits(q.ctypes.data, kc.ctypes.data, w.ctypes.data, rows, n, H, d, kstride,
+                                   logits.ctypes.data, absterm.ctypes.data)
+    if rc != ORACLE_OK:
+        raise ValueError("oracle_indexer_logits failed with code %d" % rc)
+    return logits, absterm
 
 
 def kth_largest(row: np.ndarray, k: int, length: Optional[int] = None) -> float:

@@ -145,3 +145,48 @@ int oracle_topk_sorted(const float* logits, int32_t rows, int32_t n, const int32
     }
     return ORACLE_OK;
 }
+
+/*
+ * The indexer's logits: the TopK article, section 01, lists three DSA steps,
+ * the first being logits of the current query against every historical
+ * token; the article gives no formula.  Reading taken (the form the
+ * selector's causal workload mirrors: a weighted sum of eight ReLU terms):
+ * H indexer heads share one key per token, and
+ *
+ *     logits[r][t] = sum_h w[r][h] * max(0, sum_i q[r][h][i] * K[t][i])
+ *
+ * with q [rows, H, d], K [n, d] per row (kstride elements between the keys
+ * of consecutive rows; 0 when every row uses the same keys) and w [rows, H].
+ * The inputs arrive as floats (bf16 values widened exactly); the sums are
+ * taken in double precision, in index order.  absterm[r][t] (optional)
+ * receives sum_h |w[r][h]| * sum_i |q[r][h][i] * K[t][i]|, the scale of the
+ * rounding error of any float32 evaluation of the same sums.
+ */
+int oracle_indexer_logits(const float* q, const float* kc, const float* w, int32_t rows, int32_t n, int32_t H,
+                          int32_t d, int64_t kstride, double* logits, double* absterm) {
+    if (rows < 0 || n < 0 || H < 1 || d < 1 || kstride < 0) return ORACLE_ERR_ARG;
+    if (rows == 0 || n == 0) return ORACLE_OK;
+    if (!q || !kc || !w || !logits) return ORACLE_ERR_ARG;
+    for (int32_t r = 0; r < rows; ++r) {
+        const float* K = kc + (size_t)r * (size_t)kstride;
+        for (int32_t t = 0; t < n; ++t) {
+            const float* kt = K + (size_t)t * (size_t)d;
+            double acc = 0.0, mag = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                const float* qh = q + ((size_t)r * (size_t)H + (size_t)h) * (size_t)d;
+                double dot = 0.0, dmag = 0.0;
+                for (int32_t i = 0; i < d; ++i) {
+                    const double p = (double)qh[i] * (double)kt[i];
+                    dot += p;
+                    dmag += fabs(p);
+                }
+                const double wh = (double)w[(size_t)r * (size_t)H + (size_t)h];
+                acc += wh * (dot > 0.0 ? dot : 0.0);
+                mag += fabs(wh) * dmag;
+            }
+            logits[(size_t)r * (size_t)n + (size_t)t] = acc;
+            if (absterm) absterm[(size_t)r * (size_t)n + (size_t)t] = mag;
+        }
+    }
+    return ORACLE_OK;
+}

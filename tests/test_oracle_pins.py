@@ -406,3 +406,58 @@ def test_order_checker_rejects_planted_mistakes():
     row[[0, 5]] = row[[5, 0]]
     with pytest.raises(AssertionError):
         check_row_order(x, 5, 7, row)
+
+
+# ---------------------------------------------------------------- indexer logits (DSA step 1)
+
+def test_indexer_logits_closed_forms():
+    # one-hot queries pick one key coordinate per head: logits = sum_h w_h * max(0, K[t, j_h])
+    d, H, n = 8, 3, 5
+    q = np.zeros((1, H, d), np.float32)
+    picks = [1, 4, 7]
+    for h, j in enumerate(picks):
+        q[0, h, j] = 1.0
+    K = np.arange(n * d, dtype=np.float32).reshape(n, d) - 20.0
+    w = np.array([[0.5, 2.0, 0.25]], np.float32)
+    lg, ab = oracle.indexer_logits(q, K, w)
+    for t in range(n):
+        want = sum(w[0, h] * max(0.0, K[t, j]) for h, j in enumerate(picks))
+        assert lg[0, t] == want
+        assert ab[0, t] == sum(w[0, h] * abs(K[t, j]) for h, j in enumerate(picks))
+    # a query opposite to every key: every head is cut to zero by the ReLU
+    K2 = np.abs(np.random.default_rng(1).standard_normal((6, d))).astype(np.float32) + 0.5
+    q2 = -np.ones((1, 2, d), np.float32)
+    lg2, _ = oracle.indexer_logits(q2, K2, np.ones((1, 2), np.float32))
+    assert np.all(lg2 == 0.0)
+    # one head, one dimension: w * max(0, q * k)
+    lg3, _ = oracle.indexer_logits(np.array([[[3.0]]], np.float32), np.array([[2.0], [-1.0]], np.float32),
+                                   np.array([[0.5]], np.float32))
+    assert lg3.tolist() == [[3.0, 0.0]]
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_indexer_logits_match_matrix_route(shared):
+    """A second route: numpy matrix products in float64."""
+    import workloads as W
+
+    wl = W.draw(rows=3, n=300, heads=7, dim=32, k=16, seed=9, shared_keys=shared)
+    lg, ab = oracle.indexer_logits(wl.q, wl.kc, wl.w)
+    for r in range(3):
+        K = (wl.kc if shared else wl.kc[r]).astype(np.float64)
+        S = wl.q[r].astype(np.float64) @ K.T  # [H, n]
+        want = wl.w[r].astype(np.float64) @ np.maximum(S, 0.0)
+        mag = np.abs(wl.w[r].astype(np.float64)) @ (np.abs(wl.q[r].astype(np.float64)) @ np.abs(K.T))
+        assert np.allclose(lg[r], want, rtol=1e-12, atol=1e-12)
+        assert np.allclose(ab[r], mag, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_logits_linear_in_weights_and_blind_to_head_order():
+    import workloads as W
+
+    wl = W.draw(rows=2, n=64, heads=5, dim=16, k=8, seed=3)
+    lg, _ = oracle.indexer_logits(wl.q, wl.kc, wl.w)
+    lg2, _ = oracle.indexer_logits(wl.q, wl.kc, (wl.w * 2).astype(np.float32))
+    assert np.array_equal(lg2, 2 * lg)
+    perm = np.array([3, 0, 4, 1, 2])
+    lg3, _ = oracle.indexer_logits(np.ascontiguousarray(wl.q[:, perm]), wl.kc, np.ascontiguousarray(wl.w[:, perm]))
+    assert np.allclose(lg3, lg, rtol=1e-13, atol=0)

@@ -19,3 +19,11 @@ from .synth import (  # noqa: F401
     lengths_for,
     sha256_of,
 )
+from .indexer import (  # noqa: F401
+    INDEXER_CONFIGS,
+    IndexerConfig,
+    IndexerWorkload,
+    bf16_bits,
+    draw,
+    generate_indexer,
+)
