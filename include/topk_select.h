@@ -107,6 +107,49 @@ int topk_select_sorted(const float* logits, int32_t rows, int32_t n, const int32
                        int32_t* out_idx, float* out_val, topk_select_stream_t stream);
 
 /*
+ * topk_indexer_logits - the logits the selector is fed: the TopK article,
+ * section 01, step 1 of DSA-style decoding (logits of the current query
+ * against every historical token).  The article gives no formula; the one
+ * computed (the reading taken) has H indexer heads sharing one key per token:
+ *
+ *   logits[r*n + t] = sum_h w[r*H + h] *
+ *                     max(0, sum_i q[(r*H + h)*dim + i] * kc[r*kstride + t*dim + i])
+ *
+ * for t < L_r, and -INFINITY for L_r <= t < n (keys there are not read).
+ *
+ *   q        device, bf16 bit patterns, [rows, heads, dim], 16-byte aligned.
+ *   kc       device, bf16 bit patterns: the keys of row r are the [n, dim]
+ *            array at kc + r*kstride; 16-byte aligned.
+ *   w        device, float [rows, heads].
+ *   rows >= 0, n >= 1, 1 <= heads <= 64, dim one of 32, 64, 128.
+ *   kstride  elements between the keys of consecutive rows: 0 (every row
+ *            uses the same keys) or at least n*dim; a multiple of 8.
+ *   lengths  device int32 [rows] or NULL: valid lengths, clamped to [0, n].
+ *   logits   device, float [rows, n]; must not overlap the inputs.
+ *
+ * Products of bf16 values are exact in float; the sums run on the matrix
+ * cores in float, in an unspecified order, so each logit lies within
+ * (dim + heads + 2) * 2^-24 * sum_h |w| sum_i |q k| of the exact value.
+ * Errors as for topk_select (INVALID_VALUE enqueues nothing).
+ */
+int topk_indexer_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                        int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, float* logits,
+                        topk_select_stream_t stream);
+
+/*
+ * topk_indexer_select - topk_indexer_logits, then topk_select on those
+ * logits with the same lengths: the indexer and the selector of the
+ * article's section 01, steps 1 and 2.  out_idx as for topk_select.
+ *   out_logits  device, float [rows, n], receives the logits; or NULL, and
+ *               they go to a scratch area of the (device, stream) of
+ *               rows*n*4 bytes (grown with hipMalloc when needed).
+ * Two kernels are enqueued (the logits, then the selection).
+ */
+int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                        int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k,
+                        int32_t* out_idx, float* out_logits, topk_select_stream_t stream);
+
+/*
  * Launch-shape description, filled by topk_select_plan and accepted by
  * topk_select_ex.  Performance only: every plan yields the same selected sets.
  *   variant       kernel variant id (0 .. topk_select_num_variants()-1)

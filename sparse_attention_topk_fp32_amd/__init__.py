@@ -30,7 +30,11 @@ __all__ = [
     "topk_select",
     "topk_select_ex",
     "select_sorted",
+    "indexer_logits",
+    "indexer_select",
     "topk_select_sorted",
+    "topk_indexer_logits",
+    "topk_indexer_select",
     "topk_select_sorted_ex",
     "plan",
     "num_variants",
@@ -75,6 +79,22 @@ def topk_select_sorted_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optio
     p = _native.PlanT(variant, wgs_per_row, 0, 0, 0, 0)
     return _native.load().topk_select_sorted_ex(logits_ptr or None, rows, n, lengths_ptr or None, k,
                                                 out_ptr or None, val_ptr or None, stream or None, ctypes.byref(p))
+
+
+def topk_indexer_logits(q_ptr: int, kc_ptr: int, w_ptr: int, rows: int, n: int, heads: int, dim: int,
+                        kstride: int, lengths_ptr: Optional[int], logits_ptr: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the indexer logits; returns the status code."""
+    return _native.load().topk_indexer_logits(q_ptr or None, kc_ptr or None, w_ptr or None, rows, n, heads, dim,
+                                              kstride, lengths_ptr or None, logits_ptr or None, stream or None)
+
+
+def topk_indexer_select(q_ptr: int, kc_ptr: int, w_ptr: int, rows: int, n: int, heads: int, dim: int,
+                        kstride: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                        logits_ptr: Optional[int], stream: int = 0) -> int:
+    """Raw C-ABI call of the indexer logits followed by the selection."""
+    return _native.load().topk_indexer_select(q_ptr or None, kc_ptr or None, w_ptr or None, rows, n, heads, dim,
+                                              kstride, lengths_ptr or None, k, out_ptr or None,
+                                              logits_ptr or None, stream or None)
 
 
 def _stream_handle(stream) -> int:
@@ -176,6 +196,82 @@ def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optiona
             rc = topk_select_ex(x.data_ptr(), rows, n, lp, k, out.data_ptr(), sh, variant, wgs_per_row)
     _check(rc, "topk_select")
     return out[0] if squeeze else out
+
+
+def _indexer_args(q, kc, w, lengths):
+    import torch
+
+    for t, name in ((q, "q"), (kc, "kc")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
+            raise TypeError("%s must be a bfloat16 GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.float32 or w.device != q.device or not w.is_contiguous():
+        raise TypeError("w must be a contiguous float32 tensor on q's device")
+    if q.dim() != 3:
+        raise ValueError("q must be [rows, heads, dim]")
+    rows, heads, dim = q.shape
+    if w.shape != (rows, heads):
+        raise ValueError("w must be [rows, heads]")
+    if kc.device != q.device:
+        raise ValueError("kc must be on q's device")
+    if kc.dim() == 2:
+        n, kstride = kc.shape[0], 0
+    elif kc.dim() == 3 and kc.shape[0] == rows:
+        n, kstride = kc.shape[1], kc.shape[1] * kc.shape[2]
+    else:
+        raise ValueError("kc must be [n, dim] (shared by every row) or [rows, n, dim]")
+    if kc.shape[-1] != dim:
+        raise ValueError("kc's last dimension must be q's dim")
+    lp = None
+    if lengths is not None:
+        if lengths.dtype != torch.int32 or lengths.device != q.device or lengths.shape != (rows,) \
+                or not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous int32 [rows] tensor on q's device")
+        lp = lengths.data_ptr()
+    return rows, heads, dim, n, kstride, lp
+
+
+def indexer_logits(q, kc, w, lengths=None, out=None, stream=None):
+    """Indexer logits on the matrix cores: out[r, t] = sum_h w[r, h] *
+    max(0, q[r, h] . kc[t]) (kc [n, dim] shared by every row, or [rows, n,
+    dim]), -inf past the valid length.  q, kc bfloat16; w float32."""
+    import torch
+
+    rows, heads, dim, n, kstride, lp = _indexer_args(q, kc, w, lengths)
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float32, device=q.device)
+    else:
+        _check_out(out, torch.float32, rows, n, q, "out")
+    with torch.cuda.device(q.device):
+        rc = topk_indexer_logits(q.data_ptr(), kc.data_ptr(), w.data_ptr(), rows, n, heads, dim, kstride, lp,
+                                 out.data_ptr(), _stream_handle(stream))
+    _check(rc, "topk_indexer_logits")
+    return out
+
+
+def indexer_select(q, kc, w, k: int, lengths=None, out=None, out_logits=None, return_logits: bool = False,
+                   stream=None):
+    """The indexer logits, then the selection of the k largest per row
+    (unordered, as ``select``).  Returns the indices, or (indices, logits)
+    with ``return_logits`` (or ``out_logits`` given)."""
+    import torch
+
+    rows, heads, dim, n, kstride, lp = _indexer_args(q, kc, w, lengths)
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=q.device)
+    else:
+        _check_out(out, torch.int32, rows, k, q, "out")
+    want = return_logits or out_logits is not None
+    if want and out_logits is None:
+        out_logits = torch.empty((rows, n), dtype=torch.float32, device=q.device)
+    elif want:
+        _check_out(out_logits, torch.float32, rows, n, q, "out_logits")
+    with torch.cuda.device(q.device):
+        rc = topk_indexer_select(q.data_ptr(), kc.data_ptr(), w.data_ptr(), rows, n, heads, dim, kstride, lp, k,
+                                 out.data_ptr(), out_logits.data_ptr() if want else None, _stream_handle(stream))
+    _check(rc, "topk_indexer_select")
+    return (out, out_logits) if want else out
 
 
 def plan(rows: int, n: int, k: int) -> dict:

@@ -27,6 +27,8 @@ EXPORTS = (
     "topk_select_ex",
     "topk_select_sorted",
     "topk_select_sorted_ex",
+    "topk_indexer_logits",
+    "topk_indexer_select",
     "topk_select_plan",
     "topk_select_num_variants",
     "topk_select_variant_info",
@@ -78,6 +80,11 @@ def load() -> ctypes.CDLL:
         lib.topk_select_sorted.restype = ctypes.c_int
         lib.topk_select_sorted_ex.argtypes = [P, I, I, P, I, P, P, P, ctypes.POINTER(PlanT)]
         lib.topk_select_sorted_ex.restype = ctypes.c_int
+        I64 = ctypes.c_int64
+        lib.topk_indexer_logits.argtypes = [P, P, P, I, I, I, I, I64, P, P, P]
+        lib.topk_indexer_logits.restype = ctypes.c_int
+        lib.topk_indexer_select.argtypes = [P, P, P, I, I, I, I, I64, P, I, P, P, P]
+        lib.topk_indexer_select.restype = ctypes.c_int
         lib.topk_select_plan.argtypes = [I, I, I, ctypes.POINTER(PlanT)]
         lib.topk_select_plan.restype = ctypes.c_int
         lib.topk_select_num_variants.argtypes = []

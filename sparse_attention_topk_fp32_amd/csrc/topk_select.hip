@@ -51,6 +51,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -1678,6 +1679,175 @@ __global__ void __launch_bounds__(kRankBlock) topk_rank_kernel(SortParams P) {
     if (i < cnt && q == 0u) put_sorted(me, orow, vrow, prow, (uint32_t)L, above);
 }
 
+// ----------------------------------------------------------------- indexer logits
+// The logits the selector is fed (the TopK article, section 01, step 1 of
+// DSA: the current query against every historical token).  The article
+// gives no formula; the one computed here is the plainest that its
+// workloads support: H indexer heads share one key per token and
+//     logits[r][t] = sum_h w[r][h] * max(0, q[r][h] . K[r][t]),
+// q and K in bf16, products and sums in fp32.  It is a dense contraction,
+// so it runs on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = 16 heads
+// x 32 dims of the query, B = 32 dims x 16 tokens of the keys.  Operand
+// layout (64 lanes): A lane l holds head l%16, dims 8(l/16)..+7; B lane l
+// holds token l%16, dims 8(l/16)..+7 — 16 contiguous bytes of one key, one
+// 16-byte load; C lane l holds heads 4(l/16)..+3 of token l%16.  A lane
+// weights and clamps its four heads, two lane exchanges add the four head
+// groups, and each wave stores 64 consecutive logits.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct LogitParams {
+    const uint16_t* q;      // [rows, H, D] bf16
+    const uint16_t* kc;     // keys of row r at kc + r * kstride: [n, D] bf16
+    const float* w;         // [rows, H]
+    const int32_t* lengths; // [rows] or null
+    float* logits;          // [rows, n]; -inf at positions >= the valid length
+    int64_t kstride;        // elements between the keys of consecutive rows (0: shared)
+    int32_t rows, n, H;
+    int32_t gpw;            // groups of 64 tokens per wave
+    int32_t tiles;          // WGs per row
+};
+
+constexpr int kLogitBlock = 256;  // 4 waves
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// The keys of the group (64 tokens of D bf16) at K + 2 D tw bytes, read
+// contiguously: load i of a lane is bytes 1024 i + 16 lane of the group.
+// Tokens past `last` (the last valid one, relative to tw) read that one
+// instead (their values are zeroed when staged keys are used).
+template <int D, int NL>
+__device__ __forceinline__ void logits_load(u32x4_t (&r)[NL], const char* K, int tw, int last, int lane) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int off = 1024 * i + 16 * lane;
+        const int tok = min(off / (2 * D), last);
+        r[i] = *reinterpret_cast<const u32x4_t*>(K + ((size_t)(tw + tok) * D) * 2 + (off % (2 * D)));
+    }
+}
+
+// Store the loaded group in the wave's LDS region: chunk c of token r in
+// slot c ^ (r % CPR) of the token's row.
+template <int D, int NL>
+__device__ __forceinline__ void logits_stage(u32x4_t* st, const u32x4_t (&r)[NL], int lane) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int off = 1024 * i + 16 * lane;
+        const int tok = off / (2 * D), c = (off % (2 * D)) / 16;
+        st[tok * CPR + (c ^ (tok % CPR))] = r[i];
+    }
+}
+
+template <int D, int HB>
+__global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P) {
+    constexpr int KB = D / 32;
+    constexpr int CPR = D / 8;         // 16-byte chunks per key
+    constexpr int GB = 64 * D * 2;     // bytes of one group's keys (64 tokens)
+    constexpr int NL = GB / 1024;      // 16-byte loads per lane per group
+    // each wave stages its current group of keys in its own LDS region;
+    // chunk c of token r sits in slot c ^ (r % CPR) of the token's row, so
+    // the MFMA-layout reads (16 tokens, one chunk each) hit distinct banks
+    __shared__ u32x4_t stage[kLogitBlock / 64][GB / 16];
+    // the row's queries, shared by the WG's waves: chunk c of head h in slot
+    // c ^ (h % CPR) of the head's row
+    __shared__ u32x4_t qs[HB * 16 * CPR];
+    const int row = blockIdx.x / P.tiles;
+    const int tile = blockIdx.x - row * P.tiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int n = P.n, H = P.H;
+    const int L = valid_length(P.lengths, row, n);
+    {
+        const u32x4_t* const qrow = reinterpret_cast<const u32x4_t*>(P.q + (size_t)row * H * D);
+        for (int i = threadIdx.x; i < H * CPR; i += kLogitBlock) {
+            const int h = i / CPR, c = i % CPR;
+            qs[h * CPR + (c ^ (h % CPR))] = qrow[i];
+        }
+    }
+    __syncthreads();  // before any wave leaves
+    // this wave's tokens: gpw consecutive groups of 64
+    const int t0 = (tile * (kLogitBlock / 64) + wave) * P.gpw * 64;
+    if (t0 >= n) return;
+    const int t1 = min(t0 + P.gpw * 64, n);
+    float* const lrow = P.logits + (size_t)row * (size_t)n;
+    const float ninf = -__builtin_huge_valf();
+    const int tv = min(t1, L);  // valid tokens end here
+    for (int t = max(t0, tv) + lane; t < t1; t += 64) lrow[t] = ninf;
+    if (t0 >= tv) return;
+    const int ng = (tv - t0 + 63) / 64;  // groups holding valid tokens
+    // queries (A operands, from LDS) and the weights of this lane's four
+    // heads per block, once for all of the wave's groups; padding heads are
+    // zero
+    bf16x8_t a[HB][KB];
+    float wt[HB][4];
+    const bf16x8_t zero = {};
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 16 + m;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int c = kb * 4 + g;
+            const bf16x8_t x = __builtin_bit_cast(bf16x8_t, qs[h * CPR + (c ^ (h % CPR))]);
+            a[hb][kb] = h < H ? x : zero;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = hb * 16 + 4 * g + i;
+            const float x = P.w[(size_t)row * H + min(hh, H - 1)];
+            wt[hb][i] = hh < H ? x : 0.0f;
+        }
+    }
+    const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kstride);
+    u32x4_t* const st = stage[wave];
+    auto compute_store = [&](int tw) __attribute__((always_inline)) {
+        float v[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int tok = blk * 16 + m;
+            const bool ok = tw + tok < L;
+            bf16x8_t b[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int c = kb * 4 + g;  // dims 32 kb + 8 g .. +7
+                const bf16x8_t x = __builtin_bit_cast(bf16x8_t, st[tok * CPR + (c ^ (tok % CPR))]);
+                b[kb] = ok ? x : zero;
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hb][kb], b[kb], acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part += wt[hb][i] * fmaxf(acc[i], 0.0f);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            v[blk] = part;
+        }
+        // lane l stores token tw + l: block l/16, token l%16 of it
+        const float mine = g == 0 ? v[0] : (g == 1 ? v[1] : (g == 2 ? v[2] : v[3]));
+        const int t = tw + lane;
+        if (t < t1) lrow[t] = t < L ? mine : ninf;
+    };
+    // the next group's loads are in flight while the current one is
+    // computed from LDS; the wave's region is its own, so no barrier
+    u32x4_t r[NL];
+    logits_load<D, NL>(r, K, t0, L - 1 - t0, lane);
+    for (int gi = 0; gi < ng; ++gi) {
+        const int tw = t0 + gi * 64;
+        logits_stage<D, NL>(st, r, lane);
+        if (gi + 1 < ng) logits_load<D, NL>(r, K, tw + 64, L - 1 - (tw + 64), lane);
+        compute_store(tw);
+    }
+}
+
 // ----------------------------------------------------------------- host side
 
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
@@ -1754,9 +1924,11 @@ struct Workspace {
     size_t bytes = 0;
     void* aux = nullptr;  // ordered output: recorded keys, merge buffers (no clearing needed)
     size_t aux_bytes = 0;
+    void* lg = nullptr;   // indexer selection without a logits output: the logits
+    size_t lg_bytes = 0;
 };
 
-std::mutex g_mu;
+std::recursive_mutex g_mu;  // recursive: the indexer entry point holds it across its launches
 std::map<int, DeviceInfo> g_dev;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
@@ -1905,24 +2077,28 @@ int get_workspace(int dev, hipStream_t stream, size_t need, Workspace** out) {
     return TOPK_SELECT_SUCCESS;
 }
 
-int get_aux(hipStream_t stream, Workspace* w, size_t need) {
-    if (w->aux_bytes < need) {
-        if (w->aux) {
+// Grow-only scratch that needs no clearing (the old one is freed once the
+// stream has finished with it).
+int grow_scratch(hipStream_t stream, void** ptr, size_t* bytes, size_t need) {
+    if (*bytes < need) {
+        if (*ptr) {
             if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            (void)hipFree(w->aux);
-            w->aux = nullptr;
-            w->aux_bytes = 0;
+            (void)hipFree(*ptr);
+            *ptr = nullptr;
+            *bytes = 0;
         }
         void* p = nullptr;
         if (hipMalloc(&p, need) != hipSuccess) {
             (void)hipGetLastError();
             return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
         }
-        w->aux = p;
-        w->aux_bytes = need;
+        *ptr = p;
+        *bytes = need;
     }
     return TOPK_SELECT_SUCCESS;
 }
+
+int get_aux(hipStream_t stream, Workspace* w, size_t need) { return grow_scratch(stream, &w->aux, &w->aux_bytes, need); }
 
 bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -1973,7 +2149,7 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
-    std::lock_guard<std::mutex> lock(g_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_mu);
     DeviceInfo* d = nullptr;
     rc = device_info(dev, &d);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
@@ -2060,9 +2236,135 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     return TOPK_SELECT_SUCCESS;
 }
 
+// ---- indexer logits and the selection on them
+
+int validate_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
+                     int32_t dim, int64_t kstride, const int32_t* lengths, const float* logits) {
+    if (rows < 0 || n < 1 || heads < 1 || heads > 64 || kstride < 0) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (dim != 32 && dim != 64 && dim != 128) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (rows == 0) return TOPK_SELECT_SUCCESS;
+    if (!q || !kc || !w) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (((uintptr_t)q & 15) || ((uintptr_t)kc & 15) || ((uintptr_t)w & 3) || ((uintptr_t)lengths & 3) ||
+        (kstride % 8) != 0)
+        return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (kstride != 0 && kstride < (int64_t)n * dim) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (logits) {
+        if ((uintptr_t)logits & 3) return TOPK_SELECT_ERROR_INVALID_VALUE;
+        const size_t lb = (size_t)rows * (size_t)n * 4u;
+        const size_t kb = ((kstride ? (size_t)(rows - 1) * (size_t)kstride : 0u) + (size_t)n * dim) * 2u;
+        if (overlaps(logits, lb, q, (size_t)rows * heads * dim * 2u) || overlaps(logits, lb, kc, kb) ||
+            overlaps(logits, lb, w, (size_t)rows * heads * 4u) || overlaps(logits, lb, lengths, (size_t)rows * 4u))
+            return TOPK_SELECT_ERROR_INVALID_VALUE;
+    }
+    return TOPK_SELECT_SUCCESS;
+}
+
+template <int D, int HB>
+void launch_logits_t(unsigned grid, hipStream_t stream, const LogitParams& p) {
+    topk_logits_kernel<D, HB><<<grid, kLogitBlock, 0, stream>>>(p);
+}
+
+int launch_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
+                  int32_t dim, int64_t kstride, const int32_t* lengths, float* logits, hipStream_t stream) {
+    LogitParams p;
+    p.q = q;
+    p.kc = kc;
+    p.w = w;
+    p.lengths = lengths;
+    p.logits = logits;
+    p.kstride = kstride;
+    p.rows = rows;
+    p.n = n;
+    p.H = heads;
+    // groups of 64 tokens per wave: one when the grid is small (every
+    // group its own wave), more for long or many rows, so that each wave
+    // streams several groups with the next one's keys in flight (about two
+    // WGs per CU resident, the grid a few times that)
+    int cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t groups = (int64_t)rows * ((n + 63) / 64);
+    const int64_t resident_waves = (int64_t)cus * 2 * (kLogitBlock / 64);
+    int64_t gpw = (groups + 4 * resident_waves - 1) / (4 * resident_waves);
+    p.gpw = (int32_t)(gpw < 1 ? 1 : (gpw > 8 ? 8 : gpw));
+    const int64_t tok_wg = (int64_t)p.gpw * kLogitBlock;
+    p.tiles = (int32_t)((n + tok_wg - 1) / tok_wg);
+    const int64_t grid = (int64_t)rows * p.tiles;
+    if (grid > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    const int hb = heads <= 16 ? 1 : (heads <= 32 ? 2 : 4);
+    (void)hipGetLastError();
+    const unsigned g = (unsigned)grid;
+    if (dim == 32) {
+        if (hb == 1) launch_logits_t<32, 1>(g, stream, p);
+        else if (hb == 2) launch_logits_t<32, 2>(g, stream, p);
+        else launch_logits_t<32, 4>(g, stream, p);
+    } else if (dim == 64) {
+        if (hb == 1) launch_logits_t<64, 1>(g, stream, p);
+        else if (hb == 2) launch_logits_t<64, 2>(g, stream, p);
+        else launch_logits_t<64, 4>(g, stream, p);
+    } else {
+        if (hb == 1) launch_logits_t<128, 1>(g, stream, p);
+        else if (hb == 2) launch_logits_t<128, 2>(g, stream, p);
+        else launch_logits_t<128, 4>(g, stream, p);
+    }
+    return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
+}
+
+int run_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
+                int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k, int32_t* out_idx, float* logits,
+                hipStream_t stream) {
+    int rc = validate_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, logits);
+    if (rc != TOPK_SELECT_SUCCESS) return rc;
+    if (k < 1 || k > n) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (rows == 0) return TOPK_SELECT_SUCCESS;
+    if (!out_idx || ((uintptr_t)out_idx & 3)) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    const size_t ob = (size_t)rows * (size_t)k * 4u;
+    if (overlaps(out_idx, ob, q, (size_t)rows * heads * dim * 2u) || overlaps(out_idx, ob, w, (size_t)rows * heads * 4u) ||
+        overlaps(out_idx, ob, kc, ((kstride ? (size_t)(rows - 1) * (size_t)kstride : 0u) + (size_t)n * dim) * 2u))
+        return TOPK_SELECT_ERROR_INVALID_VALUE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
+    std::lock_guard<std::recursive_mutex> lock(g_mu);  // held across both launches (scratch stays put)
+    float* lg = logits;
+    if (!lg) {
+        Workspace& ws = g_ws[{dev, (uintptr_t)stream}];
+        rc = grow_scratch(stream, &ws.lg, &ws.lg_bytes, (size_t)rows * (size_t)n * 4u);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+        lg = reinterpret_cast<float*>(ws.lg);
+    }
+    rc = launch_logits(q, kc, w, rows, n, heads, dim, kstride, lengths, lg, stream);
+    if (rc != TOPK_SELECT_SUCCESS) return rc;
+    return run(lg, rows, n, lengths, k, out_idx, false, nullptr, stream, nullptr);
+}
+
 }  // namespace tks
 
 extern "C" {
+
+int topk_indexer_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                        int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, float* logits,
+                        topk_select_stream_t stream) {
+    try {
+        int rc = tks::validate_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, logits);
+        if (rc != TOPK_SELECT_SUCCESS || rows == 0) return rc;
+        if (!logits) return TOPK_SELECT_ERROR_INVALID_VALUE;
+        return tks::launch_logits(q, kc, w, rows, n, heads, dim, kstride, lengths, logits, (hipStream_t)stream);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
+int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                        int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k,
+                        int32_t* out_idx, float* out_logits, topk_select_stream_t stream) {
+    try {
+        return tks::run_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, k, out_idx, out_logits,
+                                (hipStream_t)stream);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
 
 int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                 int32_t* out_idx, topk_select_stream_t stream) {
@@ -2108,7 +2410,7 @@ int topk_select_plan(int32_t rows, int32_t n, int32_t k, topk_select_plan_t* pla
     try {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
-        std::lock_guard<std::mutex> lock(tks::g_mu);
+        std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
         tks::DeviceInfo* d = nullptr;
         int rc = tks::device_info(dev, &d);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
@@ -2148,7 +2450,7 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
         if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-        std::lock_guard<std::mutex> lock(tks::g_mu);
+        std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
         auto it = tks::g_ws.find({dev, (uintptr_t)stream});
         if (it == tks::g_ws.end() || !it->second.base) return TOPK_SELECT_SUCCESS;
         uint32_t v = 0;
@@ -2168,16 +2470,16 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
 
 int topk_select_release_workspace(void) {
     try {
-        std::lock_guard<std::mutex> lock(tks::g_mu);
+        std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
         int rc = TOPK_SELECT_SUCCESS;
         for (auto& kv : tks::g_ws) {
-            if (kv.second.base) {
+            if (kv.second.base || kv.second.aux || kv.second.lg) {
                 int cur = 0;
                 (void)hipGetDevice(&cur);
                 (void)hipSetDevice(kv.first.first);
                 if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                if (hipFree(kv.second.base) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                if (kv.second.aux && hipFree(kv.second.aux) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+                for (void* p : {kv.second.base, kv.second.aux, kv.second.lg})
+                    if (p && hipFree(p) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
                 (void)hipSetDevice(cur);
             }
         }

@@ -27,7 +27,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(topk_select\w*)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(topk_\w*)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -93,6 +93,35 @@ def test_sorted_argument_checks_answer_before_any_hip_call(lib):
     assert call(a, 2, 16, v, 4, o, v + 4) == INV  # values overlap lengths
     assert call(a, 2, 16, None, 4, a + 8, v) == INV  # out overlaps logits
     assert lib.topk_select_sorted_ex(a, 1, 16, None, 4, o, v, None, None) == INV  # no plan
+
+
+def test_indexer_argument_checks_answer_before_any_hip_call(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    INV = _native.ERROR_INVALID_VALUE
+    q, kc, w, o, lg = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+    def logits(q_=q, kc_=kc, w_=w, rows=2, n=64, heads=16, dim=64, kstride=0, lengths=None, out=lg):
+        return lib.topk_indexer_logits(q_, kc_, w_, rows, n, heads, dim, kstride, lengths, out, None)
+
+    def select(k=8, out=o, logits_out=None, **kw):
+        a = dict(q_=q, kc_=kc, w_=w, rows=2, n=64, heads=16, dim=64, kstride=0, lengths=None)
+        a.update(kw)
+        return lib.topk_indexer_select(a["q_"], a["kc_"], a["w_"], a["rows"], a["n"], a["heads"], a["dim"],
+                                       a["kstride"], a["lengths"], k, out, logits_out, None)
+
+    assert logits(rows=0) == _native.SUCCESS
+    assert logits(heads=0) == INV and logits(heads=65) == INV
+    assert logits(dim=48) == INV and logits(dim=256) == INV
+    assert logits(kstride=4) == INV  # not a multiple of 8 elements
+    assert logits(kstride=64 * 64 - 8) == INV  # rows' keys would overlap
+    assert logits(q_=q + 8) == INV and logits(kc_=kc + 4) == INV  # 16-byte alignment
+    assert logits(out=None) == INV
+    assert logits(out=q + 16) == INV  # logits overlap the queries
+    assert select(k=65) == INV and select(k=0) == INV
+    assert select(out=None) == INV
+    assert select(out=q) == INV  # indices overlap the queries
+    assert select(rows=0) == _native.SUCCESS
 
 
 def test_variant_table(lib):

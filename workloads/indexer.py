@@ -87,7 +87,7 @@ def draw(rows: int, n: int, heads: int, dim: int, k: int, seed: int, shared_keys
         kc[:] = bf16_round(_rng(seed, 1 << 31).standard_normal((n, dim), dtype=np.float32))
     L = None
     if lengths == "uniform":
-        L = _rng(seed, _LENGTH_STREAM).integers(min(2048, n), n, size=rows, endpoint=True).astype(np.int32)
+        L = _rng(seed, _LENGTH_STREAM).integers(min(2048, max(1, n // 4)), n, size=rows, endpoint=True).astype(np.int32)
     return IndexerWorkload(config, q, kc, w, L, k)
 
 
