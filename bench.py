@@ -128,6 +128,43 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
     }
 
 
+def bench_indexer(torch, tks, W, name: str, steps: int, warmup: int):
+    """The indexer producer (DSA step 1) and producer + selection, cold: key
+    copies rotated (>= 512 MiB).  Seconds per launch."""
+    wl = W.generate_indexer(name)
+    rows, H, d = wl.q.shape
+    n = wl.kc.shape[-2]
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    w = torch.from_numpy(wl.w).cuda()
+    L = None if wl.lengths is None else torch.from_numpy(wl.lengths).cuda()
+    kcs = [torch.from_numpy(wl.kc).cuda().to(torch.bfloat16)]
+    copies = int(max(2, min(256, (512 << 20) // (kcs[0].numel() * 2) + 1)))
+    for _ in range(copies - 1):
+        kcs.append(kcs[0].clone())
+    lg = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    out = torch.empty((rows, wl.k), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    t_logits, _ = time_graph(torch, [(lambda kc: (lambda: tks.indexer_logits(q, kc, w, lengths=L, out=lg)))(kc)
+                                     for kc in kcs], steps, warmup, stream)
+    t_select, _ = time_graph(torch, [(lambda kc: (lambda: tks.indexer_select(q, kc, w, wl.k, lengths=L, out=out,
+                                                                             out_logits=lg)))(kc)
+                                     for kc in kcs], steps, warmup, stream)
+    if tks.device_status(stream):
+        raise RuntimeError("device-side error flags raised during the indexer benchmark")
+    valid = n * rows if wl.lengths is None else int(np.minimum(wl.lengths.astype(np.int64), n).sum())
+    # algorithmic bytes of the logits: one read of the valid keys, the
+    # queries and weights, one write of the logits row
+    nbytes = valid * d * 2 + rows * H * d * 2 + rows * H * 4 + rows * n * 4
+    flops = 2 * valid * H * d
+    return {"workload": name, "rows": rows, "n": n, "heads": H, "dim": d, "k": wl.k,
+            "us_logits": round(t_logits * 1e6, 3), "us_logits_and_select": round(t_select * 1e6, 3),
+            "algorithmic_bytes_logits": nbytes, "achieved_GBps": round(nbytes / t_logits / 1e9, 3),
+            "hbm_frac": round(nbytes / t_logits / 1e9 / HBM_PEAK_GBPS, 6),
+            "mfma_TFLOPs": round(flops / t_logits / 1e12, 3),
+            "timing": "HIP-graph replay, key copies rotated (cold)"}
+
+
 def kernel_source_sha256() -> str:
     import hashlib
 
@@ -188,6 +225,8 @@ def main() -> int:
                     help="comma-separated further workloads reported beside the headline ('' for none)")
     ap.add_argument("--ordered-workloads", default="b1_n128k_bf16,b64_n128k_ragged,b4096_n64k_causal_relu8",
                     help="workloads also timed with the ordered output (indices and values)")
+    ap.add_argument("--indexer-workloads", default="idx_b1_n128k_h64_d128,idx_b64_n16k_h64_d128_ragged",
+                    help="indexer producer workloads (logits on the matrix cores, then the selection)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-copies", type=int, default=0,
                     help="input copies rotated for the cold-cache timing (0: enough to exceed 512 MiB)")
@@ -237,6 +276,11 @@ def main() -> int:
             st = int(max(20, min(args.steps // 4, (1 << 30) // (c.rows * c.n * 4))))
             ordered.append(bench_workload(torch, tks, W, name, st, min(args.warmup, st), copies_for(name),
                                           False, ordered=True))
+
+    indexer = []
+    if not args.eager_only:
+        for name in [x for x in args.indexer_workloads.split(",") if x]:
+            indexer.append(bench_indexer(torch, tks, W, name, 200, 20))
 
     if args.calibrate_copy_mib:
         calibrate_copy(torch, args.calibrate_copy_mib)
@@ -308,6 +352,7 @@ def main() -> int:
         "achieved_GBps": round((o["bytes"] + 4 * o["rows"] * o["k"]) / o["t_cold"] / 1e9, 3),
         "hbm_frac": round((o["bytes"] + 4 * o["rows"] * o["k"]) / o["t_cold"] / 1e9 / HBM_PEAK_GBPS, 6),
         "algorithmic_bytes_per_launch": o["bytes"] + 4 * o["rows"] * o["k"]} for o in ordered]
+    res["indexer"] = indexer
     if not args.no_cpu:
         sec_per_row, reps = cpu_baseline(head["x"], head["k"])
         res["cpu_baseline"] = {

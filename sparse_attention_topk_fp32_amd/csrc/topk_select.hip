@@ -100,6 +100,10 @@ struct KParams {
 
 // ----------------------------------------------------------------- device helpers
 
+// 16 bytes as a native vector (register arrays of the uint4 struct can be
+// placed in scratch memory when they are passed around)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Mapping step: float -> unsigned key with key(a) < key(b) iff a < b for
 // non-NaN values.  Adding +0.0 turns -0.0 into +0.0 (IEEE round to nearest)
 // and leaves every other value, subnormals included, unchanged, so -0.0 and
@@ -1696,7 +1700,6 @@ __global__ void __launch_bounds__(kRankBlock) topk_rank_kernel(SortParams P) {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct LogitParams {
     const uint16_t* q;      // [rows, H, D] bf16
