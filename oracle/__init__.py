@@ -16,6 +16,8 @@ Contents
 * ``indexer_logits`` - the logits the selector is fed (DSA step 1 of the
   article's section 01), in double precision from bf16 inputs, with the
   magnitude of the summed terms (the scale of float32 rounding errors).
+* ``sparse_attention`` - attention of the query heads over the selected
+  positions only (DSA step 3), in double precision, with the error scales.
 * ``pages_radix`` - the article's radix-select method restated in Python
   (mapping, digit histograms, threshold bucket, collection), a second route
   used to pin the first.
@@ -25,7 +27,11 @@ rows, the article's method (``pages_radix``), numpy's stable argsort, closed
 forms, the worked value the article prints (839 -> 100), and the selection
 invariants; for the indexer logits, closed forms (one-hot queries, queries
 opposite to every key), numpy matrix products in float64, linearity in the
-weights and independence of the head order.  No oracle function is left
+weights and independence of the head order; for the attention over the
+selected positions, closed forms (one position gives its value row, equal
+scores the mean of the value rows, none gives zeros), numpy matrix products
+and softmax in float64, independence of the slot order, linearity in the
+values and invariance to a score shift.  No oracle function is left
 unpinned.
 """
 
@@ -76,6 +82,9 @@ def _load():
             lib.oracle_topk_sorted.restype = ctypes.c_int
             lib.oracle_indexer_logits.argtypes = [P, P, P, I, I, I, I, ctypes.c_int64, P, P]
             lib.oracle_indexer_logits.restype = ctypes.c_int
+            lib.oracle_sparse_attention.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int64, I, ctypes.c_double,
+                                                    P, P, P]
+            lib.oracle_sparse_attention.restype = ctypes.c_int
             lib.oracle_kth_largest.argtypes = [P, I, I, I, P]
             lib.oracle_kth_largest.restype = ctypes.c_int
             _lib = lib
@@ -155,6 +164,35 @@ def indexer_logits(q: np.ndarray, kc: np.ndarray, w: np.ndarray):
     if rc != ORACLE_OK:
         raise ValueError("oracle_indexer_logits failed with code %d" % rc)
     return logits, absterm
+
+
+def sparse_attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, idx: np.ndarray, scale: float):
+    """Attention over the selected positions: q [rows, H, d]; kc, vc [n, d]
+    (shared by every row) or [rows, n, d]; idx int32 [rows, k] (-1: no
+    position).  Returns (out, mag, smax): out [rows, H, d] float64 =
+    sum_j softmax_j(scale q . K[idx_j]) V[idx_j]; mag [rows, H, d] = sum_j
+    p_j |V[idx_j]|; smax [rows, H] = max_j scale * sum_i |q_i K[idx_j]_i|."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    kc = np.ascontiguousarray(kc, dtype=np.float32)
+    vc = np.ascontiguousarray(vc, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    rows, H, d = q.shape
+    k = idx.shape[1]
+    assert idx.shape == (rows, k) and kc.shape == vc.shape
+    if kc.ndim == 2:
+        n, kvstride = kc.shape[0], 0
+    else:
+        assert kc.shape[0] == rows
+        n, kvstride = kc.shape[1], kc.shape[1] * d
+    out = np.empty((rows, H, d), np.float64)
+    mag = np.empty((rows, H, d), np.float64)
+    smax = np.empty((rows, H), np.float64)
+    rc = lib.oracle_sparse_attention(q.ctypes.data, kc.ctypes.data, vc.ctypes.data, idx.ctypes.data, rows, n, H, d,
+                                     kvstride, k, float(scale), out.ctypes.data, mag.ctypes.data, smax.ctypes.data)
+    if rc != ORACLE_OK:
+        raise ValueError("oracle_sparse_attention failed with code %d" % rc)
+    return out, mag, smax
 
 
 def kth_largest(row: np.ndarray, k: int, length: Optional[int] = None) -> float:

@@ -190,3 +190,89 @@ int oracle_indexer_logits(const float* q, const float* kc, const float* w, int32
     }
     return ORACLE_OK;
 }
+
+/*
+ * Attention over the selected positions: the TopK article, section 01,
+ * step 3 of DSA-style decoding (attention computed only on the keys and
+ * values of the k selected positions).  The article gives no formula;
+ * the one taken is plain scaled dot-product attention of each query head
+ * over the selected positions, keys and values shared by the heads:
+ *
+ *     s_j = scale * q[r][h] . K[r][idx_j],   p_j = exp(s_j) / sum_j' exp(s_j')
+ *     out[r][h][:] = sum_j p_j * V[r][idx_j][:]
+ *
+ * over the slots j with idx_j >= 0 (a -1 slot holds no position); a row
+ * with no such slot gives zeros.  q [rows, H, d]; the keys and values of
+ * row r are [n, d] arrays at kc + r*kvstride and vc + r*kvstride; idx
+ * [rows, k].  Double precision, softmax with its maximum subtracted.
+ * mag[r][h][c] (optional) receives sum_j p_j * |V[idx_j][c]| and smax[r][h]
+ * (optional) max_j scale * sum_i |q_i K[idx_j]_i|: the scales of float32
+ * rounding errors.
+ */
+int oracle_sparse_attention(const float* q, const float* kc, const float* vc, const int32_t* idx, int32_t rows,
+                            int32_t n, int32_t H, int32_t d, int64_t kvstride, int32_t k, double scale,
+                            double* out, double* mag, double* smax) {
+    if (rows < 0 || n < 1 || H < 1 || d < 1 || k < 1 || kvstride < 0) return ORACLE_ERR_ARG;
+    if (rows == 0) return ORACLE_OK;
+    if (!q || !kc || !vc || !idx || !out) return ORACLE_ERR_ARG;
+    double* s = (double*)malloc(sizeof(double) * (size_t)k);
+    double* sa = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!s || !sa) {
+        free(s);
+        free(sa);
+        return ORACLE_ERR_NOMEM;
+    }
+    int rc = ORACLE_OK;
+    for (int32_t r = 0; r < rows && rc == ORACLE_OK; ++r) {
+        const float* K = kc + (size_t)r * (size_t)kvstride;
+        const float* V = vc + (size_t)r * (size_t)kvstride;
+        const int32_t* ix = idx + (size_t)r * (size_t)k;
+        for (int32_t h = 0; h < H; ++h) {
+            const float* qh = q + ((size_t)r * (size_t)H + (size_t)h) * (size_t)d;
+            double* o = out + ((size_t)r * (size_t)H + (size_t)h) * (size_t)d;
+            double* mg = mag ? mag + ((size_t)r * (size_t)H + (size_t)h) * (size_t)d : NULL;
+            double best = -INFINITY, bestabs = 0.0;
+            int any = 0;
+            for (int32_t j = 0; j < k; ++j) {
+                if (ix[j] < 0) continue;
+                if (ix[j] >= n) {
+                    rc = ORACLE_ERR_ARG;
+                    break;
+                }
+                const float* kt = K + (size_t)ix[j] * (size_t)d;
+                double dot = 0.0, dabs = 0.0;
+                for (int32_t i = 0; i < d; ++i) {
+                    dot += (double)qh[i] * (double)kt[i];
+                    dabs += fabs((double)qh[i] * (double)kt[i]);
+                }
+                s[j] = scale * dot;
+                sa[j] = fabs(scale) * dabs;
+                if (s[j] > best) best = s[j];
+                if (sa[j] > bestabs) bestabs = sa[j];
+                any = 1;
+            }
+            if (rc != ORACLE_OK) break;
+            for (int32_t c = 0; c < d; ++c) {
+                o[c] = 0.0;
+                if (mg) mg[c] = 0.0;
+            }
+            if (smax) smax[(size_t)r * (size_t)H + (size_t)h] = bestabs;
+            if (!any) continue;
+            double den = 0.0;
+            for (int32_t j = 0; j < k; ++j)
+                if (ix[j] >= 0) den += exp(s[j] - best);
+            for (int32_t j = 0; j < k; ++j) {
+                if (ix[j] < 0) continue;
+                const double p = exp(s[j] - best) / den;
+                const float* vt = V + (size_t)ix[j] * (size_t)d;
+                for (int32_t c = 0; c < d; ++c) {
+                    o[c] += p * (double)vt[c];
+                    if (mg) mg[c] += p * fabs((double)vt[c]);
+                }
+            }
+        }
+    }
+    free(s);
+    free(sa);
+    return rc;
+}

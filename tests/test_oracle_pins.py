@@ -461,3 +461,59 @@ def test_indexer_logits_linear_in_weights_and_blind_to_head_order():
     perm = np.array([3, 0, 4, 1, 2])
     lg3, _ = oracle.indexer_logits(np.ascontiguousarray(wl.q[:, perm]), wl.kc, np.ascontiguousarray(wl.w[:, perm]))
     assert np.allclose(lg3, lg, rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------- attention over the selected positions (DSA step 3)
+
+def test_sparse_attention_closed_forms():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((10, 8)).astype(np.float32)
+    V = rng.standard_normal((10, 8)).astype(np.float32)
+    q = rng.standard_normal((1, 3, 8)).astype(np.float32)
+    # one selected position: its value row, whatever the scores
+    out, _, _ = oracle.sparse_attention(q, K, V, np.array([[-1, 6, -1]], np.int32), 0.7)
+    assert np.array_equal(out[0], np.repeat(V[6][None].astype(np.float64), 3, axis=0))
+    # equal scores (zero query): the mean of the selected value rows
+    sel = [1, 4, 9, 0]
+    out, _, _ = oracle.sparse_attention(np.zeros((1, 2, 8), np.float32), K, V, np.array([sel], np.int32), 1.0)
+    assert np.allclose(out[0], V[sel].astype(np.float64).mean(axis=0)[None], rtol=1e-14, atol=1e-15)
+    # no selected position: zeros
+    out, _, _ = oracle.sparse_attention(q, K, V, np.full((1, 4), -1, np.int32), 1.0)
+    assert np.all(out == 0.0)
+
+
+def test_sparse_attention_matches_numpy_route_and_ignores_slot_order():
+    import workloads as W
+
+    wl = W.draw_attention(rows=3, n=200, heads=5, dim=16, k=40, seed=8, lengths="uniform")
+    scale = 0.25
+    out, mag, smax = oracle.sparse_attention(wl.q, wl.kc, wl.vc, wl.idx, scale)
+    for r in range(3):
+        sel = wl.idx[r][wl.idx[r] >= 0]
+        K = wl.kc[r][sel].astype(np.float64)
+        V = wl.vc[r][sel].astype(np.float64)
+        S = scale * (wl.q[r].astype(np.float64) @ K.T)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        assert np.allclose(out[r], P @ V, rtol=1e-12, atol=1e-12)
+        assert np.allclose(mag[r], P @ np.abs(V), rtol=1e-12, atol=1e-12)
+        assert np.allclose(smax[r], (scale * (np.abs(wl.q[r].astype(np.float64)) @ np.abs(K.T))).max(axis=1))
+    perm = np.random.default_rng(1).permutation(wl.idx.shape[1])
+    out2, _, _ = oracle.sparse_attention(wl.q, wl.kc, wl.vc, np.ascontiguousarray(wl.idx[:, perm]), scale)
+    assert np.allclose(out2, out, rtol=1e-13, atol=1e-14)
+
+
+def test_sparse_attention_is_linear_in_values_and_shift_invariant_in_scores():
+    import workloads as W
+
+    wl = W.draw_attention(rows=2, n=64, heads=3, dim=8, k=10, seed=5, shared_kv=True)
+    out, _, _ = oracle.sparse_attention(wl.q, wl.kc, wl.vc, wl.idx, 0.5)
+    out2, _, _ = oracle.sparse_attention(wl.q, wl.kc, (2 * wl.vc).astype(np.float32), wl.idx, 0.5)
+    assert np.allclose(out2, 2 * out, rtol=1e-14, atol=1e-15)
+    # a key component every selected key shares adds the same score to all:
+    # append a constant column to the keys and a matching query column
+    kc2 = np.concatenate([wl.kc, np.ones((wl.kc.shape[0], 1), np.float32)], axis=1)
+    vc2 = np.concatenate([wl.vc, np.zeros((wl.vc.shape[0], 1), np.float32)], axis=1)
+    q2 = np.concatenate([wl.q, np.full(wl.q.shape[:2] + (1,), 3.0, np.float32)], axis=2)
+    out3, _, _ = oracle.sparse_attention(q2, kc2, vc2, wl.idx, 0.5)
+    assert np.allclose(out3[:, :, :-1], out, rtol=1e-12, atol=1e-13)

@@ -27,3 +27,10 @@ from .indexer import (  # noqa: F401
     draw,
     generate_indexer,
 )
+from .attention import (  # noqa: F401
+    ATTENTION_CONFIGS,
+    AttentionConfig,
+    AttentionWorkload,
+    draw_attention,
+    generate_attention,
+)
