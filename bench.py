@@ -165,6 +165,38 @@ def bench_indexer(torch, tks, W, name: str, steps: int, warmup: int):
             "timing": "HIP-graph replay, key copies rotated (cold)"}
 
 
+def bench_attention(torch, tks, W, name: str, steps: int, warmup: int):
+    """Attention over the selected positions (DSA step 3), cold: copies of
+    the keys and values rotated (>= 512 MiB).  Seconds per call."""
+    import math
+
+    wl = W.generate_attention(name)
+    rows, H, d = wl.q.shape
+    k = wl.idx.shape[1]
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    idx = torch.from_numpy(wl.idx).cuda()
+    kv0 = (torch.from_numpy(wl.kc).cuda().to(torch.bfloat16), torch.from_numpy(wl.vc).cuda().to(torch.bfloat16))
+    copies = int(max(2, min(256, (512 << 20) // (2 * kv0[0].numel() * 2) + 1)))
+    kvs = [kv0] + [(kv0[0].clone(), kv0[1].clone()) for _ in range(copies - 1)]
+    out = torch.empty((rows, H, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+    t, _ = time_graph(torch, [(lambda kc, vc: (lambda: tks.sparse_attention(q, kc, vc, idx, scale, out=out)))(kc, vc)
+                              for kc, vc in kvs], steps, warmup, stream)
+    if tks.device_status(stream):
+        raise RuntimeError("device-side error flags raised during the attention benchmark")
+    sel = int((wl.idx >= 0).sum())
+    # algorithmic bytes: the selected keys and values gathered once, the
+    # queries, the positions, the output
+    nbytes = sel * d * 2 * 2 + rows * H * d * 2 + rows * k * 4 + rows * H * d * 4
+    flops = 4 * sel * H * d
+    return {"workload": name, "rows": rows, "heads": H, "dim": d, "k": k, "us": round(t * 1e6, 3),
+            "algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / t / 1e9, 3),
+            "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 6), "mfma_TFLOPs": round(flops / t / 1e12, 3),
+            "timing": "HIP-graph replay, key/value copies rotated (cold)"}
+
+
 def kernel_source_sha256() -> str:
     import hashlib
 
@@ -227,6 +259,9 @@ def main() -> int:
                     help="workloads also timed with the ordered output (indices and values)")
     ap.add_argument("--indexer-workloads", default="idx_b1_n128k_h64_d128,idx_b64_n16k_h64_d128_ragged",
                     help="indexer producer workloads (logits on the matrix cores, then the selection)")
+    ap.add_argument("--attention-workloads",
+                    default="att_b1_n128k_h16_d128_k2048,att_b64_n16k_h16_d128_k2048_ragged",
+                    help="attention over the selected positions (the step after the selection)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-copies", type=int, default=0,
                     help="input copies rotated for the cold-cache timing (0: enough to exceed 512 MiB)")
@@ -281,6 +316,11 @@ def main() -> int:
     if not args.eager_only:
         for name in [x for x in args.indexer_workloads.split(",") if x]:
             indexer.append(bench_indexer(torch, tks, W, name, 200, 20))
+
+    attention = []
+    if not args.eager_only:
+        for name in [x for x in args.attention_workloads.split(",") if x]:
+            attention.append(bench_attention(torch, tks, W, name, 200, 20))
 
     if args.calibrate_copy_mib:
         calibrate_copy(torch, args.calibrate_copy_mib)
@@ -353,6 +393,7 @@ def main() -> int:
         "hbm_frac": round((o["bytes"] + 4 * o["rows"] * o["k"]) / o["t_cold"] / 1e9 / HBM_PEAK_GBPS, 6),
         "algorithmic_bytes_per_launch": o["bytes"] + 4 * o["rows"] * o["k"]} for o in ordered]
     res["indexer"] = indexer
+    res["attention"] = attention
     if not args.no_cpu:
         sec_per_row, reps = cpu_baseline(head["x"], head["k"])
         res["cpu_baseline"] = {

@@ -150,6 +150,41 @@ int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, i
                         int32_t* out_idx, float* out_logits, topk_select_stream_t stream);
 
 /*
+ * topk_sparse_attention - attention over the selected positions: the TopK
+ * article, section 01, step 3 of DSA-style decoding (attention computed only
+ * on the keys and values of the k selected positions).  The article gives
+ * no formula; computed (the reading taken) is plain scaled dot-product
+ * attention of each query head over the slots of idx[r] that hold a
+ * position, keys and values shared by the heads:
+ *
+ *   s_j = scale * q[r][h] . K[r][idx[r][j]],   p_j = exp(s_j) / sum_j' exp(s_j')
+ *   out[(r*heads + h)*dim + c] = sum_j p_j * V[r][idx[r][j]][c]
+ *
+ *   q        device, bf16 bit patterns, [rows, heads, dim], 16-byte aligned.
+ *   kc, vc   device, bf16: the keys / values of row r are the [n, dim]
+ *            arrays at kc + r*kvstride / vc + r*kvstride; 16-byte aligned.
+ *   idx      device, int32 [rows, k]: positions, e.g. topk_select's output;
+ *            -1 or any value outside [0, n) holds no position.
+ *   scale    finite score scale (commonly 1/sqrt(dim)).
+ *   out      device, float [rows, heads, dim]; a row whose slots hold no
+ *            position gets zeros.  Must not overlap the inputs.
+ *   rows >= 0, n >= 1, 1 <= heads <= 64, dim one of 32, 64, 128, k >= 1,
+ *   kvstride 0 (shared keys and values) or at least n*dim, a multiple of 8.
+ *
+ * Precision: bf16 products are exact in float and the scores are summed in
+ * float; the softmax weights are rounded to bf16 for the P.V product on the
+ * matrix cores.  Each output lies within
+ *   (2 (dim + 2) 2^-24 smax + 2^-8 + (k + 64) 2^-24 + 2^-20) * sum_j p_j |V[idx_j][c]|
+ * of the exact value, smax = max_j scale * sum_i |q_i K[idx_j]_i|.
+ * Two kernels are enqueued (per chunk of 64 slots, then the combination);
+ * scratch of rows * ceil(k/64) * heads * (dim + 2) * 4 bytes per (device,
+ * stream), grown with hipMalloc when needed.  Errors as for topk_select.
+ */
+int topk_sparse_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
+                          int32_t rows, int32_t n, int32_t heads, int32_t dim, int64_t kvstride, int32_t k,
+                          float scale, float* out, topk_select_stream_t stream);
+
+/*
  * Launch-shape description, filled by topk_select_plan and accepted by
  * topk_select_ex.  Performance only: every plan yields the same selected sets.
  *   variant       kernel variant id (0 .. topk_select_num_variants()-1)

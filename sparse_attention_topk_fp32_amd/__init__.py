@@ -32,6 +32,7 @@ __all__ = [
     "select_sorted",
     "indexer_logits",
     "indexer_select",
+    "sparse_attention",
     "topk_select_sorted",
     "topk_indexer_logits",
     "topk_indexer_select",
@@ -198,7 +199,9 @@ def select(logits, k: int, lengths=None, out=None, stream=None, variant: Optiona
     return out[0] if squeeze else out
 
 
-def _indexer_args(q, kc, w, lengths):
+def _qk_args(q, kc):
+    """Shapes of bfloat16 queries [rows, heads, dim] and keys [n, dim]
+    (shared by every row) or [rows, n, dim]: (rows, heads, dim, n, kstride)."""
     import torch
 
     for t, name in ((q, "q"), (kc, "kc")):
@@ -206,13 +209,9 @@ def _indexer_args(q, kc, w, lengths):
             raise TypeError("%s must be a bfloat16 GPU tensor" % name)
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-    if not isinstance(w, torch.Tensor) or w.dtype != torch.float32 or w.device != q.device or not w.is_contiguous():
-        raise TypeError("w must be a contiguous float32 tensor on q's device")
     if q.dim() != 3:
         raise ValueError("q must be [rows, heads, dim]")
     rows, heads, dim = q.shape
-    if w.shape != (rows, heads):
-        raise ValueError("w must be [rows, heads]")
     if kc.device != q.device:
         raise ValueError("kc must be on q's device")
     if kc.dim() == 2:
@@ -223,6 +222,17 @@ def _indexer_args(q, kc, w, lengths):
         raise ValueError("kc must be [n, dim] (shared by every row) or [rows, n, dim]")
     if kc.shape[-1] != dim:
         raise ValueError("kc's last dimension must be q's dim")
+    return rows, heads, dim, n, kstride
+
+
+def _indexer_args(q, kc, w, lengths):
+    import torch
+
+    rows, heads, dim, n, kstride = _qk_args(q, kc)
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.float32 or w.device != q.device or not w.is_contiguous():
+        raise TypeError("w must be a contiguous float32 tensor on q's device")
+    if w.shape != (rows, heads):
+        raise ValueError("w must be [rows, heads]")
     lp = None
     if lengths is not None:
         if lengths.dtype != torch.int32 or lengths.device != q.device or lengths.shape != (rows,) \
@@ -272,6 +282,47 @@ def indexer_select(q, kc, w, k: int, lengths=None, out=None, out_logits=None, re
                                  out.data_ptr(), out_logits.data_ptr() if want else None, _stream_handle(stream))
     _check(rc, "topk_indexer_select")
     return (out, out_logits) if want else out
+
+
+def topk_sparse_attention(q_ptr: int, kc_ptr: int, vc_ptr: int, idx_ptr: int, rows: int, n: int, heads: int,
+                          dim: int, kvstride: int, k: int, scale: float, out_ptr: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the attention over the selected positions."""
+    return _native.load().topk_sparse_attention(q_ptr or None, kc_ptr or None, vc_ptr or None, idx_ptr or None,
+                                                rows, n, heads, dim, kvstride, k, float(scale), out_ptr or None,
+                                                stream or None)
+
+
+def sparse_attention(q, kc, vc, idx, scale: Optional[float] = None, out=None, stream=None):
+    """Attention of the query heads over the selected positions only:
+    out[r, h] = sum_j softmax_j(scale q[r, h] . kc[idx[r, j]]) vc[idx[r, j]]
+    (slots holding -1 are skipped).  q [rows, heads, dim] bfloat16; kc, vc
+    bfloat16 [n, dim] (shared by every row) or [rows, n, dim]; idx int32
+    [rows, k] (e.g. from ``select``); scale defaults to 1/sqrt(dim).
+    Returns float32 [rows, heads, dim]."""
+    import math
+
+    import torch
+
+    rows, heads, dim, n, kvstride = _qk_args(q, kc)
+    if not isinstance(vc, torch.Tensor) or vc.dtype != torch.bfloat16 or vc.shape != kc.shape \
+            or vc.device != q.device or not vc.is_contiguous():
+        raise ValueError("vc must be a contiguous bfloat16 tensor shaped like kc on q's device")
+    if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != rows \
+            or idx.device != q.device or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 [rows, k] tensor on q's device")
+    k = idx.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if out is None:
+        out = torch.empty((rows, heads, dim), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (rows, heads, dim) or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 [rows, heads, dim] tensor on q's device")
+    with torch.cuda.device(q.device):
+        rc = topk_sparse_attention(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), idx.data_ptr(), rows, n, heads, dim,
+                                   kvstride, k, scale, out.data_ptr(), _stream_handle(stream))
+    _check(rc, "topk_sparse_attention")
+    return out
 
 
 def plan(rows: int, n: int, k: int) -> dict:

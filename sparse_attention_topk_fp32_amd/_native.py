@@ -29,6 +29,7 @@ EXPORTS = (
     "topk_select_sorted_ex",
     "topk_indexer_logits",
     "topk_indexer_select",
+    "topk_sparse_attention",
     "topk_select_plan",
     "topk_select_num_variants",
     "topk_select_variant_info",
@@ -85,6 +86,8 @@ def load() -> ctypes.CDLL:
         lib.topk_indexer_logits.restype = ctypes.c_int
         lib.topk_indexer_select.argtypes = [P, P, P, I, I, I, I, I64, P, I, P, P, P]
         lib.topk_indexer_select.restype = ctypes.c_int
+        lib.topk_sparse_attention.argtypes = [P, P, P, P, I, I, I, I, I64, I, ctypes.c_float, P, P]
+        lib.topk_sparse_attention.restype = ctypes.c_int
         lib.topk_select_plan.argtypes = [I, I, I, ctypes.POINTER(PlanT)]
         lib.topk_select_plan.restype = ctypes.c_int
         lib.topk_select_num_variants.argtypes = []

@@ -124,6 +124,25 @@ def test_indexer_argument_checks_answer_before_any_hip_call(lib):
     assert select(rows=0) == _native.SUCCESS
 
 
+def test_sparse_attention_argument_checks_answer_before_any_hip_call(lib):
+    from sparse_attention_topk_fp32_amd import _native
+
+    INV = _native.ERROR_INVALID_VALUE
+    q, kc, vc, ix, o = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+    def call(q_=q, kc_=kc, vc_=vc, idx=ix, rows=2, n=64, heads=16, dim=64, kvstride=0, k=8, scale=0.125, out=o):
+        return lib.topk_sparse_attention(q_, kc_, vc_, idx, rows, n, heads, dim, kvstride, k, scale, out, None)
+
+    assert call(rows=0) == _native.SUCCESS
+    assert call(heads=0) == INV and call(heads=65) == INV
+    assert call(dim=48) == INV and call(k=0) == INV
+    assert call(kvstride=12) == INV and call(kvstride=64 * 64 - 8) == INV
+    assert call(scale=float("nan")) == INV and call(scale=float("inf")) == INV
+    assert call(vc_=vc + 8) == INV and call(idx=ix + 2) == INV
+    assert call(out=None) == INV and call(idx=None) == INV
+    assert call(out=q) == INV  # output overlaps the queries
+
+
 def test_variant_table(lib):
     from sparse_attention_topk_fp32_amd import _native
 
