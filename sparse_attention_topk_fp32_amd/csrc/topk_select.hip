@@ -1143,20 +1143,47 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         lo = b > lo ? b : lo;
     };
     {
-        uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
         const uint32_t lane = lane_id();
         stream([&](const uint32_t* keys, int ct) {
             if (!keep) return;  // overflowed: the fallback re-reads the row
-            if (ct == 0) {  // the first tile: histogram of every element
-#pragma unroll
-                for (int i = 0; i < ITEMS; ++i)
-                    if (keys[i] != 0u) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
-            }
             // valid elements read once this tile is done
             const uint32_t seen = (uint32_t)min(L, 4 * min(nchunks, ct + TILE_CHUNKS) - off);
             if (ct == 0) {
-                lds_sync();  // the first tile's histogram is complete
-                raise_bound(seen);
+                // the first bound, from the first tile: the 12-bit bin of the
+                // element of rank bound_rank(seen), in two steps — its top 8
+                // bits (256-bin histogram, 16 copies), then its next 4 bits
+                // among the elements of that 8-bit bin (16 bins).  The union
+                // is all zero here.
+                uint32_t* const h8c = sm.h.h8 + (tid % kCopies) * 257;
+#pragma unroll
+                for (int i = 0; i < ITEMS; ++i)
+                    if (keys[i] != 0u) atomicAdd(&h8c[keys[i] >> 24], 1u);
+                lds_sync();
+                uint32_t b8, ab8, hb8;
+                const uint32_t rk = bound_rank(seen);
+                local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rk, sm.scan, sm.sel, P.status, b8, ab8,
+                                                              hb8);
+                if (hb8 > 0u) {
+                    uint32_t* const h4 = sm.h.h12 + kCopies * 257 + (tid % kCopies) * 17;  // past the 8-bit copies
+#pragma unroll
+                    for (int i = 0; i < ITEMS; ++i)
+                        if ((keys[i] != 0u) & ((keys[i] >> 24) == b8)) atomicAdd(&h4[(keys[i] >> 20) & 15u], 1u);
+                    lds_sync();
+                    if (tid < 64) {
+                        // lane l: sub-bin 15 - l (descending), summed over the copies
+                        uint32_t c = 0;
+                        if (tid < 16) {
+#pragma unroll
+                            for (int q = 0; q < kCopies; ++q) c += sm.h.h12[kCopies * 257 + q * 17 + 15 - tid];
+                        }
+                        const uint32_t inc = wave_inclusive_scan(c);
+                        const uint32_t need4 = rk - ab8;  // 1-based rank inside the 8-bit bin
+                        if (tid < 16 && inc - c < need4 && need4 <= inc) sm.sel[3] = 15u - (uint32_t)tid;
+                    }
+                    lds_sync();
+                    const uint32_t b12 = (b8 << 4) | uniform(sm.sel[3]);
+                    lo = b12 > lo ? b12 : lo;
+                }
             }
             // append: lanes count their candidates, a wave prefix ranks
             // them, one LDS atomic per wave reserves the wave's range
