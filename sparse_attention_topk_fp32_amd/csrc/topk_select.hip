@@ -1134,13 +1134,25 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) atomicAdd(&hcb[(uint32_t)(sm.cand[i] >> (64 - F))], 1u);
         lds_sync();
     };
-    // raise the bound from the histogram of the first `seen` elements (only
-    // its bins at or above the bound need to be exact)
-    auto raise_bound = [&](uint32_t seen) {
-        uint32_t b, ab, hbx;
-        local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, bound_rank(seen), sm.scan, sm.sel, P.status, b, ab,
-                                                 hbx);
-        lo = b > lo ? b : lo;
+    // the element of rank `rank` among the buffered entries (all at or above
+    // lo), over a 256-bin window of first-digit bins lo .. lo+254, the last
+    // bin taking everything above: its window bin, the count above it and
+    // the count in it (0 when there are fewer entries)
+    auto window_select = [&](uint32_t rank, uint32_t& bw, uint32_t& ab, uint32_t& hbw) {
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
+            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        }
+        lds_sync();
+        {
+            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
+            for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
+                const uint32_t bin = (uint32_t)(sm.cand[i] >> (64 - F));
+                atomicAdd(&hcw[min(bin - lo, 255u)], 1u);
+            }
+        }
+        lds_sync();
+        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rank, sm.scan, sm.sel, P.status, bw, ab, hbw);
     };
     {
         const uint32_t lane = lane_id();
@@ -1218,9 +1230,14 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 return;
             }
             if (used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks) {
-                // tighter bound from more data, and drop what fell below it
-                hist_from_buffer();
-                raise_bound(seen);
+                // tighter bound from more data, and drop what fell below it:
+                // the bin of the entry of rank bound_rank(seen), or the top of
+                // the window when it lies above (still a lower bound)
+                {
+                    uint32_t bw, ab, hbw;
+                    window_select(bound_rank(seen), bw, ab, hbw);
+                    if (hbw > 0u) lo = min(lo + bw, (uint32_t)NB0 - 1u);
+                }
                 const uint32_t lob = lo;
                 uint32_t n1, n2;
                 walk([&](uint64_t e) { return (uint32_t)(e >> (64 - F)) >= lob ? 2u : 0u; },
@@ -1238,25 +1255,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     bool whole = false;
     uint32_t b0 = 0, above = 0;
     if (keep) {
-        // the threshold bin, from the buffer: first over a 256-bin window of
-        // first-digit bins lo .. lo+254 (the last bin takes everything above;
-        // every buffered entry is at or above lo), which normally holds it;
-        // else over all 4096 bins
-        {
-            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
-            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        }
-        lds_sync();
-        {
-            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
-            for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
-                const uint32_t bin = (uint32_t)(sm.cand[i] >> (64 - F));
-                atomicAdd(&hcw[min(bin - lo, 255u)], 1u);
-            }
-        }
-        lds_sync();
+        // the threshold bin, from the buffer: first over the 256-bin window
+        // above lo, which normally holds it; else over all 4096 bins
         uint32_t bw;
-        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, bw, above, hb);
+        window_select(need, bw, above, hb);
         if (hb > 0u && bw < 255u) {
             b0 = lo + bw;
         } else {
