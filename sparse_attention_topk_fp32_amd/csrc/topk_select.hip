@@ -825,8 +825,11 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     // order from a block scan, into a compact LDS list (the histogram
     // space, in chunks); place the list's entries with all lanes busy.
     const uint32_t kp = pf.kpfx, km = pf.kmask;
+    // the key prefix has no bits outside its mask, so (key & km) >= kp
+    // is key >= kp; the lower bound 1 also drops empty slots (key 0)
+    const uint32_t kp1 = kp > 1u ? kp : 1u;
     auto selected = [&](uint32_t key, uint32_t ni) -> bool {
-        if (!idx_rounds) return ((key & km) >= kp) & (key != 0u);
+        if (!idx_rounds) return key >= kp1;
         uint32_t slot;
         return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
     };
