@@ -130,3 +130,43 @@ def test_decode_pipeline_indexer_selection_attention(torch_gpu):
     idx_h = idx.cpu().numpy()
     assert np.array_equal(np.sort(idx_h, 1), np.sort(oracle.topk(logits.cpu().numpy(), k, ix.lengths), 1))
     assert_attention_close(at.q, at.kc, at.vc, idx_h, 1.0 / math.sqrt(128), out.cpu().numpy())
+
+
+def test_graph_replay_of_indexer_and_attention(torch_gpu):
+    """Both steps captured in one HIP graph and replayed, with eager work and
+    synchronisations between replays: every replay gives the eager result."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    torch = torch_gpu
+    rows, n, k = 3, 9000, 256
+    ix = W.draw(rows, n, heads=16, dim=64, k=k, seed=12, lengths="uniform")
+    at = W.draw_attention(rows, n, heads=16, dim=64, k=k, seed=13)
+    _say("graph replay x3: indexer selection then attention")
+    q, kc, w = _bf16(torch, ix.q), _bf16(torch, ix.kc), torch.from_numpy(ix.w).cuda()
+    L = torch.from_numpy(ix.lengths).cuda()
+    aq, ak, av = _bf16(torch, at.q), _bf16(torch, at.kc), _bf16(torch, at.vc)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    out = torch.zeros((rows, 16, 64), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        e_idx = tks.indexer_select(q, kc, w, k, lengths=L).clone()
+        tks.sparse_attention(aq, ak, av, e_idx)  # allocates the scratch outside the capture
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            tks.indexer_select(q, kc, w, k, lengths=L, out=idx)
+            tks.sparse_attention(aq, ak, av, idx, out=out)
+    want_sets = torch.sort(e_idx, dim=1).values
+    for rep in range(3):
+        idx.fill_(-7)
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.sort(idx, dim=1).values, want_sets), rep
+        # the slot order may differ from the eager call (so may the rounding
+        # of the chunked softmax): check each replay against the oracle
+        assert_attention_close(at.q, at.kc, at.vc, idx.cpu().numpy(), 1.0 / math.sqrt(64), out.cpu().numpy())
+        _ = tks.indexer_select(q, kc, w, k, lengths=L)
+        torch.cuda.synchronize()
+    assert tks.device_status(s) == 0
