@@ -78,9 +78,7 @@ struct alignas(256) RowWorkspace {
     uint64_t hist[2][kRounds][kMergeCopies][256];  // (arrivals << 32) | count
     uint64_t stage[2][kCap];                       // final-bucket composites; 0 = not written yet
     uint32_t parity;                               // half used by the next launch
-    uint32_t used_rounds[2];                       // what each half holds (cleared by the next launch)
-    uint32_t used_copies[2];
-    uint32_t used_stage[2];
+    uint32_t used[2];  // what each half holds, cleared by the next launch: rounds | copies << 4 | stage entries << 8
     uint32_t pad[57];
 };
 
@@ -509,6 +507,9 @@ __device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, int mslot, boo
                     raise_flag(status, kFlagTimeout);
                     break;
                 }
+                // many WGs: back off between polls, which otherwise crowd
+                // the channel that holds the counts (measured)
+                if (G > 64) __builtin_amdgcn_s_sleep(2);
             }
             tot = (uint32_t)v0 + (uint32_t)v1 + (uint32_t)v2 + (uint32_t)v3;
             pre = (uint32_t)old + (mc > 0 ? (uint32_t)v0 : 0u) + (mc > 1 ? (uint32_t)v1 : 0u) +
@@ -584,6 +585,10 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     const bool multi = Geff > 1;
     RowWorkspace* const ws = multi ? P.ws + row : nullptr;
     const int p = multi ? (int)(ld_dev(&ws->parity) & 1u) : 0;
+    // what the previous launch left to clear (read by the finishing WG now,
+    // off the critical path at the end)
+    const uint32_t used0 = (multi && w == 0) ? ld_dev(&ws->used[0]) : 0u;
+    const uint32_t used1 = (multi && w == 0) ? ld_dev(&ws->used[1]) : 0u;
     const int C = P.mcopies;
     const int idx_bits = P.idx_bits;
     const int nrounds = num_rounds(idx_bits);
@@ -942,17 +947,17 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         // clear the half the previous launch used, record this launch's use
         // and hand the other half to the next launch
         const int op = p ^ 1;
-        const uint32_t ur = min(ld_dev(&ws->used_rounds[op]), (uint32_t)kRounds);
-        const uint32_t uc = min(ld_dev(&ws->used_copies[op]), (uint32_t)kMergeCopies);
-        const uint32_t us = min(ld_dev(&ws->used_stage[op]), (uint32_t)kCap);
+        const uint32_t prev = op ? used1 : used0;
+        const uint32_t ur = min(prev & 15u, (uint32_t)kRounds);
+        const uint32_t uc = min((prev >> 4) & 15u, (uint32_t)kMergeCopies);
+        const uint32_t us = min(prev >> 8, (uint32_t)kCap);
         uint64_t* const h = &ws->hist[op][0][0][0];
         for (uint32_t i = tid; i < ur * kMergeCopies * 256u; i += BLOCK)
             if ((i / 256u) % kMergeCopies < uc) st_dev(&h[i], (uint64_t)0);
         for (uint32_t i = tid; i < us; i += BLOCK) st_dev(&ws->stage[op][i], (uint64_t)0);
         if (tid == 0) {
-            st_dev(&ws->used_rounds[p], (uint32_t)(last_slot + 1));
-            st_dev(&ws->used_copies[p], (uint32_t)C);
-            st_dev(&ws->used_stage[p], whole ? 0u : (hb > (uint32_t)kCap ? (uint32_t)kCap : hb));
+            const uint32_t stage = whole ? 0u : (hb > (uint32_t)kCap ? (uint32_t)kCap : hb);
+            st_dev(&ws->used[p], (uint32_t)(last_slot + 1) | ((uint32_t)C << 4) | (stage << 8));
             st_dev(&ws->parity, (uint32_t)op);
         }
     }
