@@ -1803,6 +1803,17 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
     const int m = lane & 15, g = lane >> 4;
     const int n = P.n, H = P.H;
     const int L = valid_length(P.lengths, row, n);
+    // this wave's tokens: gpw consecutive groups of 64
+    const int t0 = (tile * (kLogitBlock / 64) + wave) * P.gpw * 64;
+    const int t1 = min(t0 + P.gpw * 64, n);
+    const int tv = min(t1, L);  // valid tokens end here
+    const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kstride);
+    // a wave that streams several groups has its first group's keys in
+    // flight while the queries are staged (measured: for one group per
+    // wave the keys are better issued after the queries)
+    u32x4_t r[NL];
+    const bool early = P.gpw > 1 && t0 < tv;
+    if (early) logits_load<D, NL>(r, K, t0, L - 1 - t0, lane);
     {
         const u32x4_t* const qrow = reinterpret_cast<const u32x4_t*>(P.q + (size_t)row * H * D);
         for (int i = threadIdx.x; i < H * CPR; i += kLogitBlock) {
@@ -1811,13 +1822,9 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
         }
     }
     __syncthreads();  // before any wave leaves
-    // this wave's tokens: gpw consecutive groups of 64
-    const int t0 = (tile * (kLogitBlock / 64) + wave) * P.gpw * 64;
     if (t0 >= n) return;
-    const int t1 = min(t0 + P.gpw * 64, n);
     float* const lrow = P.logits + (size_t)row * (size_t)n;
     const float ninf = -__builtin_huge_valf();
-    const int tv = min(t1, L);  // valid tokens end here
     for (int t = max(t0, tv) + lane; t < t1; t += 64) lrow[t] = ninf;
     if (t0 >= tv) return;
     const int ng = (tv - t0 + 63) / 64;  // groups holding valid tokens
@@ -1843,7 +1850,6 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
             wt[hb][i] = hh < H ? x : 0.0f;
         }
     }
-    const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kstride);
     u32x4_t* const st = stage[wave];
     auto compute_store = [&](int tw) __attribute__((always_inline)) {
         float v[4];
@@ -1878,8 +1884,7 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
     };
     // the next group's loads are in flight while the current one is
     // computed from LDS; the wave's region is its own, so no barrier
-    u32x4_t r[NL];
-    logits_load<D, NL>(r, K, t0, L - 1 - t0, lane);
+    if (!early) logits_load<D, NL>(r, K, t0, L - 1 - t0, lane);
     for (int gi = 0; gi < ng; ++gi) {
         const int tw = t0 + gi * 64;
         logits_stage<D, NL>(st, r, lane);
@@ -2586,13 +2591,13 @@ int launch_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t
     // groups of 64 tokens per wave: one when the grid is small (every
     // group its own wave), more for long or many rows, so that each wave
     // streams several groups with the next one's keys in flight (about two
-    // WGs per CU resident, the grid a few times that)
+    // WGs per CU resident, the grid about that many: fewer WG starts)
     int cus = 256;
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t groups = (int64_t)rows * ((n + 63) / 64);
     const int64_t resident_waves = (int64_t)cus * 2 * (kLogitBlock / 64);
-    int64_t gpw = (groups + 4 * resident_waves - 1) / (4 * resident_waves);
+    int64_t gpw = (groups + resident_waves - 1) / resident_waves;
     p.gpw = (int32_t)(gpw < 1 ? 1 : (gpw > 8 ? 8 : gpw));
     const int64_t tok_wg = (int64_t)p.gpw * kLogitBlock;
     p.tiles = (int32_t)((n + tok_wg - 1) / tok_wg);
