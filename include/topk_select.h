@@ -22,8 +22,9 @@
  *  - -0.0 and +0.0 are equal (they tie); infinities and subnormals are
  *    ordinary values; NaN logits are outside the contract (no error is
  *    raised, the result for such a row is unspecified but memory-safe);
- *  - the output order within a row is unspecified (the selected set is
- *    exact and unique).
+ *  - the output order within a row is unspecified and may differ between
+ *    calls (elements are placed through atomic counters); the selected set
+ *    is exact and unique.  topk_select_sorted gives a fully determined order.
  *
  * All pointers named "device" point to memory on the calling thread's current
  * HIP device.  The library never takes ownership of caller memory.
