@@ -833,11 +833,6 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     // the key prefix has no bits outside its mask, so (key & km) >= kp
     // is key >= kp; the lower bound 1 also drops empty slots (key 0)
     const uint32_t kp1 = kp > 1u ? kp : 1u;
-    auto selected = [&](uint32_t key, uint32_t ni) -> bool {
-        if (!idx_rounds) return key >= kp1;
-        uint32_t slot;
-        return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
-    };
     // place one selected element (a winner or a bucket element)
     auto place = [&](uint32_t key, uint32_t ni) {
         uint32_t slot = bslot;
@@ -865,6 +860,9 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             overflow = true;
         }
     };
+    // with few elements per thread the selection test is chosen once,
+    // outside the per-element pass
+    auto collect = [&](auto&& selected) {
     if constexpr (ITEMS <= 8) {
         // few elements per thread: place them directly
         visit([&](uint32_t key, uint32_t ni) {
@@ -894,6 +892,24 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         }
         lds_sync();
     }
+    }
+    };
+    if constexpr (ITEMS <= 8) {
+        if (!idx_rounds) {
+            collect([&](uint32_t key, uint32_t) -> bool { return key >= kp1; });
+        } else {
+            collect([&](uint32_t key, uint32_t ni) -> bool {
+                uint32_t slot;
+                return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
+            });
+        }
+    } else {
+        // one instance of the three steps (measured faster here)
+        collect([&](uint32_t key, uint32_t ni) -> bool {
+            if (!idx_rounds) return key >= kp1;
+            uint32_t slot;
+            return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
+        });
     }
     if (overflow) raise_flag(P.status, kFlagCapacity);
 
