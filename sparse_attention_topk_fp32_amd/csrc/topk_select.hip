@@ -64,6 +64,7 @@ constexpr int kCap = 4096;        // final bucket size handed to one WG (entries
 constexpr int kSmall = 256;       // bucket ranked exactly by comparisons
 constexpr int kRounds = 9;        // merge rounds: a window round, then up to 4 key + 4 index digits
 constexpr int kCopies = 16;       // LDS copies of the 256-bin histogram (against atomic conflicts)
+constexpr int kWinLength = 524288;  // rows at least this long take the sampled window round
 constexpr int kMergeCopies = 4;   // global copies of a row's histogram per round (WG w -> copy w mod C)
 constexpr uint32_t kFlagTimeout = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
@@ -548,9 +549,11 @@ __device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, int mslot, boo
 // ----------------------------------------------------------------- the kernel
 //
 // BLOCK threads per WG; ITEMS logits per thread per tile; RESIDENT: the
-// slice is one tile kept in VGPRs across passes (else re-read every pass).
+// slice is one tile kept in VGPRs across passes (else re-read every pass);
+// KEYS: the keys of the output are recorded (ordered output); WIN: rows of
+// kWinLength or more take the sampled window round.
 
-template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS>
+template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS, bool WIN>
 __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "one bin per thread in the 256-bin rounds");
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     // loaded together with the slice.  Only long rows (split over many WGs,
     // where a second merge round is expensive) take the window round: for
     // shorter rows its extra steps cost more than they save (measured).
-    const bool try_win = L >= 524288;
+    const bool try_win = WIN && L >= kWinLength;
     const int nsc = min(nchunks, BLOCK);
     uint4 sraw = uint4{0u, 0u, 0u, 0u};
     if (try_win && tid < nsc) sraw = *reinterpret_cast<const uint4*>(base + (uint32_t)tid * 16u);
@@ -2179,20 +2182,35 @@ __global__ void __launch_bounds__(D) topk_attn_combine_kernel(AttnParams P) {
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
 using OccFn = int (*)(int*, int);
 
+// The window round's code is compiled only into the instances that can
+// meet a row that long (measured: the unused code alone costs C2 0.45 µs).
 template <int B, int I, bool R>
 void launch_variant(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    if (p.keys) hipLaunchKernelGGL((topk_select_kernel<B, I, R, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((topk_select_kernel<B, I, R, false>), grid, block, 0, s, p);
+    const bool win = p.n >= kWinLength;
+    if (p.keys) {
+        if (win) hipLaunchKernelGGL((topk_select_kernel<B, I, R, true, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((topk_select_kernel<B, I, R, true, false>), grid, block, 0, s, p);
+    } else {
+        if (win) hipLaunchKernelGGL((topk_select_kernel<B, I, R, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((topk_select_kernel<B, I, R, false, false>), grid, block, 0, s, p);
+    }
 }
 
-// co-resident WGs per CU: the smaller figure of the two instantiations
+// co-resident WGs per CU: the smallest figure of the instantiations
 template <int B, int I, bool R>
 int occupancy_variant(int* nb, int block) {
-    int a = 0, b = 0;
-    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_select_kernel<B, I, R, false>, block, 0);
-    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_select_kernel<B, I, R, true>, block, 0);
-    *nb = a < b ? a : b;
-    return r1 != 0 ? r1 : r2;
+    int c[4] = {0, 0, 0, 0};
+    int r[4];
+    r[0] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[0], topk_select_kernel<B, I, R, false, false>, block, 0);
+    r[1] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[1], topk_select_kernel<B, I, R, true, false>, block, 0);
+    r[2] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[2], topk_select_kernel<B, I, R, false, true>, block, 0);
+    r[3] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[3], topk_select_kernel<B, I, R, true, true>, block, 0);
+    int m = c[0];
+    for (int i = 1; i < 4; ++i) m = c[i] < m ? c[i] : m;
+    *nb = m;
+    for (int i = 0; i < 4; ++i)
+        if (r[i] != 0) return r[i];
+    return 0;
 }
 
 template <int B, int I, int D>

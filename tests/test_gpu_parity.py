@@ -253,6 +253,24 @@ def test_every_variant_and_split(torch_gpu, case):
     assert ran >= 8
 
 
+@pytest.mark.parametrize("shape", [None, (7, 32), (8, 64)])
+def test_window_round_length_boundary(torch_gpu, shape):
+    """Rows around the length from which the sampled 12-bit window round is
+    taken (524,288), in a call long enough to compile it in: rows at, above
+    and one below the boundary, with ties (bf16-rounded values)."""
+    rng = np.random.default_rng(524288)
+    n = 600000
+    x = W.bf16_round(rng.standard_normal((3, n)).astype(np.float32))
+    lengths = np.array([n, 524288, 524287], np.int32)
+    variant, wgs = shape if shape is not None else (None, None)
+    _say("window boundary rows=3 n=%d lengths=%s shape=%s" % (n, lengths.tolist(), shape))
+    got = run_gpu(torch_gpu, x, 2048, lengths, variant=variant, wgs=wgs)
+    assert_parity(x, 2048, lengths, got)
+    _say("window boundary 1 x 524288, no lengths")
+    got = run_gpu(torch_gpu, x[:1, :524288], 2048, None, variant=variant, wgs=wgs)
+    assert_parity(x[:1, :524288], 2048, None, got)
+
+
 # ----------------------------------------------------------------- calling conventions
 
 def test_repeat_calls_are_deterministic(torch_gpu):
