@@ -54,6 +54,7 @@
 #include <initializer_list>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "topk_select.h"
@@ -682,6 +683,22 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             }
         }
     };
+    // f(key, ~index) for every slot of the slice, re-read from global
+    // memory in a rolled loop: the rare index-digit rounds use it, so that
+    // their code stays small (at these sizes the code a launch runs costs
+    // instruction fetches)
+    auto visit_global = [&](auto&& f) {
+#pragma unroll 1
+        for (int c = c_begin + tid; c < c_end; c += BLOCK) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (uint32_t)c * 16u);
+            const int e0 = 4 * c - off;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = (uint32_t)(e0 + e) < (uint32_t)L;
+                f(ok ? key_of(__uint_as_float(v[e])) : 0u, ~(uint32_t)(e0 + e));
+            }
+        }
+    };
     auto opaque_keys = [&]() {
         if constexpr (RESIDENT) {
             // stops the optimiser from hoisting per-element values out of
@@ -795,7 +812,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
                 });
             } else {
                 const int sh = digit_shift(F, r, idx_bits);
-                visit([&](uint32_t key, uint32_t ni) {
+                visit_global([&](uint32_t key, uint32_t ni) {
                     if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
                 });
             }
@@ -836,11 +853,12 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     // the key prefix has no bits outside its mask, so (key & km) >= kp
     // is key >= kp; the lower bound 1 also drops empty slots (key 0)
     const uint32_t kp1 = kp > 1u ? kp : 1u;
-    // place one selected element (a winner or a bucket element)
-    auto place = [&](uint32_t key, uint32_t ni) {
+    // place one selected element (a winner or a bucket element); IDX: the
+    // rounds went into the index digits
+    auto place = [&](uint32_t key, uint32_t ni, auto idx) {
         uint32_t slot = bslot;
         bool ab;
-        if (!idx_rounds) {
+        if constexpr (!decltype(idx)::value) {
             const uint32_t s = key & km;
             ab = s > kp;
             if (ab) slot = key_slot(key, s ^ kp, fd, idx_bits);
@@ -863,13 +881,12 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
             overflow = true;
         }
     };
-    // with few elements per thread the selection test is chosen once,
-    // outside the per-element pass
+    // the key-digit case (index-digit rounds are collected below)
     auto collect = [&](auto&& selected) {
     if constexpr (ITEMS <= 8) {
         // few elements per thread: place them directly
         visit([&](uint32_t key, uint32_t ni) {
-            if (selected(key, ni)) place(key, ni);
+            if (selected(key, ni)) place(key, ni, std::false_type{});
         });
     } else {
     uint32_t nsel = 0;
@@ -891,27 +908,19 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
         const uint32_t nl = min(LISTN, tot_sel - c0);
         for (uint32_t i = tid; i < nl; i += BLOCK) {
             const uint64_t e = list[i];
-            place((uint32_t)(e >> 32), (uint32_t)e);
+            place((uint32_t)(e >> 32), (uint32_t)e, std::false_type{});
         }
         lds_sync();
     }
     }
     };
-    if constexpr (ITEMS <= 8) {
-        if (!idx_rounds) {
-            collect([&](uint32_t key, uint32_t) -> bool { return key >= kp1; });
-        } else {
-            collect([&](uint32_t key, uint32_t ni) -> bool {
-                uint32_t slot;
-                return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
-            });
-        }
+    if (!idx_rounds) {
+        collect([&](uint32_t key, uint32_t) -> bool { return key >= kp1; });
     } else {
-        // one instance of the three steps (measured faster here)
-        collect([&](uint32_t key, uint32_t ni) -> bool {
-            if (!idx_rounds) return key >= kp1;
+        // ties beyond the key digits (rare): the slice is re-read
+        visit_global([&](uint32_t key, uint32_t ni) {
             uint32_t slot;
-            return classify(key, ni, pf, fd, idx_bits, &slot) != 0u;
+            if (classify(key, ni, pf, fd, idx_bits, &slot) != 0u) place(key, ni, std::true_type{});
         });
     }
     if (overflow) raise_flag(P.status, kFlagCapacity);
