@@ -1002,6 +1002,7 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 // Positions come from two wave-aggregated LDS counters (winners, bucket).
 
 constexpr int kRowsCap = 4608;  // candidate buffer of the one-WG-per-row kernel (entries)
+constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered entries is refined
 
 template <int BLOCK>
 struct RowsSmem {
@@ -1100,17 +1101,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
     };
 
-    // ---------------- first pass: every element at or above a lower bound
-    // `lo` (a first-digit bin) kept in LDS.  The bound is an estimate: the
-    // bin of the element of rank 1.25 * k * seen / L + 64 among the `seen`
-    // elements read so far, where the k-th largest of the row is expected
-    // near rank k * seen / L.  It is taken from a 12-bit histogram of the
-    // first tile and raised (with the buffer compacted) whenever the buffer
-    // fills up, from a histogram of the buffer.  The buffer then holds every
-    // element at or above `lo`, so the histogram of the buffer is exact for
-    // the bins at or above `lo`; when the row's threshold bin b0 is found
-    // there (checked below), everything selected is in it.  Otherwise, or
-    // when the buffer overflowed, the row is finished with re-reads.
+    // ---------------- first pass: every element whose key is at or above a
+    // lower bound `lo_key` kept in LDS.  The bound is an estimate: the
+    // first-digit bin (12 bits) of the element of rank 1.25 * k * seen / L +
+    // 64 among the `seen` elements read so far, where the k-th largest of the
+    // row is expected near rank k * seen / L (in a dense bin, also that
+    // element's next 8 key bits).  It is taken from the first tile and
+    // raised (with the buffer compacted) whenever the buffer fills up, from
+    // histograms of the buffer.  The buffer then holds every element whose
+    // key is at or above the bound; when it holds at least k entries, the
+    // k-th largest of the buffer is the row's and everything selected is in
+    // it.  Otherwise, or when the buffer overflowed twice on one tile, the
+    // row is finished with re-reads.
     {
         uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
         for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
@@ -1120,7 +1122,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     lds_sync();
     bool keep = true;   // candidates are being buffered
     uint32_t used = 0;  // buffered entries
-    uint32_t lo = 0;    // running lower bound (first-digit bin)
+    // running lower bound on the keys kept: a first-digit bin, refined by
+    // the next 8 key bits where that bin is dense (at least 1: empty slots
+    // are never kept)
+    uint32_t lo_key = 1u;
     // Walk the buffer in slices of RC * BLOCK entries: every thread reads its
     // RC entries, a block scan numbers the chosen ones, and f(entry, kind,
     // rank) places them.  Kinds: pred returns 0 (drop), 1 or 2, counted
@@ -1170,11 +1175,13 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) atomicAdd(&hcb[(uint32_t)(sm.cand[i] >> (64 - F))], 1u);
         lds_sync();
     };
-    // the element of rank `rank` among the buffered entries (all at or above
-    // lo), over a 256-bin window of first-digit bins lo .. lo+254, the last
-    // bin taking everything above: its window bin, the count above it and
-    // the count in it (0 when there are fewer entries)
+    // the element of rank `rank` among the buffered entries (all in
+    // first-digit bins at or above lo, the bound's bin), over a 256-bin
+    // window of bins lo .. lo+254, the last bin taking everything above: its
+    // window bin, the count above it and the count in it (0 when there are
+    // fewer entries)
     auto window_select = [&](uint32_t rank, uint32_t& bw, uint32_t& ab, uint32_t& hbw) {
+        const uint32_t lo = lo_key >> (32 - F);
         {
             uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
             for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
@@ -1189,6 +1196,25 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
         lds_sync();
         local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rank, sm.scan, sm.sel, P.status, bw, ab, hbw);
+    };
+    // the element of rank `rank` among the buffered entries of first-digit
+    // bin b: its next 8 key bits (sub-bin s8), the count above it in the bin
+    // and the count in it (0 when there are fewer entries)
+    auto sub_select = [&](uint32_t b, uint32_t rank, uint32_t& s8, uint32_t& a8, uint32_t& h8v) {
+        {
+            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
+            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+        }
+        lds_sync();
+        {
+            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
+            for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
+                const uint32_t key = (uint32_t)(sm.cand[i] >> 32);
+                if ((key >> (32 - F)) == b) atomicAdd(&hcw[(key >> (32 - F - 8)) & 0xFFu], 1u);
+            }
+        }
+        lds_sync();
+        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rank, sm.scan, sm.sel, P.status, s8, a8, h8v);
     };
     {
         const uint32_t lane = lane_id();
@@ -1230,57 +1256,82 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                     }
                     lds_sync();
                     const uint32_t b12 = (b8 << 4) | uniform(sm.sel[3]);
-                    lo = b12 > lo ? b12 : lo;
+                    lo_key = max(lo_key, b12 << (32 - F));
                 }
             }
             // append: lanes count their candidates, a wave prefix ranks
-            // them, one LDS atomic per wave reserves the wave's range
-            uint32_t c = 0;
+            // them, one LDS atomic per wave reserves the wave's range.  A
+            // tile that overflows the buffer (its entries past the end are
+            // lost) raises the bound from what is buffered, drops its own
+            // entries and is appended once more from the registers; a
+            // second overflow gives up (the re-reading path below).
+            for (int pass = 0;; ++pass) {
+                uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < ITEMS; ++i) c += (keys[i] != 0u) & ((keys[i] >> (32 - F)) >= lo);
-            const uint32_t ic = wave_inclusive_scan(c);
-            const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
-            if (tw) {
-                uint32_t wb = 0;
-                if (lane == 0) wb = atomicAdd(&sm.ctr[4], tw);
-                uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + ic - c;
-                const int ibase = 4 * (ct + tid) - off;
+                for (int i = 0; i < ITEMS; ++i) c += keys[i] >= lo_key;
+                const uint32_t ic = wave_inclusive_scan(c);
+                const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
+                if (tw) {
+                    uint32_t wb = 0;
+                    if (lane == 0) wb = atomicAdd(&sm.ctr[4], tw);
+                    uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + ic - c;
+                    const int ibase = 4 * (ct + tid) - off;
 #pragma unroll
-                for (int j = 0; j < CHUNKS; ++j) {
+                    for (int j = 0; j < CHUNKS; ++j) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t key = keys[4 * j + e];
-                        if ((key != 0u) & ((key >> (32 - F)) >= lo)) {
-                            if (pos < (uint32_t)kRowsCap)
-                                sm.cand[pos] = ((uint64_t)key << 32) |
-                                               (uint64_t)~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                            ++pos;
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t key = keys[4 * j + e];
+                            if (key >= lo_key) {
+                                if (pos < (uint32_t)kRowsCap)
+                                    sm.cand[pos] = ((uint64_t)key << 32) |
+                                                   (uint64_t)~(uint32_t)(ibase + 4 * BLOCK * j + e);
+                                ++pos;
+                            }
                         }
                     }
                 }
-            }
-            lds_sync();
-            used = uniform(sm.ctr[4]);
-            if (used > (uint32_t)kRowsCap) {  // entries were lost
-                keep = false;
-                return;
-            }
-            if (used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks) {
-                // tighter bound from more data, and drop what fell below it:
-                // the bin of the entry of rank bound_rank(seen), or the top of
-                // the window when it lies above (still a lower bound)
-                {
-                    uint32_t bw, ab, hbw;
-                    window_select(bound_rank(seen), bw, ab, hbw);
-                    if (hbw > 0u) lo = min(lo + bw, (uint32_t)NB0 - 1u);
+                lds_sync();
+                used = uniform(sm.ctr[4]);
+                const bool over = used > (uint32_t)kRowsCap;  // entries of this tile were lost
+                if (over && pass > 0) {
+                    keep = false;
+                    return;
                 }
-                const uint32_t lob = lo;
+                if (!over && !(used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks)) break;
+                if (over) used = (uint32_t)kRowsCap;
+                // tighter bound from more data, and drop what fell below it
+                // (and, after an overflow, this tile's entries): the bin of
+                // the entry of rank bound_rank(seen), or the top of the
+                // window when it lies above (still a lower bound)
+                {
+                    const uint32_t rk = bound_rank(seen);
+                    uint32_t bw, ab, hbw;
+                    window_select(rk, bw, ab, hbw);
+                    if (hbw > 0u) {
+                        const uint32_t b12 = min((lo_key >> (32 - F)) + bw, (uint32_t)NB0 - 1u);
+                        uint32_t nk = b12 << (32 - F);
+                        if (bw < 255u && hbw > kRowsDenseBin) {
+                            // a dense bin: the entry's next 8 key bits too
+                            uint32_t s8, a8, h8v;
+                            sub_select(b12, rk - ab, s8, a8, h8v);
+                            if (h8v > 0u) nk |= s8 << (32 - F - 8);
+                        }
+                        lo_key = max(lo_key, nk);
+                    }
+                }
+                const uint32_t lob = lo_key;
+                // this tile's index range (empty when nothing was lost)
+                const int xlo = over ? 4 * ct - off : 0, xhi = over ? 4 * (ct + TILE_CHUNKS) - off : 0;
                 uint32_t n1, n2;
-                walk([&](uint64_t e) { return (uint32_t)(e >> (64 - F)) >= lob ? 2u : 0u; },
+                walk([&](uint64_t e) {
+                         const int idx = (int)~(uint32_t)e;
+                         return ((uint32_t)(e >> 32) >= lob) & ((idx < xlo) | (idx >= xhi)) ? 2u : 0u;
+                     },
                      [&](uint64_t e, uint32_t, uint32_t r) { sm.cand[r] = e; }, n1, n2);
                 used = n2;
                 if (tid == 0) sm.ctr[4] = n2;
                 lds_sync();
+                if (!over) break;
             }
         });
     }
@@ -1292,17 +1343,21 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     uint32_t b0 = 0, above = 0;
     if (keep) {
         // the threshold bin, from the buffer: first over the 256-bin window
-        // above lo, which normally holds it; else over all 4096 bins
+        // from the bound's bin, which normally holds it; else over all 4096
+        // bins
         uint32_t bw;
         window_select(need, bw, above, hb);
         if (hb > 0u && bw < 255u) {
-            b0 = lo + bw;
+            b0 = (lo_key >> (32 - F)) + bw;
         } else {
             hist_from_buffer();
             local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
         }
     }
-    if (keep && hb > 0u && b0 >= lo) {
+    // one finisher call for both paths (its code inlined once)
+    uint32_t fin_m = 0;
+    int fin_r0 = 1;
+    if (keep && hb > 0u && b0 >= (lo_key >> (32 - F))) {
         need -= above;
         W += above;
         pf.add(F, 0, b0, idx_bits);
@@ -1337,107 +1392,114 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         const bool bad = nw != W || nbk != hb;
         if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
         if (whole) return;
-        lds_sync();
-        finish_bucket<BLOCK>(sm.cand, hb, need, W, pf, 1, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
-                                &sm.ctr[2], out, okey, k, P.status);
-        return;
-    }
-    // ---------------- fallback: the full first-digit histogram by a second
-    // read, then rounds and collection by further reads
-    {
-        {
-            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
-            for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-            if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-        }
-        lds_sync();
-        uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
-        stream([&](const uint32_t* keys, int) {
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i)
-                if (keys[i] != 0u) atomicAdd(&hc[keys[i] >> (32 - F)], 1u);
-        });
-        lds_sync();
-    }
-    local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
-    need -= above;
-    W += above;
-    pf.add(F, 0, b0, idx_bits);
-    whole = hb == need;
-    // ---------------- further rounds (only when the bucket is still large)
-    for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
-        {
-            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
-            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        }
-        lds_sync();
-        uint32_t* const hc = sm.h.h8 + (tid % kCopies) * 257;
-        const int sh = digit_shift(F, r, idx_bits);
-        const uint32_t dm = digit_mask(F, r);
-        stream([&](const uint32_t* keys, int ct) {
-            const int ibase = 4 * (ct + tid) - off;
-#pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t key = keys[4 * j + e];
-                    const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                    if (pf.match(key, ni)) atomicAdd(&hc[((r < 4 ? key : ni) >> sh) & dm], 1u);
+        fin_m = hb;
+        fin_r0 = 1;
+    } else {
+        // ---------------- fallback: the full first-digit histogram by a second
+        // read, then rounds and collection by further reads.  Rare (the
+        // estimated bound failed), so its passes are rolled loops of U chunks
+        // per lane: small code and few registers beside the streaming pass
+        // above (measured: the fallback written like the first pass, unrolled
+        // over whole tiles, costs that pass 14 % on the causal batch).
+        constexpr int U = 2;
+        auto reread = [&](auto&& f) {
+    #pragma unroll 1
+            for (int c0 = 0; c0 < nchunks; c0 += U * BLOCK) {
+                u32x4_t v[U];
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * BLOCK + tid;
+                    v[u] = *reinterpret_cast<const u32x4_t*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
                 }
+                uint32_t kk[4 * U], nn[4 * U];  // keys (0: empty slot) and ~indices
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * BLOCK + tid;
+                    const int e0 = 4 * c - off;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                        kk[4 * u + e] = ok ? key_of(__uint_as_float(v[u][e])) : 0u;
+                        nn[4 * u + e] = ~(uint32_t)(e0 + e);
+                    }
+                }
+                f(kk, nn);
             }
-        });
-        lds_sync();
-        uint32_t b, above;
-        local_select<BLOCK, 256, kCopies, 257>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, b, above, hb);
+        };
+        {
+            {
+                uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
+                for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
+                if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
+            }
+            lds_sync();
+            uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
+            reread([&](const uint32_t* kk, const uint32_t*) {
+    #pragma unroll
+                for (int i = 0; i < 4 * U; ++i)
+                    if (kk[i] != 0u) atomicAdd(&hc[kk[i] >> (32 - F)], 1u);
+            });
+            lds_sync();
+        }
+        local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
         need -= above;
         W += above;
-        pf.add(F, r, b, idx_bits);
-        R = r;
+        pf.add(F, 0, b0, idx_bits);
         whole = hb == need;
-    }
-    // ---------------- collection: winners to the output, the bucket to LDS
-    // (or to the output when it is taken whole).  Positions per tile: each
-    // lane counts its winners and bucket elements, a wave prefix (DPP) ranks
-    // the lanes, and one LDS atomic per wave and kind reserves the wave's
-    // range.
-    static_assert(ITEMS <= 32, "per-lane selection masks are 32 bits");
-    bool overflow = false;
-    const uint32_t lane = lane_id();
-    stream([&](const uint32_t* keys, int ct) {
-        const int ibase = 4 * (ct + tid) - off;
-        uint32_t mw = 0, mbk = 0;  // this lane's winners / bucket elements, one bit per slot
-#pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t key = keys[4 * j + e];
-                const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                const bool a = (key != 0u) & pf.above(key, ni);
-                const bool m = pf.match(key, ni);
-                mw |= (uint32_t)a << (4 * j + e);
-                mbk |= (uint32_t)m << (4 * j + e);
+        // ---------------- further rounds (only when the bucket is still large)
+        for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
+            {
+                uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
+                for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
             }
+            lds_sync();
+            uint32_t* const hc = sm.h.h8 + (tid % kCopies) * 257;
+            const int sh = digit_shift(F, r, idx_bits);
+            const uint32_t dm = digit_mask(F, r);
+            reread([&](const uint32_t* kk, const uint32_t* nn) {
+    #pragma unroll
+                for (int i = 0; i < 4 * U; ++i)
+                    if (pf.match(kk[i], nn[i])) atomicAdd(&hc[((r < 4 ? kk[i] : nn[i]) >> sh) & dm], 1u);
+            });
+            lds_sync();
+            uint32_t b, above;
+            local_select<BLOCK, 256, kCopies, 257>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, b, above, hb);
+            need -= above;
+            W += above;
+            pf.add(F, r, b, idx_bits);
+            R = r;
+            whole = hb == need;
         }
-        const uint32_t nw = (uint32_t)__builtin_popcount(mw), nb = (uint32_t)__builtin_popcount(mbk);
-        const uint32_t iw = wave_inclusive_scan(nw), ib = wave_inclusive_scan(nb);
-        const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)iw, 63);
-        const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, 63);
-        if (tw | tb) {
-            uint32_t bw = 0, bb = 0;
-            if (lane == 0) {
-                if (tw) bw = atomicAdd(&sm.ctr[0], tw);
-                if (tb) bb = atomicAdd(&sm.ctr[1], tb);
+        // ---------------- collection: winners to the output, the bucket to LDS
+        // (or to the output when it is taken whole).  Positions per step: each
+        // lane counts its winners and bucket elements, a wave prefix (DPP) ranks
+        // the lanes, and one LDS atomic per wave and kind reserves the wave's
+        // range.
+        bool overflow = false;
+        const uint32_t lane = lane_id();
+        reread([&](const uint32_t* kk, const uint32_t* nn) {
+            uint32_t mw = 0, mbk = 0;  // this lane's winners / bucket elements, one bit per slot
+    #pragma unroll
+            for (int i = 0; i < 4 * U; ++i) {
+                mw |= (uint32_t)((kk[i] != 0u) & pf.above(kk[i], nn[i])) << i;
+                mbk |= (uint32_t)pf.match(kk[i], nn[i]) << i;
             }
-            uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)bw, 0) + iw - nw;
-            uint32_t pb = (uint32_t)__builtin_amdgcn_readlane((int)bb, 0) + ib - nb;
-#pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int slot = 4 * j + e;
-                    const uint32_t key = keys[slot];
-                    const uint32_t ni = ~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                    if ((mw >> slot) & 1u) {
+            const uint32_t nw = (uint32_t)__builtin_popcount(mw), nb = (uint32_t)__builtin_popcount(mbk);
+            const uint32_t iw = wave_inclusive_scan(nw), ib = wave_inclusive_scan(nb);
+            const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)iw, 63);
+            const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, 63);
+            if (tw | tb) {
+                uint32_t bw = 0, bb = 0;
+                if (lane == 0) {
+                    if (tw) bw = atomicAdd(&sm.ctr[0], tw);
+                    if (tb) bb = atomicAdd(&sm.ctr[1], tb);
+                }
+                uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)bw, 0) + iw - nw;
+                uint32_t pb = (uint32_t)__builtin_amdgcn_readlane((int)bb, 0) + ib - nb;
+    #pragma unroll
+                for (int i = 0; i < 4 * U; ++i) {
+                    const uint32_t key = kk[i], ni = nn[i];
+                    if ((mw >> i) & 1u) {
                         if (pw < W) {
                             out[pw] = (int32_t)~ni;
                             if (okey) okey[pw] = key;
@@ -1445,7 +1507,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                             overflow = true;
                         }
                         ++pw;
-                    } else if ((mbk >> slot) & 1u) {
+                    } else if ((mbk >> i) & 1u) {
                         if (whole) {
                             if (W + pb < (uint32_t)k) {
                                 out[W + pb] = (int32_t)~ni;
@@ -1462,13 +1524,15 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                     }
                 }
             }
-        }
-    });
-    if (overflow) raise_flag(P.status, kFlagCapacity);
-    if (whole) return;
+        });
+        if (overflow) raise_flag(P.status, kFlagCapacity);
+        if (whole) return;
+        fin_m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
+        fin_r0 = R + 1;
+    }
     lds_sync();
-    finish_bucket<BLOCK>(sm.cand, hb > (uint32_t)kCap ? (uint32_t)kCap : hb, need, W, pf, R + 1, F, idx_bits,
-                            false, sm.h.h8, sm.small, sm.scan, sm.sel, &sm.ctr[2], out, okey, k, P.status);
+    finish_bucket<BLOCK>(sm.cand, fin_m, need, W, pf, fin_r0, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
+                            &sm.ctr[2], out, okey, k, P.status);
 }
 
 // ----------------------------------------------------------------- ordered output
