@@ -183,6 +183,30 @@ def test_edge_case_one_wg_per_row(torch_gpu, request, x, k, lengths):
         assert_parity(x2, k, lengths, got)
 
 
+def _drifting_rows():
+    """Rows whose first tile misjudges the bound of the one-WG-per-row
+    kernels: a run of large values after a normal first tile (a tile that
+    overflows the candidate buffer), a rising trend, a dense value band at
+    the threshold (many elements in one 12-bit bin), and a control row."""
+    rng = np.random.default_rng(2048)
+    n = 65536
+    x = rng.standard_normal((5, n)).astype(np.float32)
+    x[0, 8192:4 * 8192] += 10.0
+    x[1] += np.arange(n, dtype=np.float32) / 4000.0
+    x[2, :] = 1.0 + rng.integers(0, 64, n).astype(np.float32) / 4096.0  # 64 values inside one 12-bit bin
+    x[3, 8192:9000] += 10.0  # fewer than k large ones: the bound overshoots
+    lengths = np.array([n, n, n, n, 50000], np.int32)
+    return x, lengths
+
+
+def test_drifting_rows_one_wg_per_row(torch_gpu):
+    x, lengths = _drifting_rows()
+    for v in _one_wg_per_row_variants():
+        _say("drifting rows variant %d" % v)
+        got = run_gpu(torch_gpu, x, 2048, lengths, variant=v, wgs=1)
+        assert_parity(x, 2048, lengths, got)
+
+
 @pytest.mark.parametrize("offset", [1, 2, 3])
 def test_unaligned_rows_one_wg_per_row(torch_gpu, offset):
     rng = np.random.default_rng(10 + offset)

@@ -90,6 +90,16 @@ def test_sorted_edge_case_one_wg_per_row(torch_gpu, request, x, k, lengths):
         assert_sorted_parity(x2, k, lengths, idx, vals)
 
 
+def test_sorted_drifting_rows_one_wg_per_row(torch_gpu):
+    from tests.test_gpu_parity import _drifting_rows
+
+    x, lengths = _drifting_rows()
+    for v in _one_wg_per_row_variants():
+        _say("sorted drifting rows variant %d" % v)
+        idx, vals = run_sorted(torch_gpu, x, 2048, lengths, variant=v, wgs=1)
+        assert_sorted_parity(x, 2048, lengths, idx, vals)
+
+
 @pytest.mark.parametrize("case", ["ties_bf16_131072", "tie_storm_40000", "ragged_4rows"])
 def test_sorted_every_variant_and_split(torch_gpu, case):
     """Every selection kernel path records the keys the sort uses."""
