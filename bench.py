@@ -271,8 +271,8 @@ def main() -> int:
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build's selector runs on a single GPU "
-              "(rows shard across GPUs with no communication; see the design notes). "
+        print("bench.py measures one GPU only: the selector runs on a single GPU "
+              "(a batch shards by rows across GPUs with no communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
