@@ -183,6 +183,23 @@ def test_edge_case_one_wg_per_row(torch_gpu, request, x, k, lengths):
         assert_parity(x2, k, lengths, got)
 
 
+@pytest.mark.parametrize("case", ["normal", "tie_storm"])
+def test_rows_past_2_pow_24(torch_gpu, case):
+    """A row longer than 2^24 (indices need all 32 index bits; the default
+    shape streams it over many WGs): normal values, and a tie storm whose
+    threshold is settled on the index digits."""
+    rng = np.random.default_rng(24)
+    n = (1 << 24) + 5
+    if case == "normal":
+        x = rng.standard_normal(n, dtype=np.float32)
+    else:
+        x = np.full(n, 1.5, np.float32)
+        x[rng.integers(0, n, 700)] = 2.5
+    _say("row past 2^24: n=%d case=%s" % (n, case))
+    got = run_gpu(torch_gpu, x[None], 2048)
+    assert_parity(x[None], 2048, None, got)
+
+
 def _drifting_rows():
     """Rows whose first tile misjudges the bound of the one-WG-per-row
     kernels: a run of large values after a normal first tile (a tile that
