@@ -198,6 +198,10 @@ def test_rows_past_2_pow_24(torch_gpu, case):
     _say("row past 2^24: n=%d case=%s" % (n, case))
     got = run_gpu(torch_gpu, x[None], 2048)
     assert_parity(x[None], 2048, None, got)
+    for v in _one_wg_per_row_variants():
+        _say("row past 2^24: case=%s variant %d (one WG)" % (case, v))
+        got = run_gpu(torch_gpu, x[None], 2048, variant=v, wgs=1)
+        assert_parity(x[None], 2048, None, got)
 
 
 def _drifting_rows():
