@@ -96,6 +96,7 @@ struct KParams {
     int32_t idx_bits;       // bits of the index that vary (multiple of 8, 8..32)
     int32_t mcopies;        // global histogram copies used (1..kMergeCopies)
     uint32_t* keys;         // [rows, k]: key of the element at each output slot (ordered output), or null
+    int32_t ahead;          // one WG per row: rows from a row to the one whose first tile it touches (0: none)
 };
 
 // ----------------------------------------------------------------- device helpers
@@ -1335,6 +1336,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             }
         });
     }
+    // the first tile of the row `ahead` rows on (the one that probably runs
+    // next on this WG's XCD) is touched now: its loads then hit the caches
+    uint32_t sink = 0;
+    if (P.ahead > 0 && row + P.ahead < P.rows && tid * 16 < n)
+        sink = *reinterpret_cast<const uint32_t*>(P.logits + (size_t)(row + P.ahead) * (size_t)n + tid * 16);
+    auto done = [&]() { __asm__ volatile("" ::"v"(sink)); };
     lds_sync();
     Prefix pf{0u, 0u, 0u, 0u};
     uint32_t need = (uint32_t)k, W = 0, hb = 0;
@@ -1391,7 +1398,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
              nw, nbk);
         const bool bad = nw != W || nbk != hb;
         if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
-        if (whole) return;
+        if (whole) {
+            done();
+            return;
+        }
         fin_m = hb;
         fin_r0 = 1;
     } else {
@@ -1526,13 +1536,17 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             }
         });
         if (overflow) raise_flag(P.status, kFlagCapacity);
-        if (whole) return;
+        if (whole) {
+            done();
+            return;
+        }
         fin_m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
         fin_r0 = R + 1;
     }
     lds_sync();
     finish_bucket<BLOCK>(sm.cand, fin_m, need, W, pf, fin_r0, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
                             &sm.ctr[2], out, okey, k, P.status);
+    done();
 }
 
 // ----------------------------------------------------------------- ordered output
@@ -2612,6 +2626,7 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.chunks_per_wg = L.chunks_per_wg;
     P.idx_bits = idx_bits_for(n);
     P.mcopies = L.G <= 16 ? 1 : (L.G <= 32 ? 2 : kMergeCopies);
+    P.ahead = var.rows_kernel ? d->capacity[L.variant] : 0;
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
