@@ -44,6 +44,8 @@
 //  * The per-row workspace is double-buffered by launch parity: a launch
 //    uses one half, and its finishing WG clears the half the previous launch
 //    used, so no clearing launch or end-of-kernel barrier is needed.
+//  * Batches of many rows take one WG per row instead, reading the row once
+//    and keeping only the elements above a running bound on chip (below).
 
 #include <hip/hip_runtime.h>
 
@@ -996,11 +998,15 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 //
 // Batches of many rows: one WG owns a whole row and streams it in tiles of
 // BLOCK x ITEMS logits, the next PD tiles' loads in flight while the
-// current one is processed.  The first digit is 12 bits wide (4096 bins), which for
-// typical rows leaves a bucket of at most 4096 after one pass; a second pass
-// (re-reading the row, by then in the device's caches) writes the winners
-// and gathers the bucket into LDS; the on-chip finish does the rest.
-// Positions come from two wave-aggregated LDS counters (winners, bucket).
+// current one is processed.  During that single read it keeps every element
+// whose key is at or above a running lower bound in an LDS buffer (the
+// bound estimated from the elements seen so far and raised as the buffer
+// fills); when the buffer ends up holding at least k elements, the row's
+// k-th largest is the buffer's and the row is finished from LDS: a 12-bit
+// first digit (4096 bins), winners out, the threshold bin to the on-chip
+// finish.  Otherwise the row is finished with re-reads (a full 12-bit
+// histogram, more rounds while the bucket is large, a collection pass whose
+// positions come from two wave-aggregated LDS counters).
 
 constexpr int kRowsCap = 4608;  // candidate buffer of the one-WG-per-row kernel (entries)
 constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered entries is refined
