@@ -2559,7 +2559,11 @@ SortShape sort_shape(int32_t rows, int32_t k) {
     SortShape s;
     s.rank = k <= kRankMax && (int64_t)rows * (int64_t)k * (int64_t)k <= (int64_t)1 << 25;
     s.rank_wgs = k / 16 < 1 ? 1 : (k / 16 > 128 ? 128 : k / 16);
-    if (k <= 1024) { s.block = 256; s.items = 4; }
+    if (rows <= 128) {
+        // few rows (fewer WGs than CUs): the most threads per row
+        s.block = 1024;
+        s.items = k <= 1024 ? 1 : (k <= 2048 ? 2 : (k <= 4096 ? 4 : 8));
+    } else if (k <= 1024) { s.block = 256; s.items = 4; }
     else if (k <= 2048) { s.block = 512; s.items = 4; }
     else if (k <= 4096) { s.block = 1024; s.items = 4; }
     else { s.block = 1024; s.items = 8; }
@@ -2572,6 +2576,8 @@ void launch_sort(const SortShape& sh, int32_t rows, hipStream_t stream, const So
     const dim3 grid((unsigned)((int64_t)rows * sh.nruns));
     if (sh.block == 256) topk_sort_kernel<256, 4><<<grid, 256, 0, stream>>>(p);
     else if (sh.block == 512) topk_sort_kernel<512, 4><<<grid, 512, 0, stream>>>(p);
+    else if (sh.items == 1) topk_sort_kernel<1024, 1><<<grid, 1024, 0, stream>>>(p);
+    else if (sh.items == 2) topk_sort_kernel<1024, 2><<<grid, 1024, 0, stream>>>(p);
     else if (sh.items == 4) topk_sort_kernel<1024, 4><<<grid, 1024, 0, stream>>>(p);
     else topk_sort_kernel<1024, 8><<<grid, 1024, 0, stream>>>(p);
 }
