@@ -1110,9 +1110,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 
     // ---------------- first pass: every element whose key is at or above a
     // lower bound `lo_key` kept in LDS.  The bound is an estimate: the
-    // first-digit bin (12 bits) of the element of rank 1.25 * k * seen / L +
-    // 64 among the `seen` elements read so far, where the k-th largest of the
-    // row is expected near rank k * seen / L (in a dense bin, also that
+    // first-digit bin (12 bits) of the element of rank 1.125 * k * seen / L
+    // + 16 among the `seen` elements read so far, where the k-th largest of
+    // the row is expected near rank k * seen / L (in a dense bin, also that
     // element's next 8 key bits).  It is taken from the first tile and
     // raised (with the buffer compacted) whenever the buffer fills up, from
     // histograms of the buffer.  The buffer then holds every element whose
@@ -1169,7 +1169,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     };
     // rank of the bound after `seen` valid elements
     auto bound_rank = [&](uint32_t seen) -> uint32_t {
-        const uint64_t est = ((uint64_t)k * seen * 5u) / (4u * (uint64_t)L) + 64u;
+        // the margin at the end of the row, k / 8, is several standard
+        // deviations of the count above a fixed rank for values drawn alike
+        // along the row; a looser bound buffers (and later partitions) more
+        const uint64_t est = ((uint64_t)k * seen * 9u) / (8u * (uint64_t)L) + 16u;
         return (uint32_t)(est < seen ? est : seen);
     };
     // the first-digit histogram of the buffered entries
