@@ -1008,7 +1008,9 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 // histogram, more rounds while the bucket is large, a collection pass whose
 // positions come from two wave-aggregated LDS counters).
 
-constexpr int kRowsCap = 4608;  // candidate buffer of the one-WG-per-row kernel (entries)
+// candidate buffer of the one-WG-per-row kernel (entries): as large as two
+// WGs per CU allow with some LDS to spare (78 KB per WG)
+constexpr int kRowsCap = 5376;
 constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered entries is refined
 
 template <int BLOCK>
