@@ -208,15 +208,18 @@ def _drifting_rows():
     """Rows whose first tile misjudges the bound of the one-WG-per-row
     kernels: a run of large values after a normal first tile (a tile that
     overflows the candidate buffer), a rising trend, a dense value band at
-    the threshold (many elements in one 12-bit bin), and a control row."""
+    the threshold (many elements in one 12-bit bin), a control row, and a
+    falling trend (the first tile's bound is too high for the rest of the
+    row: fewer than k elements end up buffered)."""
     rng = np.random.default_rng(2048)
     n = 65536
-    x = rng.standard_normal((5, n)).astype(np.float32)
+    x = rng.standard_normal((6, n)).astype(np.float32)
     x[0, 8192:4 * 8192] += 10.0
     x[1] += np.arange(n, dtype=np.float32) / 4000.0
     x[2, :] = 1.0 + rng.integers(0, 64, n).astype(np.float32) / 4096.0  # 64 values inside one 12-bit bin
     x[3, 8192:9000] += 10.0  # fewer than k large ones: the bound overshoots
-    lengths = np.array([n, n, n, n, 50000], np.int32)
+    x[5] -= np.arange(n, dtype=np.float32) / 4000.0
+    lengths = np.array([n, n, n, n, 50000, n], np.int32)
     return x, lengths
 
 
