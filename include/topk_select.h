@@ -22,9 +22,12 @@
  *  - -0.0 and +0.0 are equal (they tie); infinities and subnormals are
  *    ordinary values; NaN logits are outside the contract (no error is
  *    raised, the result for such a row is unspecified but memory-safe);
- *  - the output order within a row is unspecified and may differ between
- *    calls (elements are placed through atomic counters); the selected set
- *    is exact and unique.  topk_select_sorted gives a fully determined order.
+ *  - the output order within a row is unspecified, but it is a function of
+ *    the row's values and the launch shape alone (every position comes from
+ *    a block scan or an exact rank, none from the order in which atomic
+ *    operations or workgroups complete), so repeated calls on the same input
+ *    write identical bytes; the selected set is exact and unique.
+ *    topk_select_sorted gives the set ordered by value.
  *
  * All pointers named "device" point to memory on the calling thread's current
  * HIP device.  The library never takes ownership of caller memory.
@@ -48,7 +51,9 @@ enum {
     TOPK_SELECT_ERROR_OUT_OF_MEMORY = 2, /* workspace allocation failed; nothing was enqueued */
     TOPK_SELECT_ERROR_LAUNCH = 3,        /* a HIP call or the kernel launch failed */
     TOPK_SELECT_ERROR_NO_DEVICE = 4,     /* no usable HIP device is current */
-    TOPK_SELECT_ERROR_DEVICE_FLAG = 5    /* a kernel raised a device-side error flag */
+    TOPK_SELECT_ERROR_DEVICE_FLAG = 5,   /* a kernel raised a device-side error flag */
+    TOPK_SELECT_ERROR_CAPTURE = 6        /* scratch would have to be allocated while the stream is
+                                            being captured into a graph; nothing was enqueued */
 };
 
 /* hipStream_t, passed as an opaque pointer so this header needs no HIP headers.
@@ -63,7 +68,7 @@ typedef void* topk_select_stream_t;
  *            4-byte aligned (16-byte alignment of rows is used when present,
  *            but not required).  Read only.
  *   rows     number of rows, >= 0.  rows == 0 is a successful no-op.
- *   n        row length, >= 1.
+ *   n        row length, 1 <= n <= 2^30.
  *   lengths  device, const int32_t[rows], or NULL.  Valid length per row; read
  *            on the device and clamped to [0, n].
  *   k        number of indices per row, 1 <= k <= n.
@@ -78,7 +83,16 @@ typedef void* topk_select_stream_t;
  * per (device, stream), allocated on first use and grown as needed (the first
  * call for a new (device, stream) or a larger shape allocates and clears it
  * with hipMalloc/hipMemsetAsync; later calls of that size allocate nothing).
- * Thread-safe; calls on different streams use different workspaces.
+ * A buffer replaced by a larger one is kept until
+ * topk_select_release_workspace, so graphs captured earlier stay valid.
+ * While the stream is being captured into a graph, a call that would have to
+ * allocate returns TOPK_SELECT_ERROR_CAPTURE and enqueues nothing: call once
+ * with the same (or a larger) shape on that stream before capturing.
+ * Thread-safe: calls from several host threads are serialised on the host
+ * while they enqueue; calls on different streams use different workspaces
+ * and may run concurrently on the device (a row's workgroups wait only for
+ * workgroups of the same launch that were dispatched before them, so no
+ * co-residency is required).  Calls on one stream run in stream order.
  */
 int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                 int32_t* out_idx, topk_select_stream_t stream);
@@ -229,9 +243,14 @@ int topk_select_variant_info(int32_t v, topk_select_plan_t* plan);
 /*
  * Waits for `stream`, then reads and clears the device-side error flags of
  * the workspace of (current device, stream) and stores them in *flags (0 when
- * none were raised or no workspace exists).  Flags: 1 = a cross-workgroup
- * wait exceeded its time bound, 2 = an internal capacity check failed.
- * Returns DEVICE_FLAG when any flag was set, SUCCESS otherwise.
+ * none were raised or no workspace exists).  Flags: 1 = a wait for another
+ * workgroup exceeded its time bound (2 s; the waiting workgroup then
+ * finished its rows by itself, and its output is still exact), 2 = an
+ * internal capacity check failed.  After flag 1 the workspace may hold
+ * counts or candidates written after their row was finished; this call
+ * clears the whole workspace then, and a later call on the stream is exact
+ * only after it.  Returns DEVICE_FLAG when any flag was set, SUCCESS
+ * otherwise.
  */
 int topk_select_device_status(topk_select_stream_t stream, int32_t* flags);
 

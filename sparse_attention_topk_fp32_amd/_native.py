@@ -20,6 +20,7 @@ ERROR_OUT_OF_MEMORY = 2
 ERROR_LAUNCH = 3
 ERROR_NO_DEVICE = 4
 ERROR_DEVICE_FLAG = 5
+ERROR_CAPTURE = 6
 
 # Names declared in include/topk_select.h.
 EXPORTS = (

@@ -13,39 +13,29 @@
 //  * Section 03: keep the surviving candidates on chip once the bucket is
 //    small, and stop the screening over global memory once the bucket holds
 //    at most 4096 elements; wide vector loads.
-//  * Section 5: one row split over several blocks that merge their
-//    histograms and continue together; -1 for empty output slots.
+//  * Section 5: one row split over several blocks that cooperate; -1 for
+//    empty output slots.
 //
 // MI355X design (not a translation of the article's Triton/CUDA kernels):
-//  * A row is cut into slices of 16-byte chunks, one workgroup (WG) per
-//    slice, G WGs per row.  Resident variants load their slice once, fuse the
-//    key map into the load and keep the keys in VGPRs for every later pass;
-//    streaming variants re-read their slice in each pass (rows too long to
-//    keep on chip).
 //  * Ties are made unique by ranking the 64-bit composite
 //    (key << 32 | ~index): larger composite = larger value, or equal value and
-//    smaller index.  Rounds run over 8-bit digits of the key and, only when a
-//    value is tied past capacity, of the index.
-//  * Merge of a round across the G WGs of a row: each WG adds
-//    (1 << 32 | count) for each of the 256 bins into the row's global
-//    histogram with one 64-bit device-scope atomic per bin, and polls the bin
-//    until its arrival field reaches G; no separate barrier, no cache fence.
-//    The value the atomic returns is the count of the WGs that added before
-//    this one, which gives every WG a private, disjoint range of output
-//    positions inside each bin.  Every WG selects the threshold bin itself
-//    from the merged counts.
-//  * Elements above the threshold bin are written straight to the output by
-//    the WG holding them, at (start of their bin) + (the WG's range) + (rank
-//    inside the WG, from a wave-aggregated LDS counter).  Once the threshold
-//    bucket holds at most 4096 elements, its (key, index) composites go to a
-//    candidate buffer (LDS for G == 1, the row's global stage for G > 1) and
-//    one WG finishes on chip: more digit rounds in LDS while more than 256
-//    remain, then an exact rank.
-//  * The per-row workspace is double-buffered by launch parity: a launch
-//    uses one half, and its finishing WG clears the half the previous launch
-//    used, so no clearing launch or end-of-kernel barrier is needed.
-//  * Batches of many rows take one WG per row instead, reading the row once
-//    and keeping only the elements above a running bound on chip (below).
+//    smaller index.  Every selection below is an exact selection of the k
+//    largest composites, so the result is the article's (ties at the
+//    threshold to the lowest index).
+//  * Few rows (batch-1 decode): a row is cut into slices of 16-byte chunks,
+//    one workgroup (WG) per slice.  Every WG of the row reads the same
+//    sample of the row (blocks of chunks spread along it) and takes from it a
+//    lower bound on the row's k-th largest key; it then writes the
+//    composites of its slice at or above the bound to a region of its own
+//    and publishes how many it wrote.  Only the row's last WG waits: it
+//    gathers the regions in WG order into LDS and selects exactly on chip
+//    (range-adaptive 256-bin rounds, then an exact rank).  No WG waits for a
+//    later one, so no co-residency is required, and every position comes
+//    from a block scan, so the output order is the same on every call.
+//  * Many rows: one WG per row streams the row once, keeping the elements at
+//    or above a running bound in LDS, then the same on-chip selection.
+//  * When a bound overshoots or the candidates do not fit on chip, one WG
+//    finishes the row exactly by passes over it in global memory.
 
 #include <hip/hip_runtime.h>
 
@@ -58,48 +48,60 @@
 #include <mutex>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "topk_select.h"
 
 namespace tks {
 
-constexpr int kCap = 4096;        // final bucket size handed to one WG (entries)
 constexpr int kSmall = 256;       // bucket ranked exactly by comparisons
-constexpr int kRounds = 9;        // merge rounds: a window round, then up to 4 key + 4 index digits
-constexpr int kCopies = 16;       // LDS copies of the 256-bin histogram (against atomic conflicts)
-constexpr int kWinLength = 524288;  // rows at least this long take the sampled window round
-constexpr int kMergeCopies = 4;   // global copies of a row's histogram per round (WG w -> copy w mod C)
+constexpr int kCopies = 16;       // LDS copies of a 256-bin histogram (against atomic conflicts)
+constexpr int kStride = 260;      // words per copy: 256 bins, a spare slot, 16-byte aligned
+constexpr int kBufCap = 7168;     // candidate buffer of the split kernel's finishing WG (entries)
+constexpr int kMaxSplit = 256;    // WGs per row of the split kernel
+constexpr int kSampleMax = 4096;  // chunks in a row's sample (split kernel)
 constexpr uint32_t kFlagTimeout = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
-// Bound on a cross-workgroup wait, in ticks of the 100 MHz constant clock
-// (s_memrealtime): 2 s, far beyond any legitimate wait.
+// Bound on a wait for another workgroup, in ticks of the 100 MHz constant
+// clock (s_memrealtime): 2 s, far beyond any legitimate wait.
 constexpr uint64_t kSpinLimitTicks = 200000000ull;
 
-// Per-row scratch for rows spread over several workgroups, in two halves
-// selected by the parity of the launch.  All cross-workgroup traffic uses
-// device-scope atomic operations, performed at the device's coherence point.
-struct alignas(256) RowWorkspace {
-    uint64_t hist[2][kRounds][kMergeCopies][256];  // (arrivals << 32) | count
-    uint64_t stage[2][kCap];                       // final-bucket composites; 0 = not written yet
-    uint32_t parity;                               // half used by the next launch
-    uint32_t used[2];  // what each half holds, cleared by the next launch: rounds | copies << 4 | stage entries << 8
-    uint32_t pad[57];
+#ifdef TKS_TEST_HOOKS
+// Test builds only: the wait bound can be set from the host (0: give up
+// before the first poll), so that the give-up path can be exercised with
+// every kernel still ending normally.
+__device__ uint64_t g_spin_limit = kSpinLimitTicks;
+__device__ __forceinline__ uint64_t spin_limit() { return g_spin_limit; }
+#else
+__device__ __forceinline__ constexpr uint64_t spin_limit() { return kSpinLimitTicks; }
+#endif
+
+// Per-row coordination of the split kernel: the candidate count of each WG,
+// tagged with the launch's epoch, and the epoch itself (advanced by the
+// row's last WG at the end of every launch).
+struct alignas(64) SplitRow {
+    uint64_t cnt[kMaxSplit];  // (tag << 32) | candidates written by WG w; 0 = not published
+    uint32_t epoch;
+    uint32_t pad[15];
 };
 
 struct KParams {
     const float* logits;
     const int32_t* lengths;
     int32_t* out;
-    RowWorkspace* ws;       // per row, when G > 1
+    uint32_t* keys;         // [rows, k]: key of the element at each output slot (ordered output), or null
     uint32_t* status;
+    SplitRow* rws;          // split kernel, several WGs per row: per-row counts and epoch
+    uint64_t* stage;        // split kernel: [rows][G][region] candidate composites, 0 where unused
     int32_t rows, n, k;
     int32_t G;              // workgroups per row
     int32_t chunks_per_wg;  // 16-byte chunks in one WG's slice
-    int32_t idx_bits;       // bits of the index that vary (multiple of 8, 8..32)
-    int32_t mcopies;        // global histogram copies used (1..kMergeCopies)
-    uint32_t* keys;         // [rows, k]: key of the element at each output slot (ordered output), or null
+    int32_t region;         // entries of one WG's region in the stage
+    int32_t sample_chunks;  // split kernel: chunks in a row's sample (a multiple of 16)
     int32_t ahead;          // one WG per row: rows from a row to the one whose first tile it touches (0: none)
 };
+
+__device__ __forceinline__ uint32_t make_tag(uint32_t epoch) { return 0x80000000u | (epoch & 0x7FFFFFFFu); }
 
 // ----------------------------------------------------------------- device helpers
 
@@ -118,12 +120,19 @@ __device__ __forceinline__ uint32_t key_of(float x) {
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+    return ((uint64_t)key << 32) | (uint64_t)~idx;
+}
+
 __device__ __forceinline__ uint32_t lane_id() {
     return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
 // A value every lane holds identically: make it scalar.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    return ((uint64_t)uniform((uint32_t)(v >> 32)) << 32) | (uint64_t)uniform((uint32_t)v);
+}
 
 __device__ __forceinline__ void raise_flag(uint32_t* status, uint32_t f) {
     __hip_atomic_fetch_or(status, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -138,14 +147,16 @@ template <typename T>
 __device__ __forceinline__ void st_dev(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <typename T>
-__device__ __forceinline__ T add_dev(T* p, T v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Workgroup barrier that orders LDS only (global data crossing WGs goes
 // through device-scope atomics, global data inside a WG is never re-read).
 __device__ __forceinline__ void lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int valid_length(const int32_t* lengths, int row, int n) {
+    if (!lengths) return n;
+    const int L = lengths[row];
+    return L < 0 ? 0 : (L > n ? n : L);
+}
 
 // Inclusive scan across the 64 lanes of a wave with DPP lane moves: shifts
 // by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of a row is
@@ -160,26 +171,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// Block-wide exclusive scan (thread order) of one counter over the first NT
-// threads (NT a multiple of 64, <= BLOCK); every thread of the block calls
-// it.  Returns this thread's exclusive prefix.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, uint32_t* s_w /* [NT / 64] */) {
-    constexpr int NW = NT / 64;
-    const uint32_t wid = threadIdx.x / 64;
-    const uint32_t ia = wave_inclusive_scan(a);
-    if (wid < NW && lane_id() == 63) s_w[wid] = ia;
-    lds_sync();
-    uint32_t pa = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-        if ((uint32_t)i < wid) pa += s_w[i];
-    lds_sync();  // s_w may be reused right after
-    return pa + ia - a;
-}
-
 // Block-wide exclusive scan over all BLOCK threads that also returns the
-// total (uniform).
+// total (uniform).  Two barriers; s_w may be reused right after.
 template <int BLOCK>
 __device__ __forceinline__ uint32_t block_scan_total(uint32_t a, uint32_t* s_w /* [BLOCK / 64] */, uint32_t& total) {
     constexpr int NW = BLOCK / 64;
@@ -188,7 +181,7 @@ __device__ __forceinline__ uint32_t block_scan_total(uint32_t a, uint32_t* s_w /
     if (lane_id() == 63) s_w[wid] = ia;
     lds_sync();
     uint32_t pa = 0, tot = 0;
-#pragma unroll
+#pragma unroll 4
     for (int i = 0; i < NW; ++i) {
         const uint32_t v = s_w[i];
         if ((uint32_t)i < wid) pa += v;
@@ -199,116 +192,42 @@ __device__ __forceinline__ uint32_t block_scan_total(uint32_t a, uint32_t* s_w /
     return pa + ia - a;
 }
 
-// Digit schedule: rounds 0..3 cut the key from the top, the first digit
-// F bits wide (8 or 12) and the others 8 bits (the last key digit keeps what
-// is left); later rounds cut the varying low idx_bits of ~index (its top
-// 32 - idx_bits bits are ones for every valid index).  shift: bit position
-// of round r's digit inside its 32-bit word; width: its bits.
-__device__ __forceinline__ int digit_shift(int F, int r, int idx_bits) {
-    if (r < 4) {
-        const int s = 32 - F - 8 * r;
-        return s < 0 ? 0 : s;
-    }
-    return idx_bits - 8 - 8 * (r - 4);
-}
-__device__ __forceinline__ int digit_width(int F, int r) {
-    if (r == 0) return F;
-    if (r < 4) return min(8, 32 - F - 8 * (r - 1));
-    return 8;
-}
-__device__ __forceinline__ uint32_t digit_mask(int F, int r) { return (1u << digit_width(F, r)) - 1u; }
-__device__ __forceinline__ int num_rounds(int idx_bits) { return 4 + idx_bits / 8; }
-
-// The composite prefix resolved so far: key bits (kpfx under kmask) and
-// ~index bits (ipfx under imask).
-struct Prefix {
-    uint32_t kpfx, kmask, ipfx, imask;
-    // value selects only (a branch that picks the field to update would
-    // put the struct in scratch memory)
-    __device__ void add(int F, int r, uint32_t b, int idx_bits) {
-        const int s = digit_shift(F, r, idx_bits);
-        const bool in_key = r < 4;
-        const uint32_t bb = b << s, mm = digit_mask(F, r) << s;
-        kpfx |= in_key ? bb : 0u;
-        kmask |= in_key ? mm : 0u;
-        ipfx |= in_key ? 0u : bb;
-        imask |= in_key ? 0u : mm;
-    }
-    // Does the element (key, ~index) match the prefix?
-    __device__ __forceinline__ bool match(uint32_t key, uint32_t ni) const {
-        return (key != 0u) & ((key & kmask) == kpfx) & ((ni & imask) == ipfx);
-    }
-    // Is the element above the prefix (a winner of some round done)?
-    __device__ __forceinline__ bool above(uint32_t key, uint32_t ni) const {
-        const uint32_t s = key & kmask;
-        return (s > kpfx) | ((s == kpfx) & ((ni & imask) > ipfx));
-    }
-};
-
-// Where the first round's digit comes from: the top F bits of the key, or
-// (win) the 12-bit first digit seen through a window of 256 bins starting
-// at bin LO (bins above the window fold into its top bin).
-struct FirstDigit {
-    int F;
-    bool win;
-    uint32_t LO;
-    __device__ __forceinline__ uint32_t of(uint32_t key) const {
-        return win ? min((key >> 20) - LO, 255u) : key >> (32 - F);
-    }
-};
-
-// Position-counter slot (256 * round + digit) of a winner whose key differs
-// from the prefix, x = the differing key bits (non-zero): the round is the
-// one whose digit holds the top differing bit.
-__device__ __forceinline__ uint32_t key_slot(uint32_t key, uint32_t x, const FirstDigit& fd, int idx_bits) {
-    const int p = 31 - __builtin_clz(x);
-    if (p >= 32 - fd.F) return fd.of(key);
-    const int r = 1 + (31 - fd.F - p) / 8;
-    return 256u * (uint32_t)r + ((key >> digit_shift(fd.F, r, idx_bits)) & digit_mask(fd.F, r));
-}
-
-// Relation of an element to the prefix after the rounds done: returns 1 when
-// it is above it (a winner; *slot = its position-counter slot), 2 when it
-// matches it (in the bucket), 0 otherwise.  Composites compare as
-// (key, ~index) pairs.
-__device__ __forceinline__ uint32_t classify(uint32_t key, uint32_t ni, const Prefix& pf, const FirstDigit& fd,
-                                             int idx_bits, uint32_t* slot) {
-    if (key == 0u) return 0u;
-    const uint32_t s = key & pf.kmask;
-    if (s != pf.kpfx) {
-        if (s < pf.kpfx) return 0u;
-        *slot = key_slot(key, s ^ pf.kpfx, fd, idx_bits);
-        return 1u;
-    }
-    const uint32_t t = ni & pf.imask;
-    if (t == pf.ipfx) return 2u;
-    if (t < pf.ipfx) return 0u;
-    const int lead = __builtin_clz(t ^ pf.ipfx) - (32 - idx_bits);  // leading bit inside the index digits
-    const int r = 4 + lead / 8;
-    *slot = (uint32_t)r * 256u + ((ni >> digit_shift(fd.F, r, idx_bits)) & 0xFFu);
-    return 1u;
-}
-
-// Shared state of one WG.
+// Positions in thread order for a running list: each thread appends `cnt`
+// entries; returns the thread's first position and advances `total` by the
+// block's sum (uniform).  One barrier: the two halves of s2 are used in turn
+// (`par` flips), so a half is written again only after every wave has passed
+// the next call's barrier, i.e. after it was read.
 template <int BLOCK>
-struct Smem {
-    alignas(16) uint32_t hist[kCopies * 257];  // histogram copies (stride 257 words)
-    uint32_t pos[kRounds * 256];        // output / stage position counters per (round, bin)
-    uint64_t cand[kCap];                // final bucket, on chip
-    uint64_t small[kSmall];             // last few candidates, ranked exactly
-    uint32_t scan[BLOCK / 64];
-    uint32_t sel[4];                    // threshold bin, count above it, count in it
-    uint32_t ctr[2];                    // finisher position counters
-};
+__device__ __forceinline__ uint32_t block_append(uint32_t cnt, uint32_t* s2 /* [2][BLOCK / 64] */, int& par,
+                                                 uint32_t& total) {
+    constexpr int NW = BLOCK / 64;
+    const uint32_t wid = threadIdx.x / 64;
+    uint32_t* const s = s2 + par * NW;
+    par ^= 1;
+    const uint32_t inc = wave_inclusive_scan(cnt);
+    if (lane_id() == 63) s[wid] = inc;
+    lds_sync();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll 4
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t v = s[i];
+        if ((uint32_t)i < wid) pre += v;
+        tot += v;
+    }
+    const uint32_t first = total + pre + inc - cnt;
+    total += uniform(tot);
+    return first;
+}
 
 // Thresholding step on one WG's own histogram: NB bins held as NC LDS
 // copies of stride STRIDE words.  Owner threads take NB / OWNERS bins each,
 // in descending bin order across threads, so one block scan over the
 // owners' sums locates the bin b that holds the element of rank `need`
-// (1-based, from the top).  Returns b, the count above b and the count in b.
+// (1-based, from the top).  Returns b, the count above b and the count in b
+// (0, 0, 0 when there are fewer elements: an error unless !STRICT).
 template <int BLOCK, int NB, int NC, int STRIDE, bool STRICT = true>
-__device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_sub, uint32_t need, uint32_t* scan,
-                                             uint32_t* sel, uint32_t* status, uint32_t& b_out, uint32_t& above_out,
+__device__ __forceinline__ void local_select(const uint32_t* h, uint32_t need, uint32_t* scan, uint32_t* sel,
+                                             uint32_t* status, uint32_t& b_out, uint32_t& above_out,
                                              uint32_t& hb_out) {
     constexpr int OWNERS = NB < BLOCK ? NB : BLOCK;
     constexpr int OWN = NB / OWNERS;
@@ -322,15 +241,15 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
         const int bin = NB - 1 - (t * OWN + i);
         uint32_t c = 0;
         if (owner) {
-#pragma unroll
+#pragma unroll 4
             for (int q = 0; q < NC; ++q) c += h[q * STRIDE + bin];
-            if (bin == 0) c -= bin0_sub;
         }
         cnt[i] = c;
         tot += c;
     }
     if (t == 0) sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
-    uint32_t above = block_exclusive_scan<OWNERS>(tot, scan);
+    uint32_t tot_all;
+    uint32_t above = block_scan_total<BLOCK>(owner ? tot : 0u, scan, tot_all);
     if (owner && above < need && need <= above + tot) {
 #pragma unroll
         for (int i = 0; i < OWN; ++i) {
@@ -345,7 +264,7 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
     lds_sync();
     uint32_t b = uniform(sel[0]), ab = uniform(sel[1]), hb = uniform(sel[2]);
     lds_sync();
-    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need` (an error unless !STRICT)
+    if (hb == 0xFFFFFFFFu) {
         if (STRICT && t == 0) raise_flag(status, kFlagCapacity);
         b = 0; ab = 0; hb = 0;
     }
@@ -354,216 +273,414 @@ __device__ __forceinline__ void local_select(const uint32_t* h, uint32_t bin0_su
     hb_out = hb;
 }
 
-// On-chip finish of the final bucket: the m composites in cand all match
-// the prefix pf (rounds done: < r0); `need` of them remain to be selected,
-// at output positions W..W+need-1.  More digit rounds in LDS while more
-// than kSmall match, then an exact rank of the rest.  Uses the scratch
-// `hist` (kCopies x 257 words), `small`, `scan`, `sel` and the counter
-// `ctr`.  Every thread of the WG calls it.
-template <int BLOCK>
-__device__ __forceinline__ void finish_bucket(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W, Prefix pf, int r0,
-                              int F, int idx_bits, bool cleared, uint32_t* hist, uint64_t* small, uint32_t* scan,
-                              uint32_t* sel, uint32_t* ctr, int32_t* out, uint32_t* okey, int k,
-                              uint32_t* status) {
-    const int tid = threadIdx.x;
-    const int nrounds = num_rounds(idx_bits);
-    auto c_match = [&](uint64_t c) { return pf.match((uint32_t)(c >> 32), (uint32_t)c); };
-    auto c_digit = [&](uint64_t c, int r) -> uint32_t {
-        const int s = digit_shift(F, r, idx_bits);
-        return ((r < 4 ? (uint32_t)(c >> 32) : (uint32_t)c) >> s) & digit_mask(F, r);
-    };
-    // f(entry) for every candidate, four LDS loads in flight per thread
-    // (entries past m read as 0, which matches no prefix)
-    auto for_each_cand = [&](auto&& f) {
-        for (uint32_t i0 = 0; i0 < m; i0 += 4u * BLOCK) {
-            uint64_t c[4];
+// Wave 0 locates, in an NC-copy 256-bin histogram (copy stride kStride
+// words, 16-byte aligned), the bin b holding the element of rank `need`
+// (1-based, from the top bin down) and writes b, the count above b and the
+// count in b to sel[0..2] (0, 0, 0 when the histogram holds fewer
+// elements).  Lane l owns bins 255 - 4l .. 252 - 4l (descending across
+// lanes), four consecutive words that it reads from every copy with one
+// 16-byte load (eight copies' loads in flight together); one wave scan over
+// the lanes' sums.  Only wave 0 calls it; the caller syncs before sel is read.
+template <int NC>
+__device__ __forceinline__ void wave_select256(const uint32_t* h, uint32_t need, uint32_t* sel) {
+    const uint32_t l = lane_id();
+    const uint32_t top = 255u - 4u * l;
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;  // bins top, top-1, top-2, top-3
+    constexpr int QB = NC < 8 ? NC : 8;        // copies read per batch (registers)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                c[u] = i < m ? cand[i] : 0ull;
-            }
+    for (int q0 = 0; q0 < NC; q0 += QB) {
+        uint4 v[QB];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) f(c[u]);
+        for (int q = 0; q < QB; ++q) v[q] = *reinterpret_cast<const uint4*>(h + (q0 + q) * kStride + (top - 3u));
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            c0 += v[q].w;
+            c1 += v[q].z;
+            c2 += v[q].y;
+            c3 += v[q].x;
         }
-    };
-    int r = r0;
-    uint32_t mb = m;        // entries still matching the prefix
-    bool in_small = false;  // they are already gathered in small[0 .. ctr[1])
-    while (mb > (uint32_t)kSmall && r < nrounds) {
-        if (!cleared) {
-            uint4* const h4 = reinterpret_cast<uint4*>(hist);
-            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-            if (tid < 2) ctr[tid] = 0u;
-            lds_sync();
-        }
-        cleared = false;
-        uint32_t* const hc = hist + (tid % kCopies) * 257;
-        for_each_cand([&](uint64_t c) {
-            if (c_match(c)) atomicAdd(&hc[c_digit(c, r)], 1u);
-        });
-        lds_sync();
-        uint32_t b, above, nb;
-        local_select<BLOCK, 256, kCopies, 257>(hist, 0u, need, scan, sel, status, b, above, nb);
-        const uint32_t need2 = need - above;
-        const bool all = nb == need2;
-        const bool gather = !all && nb <= (uint32_t)kSmall;
-        // winners of this round (digit above b), and the bin itself when
-        // taken whole; a small enough bin is gathered for the exact rank
-        for_each_cand([&](uint64_t c) {
-            const uint32_t d = c_digit(c, r);
-            if (!c_match(c)) return;
-            if (d > b || (all && d == b)) {
-                const uint32_t pos = W + atomicAdd(&ctr[0], 1u);
-                if (pos < (uint32_t)k) {
-                    out[pos] = (int32_t)~(uint32_t)c;
-                    if (okey) okey[pos] = (uint32_t)(c >> 32);
-                } else {
-                    raise_flag(status, kFlagCapacity);
+    }
+    const uint32_t t = c0 + c1 + c2 + c3;
+    const uint32_t inc = wave_inclusive_scan(t);
+    const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    uint32_t ex = inc - t;
+    if (ex < need && need <= inc) {
+        uint32_t b = top, c = c0;
+        if (need > ex + c0) {
+            ex += c0;
+            b = top - 1u;
+            c = c1;
+            if (need > ex + c1) {
+                ex += c1;
+                b = top - 2u;
+                c = c2;
+                if (need > ex + c2) {
+                    ex += c2;
+                    b = top - 3u;
+                    c = c3;
                 }
-            } else if (gather && d == b) {
-                const uint32_t pos = atomicAdd(&ctr[1], 1u);
-                if (pos < (uint32_t)kSmall) small[pos] = c;
             }
-        });
-        need = need2;
-        W += above;
-        pf.add(F, r, b, idx_bits);
-        mb = nb;
-        ++r;
-        lds_sync();
-        if (all) return;
-        in_small = gather;
+        }
+        sel[0] = b;
+        sel[1] = ex;
+        sel[2] = c;
     }
-    if (!in_small) {
-        // the few candidates still matching, gathered
-        if (tid == 1) ctr[1] = 0u;
-        lds_sync();
-        for_each_cand([&](uint64_t c) {
-            if (c_match(c)) {
-                const uint32_t pos = atomicAdd(&ctr[1], 1u);
-                if (pos < (uint32_t)kSmall) small[pos] = c;
-            }
-        });
-        lds_sync();
-    }
-    uint32_t ms = uniform(ctr[1]);
-    if (ms > (uint32_t)kSmall) {
-        if (tid == 0) raise_flag(status, kFlagCapacity);
-        ms = kSmall;
-    }
-    // exact rank by comparison, P lanes per candidate (each compares a
-    // strided share, then the lanes add up their counts)
-    uint32_t P = 1;
-    while (P < 64u && 2u * P * ms <= (uint32_t)BLOCK) P *= 2u;
-    const uint32_t i = (uint32_t)tid / P, q = (uint32_t)tid % P;
-    const uint64_t c = i < ms ? small[i] : 0ull;
-    uint32_t rank = 0;
-    if (i < ms) {
-        for (uint32_t j = q; j < ms; j += P) rank += small[j] > c;
-    }
-    for (uint32_t sft = 32u; sft >= 1u; sft >>= 1) {
-        if (sft < P) rank += (uint32_t)__shfl_xor((int)rank, (int)sft);
-    }
-    if (i < ms && q == 0u && rank < need && W + rank < (uint32_t)k) {
-        out[W + rank] = (int32_t)~(uint32_t)c;
-        if (okey) okey[W + rank] = (uint32_t)(c >> 32);
+    if (all < need && l == 0) {
+        sel[0] = 0u;
+        sel[1] = 0u;
+        sel[2] = 0u;
     }
 }
 
-// Thresholding step for round r from the LDS histogram copies (the first
-// 256 threads own one bin each, thread t the bin 255 - t, so thread order is
-// descending bin order).  With G > 1 the counts are merged across the row's
-// WGs first.  Finds the bin b holding the element of rank `need` (1-based,
-// from the top) and sets the position counters of the bins at and above b:
-// winners of bin j > b go to W + (count above j) + (this WG's range in j);
-// the bucket bin b goes to the output the same way when it is taken whole
-// (`need` == count in b after the elements above), else to positions
-// (this WG's range in b) of the candidate buffer.
-template <int BLOCK>
-__device__ __forceinline__ void threshold(Smem<BLOCK>& sm, int r, int mslot, bool strict, uint32_t bin0_sub,
-                                          uint32_t need, uint32_t W, RowWorkspace* ws, int p, int C, int w, int G,
-                                          uint32_t* status, uint32_t& b_out, uint32_t& above_out, uint32_t& hb_out) {
-    const int t = threadIdx.x;
-    const bool owner = t < 256;
-    const int j = 255 - t;
-    uint32_t tot = 0, pre = 0;
-    if (owner) {
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int c = 0; c < kCopies; ++c) cnt += sm.hist[c * 257 + j];
-        if (j == 0) cnt -= bin0_sub;
-        if (G > 1) {
-            uint64_t* h = &ws->hist[p][mslot][0][0];
-            const int mc = w % C;
-            const uint64_t old = add_dev(&h[mc * 256 + j], (uint64_t)((1ull << 32) | cnt));
-            // poll the copies (all loads in flight together) until every
-            // WG of the row has added
-            uint64_t v0, v1, v2, v3;
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            for (;;) {
-                v0 = ld_dev(&h[j]);
-                v1 = C > 1 ? ld_dev(&h[256 + j]) : 0ull;
-                v2 = C > 2 ? ld_dev(&h[512 + j]) : 0ull;
-                v3 = C > 3 ? ld_dev(&h[768 + j]) : 0ull;
-                const uint32_t arr = (uint32_t)(v0 >> 32) + (uint32_t)(v1 >> 32) + (uint32_t)(v2 >> 32) +
-                                     (uint32_t)(v3 >> 32);
-                if (arr >= (uint32_t)G) break;
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-                    raise_flag(status, kFlagTimeout);
-                    break;
-                }
-                // many WGs: back off between polls, which otherwise crowd
-                // the channel that holds the counts (measured)
-                if (G > 64) __builtin_amdgcn_s_sleep(2);
-            }
-            tot = (uint32_t)v0 + (uint32_t)v1 + (uint32_t)v2 + (uint32_t)v3;
-            pre = (uint32_t)old + (mc > 0 ? (uint32_t)v0 : 0u) + (mc > 1 ? (uint32_t)v1 : 0u) +
-                  (mc > 2 ? (uint32_t)v2 : 0u);
-        } else {
-            tot = cnt;
-        }
-    }
-    if (t == 0) sm.sel[2] = 0xFFFFFFFFu;  // "not found" until an owner writes
-    const uint32_t excl = block_exclusive_scan<256>(owner ? tot : 0u, sm.scan);
-    if (owner && excl < need && need <= excl + tot) {
-        sm.sel[0] = (uint32_t)j;
-        sm.sel[1] = excl;
-        sm.sel[2] = tot;
-    }
-    lds_sync();
-    uint32_t b = uniform(sm.sel[0]), above = uniform(sm.sel[1]), hb = uniform(sm.sel[2]);
-    if (hb == 0xFFFFFFFFu) {  // fewer elements than `need`: an error unless !strict
-        if (strict && t == 0) raise_flag(status, kFlagCapacity);
-        b_out = 0;
-        above_out = 0;
-        hb_out = strict ? 0u : 0xFFFFFFFFu;
-        lds_sync();
-        return;
-    }
-    if (owner && (uint32_t)j >= b) {
-        const bool whole = (uint32_t)j > b || hb == need - above;
-        sm.pos[r * 256 + j] = whole ? W + excl + pre : pre;
-    }
-    lds_sync();
-    b_out = b;
-    above_out = above;
-    hb_out = hb;
+__device__ __forceinline__ void clear_words(uint32_t* p, int nwords, int tid, int nthreads) {
+    uint4* const p4 = reinterpret_cast<uint4*>(p);
+    for (int i = tid; i < nwords / 4; i += nthreads) p4[i] = uint4{0u, 0u, 0u, 0u};
+    if (tid < nwords % 4) p[nwords / 4 * 4 + tid] = 0u;
 }
 
-// ----------------------------------------------------------------- the kernel
+// Write output slot `pos` of a row from composite c (and its key when the
+// keys are recorded for the ordered output).
+// (positions past k are dropped: the selection checks its counts instead)
+__device__ __forceinline__ void put_out(int32_t* out, uint32_t* okey, uint32_t pos, uint64_t c, int k,
+                                        uint32_t*) {
+    if (pos < (uint32_t)k) {
+        out[pos] = (int32_t)~(uint32_t)c;
+        if (okey) okey[pos] = (uint32_t)(c >> 32);
+    }
+}
+
+// ----------------------------------------------------------------- on-chip selection
 //
-// BLOCK threads per WG; ITEMS logits per thread per tile; RESIDENT: the
-// slice is one tile kept in VGPRs across passes (else re-read every pass);
-// KEYS: the keys of the output are recorded (ordered output); WIN: rows of
-// kWinLength or more take the sampled window round.
+// Bin of a candidate in the first round of select_buffer: a window of 256
+// bins of 2^16 keys each from the bound lo (every candidate's key is at
+// least lo); the top bin also takes every key above the window.
+__device__ __forceinline__ uint32_t window_bin(uint64_t c, uint32_t lo) {
+    const uint32_t d = ((uint32_t)(c >> 32) - lo) >> 16;
+    return d < 255u ? d : 255u;
+}
 
-template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS, bool WIN>
-__global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
+// The `need` largest of the m distinct composites cand[0 .. m), whose keys
+// are all at least lo, go to out[W .. W + need) (the thresholding and
+// collection steps of section 02, on chip).  The entries stay where they
+// are; each round narrows the range [mn, mx] of composites still undecided.
+// The first round bins the keys in a window from lo (window_bin; its
+// histogram may have been built while the buffer was filled: `prebuilt`),
+// later rounds split the range into 256 bins of (c - mn) >> s.  Each round
+// locates the bin b holding rank `need` (wave 0), then the entries above b
+// go to the output at their rank among them in buffer order (count, one
+// block scan, place).  Once b holds at most kSmall entries they are
+// gathered (in any order) and ranked exactly.  Every position follows from
+// the buffer's order and the values alone, so the output order is
+// determined by them.  The loops are rolled: the cost of a pass is the
+// instructions its waves issue, so it scales with the entries.  Uses hist
+// (kCopies x kStride words; zero on entry unless prebuilt), small (kSmall
+// entries), scan and sel.  Every thread of the WG calls it, after a barrier
+// that follows the buffer's (and the histogram's) last write.
+template <int BLOCK>
+__device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, uint32_t need, uint32_t W,
+                                              uint32_t lo, bool prebuilt, uint32_t* hist, uint64_t* small,
+                                              uint32_t* scan, uint32_t* sel, int32_t* out, uint32_t* okey, int k,
+                                              uint32_t* status) {
+    const int tid = threadIdx.x;
+    uint32_t ms = 0;  // entries gathered in small
+    uint64_t mn = (uint64_t)lo << 32, mx = ~0ull;
+    for (int round = 0;; ++round) {
+        const uint64_t range = mx - mn;
+        const int q = range ? 64 - __builtin_clzll(range) : 0;
+        const int s = q > 8 ? q - 8 : 0;
+        if (round > 0 || !prebuilt) {
+            if (round > 0) {
+                clear_words(hist, kCopies * kStride, tid, BLOCK);
+                lds_sync();
+            }
+            uint32_t* const hc = hist + (tid % kCopies) * kStride;
+#pragma unroll 2
+            for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
+                const uint64_t c = cand[i];
+                uint32_t bin;
+                if (round == 0) {
+                    bin = window_bin(c, lo);
+                } else {
+                    const uint64_t d = c - mn;  // wraps above the range when c < mn
+                    bin = d <= range ? (uint32_t)(d >> s) : 256u;  // 256: spare slot
+                }
+                atomicAdd(&hc[bin], 1u);
+            }
+        }
+        lds_sync();
+        if (tid < 64) wave_select256<kCopies>(hist, need, sel);
+        lds_sync();
+        const uint32_t b = uniform(sel[0]), above = uniform(sel[1]), hb = uniform(sel[2]);
+        if (hb == 0u) {
+            if (tid == 0) raise_flag(status, kFlagCapacity);
+            return;
+        }
+        uint64_t blo, bhi;  // composites of bin b
+        if (round == 0) {
+            blo = ((uint64_t)lo + ((uint64_t)b << 16)) << 32;
+            bhi = b < 255u ? blo + ((1ull << 48) - 1u) : ~0ull;
+        } else {
+            blo = mn + ((uint64_t)b << s);
+            const uint64_t width = ((uint64_t)1 << s) - 1u;
+            bhi = mx - blo > width ? blo + width : mx;
+        }
+        const bool all = hb == need - above;        // the bin is taken whole
+        const bool last = all || hb <= (uint32_t)kSmall;
+        const bool gath = last & !all;              // the bin is gathered for the exact rank
+        // winners of this round: in (bhi, mx] (none when bhi == mx, and then
+        // bhi + 1 wraps); with `all` also the bin
+        const uint64_t wlo = all ? blo : bhi + 1u;
+        const bool any = all || bhi < mx;
+        // count winners (high half) and gathered entries (low half), one
+        // block scan numbers both in buffer order, then place them
+        uint32_t cnt = 0;
+        if (any | gath) {
+#pragma unroll 2
+            for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
+                const uint64_t c = cand[i];
+                cnt += ((any & (c >= wlo) & (c <= mx)) ? (1u << 16) : 0u) + ((gath & (c >= blo) & (c <= bhi)) ? 1u : 0u);
+            }
+        }
+        uint32_t tot;
+        const uint32_t pos = block_scan_total<BLOCK>(cnt, scan, tot);
+        uint32_t p = W + (pos >> 16), g = pos & 0xFFFFu;
+        if (any | gath) {
+#pragma unroll 2
+            for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
+                const uint64_t c = cand[i];
+                if (any & (c >= wlo) & (c <= mx)) {
+                    put_out(out, okey, p++, c, k, status);
+                } else if (gath & (c >= blo) & (c <= bhi)) {
+                    if (g < (uint32_t)kSmall) small[g] = c;
+                    ++g;
+                }
+            }
+        }
+        tot >>= 16;
+        if (tot != (all ? need : above)) {
+            if (tid == 0) raise_flag(status, kFlagCapacity);
+            return;
+        }
+        if (all) return;
+        W += above;
+        need -= above;
+        mn = blo;
+        mx = bhi;
+        if (last) {
+            ms = hb;
+            break;
+        }
+        lds_sync();  // the histogram is cleared next
+    }
+    // exact rank of the gathered few: P lanes per candidate (as many as the
+    // block holds, at most 64), each comparing a strided share four at a
+    // time, their counts added by lane shuffles
+    lds_sync();
+    uint32_t P = 1;
+    while (P < 64u && 2u * P * ms <= 2u * (uint32_t)BLOCK) P *= 2u;
+    for (uint32_t i0 = 0; i0 < ms; i0 += (uint32_t)BLOCK / P) {
+        const uint32_t i = i0 + (uint32_t)tid / P, qq = (uint32_t)tid % P;
+        if (i0 + (uint32_t)(tid & ~63) / P >= ms) break;  // whole waves past the end
+        const uint64_t c = i < ms ? small[i] : ~0ull;
+        uint32_t rank = 0;
+        uint32_t j = qq;
+        for (; j + 3u * P < ms; j += 4u * P)
+            rank += (uint32_t)(small[j] > c) + (uint32_t)(small[j + P] > c) + (uint32_t)(small[j + 2u * P] > c) +
+                    (uint32_t)(small[j + 3u * P] > c);
+        for (; j < ms; j += P) rank += small[j] > c;
+        for (uint32_t sft = 32u; sft >= 1u; sft >>= 1) {
+            if (sft < P) rank += (uint32_t)__shfl_xor((int)rank, (int)sft);
+        }
+        if (i < ms && qq == 0u && rank < need) put_out(out, okey, W + rank, c, k, status);
+    }
+}
+
+// Exact selection of a row by passes over it in global memory (one WG): the
+// rare case where the candidates of a bound do not fit on chip or the bound
+// overshot.  Each pass histograms the composites inside the current range
+// (4096 bins the first time, 256 later) and keeps the bin holding the k-th
+// largest, until it holds at most `cap`; a last pass sends the composites
+// above the range to the output and the range's to the buffer, in a fixed
+// order (block scans), and select_buffer finishes.  Passes are rolled loops
+// of U chunks per lane (small code beside the hot paths).
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void select_by_passes(const char* base, int off, int L, int nchunks, int k, int32_t* out,
+                                                 uint32_t* okey, uint64_t* cand, uint32_t* hist, uint64_t* small,
+                                                 uint32_t* scan, uint32_t* sel, uint32_t* status) {
+    constexpr int cap = CAP;
+    constexpr int U = 2;
+    const int tid = threadIdx.x;
+    auto reread = [&](auto&& f) {
+#pragma unroll 1
+        for (int c0 = 0; c0 < nchunks; c0 += U * BLOCK) {
+            u32x4_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * BLOCK + tid;
+                v[u] = *reinterpret_cast<const u32x4_t*>(base + (size_t)(c < nchunks ? c : 0) * 16u);
+            }
+            uint32_t kk[4 * U], ii[4 * U];  // keys (0: empty slot) and indices
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * BLOCK + tid;
+                const int e0 = 4 * c - off;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                    kk[4 * u + e] = ok ? key_of(__uint_as_float(v[u][e])) : 0u;
+                    ii[4 * u + e] = (uint32_t)(e0 + e);
+                }
+            }
+            f(kk, ii);
+        }
+    };
+    uint64_t mn = 0, mx = ~0ull;
+    uint32_t need = (uint32_t)k, W = 0, hb = 0;
+    for (int pass = 0;; ++pass) {
+        // once the range holds one key, only the valid indices' part of it
+        if ((mn >> 32) == (mx >> 32)) {
+            const uint64_t lo_i = (mn & 0xFFFFFFFF00000000ull) | (uint64_t)(0u - (uint32_t)L);
+            if (mn < lo_i) mn = lo_i;
+        }
+        const bool first = pass == 0;
+        const int nbits = first ? 12 : 8;
+        const uint64_t range = mx - mn;
+        const int q = range ? 64 - __builtin_clzll(range) : 0;
+        const int s = q > nbits ? q - nbits : 0;
+        clear_words(hist, kCopies * kStride, tid, BLOCK);
+        lds_sync();
+        uint32_t* const hc = first ? hist : hist + (tid % kCopies) * kStride;
+        const uint64_t lo = mn, hi = mx;
+        reread([&](const uint32_t* kk, const uint32_t* ii) {
+#pragma unroll
+            for (int i = 0; i < 4 * U; ++i) {
+                const uint64_t c = composite(kk[i], ii[i]);
+                if ((kk[i] != 0u) & (c >= lo) & (c <= hi)) atomicAdd(&hc[(uint32_t)((c - lo) >> s)], 1u);
+            }
+        });
+        lds_sync();
+        uint32_t b, above, hbin;
+        if (first) local_select<BLOCK, 4096, 1, 4096>(hist, need, scan, sel, status, b, above, hbin);
+        else local_select<BLOCK, 256, kCopies, kStride>(hist, need, scan, sel, status, b, above, hbin);
+        need -= above;
+        W += above;
+        hb = hbin;
+        mn += (uint64_t)b << s;
+        const uint64_t width = ((uint64_t)1 << s) - 1u;
+        if (mx - mn > width) mx = mn + width;
+        if (hb <= (uint32_t)cap || s == 0 || hb == 0u) break;
+    }
+    // collection: above the range to the output, the range to the buffer (or
+    // to the output when it is taken whole)
+    const bool all = hb == need;
+    const uint64_t lo = mn, hi = mx;
+    uint32_t n1 = 0, n2 = 0;
+    reread([&](const uint32_t* kk, const uint32_t* ii) {
+        uint32_t cnt = 0, kinds = 0;
+#pragma unroll
+        for (int i = 0; i < 4 * U; ++i) {
+            const uint64_t c = composite(kk[i], ii[i]);
+            const uint32_t kd = kk[i] == 0u ? 0u : (c > hi ? 1u : (c >= lo ? 2u : 0u));
+            kinds |= kd << (2 * i);
+            cnt += kd == 1u ? (1u << 16) : (kd == 2u ? 1u : 0u);
+        }
+        uint32_t tot;
+        const uint32_t pos = block_scan_total<BLOCK>(cnt, scan, tot);
+        uint32_t p1 = n1 + (pos >> 16), p2 = n2 + (pos & 0xFFFFu);
+#pragma unroll
+        for (int i = 0; i < 4 * U; ++i) {
+            const uint32_t kd = (kinds >> (2 * i)) & 3u;
+            if (kd == 0u) continue;
+            const uint64_t c = composite(kk[i], ii[i]);
+            if (kd == 1u) {
+                if (p1 < W) put_out(out, okey, p1, c, k, status);
+                else raise_flag(status, kFlagCapacity);
+                ++p1;
+            } else {
+                if (all) put_out(out, okey, W + p2, c, k, status);
+                else if (p2 < (uint32_t)cap) cand[p2] = c;
+                else raise_flag(status, kFlagCapacity);
+                ++p2;
+            }
+        }
+        n1 += tot >> 16;
+        n2 += tot & 0xFFFFu;
+    });
+    if (all || hb == 0u) return;
+    clear_words(hist, kCopies * kStride, tid, BLOCK);
+    lds_sync();
+    // the bucket's keys all lie in [mn >> 32, mx >> 32]; its lowest key is the window's origin
+    select_buffer<BLOCK>(cand, hb < (uint32_t)cap ? hb : (uint32_t)cap, need, W, (uint32_t)(mn >> 32), false, hist,
+                         small, scan, sel, out, okey, k, status);
+}
+
+// The 16-bit key prefix of the element of rank r (1-based, from the top)
+// among the keys the WG's threads hold (NK each, 0 = empty): its top byte
+// from a 256-bin histogram, then its second byte from a histogram of the
+// keys in that bin (h1 and h2: kCopies x kStride words each, zero on entry,
+// behind a barrier; h1 is zero again on return).  At least 1, so that the
+// bound never admits empty slots.
+template <int BLOCK, int NK>
+__device__ __forceinline__ uint32_t bound_select(const uint32_t (&ks)[NK], uint32_t r, uint32_t* h1, uint32_t* h2, uint32_t* sel) {
+    const int tid = threadIdx.x;
+    uint32_t* const hc1 = h1 + (tid % kCopies) * kStride;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) atomicAdd(&hc1[ks[i] != 0u ? ks[i] >> 24 : 256u], 1u);  // 256: spare slot
+    lds_sync();
+    if (tid < 64) wave_select256<kCopies>(h1, r, sel);
+    lds_sync();
+    const uint32_t b1 = uniform(sel[0]), a1 = uniform(sel[1]), n1 = uniform(sel[2]);
+    clear_words(h1, kCopies * kStride, tid, BLOCK);  // left zero for the caller (ordered by the next barrier)
+    if (n1 == 0u) {
+        lds_sync();
+        return 1u;
+    }
+    uint32_t* const hc2 = h2 + (tid % kCopies) * kStride;
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+        if ((ks[i] != 0u) & ((ks[i] >> 24) == b1)) atomicAdd(&hc2[(ks[i] >> 16) & 0xFFu], 1u);
+    lds_sync();
+    if (tid < 64) wave_select256<kCopies>(h2, r - a1, sel);
+    lds_sync();
+    const uint32_t b2 = uniform(sel[0]);
+    const uint32_t lo = (b1 << 24) | (b2 << 16);
+    return lo > 1u ? lo : 1u;
+}
+
+// ----------------------------------------------------------------- split kernel (few rows)
+//
+// BLOCK threads per WG, ITEMS logits per thread per tile; RESIDENT: the
+// slice is one tile (loaded once, up front); KEYS: the keys of the output
+// are recorded (ordered output); SPT: chunks of the row's sample per thread.  G WGs per row; a row of L valid logits
+// uses the first ceil(chunks / chunks_per_wg) of them, and the last of those
+// finishes the row.
+
+template <int BLOCK>
+struct SplitSmem {
+    alignas(16) uint32_t hist[kCopies * kStride];  // 256-bin histograms, kCopies copies
+    alignas(16) uint64_t cand[kBufCap];       // candidates (finishing WG); the bound's second histogram before
+    uint64_t small[kSmall];                   // the last few, ranked exactly
+    uint32_t cnt[kMaxSplit];                  // the other WGs' candidate counts (finishing WG)
+    uint32_t pre[kMaxSplit];                  // their exclusive prefix
+    uint32_t prex[kMaxSplit];                 // exclusive prefix of the counts past the speculative reads
+    uint32_t scan[BLOCK / 64];
+    uint32_t scan2[2][BLOCK / 64];
+    uint32_t sel[4];
+    uint32_t tot[2];  // the others' candidates; those past the speculative reads
+    uint32_t tag;
+    uint32_t bad;
+};
+
+template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS, int SPT>
+__global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
-    static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "one bin per thread in the 256-bin rounds");
+    static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "whole waves, 256 histogram owners");
+    static_assert(kCopies * kStride * 4 <= kBufCap * 8, "the bound's second histogram fits in the buffer");
     constexpr int CHUNKS = ITEMS / 4;            // chunks per thread per tile
     constexpr int TILE_CHUNKS = BLOCK * CHUNKS;  // chunks per tile
-    __shared__ Smem<BLOCK> sm;
+    // SPT: sample chunks per thread (the host keeps the sample within it)
+    static_assert(SPT >= 1 && SPT * BLOCK <= kSampleMax, "sample fits the block");
+    __shared__ SplitSmem<BLOCK> sm;
 
     const int tid = threadIdx.x;
     const int G = P.G;
@@ -573,424 +690,357 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
     const int k = P.k;
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
-    uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;  // recorded keys (ordered output)
-    int L = n;
-    if (P.lengths) {
-        L = P.lengths[row];
-        L = L < 0 ? 0 : (L > n ? n : L);
-    }
+    uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;
+    const int L = valid_length(P.lengths, row, n);
     if (L <= k) {  // everything valid is selected; pad with -1
         if (w == 0)
             for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
         return;
     }
-
     const int off = (int)(((uintptr_t)prow >> 2) & 3);  // elements before the first 16-byte boundary
     const int nchunks = (off + L + 3) >> 2;
-    const int Geff = min(G, (nchunks + P.chunks_per_wg - 1) / P.chunks_per_wg);  // WGs with a non-empty slice
+    const int cpw = P.chunks_per_wg;
+    const int Geff = (nchunks + cpw - 1) / cpw;  // WGs with a non-empty slice
     if (w >= Geff) return;
     const bool multi = Geff > 1;
-    RowWorkspace* const ws = multi ? P.ws + row : nullptr;
-    const int p = multi ? (int)(ld_dev(&ws->parity) & 1u) : 0;
-    // what the previous launch left to clear (read by the finishing WG now,
-    // off the critical path at the end)
-    const uint32_t used0 = (multi && w == 0) ? ld_dev(&ws->used[0]) : 0u;
-    const uint32_t used1 = (multi && w == 0) ? ld_dev(&ws->used[1]) : 0u;
-    const int C = P.mcopies;
-    const int idx_bits = P.idx_bits;
-    const int nrounds = num_rounds(idx_bits);
-
-    const int c_begin = w * P.chunks_per_wg;
-    const int c_end = min(nchunks, c_begin + P.chunks_per_wg);
-    // chunks whose four elements are all valid
-    const int cf_lo = max(c_begin, off ? 1 : 0);
-    const int cf_hi = min(c_end, (L + off) >> 2);
-    // slots of the slice that hold no element (key 0): the first-round
-    // histogram counts them in bin 0 and subtracts them after
-    const int valid = max(0, min(L, 4 * c_end - off) - max(0, 4 * c_begin - off));
-    const uint32_t n_empty = (uint32_t)(4 * (c_end - c_begin) - valid);
-
-    uint32_t keys[ITEMS];
+    const bool fin = w == Geff - 1;  // the finishing WG: every WG it waits for was dispatched before it
     const char* const base = reinterpret_cast<const char*>(prow - off);  // 16-byte aligned
+    const int c_begin = w * cpw;
+    const int c_end = min(nchunks, c_begin + cpw);
+    const int cf_lo = off ? 1 : 0;      // chunks whose four elements are all valid: [cf_lo, cf_hi)
+    const int cf_hi = (L + off) >> 2;
+    SplitRow* const rw = multi ? P.rws + row : nullptr;
+    const size_t R = (size_t)P.region;
 
-    // Load one tile: chunk c of the row is the aligned 16-byte block holding
-    // elements [4c - off, 4c - off + 4).  A chunk with at least one valid
-    // element is read whole; lanes past the slice re-read chunk 0 (valid:
-    // L > k >= 1) and hold empty slots.  All loads are issued before any is
-    // used.
+    // keys of chunk c from its 16 bytes (0 for slots outside the row)
+    auto chunk_keys = [&](int c, const uint4& v, uint32_t* kk) {
+        const uint32_t raw[4] = {v.x, v.y, v.z, v.w};
+        if (c >= cf_lo && c < cf_hi) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kk[e] = key_of(__uint_as_float(raw[e]));
+        } else {
+            const int e0 = 4 * c - off;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = (c >= 0) & (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
+                kk[e] = ok ? key_of(__uint_as_float(raw[e])) : 0u;
+            }
+        }
+    };
+    uint32_t keys[ITEMS];
+    uint4 traw[CHUNKS];
+    // one tile: chunk c = c_tile + j * BLOCK + tid of the slice, loaded raw
+    // (lanes past the slice re-read chunk 0), then turned into keys (those
+    // lanes hold empty slots)
     auto load_tile = [&](int c_tile) {
 #pragma unroll
         for (int j = 0; j < CHUNKS; ++j) {
             const int c = c_tile + j * BLOCK + tid;
-            const uint32_t byte_off = (uint32_t)(c < c_end ? c : 0) * 16u;
-            const uint4 v = *reinterpret_cast<const uint4*>(base + byte_off);
-            keys[4 * j + 0] = v.x;
-            keys[4 * j + 1] = v.y;
-            keys[4 * j + 2] = v.z;
-            keys[4 * j + 3] = v.w;
+            traw[j] = *reinterpret_cast<const uint4*>(base + (size_t)(c < c_end ? c : 0) * 16u);
         }
+    };
+    auto tile_keys = [&](int c_tile) {
 #pragma unroll
         for (int j = 0; j < CHUNKS; ++j) {
             const int c = c_tile + j * BLOCK + tid;
-            if (c >= cf_lo && c < cf_hi) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) keys[4 * j + e] = key_of(__uint_as_float(keys[4 * j + e]));
-            } else {
-                const int e0 = 4 * c - off;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = (c < c_end) & ((uint32_t)(e0 + e) < (uint32_t)L);
-                    keys[4 * j + e] = ok ? key_of(__uint_as_float(keys[4 * j + e])) : 0u;
-                }
-            }
-        }
-    };
-    // f(key, ~index) for every slot of the slice, tile by tile; element e of
-    // chunk j of a tile has index ibase + 4 * BLOCK * j + e.
-    auto visit = [&](auto&& f) {
-        auto tile = [&](int c_tile) {
-            int ibase = 4 * (c_tile + tid) - off;
-            __asm__ volatile("" : "+v"(ibase));  // indices are recomputed per visit, never kept live
-#pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f(keys[4 * j + e], ~(uint32_t)(ibase + 4 * BLOCK * j + e));
-            }
-        };
-        if constexpr (RESIDENT) {
-            tile(c_begin);
-        } else {
-            for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
-                load_tile(ct);
-                tile(ct);
-            }
-        }
-    };
-    // f(key) for every slot of the chunks in [c_begin, c_end)
-    auto visit_chunks = [&](auto&& f) {
-        auto tile = [&](int c_tile) {
-#pragma unroll
-            for (int j = 0; j < CHUNKS; ++j) {
-                if (c_tile + j * BLOCK + tid < c_end) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) f(keys[4 * j + e]);
-                }
-            }
-        };
-        if constexpr (RESIDENT) {
-            tile(c_begin);
-        } else {
-            for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
-                load_tile(ct);
-                tile(ct);
-            }
-        }
-    };
-    // f(key, ~index) for every slot of the slice, re-read from global
-    // memory in a rolled loop: the rare index-digit rounds use it, so that
-    // their code stays small (at these sizes the code a launch runs costs
-    // instruction fetches)
-    auto visit_global = [&](auto&& f) {
-#pragma unroll 1
-        for (int c = c_begin + tid; c < c_end; c += BLOCK) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (uint32_t)c * 16u);
-            const int e0 = 4 * c - off;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool ok = (uint32_t)(e0 + e) < (uint32_t)L;
-                f(ok ? key_of(__uint_as_float(v[e])) : 0u, ~(uint32_t)(e0 + e));
-            }
-        }
-    };
-    auto opaque_keys = [&]() {
-        if constexpr (RESIDENT) {
-            // stops the optimiser from hoisting per-element values out of
-            // the passes (one VGPR per element and pass)
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) __asm__ volatile("" : "+v"(keys[i]));
+            chunk_keys(c < c_end ? c : -1, traw[j], &keys[4 * j]);
         }
     };
 
-    auto clear_hist = [&]() {  // 16-byte LDS stores
-        uint4* const h4 = reinterpret_cast<uint4*>(sm.hist);
-        for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        if (tid < (kCopies * 257) % 4) sm.hist[kCopies * 257 / 4 * 4 + tid] = 0u;
-    };
-
-    // the window round's sample (the row's first chunks, one per thread) is
-    // loaded together with the slice.  Only long rows (split over many WGs,
-    // where a second merge round is expensive) take the window round: for
-    // shorter rows its extra steps cost more than they save (measured).
-    const bool try_win = WIN && L >= kWinLength;
-    const int nsc = min(nchunks, BLOCK);
-    uint4 sraw = uint4{0u, 0u, 0u, 0u};
-    if (try_win && tid < nsc) sraw = *reinterpret_cast<const uint4*>(base + (uint32_t)tid * 16u);
+    // ---- the bound.  A row that one resident WG holds whole uses its own
+    // keys: the 16-bit prefix of its k-th largest.  Otherwise every WG of
+    // the row reads the same sample, blocks of 16 chunks spread evenly from
+    // the row's first chunk to its last (all of it when the row is no
+    // longer), and takes the prefix of the sample's element of rank
+    // r = m + 5 sqrt(m) + 8, m = k S / L the expected count of the row's k
+    // largest among its S sampled logits: a rank that the sample's count
+    // above the row's k-th largest exceeds with a probability below 1e-6.
+    // The bound is a lower bound on the k-th largest key when it holds; the
+    // finishing WG checks that at least k candidates came out, else the row
+    // is finished by passes over it.
+    const bool own_sample = !multi && RESIDENT;
+    const int Sc = own_sample ? 0 : min(nchunks, P.sample_chunks);
+    const bool whole_sample = nchunks <= P.sample_chunks;
+    uint4 sraw[SPT];
+    int sc[SPT];  // the sampled chunks (-1: none)
+    if (!own_sample) {
+        // block i of nb starts at chunk floor(i * (nchunks - 16) / (nb - 1))
+        // (16.16 fixed point; the last block ends at the last chunk)
+        const int nb = Sc / 16;
+        const uint64_t step = whole_sample ? 0ull : (((uint64_t)(nchunks - 16)) << 16) / (uint64_t)(nb - 1);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int qq = u * BLOCK + tid;
+            const int blk = qq >> 4;
+            const int start = blk == nb - 1 ? nchunks - 16 : (int)(((uint64_t)blk * step) >> 16);
+            sc[u] = qq < Sc ? (whole_sample ? qq : start + (qq & 15)) : -1;
+            sraw[u] = sc[u] >= 0 ? *reinterpret_cast<const uint4*>(base + (size_t)sc[u] * 16u)
+                                 : uint4{0u, 0u, 0u, 0u};
+        }
+    }
     if constexpr (RESIDENT) load_tile(c_begin);
+    // the launch's epoch (tags the published counts), one load per WG,
+    // issued after the logits so that waiting for them does not wait for it
+    uint32_t epoch = 0;
+    if (multi && tid == 0) epoch = ld_dev(&rw->epoch);
+    // while the loads are in flight: the bound's histograms cleared
+    uint32_t* const h2 = reinterpret_cast<uint32_t*>(sm.cand);
+    clear_words(sm.hist, kCopies * kStride, tid, BLOCK);
+    clear_words(h2, kCopies * kStride, tid, BLOCK);
+    if (tid == 0) sm.bad = 0u;
+    lds_sync();
+    if constexpr (RESIDENT) tile_keys(c_begin);
+    uint32_t lo;
+    if (own_sample) {
+        lo = bound_select<BLOCK, ITEMS>(keys, (uint32_t)k, sm.hist, h2, sm.sel);
+    } else {
+        uint32_t sk[4 * SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) chunk_keys(sc[u], sraw[u], &sk[4 * u]);
+        // valid sampled logits: every chunk holds four, save the first and
+        // the last chunk of the row, which the sample always includes
+        const uint32_t S = whole_sample ? (uint32_t)L : (uint32_t)(4 * Sc - 4 * nchunks + L);
+        uint32_t r = (uint32_t)k;
+        if (!whole_sample) {
+            const float mexp = (float)k * (float)S / (float)L;
+            const float rf = ceilf(mexp + 5.0f * sqrtf(mexp) + 8.0f);
+            r = rf >= (float)S ? S : (uint32_t)rf;
+        }
+        lo = bound_select<BLOCK, 4 * SPT>(sk, r, sm.hist, h2, sm.sel);
+    }
+    const uint32_t tag = make_tag(epoch);  // thread 0's
+    if (tid == 0) sm.tag = tag;
 
-    // ---------------- screening rounds over the row
-    Prefix pf{0u, 0u, 0u, 0u};
-    uint32_t need = (uint32_t)k;  // rank still to place, counted inside the current bucket
-    uint32_t W = 0;               // winners placed so far (output positions [0, W))
-    uint32_t hb = 0;              // size of the current bucket
-    int R = 0;                    // last round done
-    bool whole = false;           // the last bucket is taken whole
-    FirstDigit fd{8, false, 0u};  // first-round digit (set by the window round when it succeeds)
-    uint32_t bwin = 0;            // the window round's threshold bin
-    int slot_base = 0;            // merge slot of round 0 of the 8-bit schedule
-
-    // -- window round.  A sample (the row's first chunks, one per thread)
-    // estimates the threshold: the first-digit bin b8 (8 bits) of its
-    // element of rank 1.25 * k * S / L + 64 (the k-th largest of the row is
-    // expected near rank k * S / L).  Then every WG histograms the 12-bit
-    // first digit of its elements at or above LO = b8 << 4 only, in a window
-    // of 256 bins from LO (the top bin also takes all bins above the
-    // window), merged like any round.  When the threshold falls inside the
-    // window below its top bin, the counts it needs are exact and the first
-    // round is done at 12-bit resolution; otherwise the row starts over with
-    // the 8-bit schedule.
-    if (try_win) {
-        uint32_t sk[4];
-        {
-            const uint32_t raw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+    // ---- candidates: the slice's composites at or above the bound, in a
+    // fixed order (tile, thread, slot).  A WG that does not finish writes
+    // them to its region and publishes their number; the finishing WG keeps
+    // its own in LDS.
+    const bool to_region = multi && !fin;
+    uint64_t* const region = to_region ? P.stage + ((size_t)row * (size_t)G + (size_t)w) * R : nullptr;
+    // the finishing WG counts its candidates into the first round's window
+    // histogram as they are placed (sm.hist is zero after the bound)
+    uint32_t* const hc = sm.hist + (tid % kCopies) * kStride;
+    uint32_t total = 0;
+    int par = 0;
+    auto place_tile = [&](int c_tile, uint32_t first) {
+        uint32_t p = first;
+#pragma unroll
+        for (int j = 0; j < CHUNKS; ++j) {
+            const int ib = 4 * (c_tile + j * BLOCK + tid) - off;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ix = 4 * tid - off + e;
-                sk[e] = (tid < nsc && ix >= 0 && ix < L) ? key_of(__uint_as_float(raw[e])) : 0u;
-            }
-        }
-        const uint32_t s_valid = (uint32_t)min(L, 4 * nsc - off);
-        const uint64_t est64 = ((uint64_t)k * s_valid * 5u) / (4u * (uint64_t)L) + 64u;
-        const uint32_t est = (uint32_t)(est64 < s_valid ? est64 : s_valid);
-        uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
-        clear_hist();
-        lds_sync();
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (sk[e] != 0u) atomicAdd(&hc[sk[e] >> 24], 1u);
-        lds_sync();
-        uint32_t b8, ab8, hb8;
-        local_select<BLOCK, 256, kCopies, 257, false>(sm.hist, 0u, est, sm.scan, sm.sel, P.status, b8, ab8, hb8);
-        const uint32_t LO = hb8 ? b8 << 4 : 0u;
-        opaque_keys();
-        clear_hist();
-        lds_sync();
-        visit_chunks([&](uint32_t key) {
-            const uint32_t b12 = key >> 20;
-            if (b12 >= LO) atomicAdd(&hc[min(b12 - LO, 255u)], 1u);
-        });
-        lds_sync();
-        uint32_t b, above, hw;
-        threshold<BLOCK>(sm, 0, 0, false, LO == 0u ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status, b, above,
-                         hw);
-        if (hw != 0xFFFFFFFFu && b < 255u) {
-            fd = FirstDigit{12, true, LO};
-            bwin = b;
-            hb = hw;
-            need -= above;
-            W += above;
-            pf.kpfx = (LO + b) << 20;
-            pf.kmask = 0xFFFu << 20;
-            whole = hb == need;
-        } else {
-            slot_base = 1;
-        }
-    }
-    const int F = fd.F;
-    if (!fd.win || (!whole && hb > (uint32_t)kCap)) {
-        for (int r = fd.win ? 1 : 0;; ++r) {
-            opaque_keys();
-            clear_hist();
-            lds_sync();
-            uint32_t* const hc = sm.hist + (tid % kCopies) * 257;
-            if (r == 0) {
-                // every slot of the slice's chunks adds into its top byte's
-                // bin; the few empty ones (key 0) land in bin 0 and are
-                // subtracted after.  Chunks past the slice are skipped.
-                visit_chunks([&](uint32_t key) { atomicAdd(&hc[key >> 24], 1u); });
-            } else if (r < 4) {
-                const int sh = digit_shift(F, r, idx_bits);
-                const uint32_t dm = digit_mask(F, r);
-                visit([&](uint32_t key, uint32_t) {
-                    if ((key != 0u) & ((key & pf.kmask) == pf.kpfx)) atomicAdd(&hc[(key >> sh) & dm], 1u);
-                });
-            } else {
-                const int sh = digit_shift(F, r, idx_bits);
-                visit_global([&](uint32_t key, uint32_t ni) {
-                    if (pf.match(key, ni)) atomicAdd(&hc[(ni >> sh) & 0xFFu], 1u);
-                });
-            }
-            lds_sync();
-            uint32_t b, above;
-            threshold<BLOCK>(sm, r, r + slot_base, true, r == 0 ? n_empty : 0u, need, W, ws, p, C, w, Geff, P.status,
-                             b, above, hb);
-            need -= above;
-            W += above;
-            pf.add(F, r, b, idx_bits);
-            R = r;
-            if (hb == need) { whole = true; break; }
-            if (hb <= (uint32_t)kCap || r + 1 >= nrounds) break;
-        }
-    }
-    const int last_slot = R + (fd.win ? 0 : slot_base);  // merge slots used: 0 .. last_slot
-
-    // ---------------- collection over the row
-    // Winners go to the output; the bucket goes to the output when taken
-    // whole, else to the candidate buffer (LDS) or the row's stage (G > 1).
-    const bool idx_rounds = R >= 4;
-    uint32_t bslot;  // position counter of the bucket: its bin in round R
-    if (R == 0) {
-        bslot = fd.win ? bwin : pf.kpfx >> 24;
-    } else {
-        const int sft = digit_shift(F, R, idx_bits);
-        bslot = (uint32_t)R * 256u + (((R < 4 ? pf.kpfx : pf.ipfx) >> sft) & digit_mask(F, R));
-    }
-    uint64_t* const gstage = multi ? &ws->stage[p][0] : nullptr;
-    bool overflow = false;
-    opaque_keys();
-    // With many elements per thread, three steps, so that the per-element
-    // work stays a compare: count the
-    // selected elements (winners and bucket) per thread; copy them, in rank
-    // order from a block scan, into a compact LDS list (the histogram
-    // space, in chunks); place the list's entries with all lanes busy.
-    const uint32_t kp = pf.kpfx, km = pf.kmask;
-    // the key prefix has no bits outside its mask, so (key & km) >= kp
-    // is key >= kp; the lower bound 1 also drops empty slots (key 0)
-    const uint32_t kp1 = kp > 1u ? kp : 1u;
-    // place one selected element (a winner or a bucket element); IDX: the
-    // rounds went into the index digits
-    auto place = [&](uint32_t key, uint32_t ni, auto idx) {
-        uint32_t slot = bslot;
-        bool ab;
-        if constexpr (!decltype(idx)::value) {
-            const uint32_t s = key & km;
-            ab = s > kp;
-            if (ab) slot = key_slot(key, s ^ kp, fd, idx_bits);
-        } else {
-            ab = classify(key, ni, pf, fd, idx_bits, &slot) == 1u;
-        }
-        const uint32_t pos = atomicAdd(&sm.pos[slot], 1u);
-        if (ab || whole) {
-            if (pos < (uint32_t)k) {
-                out[pos] = (int32_t)~ni;
-                if (okey) okey[pos] = key;
-            } else {
-                overflow = true;
-            }
-        } else if (pos < (uint32_t)kCap) {
-            const uint64_t e = ((uint64_t)key << 32) | (uint64_t)ni;
-            if (multi) st_dev(&gstage[pos], e);
-            else sm.cand[pos] = e;
-        } else {
-            overflow = true;
-        }
-    };
-    // the key-digit case (index-digit rounds are collected below)
-    auto collect = [&](auto&& selected) {
-    if constexpr (ITEMS <= 8) {
-        // few elements per thread: place them directly
-        visit([&](uint32_t key, uint32_t ni) {
-            if (selected(key, ni)) place(key, ni, std::false_type{});
-        });
-    } else {
-    uint32_t nsel = 0;
-    visit([&](uint32_t key, uint32_t ni) { nsel += selected(key, ni); });
-    uint32_t tot_sel;
-    const uint32_t my_first = block_scan_total<BLOCK>(nsel, sm.scan, tot_sel);
-    uint64_t* const list = reinterpret_cast<uint64_t*>(sm.hist);
-    constexpr uint32_t LISTN = kCopies * 257 / 2;
-    for (uint32_t c0 = 0; c0 < tot_sel; c0 += LISTN) {
-        uint32_t rk = my_first - c0;  // wraps for ranks before the chunk: never < LISTN then
-        opaque_keys();
-        visit([&](uint32_t key, uint32_t ni) {
-            if (selected(key, ni)) {
-                if (rk < LISTN) list[rk] = ((uint64_t)key << 32) | (uint64_t)ni;
-                ++rk;
-            }
-        });
-        lds_sync();
-        const uint32_t nl = min(LISTN, tot_sel - c0);
-        for (uint32_t i = tid; i < nl; i += BLOCK) {
-            const uint64_t e = list[i];
-            place((uint32_t)(e >> 32), (uint32_t)e, std::false_type{});
-        }
-        lds_sync();
-    }
-    }
-    };
-    if (!idx_rounds) {
-        collect([&](uint32_t key, uint32_t) -> bool { return key >= kp1; });
-    } else {
-        // ties beyond the key digits (rare): the slice is re-read
-        visit_global([&](uint32_t key, uint32_t ni) {
-            uint32_t slot;
-            if (classify(key, ni, pf, fd, idx_bits, &slot) != 0u) place(key, ni, std::true_type{});
-        });
-    }
-    if (overflow) raise_flag(P.status, kFlagCapacity);
-
-    if (multi && w != 0) return;  // WG 0 finishes the row
-
-    // ---------------- on-chip finish of the last bucket
-    if (!whole) {
-        uint32_t m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
-        // the finisher's first histogram is cleared while the pull's loads
-        // are in flight
-        clear_hist();
-        if (tid < 2) sm.ctr[tid] = 0u;
-        if (multi) {
-            // pull the staged bucket: every entry is non-zero once written.
-            // Eight loads in flight per thread; entries not written yet are
-            // re-polled together (bounded wait).
-            for (uint32_t i0 = 0; i0 < m; i0 += 8u * BLOCK) {
-                uint64_t v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                    v[u] = i < m ? ld_dev(&gstage[i]) : 1ull;
-                }
-                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                for (;;) {
-                    bool miss = false;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) miss |= v[u] == 0ull;
-                    if (!miss) break;
-                    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-                        raise_flag(P.status, kFlagTimeout);
-                        break;
+                const uint32_t key = keys[4 * j + e];
+                if (key >= lo) {
+                    const uint64_t c = composite(key, (uint32_t)(ib + e));
+                    if (to_region) {
+                        if (p < R) st_dev(&region[p], c);
+                    } else if (p < (uint32_t)kBufCap) {
+                        sm.cand[p] = c;
+                        atomicAdd(&hc[window_bin(c, lo)], 1u);
                     }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        if (v[u] == 0ull) v[u] = ld_dev(&gstage[i0 + (uint32_t)(u * BLOCK + tid)]);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                    if (i < m) sm.cand[i] = v[u];
+                    ++p;
                 }
             }
         }
-        lds_sync();
-        finish_bucket<BLOCK>(sm.cand, m, need, W, pf, R + 1, F, idx_bits, true, sm.hist, sm.small, sm.scan, sm.sel,
-                                sm.ctr, out, okey, k, P.status);
-    }
-
-    if (multi) {
-        // clear the half the previous launch used, record this launch's use
-        // and hand the other half to the next launch
-        const int op = p ^ 1;
-        const uint32_t prev = op ? used1 : used0;
-        const uint32_t ur = min(prev & 15u, (uint32_t)kRounds);
-        const uint32_t uc = min((prev >> 4) & 15u, (uint32_t)kMergeCopies);
-        const uint32_t us = min(prev >> 8, (uint32_t)kCap);
-        uint64_t* const h = &ws->hist[op][0][0][0];
-        for (uint32_t i = tid; i < ur * kMergeCopies * 256u; i += BLOCK)
-            if ((i / 256u) % kMergeCopies < uc) st_dev(&h[i], (uint64_t)0);
-        for (uint32_t i = tid; i < us; i += BLOCK) st_dev(&ws->stage[op][i], (uint64_t)0);
-        if (tid == 0) {
-            const uint32_t stage = whole ? 0u : (hb > (uint32_t)kCap ? (uint32_t)kCap : hb);
-            st_dev(&ws->used[p], (uint32_t)(last_slot + 1) | ((uint32_t)C << 4) | (stage << 8));
-            st_dev(&ws->parity, (uint32_t)op);
+    };
+    auto count_tile = [&]() {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) c += keys[i] >= lo;
+        return c;
+    };
+    if constexpr (RESIDENT) {
+        const uint32_t first = block_append<BLOCK>(count_tile(), &sm.scan2[0][0], par, total);
+        // the count is published before the entries are written: the
+        // finishing WG polls each entry until it is non-zero
+        if (to_region && tid == 0) st_dev(&rw->cnt[w], ((uint64_t)tag << 32) | (uint64_t)total);
+        place_tile(c_begin, first);
+    } else {
+        for (int ct = c_begin; ct < c_end; ct += TILE_CHUNKS) {
+            load_tile(ct);
+            tile_keys(ct);
+            const uint32_t first = block_append<BLOCK>(count_tile(), &sm.scan2[0][0], par, total);
+            place_tile(ct, first);
         }
+        if (to_region && tid == 0) st_dev(&rw->cnt[w], ((uint64_t)tag << 32) | (uint64_t)total);
+    }
+    if (to_region) return;
+
+    // ---- the finishing WG: its own candidates are cand[0 .. total); the
+    // other WGs' follow in WG order
+    uint32_t C = total;
+    bool ok;
+    if (multi) {
+        const int others = Geff - 1;
+        const uint32_t tagv = uniform(sm.tag);
+        const uint64_t lim = spin_limit();
+        // TPR threads per region: thread (wr, sub) polls region wr's count
+        // (sub 0) and reads its entries sub, sub + TPR, ... speculatively, in
+        // the same round trip; entries not yet written read as 0 and are
+        // polled again once the count says they exist
+        const int TPR = BLOCK / others;
+        const int wr = tid / TPR, sub = tid - wr * TPR;
+        const bool mine = wr < others;
+        uint64_t* const rb = P.stage + ((size_t)row * (size_t)G + (size_t)(mine ? wr : 0)) * R;
+        constexpr int U = 8;
+        const uint32_t E = (uint32_t)(TPR * U);  // entries read speculatively per region
+        uint64_t cv = 0;
+        if (mine && sub == 0) cv = lim ? ld_dev(&rw->cnt[wr]) : 0ull;
+        uint64_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = (uint32_t)(sub + TPR * u);
+            v[u] = (mine && j < R) ? ld_dev(&rb[j]) : 0ull;
+        }
+        if (mine && sub == 0) {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while ((uint32_t)(cv >> 32) != tagv) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= lim) {
+                    raise_flag(P.status, kFlagTimeout);
+                    sm.bad = 1u;
+                    cv = 0ull;
+                    break;
+                }
+                cv = ld_dev(&rw->cnt[wr]);
+            }
+            sm.cnt[wr] = (uint32_t)cv;
+        }
+        lds_sync();
+        // prefixes over the regions (wave 0): of the counts, and of the
+        // counts past the speculative reads
+        if (tid < 64) {
+            const int npl = (others + 63) / 64;  // regions per lane
+            uint32_t a = 0, x = 0;
+            for (int i = 0; i < npl; ++i) {
+                const int r2 = tid * npl + i;
+                if (r2 < others) {
+                    const uint32_t c = sm.cnt[r2];
+                    a += c;
+                    x += c > E ? c - E : 0u;
+                }
+            }
+            const uint32_t ia = wave_inclusive_scan(a), ix = wave_inclusive_scan(x);
+            uint32_t pa = ia - a, px = ix - x;
+            for (int i = 0; i < npl; ++i) {
+                const int r2 = tid * npl + i;
+                if (r2 < others) {
+                    const uint32_t c = sm.cnt[r2];
+                    sm.pre[r2] = pa;
+                    sm.prex[r2] = px;
+                    pa += c;
+                    px += c > E ? c - E : 0u;
+                }
+            }
+            if (tid == 63) {
+                sm.tot[0] = ia;
+                sm.tot[1] = ix;
+            }
+        }
+        lds_sync();
+        const uint32_t c_others = uniform(sm.tot[0]), X = uniform(sm.tot[1]);
+        C = total + c_others;
+        ok = sm.bad == 0u && C >= (uint32_t)k && C <= (uint32_t)kBufCap;
+        // every entry is read (when the row is finished otherwise, waited
+        // for; all missing ones polled again together), moved to the buffer
+        // and cleared for the next launch
+        {
+            const uint32_t cw = mine ? min(sm.cnt[wr], (uint32_t)R) : 0u, pw = mine ? sm.pre[wr] : 0u;
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
+                bool miss = false;
+#pragma unroll
+                for (int u = 0; u < U; ++u) miss |= ((uint32_t)(sub + TPR * u) < cw) & (v[u] == 0ull);
+                if (!miss) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= lim) {
+                    raise_flag(P.status, kFlagTimeout);
+                    sm.bad = 1u;
+                    break;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t j = (uint32_t)(sub + TPR * u);
+                    if ((j < cw) & (v[u] == 0ull)) v[u] = ld_dev(&rb[j]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t j = (uint32_t)(sub + TPR * u);
+                if (j < cw) {
+                    if (ok && v[u] != 0ull) {
+                        sm.cand[total + pw + j] = v[u];
+                        atomicAdd(&hc[window_bin(v[u], lo)], 1u);
+                    }
+                    st_dev(&rb[j], (uint64_t)0);
+                }
+            }
+        }
+        // entries past the speculative reads (regions holding more than E):
+        // entry i of that remainder is entry E + i - prex[w'] of region w',
+        // w' the last region whose prefix is at most i (binary search)
+        constexpr int UP = 8;
+        for (uint32_t i0 = 0; i0 < X; i0 += UP * BLOCK) {
+            uint64_t* addr[UP];
+            uint32_t dst[UP];
+            uint64_t vv[UP];
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+                const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
+                addr[u] = nullptr;
+                dst[u] = 0;
+                if (i < X) {
+                    int a = 0, b = others;  // prex[a] <= i < prex[b] (prex[others] taken as infinite)
+                    while (b - a > 1) {
+                        const int mid = (a + b) >> 1;
+                        if (sm.prex[mid] <= i) a = mid;
+                        else b = mid;
+                    }
+                    const uint32_t j = E + i - sm.prex[a];
+                    dst[u] = total + sm.pre[a] + j;
+                    if (j < R) addr[u] = P.stage + ((size_t)row * (size_t)G + (size_t)a) * R + j;
+                }
+                vv[u] = addr[u] ? ld_dev(addr[u]) : 1ull;
+            }
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
+                bool miss = false;
+#pragma unroll
+                for (int u = 0; u < UP; ++u) miss |= vv[u] == 0ull;
+                if (!miss) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= lim) {
+                    raise_flag(P.status, kFlagTimeout);
+                    sm.bad = 1u;
+                    break;
+                }
+#pragma unroll
+                for (int u = 0; u < UP; ++u)
+                    if (vv[u] == 0ull) vv[u] = ld_dev(addr[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+                if (!addr[u]) continue;
+                if (ok && vv[u] != 0ull) {
+                    sm.cand[dst[u]] = vv[u];
+                    atomicAdd(&hc[window_bin(vv[u], lo)], 1u);
+                }
+                st_dev(addr[u], (uint64_t)0);
+            }
+        }
+        // the counts and the epoch for the next launch
+        if (mine && sub == 0) st_dev(&rw->cnt[wr], (uint64_t)0);
+        if (tid == 0) st_dev(&rw->epoch, epoch + 1u);
+        lds_sync();
+        ok = ok && sm.bad == 0u;
+    } else {
+        ok = C >= (uint32_t)k && C <= (uint32_t)kBufCap;
+        lds_sync();
+    }
+    if (__builtin_expect(ok, 1)) {
+        select_buffer<BLOCK>(sm.cand, C, (uint32_t)k, 0u, lo, true, sm.hist, sm.small, sm.scan, sm.sel, out, okey, k,
+                             P.status);
+    } else {
+        lds_sync();
+        select_by_passes<BLOCK, kBufCap>(base, off, L, nchunks, k, out, okey, sm.cand, sm.hist, sm.small, sm.scan,
+                                         sm.sel, P.status);
     }
 }
 
@@ -1002,11 +1052,10 @@ __global__ __launch_bounds__(BLOCK) void topk_select_kernel(const KParams P) {
 // whose key is at or above a running lower bound in an LDS buffer (the
 // bound estimated from the elements seen so far and raised as the buffer
 // fills); when the buffer ends up holding at least k elements, the row's
-// k-th largest is the buffer's and the row is finished from LDS: a 12-bit
-// first digit (4096 bins), winners out, the threshold bin to the on-chip
-// finish.  Otherwise the row is finished with re-reads (a full 12-bit
-// histogram, more rounds while the bucket is large, a collection pass whose
-// positions come from two wave-aggregated LDS counters).
+// k largest are the buffer's and the on-chip selection finishes the row.
+// Otherwise the row is finished by passes over it.  Buffer positions come
+// from block scans, so the buffer's order, and with it the output order, is
+// fixed by the row's values.
 
 // candidate buffer of the one-WG-per-row kernel (entries): as large as two
 // WGs per CU allow with some LDS to spare (78 KB per WG)
@@ -1017,13 +1066,13 @@ template <int BLOCK>
 struct RowsSmem {
     union {
         uint32_t h12[2 * 4097];                  // first digit: 2 copies of 4096 bins (stride 4097)
-        alignas(16) uint32_t h8[kCopies * 257];  // later 8-bit rounds and the finisher
+        alignas(16) uint32_t h8[kCopies * kStride];  // 256-bin rounds
     } h;
-    uint64_t cand[kRowsCap];  // candidates at or above the running bound; later the final bucket
-    uint64_t small[kSmall];
+    alignas(16) uint64_t cand[kRowsCap];  // candidates at or above the running bound
+    uint64_t small[kSmall];               // the last few, ranked exactly
     uint32_t scan[BLOCK / 64];
+    uint32_t scan2[2][BLOCK / 64];
     uint32_t sel[4];
-    uint32_t ctr[5];  // winners, bucket, finisher (2), buffered entries
 };
 
 template <int BLOCK, int ITEMS, int PD, bool KEYS>
@@ -1042,11 +1091,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
     uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;  // recorded keys (ordered output)
-    int L = n;
-    if (P.lengths) {
-        L = P.lengths[row];
-        L = L < 0 ? 0 : (L > n ? n : L);
-    }
+    const int L = valid_length(P.lengths, row, n);
     if (L <= k) {  // everything valid is selected; pad with -1
         for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
         return;
@@ -1055,8 +1100,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     const int nchunks = (off + L + 3) >> 2;
     const int cf_lo = off ? 1 : 0;         // chunks whose four elements are all valid
     const int cf_hi = (L + off) >> 2;
-    const int idx_bits = P.idx_bits;
-    const int nrounds = num_rounds(idx_bits);
     const char* const base = reinterpret_cast<const char*>(prow - off);
 
     // f(keys, c_tile) for every tile of the row; slot 4j+e of a thread is
@@ -1070,7 +1113,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
                 for (int j = 0; j < CHUNKS; ++j) {
                     const int c = d * TILE_CHUNKS + j * BLOCK + tid;
-                    buf[d][j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
+                    buf[d][j] = *reinterpret_cast<const uint4*>(base + (size_t)(c < nchunks ? c : 0) * 16u);
                 }
             }
         }
@@ -1101,7 +1144,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
                         for (int j = 0; j < CHUNKS; ++j) {
                             const int c = cn + j * BLOCK + tid;
-                            buf[d][j] = *reinterpret_cast<const uint4*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
+                            buf[d][j] =
+                                *reinterpret_cast<const uint4*>(base + (size_t)(c < nchunks ? c : 0) * 16u);
                         }
                     }
                     f(keys, ct);
@@ -1110,10 +1154,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
     };
 
-    // ---------------- first pass: every element whose key is at or above a
-    // lower bound `lo_key` kept in LDS.  The bound is an estimate: the
-    // first-digit bin (12 bits) of the element of rank 1.125 * k * seen / L
-    // + 16 among the `seen` elements read so far, where the k-th largest of
+    // ---------------- the single read: every element whose key is at or
+    // above a lower bound `lo_key` kept in LDS.  The bound is an estimate:
+    // the first-digit bin (12 bits) of the element of rank 1.125 * k * seen /
+    // L + 16 among the `seen` elements read so far, where the k-th largest of
     // the row is expected near rank k * seen / L (in a dense bin, also that
     // element's next 8 key bits).  It is taken from the first tile and
     // raised (with the buffer compacted) whenever the buffer fills up, from
@@ -1121,71 +1165,51 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     // key is at or above the bound; when it holds at least k entries, the
     // k-th largest of the buffer is the row's and everything selected is in
     // it.  Otherwise, or when the buffer overflowed twice on one tile, the
-    // row is finished with re-reads.
-    {
-        uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
-        for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-        if (tid < 5) sm.ctr[tid] = 0u;
-    }
+    // row is finished by passes over it.
+    clear_words(sm.h.h12, 2 * 4097, tid, BLOCK);
     lds_sync();
     bool keep = true;   // candidates are being buffered
     uint32_t used = 0;  // buffered entries
+    int par = 0;        // half of scan2 used by the next append
     // running lower bound on the keys kept: a first-digit bin, refined by
     // the next 8 key bits where that bin is dense (at least 1: empty slots
     // are never kept)
     uint32_t lo_key = 1u;
     // Walk the buffer in slices of RC * BLOCK entries: every thread reads its
-    // RC entries, a block scan numbers the chosen ones, and f(entry, kind,
-    // rank) places them.  Kinds: pred returns 0 (drop), 1 or 2, counted
-    // separately (ranks are per kind, across slices).  A chosen entry of
-    // kind 2 may be moved to the front of the buffer: its new index is never
-    // above its old one, and each slice is read before any of it is written.
+    // RC entries, a block scan numbers the chosen ones, and f(entry, rank)
+    // places them.  pred returns 0 (drop) or 1 (keep).  A kept entry may be
+    // moved to the front of the buffer: its new index is never above its old
+    // one, and each slice is read before any of it is written.
     constexpr int RC = 3;
-    auto walk = [&](auto&& pred, auto&& f, uint32_t& n1, uint32_t& n2) {
-        n1 = 0;
-        n2 = 0;
+    auto compact = [&](auto&& pred) {
+        uint32_t n2 = 0;
         for (uint32_t i0 = 0; i0 < used; i0 += RC * BLOCK) {
             uint64_t e[RC];
-            uint32_t kinds = 0, cnt = 0;
+            uint32_t keepm = 0, cnt = 0;
 #pragma unroll
             for (int u = 0; u < RC; ++u) {
                 const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
                 e[u] = i < used ? sm.cand[i] : 0ull;
                 const uint32_t kd = i < used ? pred(e[u]) : 0u;
-                kinds |= kd << (2 * u);
-                cnt += kd == 1u ? (1u << 16) : (kd == 2u ? 1u : 0u);
+                keepm |= kd << u;
+                cnt += kd;
             }
             uint32_t tot;
-            const uint32_t pos = block_scan_total<BLOCK>(cnt, sm.scan, tot);
-            uint32_t p1 = n1 + (pos >> 16), p2 = n2 + (pos & 0xFFFFu);
+            uint32_t p = n2 + block_scan_total<BLOCK>(cnt, sm.scan, tot);
 #pragma unroll
-            for (int u = 0; u < RC; ++u) {
-                const uint32_t kd = (kinds >> (2 * u)) & 3u;
-                if (kd == 1u) f(e[u], 1u, p1++);
-                else if (kd == 2u) f(e[u], 2u, p2++);
-            }
-            n1 += tot >> 16;
-            n2 += tot & 0xFFFFu;
+            for (int u = 0; u < RC; ++u)
+                if ((keepm >> u) & 1u) sm.cand[p++] = e[u];
+            n2 += tot;
         }
+        return n2;
     };
     // rank of the bound after `seen` valid elements
     auto bound_rank = [&](uint32_t seen) -> uint32_t {
         // the margin at the end of the row, k / 8, is several standard
         // deviations of the count above a fixed rank for values drawn alike
-        // along the row; a looser bound buffers (and later partitions) more
+        // along the row; a looser bound buffers (and later selects) more
         const uint64_t est = ((uint64_t)k * seen * 9u) / (8u * (uint64_t)L) + 16u;
         return (uint32_t)(est < seen ? est : seen);
-    };
-    // the first-digit histogram of the buffered entries
-    auto hist_from_buffer = [&]() {
-        uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
-        for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-        lds_sync();
-        uint32_t* const hcb = sm.h.h12 + (tid & 1) * 4097;
-        for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) atomicAdd(&hcb[(uint32_t)(sm.cand[i] >> (64 - F))], 1u);
-        lds_sync();
     };
     // the element of rank `rank` among the buffered entries (all in
     // first-digit bins at or above lo, the bound's bin), over a 256-bin
@@ -1194,372 +1218,157 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     // fewer entries)
     auto window_select = [&](uint32_t rank, uint32_t& bw, uint32_t& ab, uint32_t& hbw) {
         const uint32_t lo = lo_key >> (32 - F);
-        {
-            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
-            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        }
+        clear_words(sm.h.h8, kCopies * kStride, tid, BLOCK);
         lds_sync();
         {
-            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
+            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * kStride;
             for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
                 const uint32_t bin = (uint32_t)(sm.cand[i] >> (64 - F));
                 atomicAdd(&hcw[min(bin - lo, 255u)], 1u);
             }
         }
         lds_sync();
-        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rank, sm.scan, sm.sel, P.status, bw, ab, hbw);
+        local_select<BLOCK, 256, kCopies, kStride, false>(sm.h.h8, rank, sm.scan, sm.sel, P.status, bw, ab, hbw);
     };
     // the element of rank `rank` among the buffered entries of first-digit
     // bin b: its next 8 key bits (sub-bin s8), the count above it in the bin
     // and the count in it (0 when there are fewer entries)
     auto sub_select = [&](uint32_t b, uint32_t rank, uint32_t& s8, uint32_t& a8, uint32_t& h8v) {
-        {
-            uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
-            for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-        }
+        clear_words(sm.h.h8, kCopies * kStride, tid, BLOCK);
         lds_sync();
         {
-            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * 257;
+            uint32_t* const hcw = sm.h.h8 + (tid % kCopies) * kStride;
             for (uint32_t i = (uint32_t)tid; i < used; i += BLOCK) {
                 const uint32_t key = (uint32_t)(sm.cand[i] >> 32);
                 if ((key >> (32 - F)) == b) atomicAdd(&hcw[(key >> (32 - F - 8)) & 0xFFu], 1u);
             }
         }
         lds_sync();
-        local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rank, sm.scan, sm.sel, P.status, s8, a8, h8v);
+        local_select<BLOCK, 256, kCopies, kStride, false>(sm.h.h8, rank, sm.scan, sm.sel, P.status, s8, a8, h8v);
     };
-    {
-        const uint32_t lane = lane_id();
-        stream([&](const uint32_t* keys, int ct) {
-            if (!keep) return;  // overflowed: the fallback re-reads the row
-            // valid elements read once this tile is done
-            const uint32_t seen = (uint32_t)min(L, 4 * min(nchunks, ct + TILE_CHUNKS) - off);
-            if (ct == 0) {
-                // the first bound, from the first tile: the 12-bit bin of the
-                // element of rank bound_rank(seen), in two steps — its top 8
-                // bits (256-bin histogram, 16 copies), then its next 4 bits
-                // among the elements of that 8-bit bin (16 bins).  The union
-                // is all zero here.
-                uint32_t* const h8c = sm.h.h8 + (tid % kCopies) * 257;
+    stream([&](const uint32_t* keys, int ct) {
+        if (!keep) return;  // overflowed: the row is finished by passes over it
+        // valid elements read once this tile is done
+        const uint32_t seen = (uint32_t)min(L, 4 * min(nchunks, ct + TILE_CHUNKS) - off);
+        if (ct == 0) {
+            // the first bound, from the first tile: the 12-bit bin of the
+            // element of rank bound_rank(seen), in two steps — its top 8
+            // bits (256-bin histogram, 16 copies), then its next 4 bits
+            // among the elements of that 8-bit bin (16 bins).  The union
+            // is all zero here.
+            uint32_t* const h8c = sm.h.h8 + (tid % kCopies) * kStride;
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                if (keys[i] != 0u) atomicAdd(&h8c[keys[i] >> 24], 1u);
+            lds_sync();
+            uint32_t b8, ab8, hb8;
+            const uint32_t rk = bound_rank(seen);
+            local_select<BLOCK, 256, kCopies, kStride, false>(sm.h.h8, rk, sm.scan, sm.sel, P.status, b8, ab8, hb8);
+            if (hb8 > 0u) {
+                uint32_t* const h4 = sm.h.h12 + kCopies * kStride + (tid % kCopies) * 17;  // past the 8-bit copies
 #pragma unroll
                 for (int i = 0; i < ITEMS; ++i)
-                    if (keys[i] != 0u) atomicAdd(&h8c[keys[i] >> 24], 1u);
+                    if ((keys[i] != 0u) & ((keys[i] >> 24) == b8)) atomicAdd(&h4[(keys[i] >> 20) & 15u], 1u);
                 lds_sync();
-                uint32_t b8, ab8, hb8;
+                if (tid < 64) {
+                    // lane l: sub-bin 15 - l (descending), summed over the copies
+                    uint32_t c = 0;
+                    if (tid < 16) {
+#pragma unroll
+                        for (int q = 0; q < kCopies; ++q) c += sm.h.h12[kCopies * kStride + q * 17 + 15 - tid];
+                    }
+                    const uint32_t inc = wave_inclusive_scan(c);
+                    const uint32_t need4 = rk - ab8;  // 1-based rank inside the 8-bit bin
+                    if (tid < 16 && inc - c < need4 && need4 <= inc) sm.sel[3] = 15u - (uint32_t)tid;
+                }
+                lds_sync();
+                const uint32_t b12 = (b8 << 4) | uniform(sm.sel[3]);
+                lo_key = max(lo_key, b12 << (32 - F));
+            }
+        }
+        // append: a block scan numbers this tile's candidates in thread
+        // order.  A tile that overflows the buffer (its entries past the end
+        // are lost) raises the bound from what is buffered, drops its own
+        // entries and is appended once more from the registers; a second
+        // overflow gives up (passes over the row finish it).
+        for (int pass = 0;; ++pass) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) c += keys[i] >= lo_key;
+            uint32_t pos = block_append<BLOCK>(c, &sm.scan2[0][0], par, used);
+            {
+                const int ibase = 4 * (ct + tid) - off;
+#pragma unroll
+                for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t key = keys[4 * j + e];
+                        if (key >= lo_key) {
+                            const uint64_t cc = composite(key, (uint32_t)(ibase + 4 * BLOCK * j + e));
+                            if (pos < (uint32_t)kRowsCap) sm.cand[pos] = cc;
+                            ++pos;
+                        }
+                    }
+                }
+            }
+            const bool over = used > (uint32_t)kRowsCap;  // entries of this tile were lost
+            if (over && pass > 0) {
+                keep = false;
+                return;
+            }
+            if (!over && !(used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks)) break;
+            if (over) used = (uint32_t)kRowsCap;
+            lds_sync();  // the appended entries are read next
+            // tighter bound from more data, and drop what fell below it
+            // (and, after an overflow, this tile's entries): the bin of
+            // the entry of rank bound_rank(seen), or the top of the
+            // window when it lies above (still a lower bound)
+            {
                 const uint32_t rk = bound_rank(seen);
-                local_select<BLOCK, 256, kCopies, 257, false>(sm.h.h8, 0u, rk, sm.scan, sm.sel, P.status, b8, ab8,
-                                                              hb8);
-                if (hb8 > 0u) {
-                    uint32_t* const h4 = sm.h.h12 + kCopies * 257 + (tid % kCopies) * 17;  // past the 8-bit copies
-#pragma unroll
-                    for (int i = 0; i < ITEMS; ++i)
-                        if ((keys[i] != 0u) & ((keys[i] >> 24) == b8)) atomicAdd(&h4[(keys[i] >> 20) & 15u], 1u);
-                    lds_sync();
-                    if (tid < 64) {
-                        // lane l: sub-bin 15 - l (descending), summed over the copies
-                        uint32_t c = 0;
-                        if (tid < 16) {
-#pragma unroll
-                            for (int q = 0; q < kCopies; ++q) c += sm.h.h12[kCopies * 257 + q * 17 + 15 - tid];
-                        }
-                        const uint32_t inc = wave_inclusive_scan(c);
-                        const uint32_t need4 = rk - ab8;  // 1-based rank inside the 8-bit bin
-                        if (tid < 16 && inc - c < need4 && need4 <= inc) sm.sel[3] = 15u - (uint32_t)tid;
+                uint32_t bw, ab, hbw;
+                window_select(rk, bw, ab, hbw);
+                if (hbw > 0u) {
+                    const uint32_t b12 = min((lo_key >> (32 - F)) + bw, (uint32_t)NB0 - 1u);
+                    uint32_t nk = b12 << (32 - F);
+                    if (bw < 255u && hbw > kRowsDenseBin) {
+                        // a dense bin: the entry's next 8 key bits too
+                        uint32_t s8, a8, h8v;
+                        sub_select(b12, rk - ab, s8, a8, h8v);
+                        if (h8v > 0u) nk |= s8 << (32 - F - 8);
                     }
-                    lds_sync();
-                    const uint32_t b12 = (b8 << 4) | uniform(sm.sel[3]);
-                    lo_key = max(lo_key, b12 << (32 - F));
+                    lo_key = max(lo_key, nk);
                 }
             }
-            // append: lanes count their candidates, a wave prefix ranks
-            // them, one LDS atomic per wave reserves the wave's range.  A
-            // tile that overflows the buffer (its entries past the end are
-            // lost) raises the bound from what is buffered, drops its own
-            // entries and is appended once more from the registers; a
-            // second overflow gives up (the re-reading path below).
-            for (int pass = 0;; ++pass) {
-                uint32_t c = 0;
-#pragma unroll
-                for (int i = 0; i < ITEMS; ++i) c += keys[i] >= lo_key;
-                const uint32_t ic = wave_inclusive_scan(c);
-                const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
-                if (tw) {
-                    uint32_t wb = 0;
-                    if (lane == 0) wb = atomicAdd(&sm.ctr[4], tw);
-                    uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, 0) + ic - c;
-                    const int ibase = 4 * (ct + tid) - off;
-#pragma unroll
-                    for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t key = keys[4 * j + e];
-                            if (key >= lo_key) {
-                                if (pos < (uint32_t)kRowsCap)
-                                    sm.cand[pos] = ((uint64_t)key << 32) |
-                                                   (uint64_t)~(uint32_t)(ibase + 4 * BLOCK * j + e);
-                                ++pos;
-                            }
-                        }
-                    }
-                }
-                lds_sync();
-                used = uniform(sm.ctr[4]);
-                const bool over = used > (uint32_t)kRowsCap;  // entries of this tile were lost
-                if (over && pass > 0) {
-                    keep = false;
-                    return;
-                }
-                if (!over && !(used > (uint32_t)kRowsCap * 3u / 4u && ct + TILE_CHUNKS < nchunks)) break;
-                if (over) used = (uint32_t)kRowsCap;
-                // tighter bound from more data, and drop what fell below it
-                // (and, after an overflow, this tile's entries): the bin of
-                // the entry of rank bound_rank(seen), or the top of the
-                // window when it lies above (still a lower bound)
-                {
-                    const uint32_t rk = bound_rank(seen);
-                    uint32_t bw, ab, hbw;
-                    window_select(rk, bw, ab, hbw);
-                    if (hbw > 0u) {
-                        const uint32_t b12 = min((lo_key >> (32 - F)) + bw, (uint32_t)NB0 - 1u);
-                        uint32_t nk = b12 << (32 - F);
-                        if (bw < 255u && hbw > kRowsDenseBin) {
-                            // a dense bin: the entry's next 8 key bits too
-                            uint32_t s8, a8, h8v;
-                            sub_select(b12, rk - ab, s8, a8, h8v);
-                            if (h8v > 0u) nk |= s8 << (32 - F - 8);
-                        }
-                        lo_key = max(lo_key, nk);
-                    }
-                }
-                const uint32_t lob = lo_key;
-                // this tile's index range (empty when nothing was lost)
-                const int xlo = over ? 4 * ct - off : 0, xhi = over ? 4 * (ct + TILE_CHUNKS) - off : 0;
-                uint32_t n1, n2;
-                walk([&](uint64_t e) {
-                         const int idx = (int)~(uint32_t)e;
-                         return ((uint32_t)(e >> 32) >= lob) & ((idx < xlo) | (idx >= xhi)) ? 2u : 0u;
-                     },
-                     [&](uint64_t e, uint32_t, uint32_t r) { sm.cand[r] = e; }, n1, n2);
-                used = n2;
-                if (tid == 0) sm.ctr[4] = n2;
-                lds_sync();
-                if (!over) break;
-            }
-        });
-    }
+            const uint32_t lob = lo_key;
+            // this tile's index range (empty when nothing was lost)
+            const int xlo = over ? 4 * ct - off : 0, xhi = over ? 4 * (ct + TILE_CHUNKS) - off : 0;
+            used = compact([&](uint64_t e) -> uint32_t {
+                const int idx = (int)~(uint32_t)e;
+                return ((uint32_t)(e >> 32) >= lob) & ((idx < xlo) | (idx >= xhi)) ? 1u : 0u;
+            });
+            lds_sync();  // the moved entries are read next
+            if (!over) break;
+        }
+    });
     // the first tile of the row `ahead` rows on (the one that probably runs
     // next on this WG's XCD) is touched now: its loads then hit the caches
     uint32_t sink = 0;
     if (P.ahead > 0 && row + P.ahead < P.rows && tid * 16 < n)
         sink = *reinterpret_cast<const uint32_t*>(P.logits + (size_t)(row + P.ahead) * (size_t)n + tid * 16);
-    auto done = [&]() { __asm__ volatile("" ::"v"(sink)); };
     lds_sync();
-    Prefix pf{0u, 0u, 0u, 0u};
-    uint32_t need = (uint32_t)k, W = 0, hb = 0;
-    int R = 0;
-    bool whole = false;
-    uint32_t b0 = 0, above = 0;
-    if (keep) {
-        // the threshold bin, from the buffer: first over the 256-bin window
-        // from the bound's bin, which normally holds it; else over all 4096
-        // bins
-        uint32_t bw;
-        window_select(need, bw, above, hb);
-        if (hb > 0u && bw < 255u) {
-            b0 = (lo_key >> (32 - F)) + bw;
-        } else {
-            hist_from_buffer();
-            local_select<BLOCK, NB0, 2, 4097, false>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
-        }
-    }
-    // one finisher call for both paths (its code inlined once)
-    uint32_t fin_m = 0;
-    int fin_r0 = 1;
-    if (keep && hb > 0u && b0 >= (lo_key >> (32 - F))) {
-        need -= above;
-        W += above;
-        pf.add(F, 0, b0, idx_bits);
-        whole = hb == need;
-        // every element at or above bin b0 is buffered: winners (above b0)
-        // to the output, the bucket (bin b0) to the front of the buffer, or
-        // to the output when it is taken whole
-        uint32_t nw, nbk;
-        const uint32_t bsel = b0;
-        const bool wh = whole;
-        const uint32_t Wv = W;
-        walk([&](uint64_t e) {
-                 const uint32_t bin = (uint32_t)(e >> (64 - F));
-                 return bin > bsel ? 1u : (bin == bsel ? 2u : 0u);
-             },
-             [&](uint64_t e, uint32_t kind, uint32_t r) {
-                 if (kind == 1u) {
-                     if (r < Wv) {
-                         out[r] = (int32_t)~(uint32_t)e;
-                         if (okey) okey[r] = (uint32_t)(e >> 32);
-                     }
-                 } else if (wh) {
-                     if (Wv + r < (uint32_t)k) {
-                         out[Wv + r] = (int32_t)~(uint32_t)e;
-                         if (okey) okey[Wv + r] = (uint32_t)(e >> 32);
-                     }
-                 } else {
-                     sm.cand[r] = e;
-                 }
-             },
-             nw, nbk);
-        const bool bad = nw != W || nbk != hb;
-        if (bad && tid == 0) raise_flag(P.status, kFlagCapacity);
-        if (whole) {
-            done();
-            return;
-        }
-        fin_m = hb;
-        fin_r0 = 1;
+    if (keep && used >= (uint32_t)k) {
+        // every buffered entry is at or above the bound (compactions drop
+        // what falls below a raised bound; appends use the current one)
+        clear_words(sm.h.h8, kCopies * kStride, tid, BLOCK);
+        lds_sync();
+        select_buffer<BLOCK>(sm.cand, used, (uint32_t)k, 0u, lo_key, false, sm.h.h8, sm.small, sm.scan, sm.sel, out,
+                             okey, k, P.status);
     } else {
-        // ---------------- fallback: the full first-digit histogram by a second
-        // read, then rounds and collection by further reads.  Rare (the
-        // estimated bound failed), so its passes are rolled loops of U chunks
-        // per lane: small code and few registers beside the streaming pass
-        // above (measured: the fallback written like the first pass, unrolled
-        // over whole tiles, costs that pass 14 % on the causal batch).
-        constexpr int U = 2;
-        auto reread = [&](auto&& f) {
-    #pragma unroll 1
-            for (int c0 = 0; c0 < nchunks; c0 += U * BLOCK) {
-                u32x4_t v[U];
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * BLOCK + tid;
-                    v[u] = *reinterpret_cast<const u32x4_t*>(base + (uint32_t)(c < nchunks ? c : 0) * 16u);
-                }
-                uint32_t kk[4 * U], nn[4 * U];  // keys (0: empty slot) and ~indices
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * BLOCK + tid;
-                    const int e0 = 4 * c - off;
-    #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool ok = (c < nchunks) & ((uint32_t)(e0 + e) < (uint32_t)L);
-                        kk[4 * u + e] = ok ? key_of(__uint_as_float(v[u][e])) : 0u;
-                        nn[4 * u + e] = ~(uint32_t)(e0 + e);
-                    }
-                }
-                f(kk, nn);
-            }
-        };
-        {
-            {
-                uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h12);
-                for (int i = tid; i < 2 * 4097 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-                if (tid < (2 * 4097) % 4) sm.h.h12[2 * 4097 / 4 * 4 + tid] = 0u;
-            }
-            lds_sync();
-            uint32_t* const hc = sm.h.h12 + (tid & 1) * 4097;
-            reread([&](const uint32_t* kk, const uint32_t*) {
-    #pragma unroll
-                for (int i = 0; i < 4 * U; ++i)
-                    if (kk[i] != 0u) atomicAdd(&hc[kk[i] >> (32 - F)], 1u);
-            });
-            lds_sync();
-        }
-        local_select<BLOCK, NB0, 2, 4097>(sm.h.h12, 0u, need, sm.scan, sm.sel, P.status, b0, above, hb);
-        need -= above;
-        W += above;
-        pf.add(F, 0, b0, idx_bits);
-        whole = hb == need;
-        // ---------------- further rounds (only when the bucket is still large)
-        for (int r = 1; !whole && hb > (uint32_t)kCap && r < nrounds; ++r) {
-            {
-                uint4* const h4 = reinterpret_cast<uint4*>(sm.h.h8);
-                for (int i = tid; i < kCopies * 257 / 4; i += BLOCK) h4[i] = uint4{0u, 0u, 0u, 0u};
-            }
-            lds_sync();
-            uint32_t* const hc = sm.h.h8 + (tid % kCopies) * 257;
-            const int sh = digit_shift(F, r, idx_bits);
-            const uint32_t dm = digit_mask(F, r);
-            reread([&](const uint32_t* kk, const uint32_t* nn) {
-    #pragma unroll
-                for (int i = 0; i < 4 * U; ++i)
-                    if (pf.match(kk[i], nn[i])) atomicAdd(&hc[((r < 4 ? kk[i] : nn[i]) >> sh) & dm], 1u);
-            });
-            lds_sync();
-            uint32_t b, above;
-            local_select<BLOCK, 256, kCopies, 257>(sm.h.h8, 0u, need, sm.scan, sm.sel, P.status, b, above, hb);
-            need -= above;
-            W += above;
-            pf.add(F, r, b, idx_bits);
-            R = r;
-            whole = hb == need;
-        }
-        // ---------------- collection: winners to the output, the bucket to LDS
-        // (or to the output when it is taken whole).  Positions per step: each
-        // lane counts its winners and bucket elements, a wave prefix (DPP) ranks
-        // the lanes, and one LDS atomic per wave and kind reserves the wave's
-        // range.
-        bool overflow = false;
-        const uint32_t lane = lane_id();
-        reread([&](const uint32_t* kk, const uint32_t* nn) {
-            uint32_t mw = 0, mbk = 0;  // this lane's winners / bucket elements, one bit per slot
-    #pragma unroll
-            for (int i = 0; i < 4 * U; ++i) {
-                mw |= (uint32_t)((kk[i] != 0u) & pf.above(kk[i], nn[i])) << i;
-                mbk |= (uint32_t)pf.match(kk[i], nn[i]) << i;
-            }
-            const uint32_t nw = (uint32_t)__builtin_popcount(mw), nb = (uint32_t)__builtin_popcount(mbk);
-            const uint32_t iw = wave_inclusive_scan(nw), ib = wave_inclusive_scan(nb);
-            const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)iw, 63);
-            const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, 63);
-            if (tw | tb) {
-                uint32_t bw = 0, bb = 0;
-                if (lane == 0) {
-                    if (tw) bw = atomicAdd(&sm.ctr[0], tw);
-                    if (tb) bb = atomicAdd(&sm.ctr[1], tb);
-                }
-                uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)bw, 0) + iw - nw;
-                uint32_t pb = (uint32_t)__builtin_amdgcn_readlane((int)bb, 0) + ib - nb;
-    #pragma unroll
-                for (int i = 0; i < 4 * U; ++i) {
-                    const uint32_t key = kk[i], ni = nn[i];
-                    if ((mw >> i) & 1u) {
-                        if (pw < W) {
-                            out[pw] = (int32_t)~ni;
-                            if (okey) okey[pw] = key;
-                        } else {
-                            overflow = true;
-                        }
-                        ++pw;
-                    } else if ((mbk >> i) & 1u) {
-                        if (whole) {
-                            if (W + pb < (uint32_t)k) {
-                                out[W + pb] = (int32_t)~ni;
-                                if (okey) okey[W + pb] = key;
-                            } else {
-                                overflow = true;
-                            }
-                        } else if (pb < (uint32_t)kCap) {
-                            sm.cand[pb] = ((uint64_t)key << 32) | (uint64_t)ni;
-                        } else {
-                            overflow = true;
-                        }
-                        ++pb;
-                    }
-                }
-            }
-        });
-        if (overflow) raise_flag(P.status, kFlagCapacity);
-        if (whole) {
-            done();
-            return;
-        }
-        fin_m = hb > (uint32_t)kCap ? (uint32_t)kCap : hb;
-        fin_r0 = R + 1;
+        select_by_passes<BLOCK, kRowsCap>(base, off, L, nchunks, k, out, okey, sm.cand, sm.h.h8, sm.small, sm.scan,
+                                          sm.sel, P.status);
     }
-    lds_sync();
-    finish_bucket<BLOCK>(sm.cand, fin_m, need, W, pf, fin_r0, F, idx_bits, false, sm.h.h8, sm.small, sm.scan, sm.sel,
-                            &sm.ctr[2], out, okey, k, P.status);
-    done();
+    __asm__ volatile("" ::"v"(sink));
 }
-
 // ----------------------------------------------------------------- ordered output
 // The ordered form of the selection: section 02 of the TopK article gives
 // radix_topk a need_sorted option that sorts the collected output in
@@ -1621,15 +1430,6 @@ __device__ __forceinline__ void put_sorted(uint64_t c, int32_t* orow, float* vro
     orow[j] = has ? (int32_t)idx : -1;
     if (vrow) vrow[j] = has ? value_of((uint32_t)(c >> 32), prow, L, idx) : -__builtin_huge_valf();
 }
-
-__device__ __forceinline__ int valid_length(const int32_t* lengths, int row, int n) {
-    if (!lengths) return n;
-    const int L = lengths[row];
-    return L < 0 ? 0 : (L > n ? n : L);
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
 
 // Keep the larger of (mine, other) when keep_max, else the smaller: one
 // 64-bit compare and two selects.
@@ -2275,40 +2075,36 @@ __global__ void __launch_bounds__(D) topk_attn_combine_kernel(AttnParams P) {
     P.out[(size_t)rh * D + c] = den > 0.0f ? num / den : 0.0f;
 }
 
+
 // ----------------------------------------------------------------- host side
 
 using LaunchFn = void (*)(dim3, dim3, hipStream_t, const KParams&);
 using OccFn = int (*)(int*, int);
 
-// The window round's code is compiled only into the instances that can
-// meet a row that long (measured: the unused code alone costs C2 0.45 µs).
+// The sample's chunks per thread are a template parameter: 1 for the usual
+// 1024-chunk sample of 1024-thread WGs (code for unused sample slots still
+// costs issue cycles), else what the sample needs.
+constexpr int split_spt(int block, int sample_chunks) { return sample_chunks <= block ? 1 : 4; }
+
 template <int B, int I, bool R>
-void launch_variant(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    const bool win = p.n >= kWinLength;
+void launch_split(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
+    const int spt = split_spt(B, p.sample_chunks);
     if (p.keys) {
-        if (win) hipLaunchKernelGGL((topk_select_kernel<B, I, R, true, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((topk_select_kernel<B, I, R, true, false>), grid, block, 0, s, p);
+        if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 1>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 4>), grid, block, 0, s, p);
     } else {
-        if (win) hipLaunchKernelGGL((topk_select_kernel<B, I, R, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((topk_select_kernel<B, I, R, false, false>), grid, block, 0, s, p);
+        if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 1>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 4>), grid, block, 0, s, p);
     }
 }
 
-// co-resident WGs per CU: the smallest figure of the instantiations
 template <int B, int I, bool R>
-int occupancy_variant(int* nb, int block) {
-    int c[4] = {0, 0, 0, 0};
-    int r[4];
-    r[0] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[0], topk_select_kernel<B, I, R, false, false>, block, 0);
-    r[1] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[1], topk_select_kernel<B, I, R, true, false>, block, 0);
-    r[2] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[2], topk_select_kernel<B, I, R, false, true>, block, 0);
-    r[3] = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c[3], topk_select_kernel<B, I, R, true, true>, block, 0);
-    int m = c[0];
-    for (int i = 1; i < 4; ++i) m = c[i] < m ? c[i] : m;
-    *nb = m;
-    for (int i = 0; i < 4; ++i)
-        if (r[i] != 0) return r[i];
-    return 0;
+int occupancy_split(int* nb, int block) {
+    int a = 0, b = 0;
+    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_split_kernel<B, I, R, false, 4>, block, 0);
+    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_split_kernel<B, I, R, true, 4>, block, 0);
+    *nb = a < b ? a : b;
+    return r1 != 0 ? r1 : r2;
 }
 
 template <int B, int I, int D>
@@ -2333,43 +2129,49 @@ struct Variant {
     OccFn occupancy;
 };
 
-#define TKS_VARIANT(B, I, R) {B, I, R ? 1 : 0, 0, &launch_variant<B, I, R>, &occupancy_variant<B, I, R>}
+#define TKS_SPLIT(B, I, R) {B, I, R ? 1 : 0, 0, &launch_split<B, I, R>, &occupancy_split<B, I, R>}
 #define TKS_ROWS(B, I, D) {B, I, 0, 1, &launch_rows<B, I, D>, &occupancy_rows<B, I, D>}
 const Variant kVariants[] = {
-    TKS_VARIANT(512, 4, true),     // 0: 2048 logits per WG
-    TKS_VARIANT(512, 8, true),     // 1: 4096
-    TKS_VARIANT(1024, 4, true),    // 2: 4096
-    TKS_VARIANT(1024, 8, true),    // 3: 8192
-    TKS_VARIANT(512, 16, true),    // 4: 8192
-    TKS_VARIANT(1024, 16, true),   // 5: 16384
-    TKS_VARIANT(512, 32, true),    // 6: 16384
-    TKS_VARIANT(1024, 32, true),   // 7: 32768
-    TKS_VARIANT(1024, 16, false),  // 8: streaming, 16384 per tile
-    TKS_VARIANT(256, 16, false),   // 9: streaming, 4096 per tile
-    TKS_ROWS(512, 16, 1),          // 10: one WG per row, 8192 per tile
-    TKS_ROWS(1024, 16, 1),         // 11: one WG per row, 16384 per tile
+    TKS_SPLIT(512, 4, true),     // 0: 2048 logits per WG
+    TKS_SPLIT(512, 8, true),     // 1: 4096
+    TKS_SPLIT(512, 16, true),    // 2: 8192
+    TKS_SPLIT(1024, 4, true),    // 3: 4096
+    TKS_SPLIT(1024, 8, true),    // 4: 8192
+    TKS_SPLIT(1024, 16, true),   // 5: 16384
+    TKS_SPLIT(1024, 32, true),   // 6: 32768
+    TKS_SPLIT(1024, 16, false),  // 7: streaming, 16384 per tile
+    TKS_SPLIT(512, 16, false),   // 8: streaming, 8192 per tile
+    TKS_ROWS(512, 16, 1),        // 9: one WG per row, 8192 per tile
+    TKS_ROWS(1024, 16, 1),       // 10: one WG per row, 16384 per tile
 };
-#undef TKS_VARIANT
+#undef TKS_SPLIT
 #undef TKS_ROWS
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 struct DeviceInfo {
     int cus = 0;
-    int capacity[kNumVariants] = {};  // co-resident WGs per variant on the whole device
+    int resident[kNumVariants] = {};  // co-resident WGs per variant on the whole device
 };
 
-// Scratch of one (device, stream): the status word, then one RowWorkspace
-// per row (row r always at the same address, whatever the row count of a
-// call).  Zeroed when allocated; kernels keep it consistent across calls.
+// Scratch of one (device, stream): the status word, then, for split
+// launches with several WGs per row, one SplitRow per row (row r always at
+// the same address, whatever the row count of a call) and the stage of
+// candidate regions.  Zeroed when allocated; the kernels leave it as they
+// found it (every count and entry they set is cleared by the row's last WG).
+// Buffers replaced by larger ones are kept until the workspace is released,
+// since captured graphs may still refer to them.
 struct Workspace {
-    void* base = nullptr;
+    void* base = nullptr;     // status word + SplitRow per row
     size_t bytes = 0;
-    void* aux = nullptr;  // ordered output: recorded keys, merge buffers (no clearing needed)
+    void* stage = nullptr;    // candidate regions
+    size_t stage_bytes = 0;
+    void* aux = nullptr;      // ordered output: recorded keys, merge buffers (no clearing needed)
     size_t aux_bytes = 0;
-    void* lg = nullptr;   // indexer selection without a logits output: the logits
+    void* lg = nullptr;       // indexer selection without a logits output: the logits
     size_t lg_bytes = 0;
-    void* at = nullptr;   // attention over the selected positions: per-chunk partials
+    void* at = nullptr;       // attention over the selected positions: per-chunk partials
     size_t at_bytes = 0;
+    std::vector<void*> retired;
 };
 
 std::recursive_mutex g_mu;  // recursive: the indexer entry point holds it across its launches
@@ -2377,6 +2179,7 @@ std::map<int, DeviceInfo> g_dev;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
 constexpr size_t kStatusBytes = 256;
+constexpr int32_t kMaxN = 1 << 30;  // longest row accepted (element offsets stay far from 32-bit limits)
 
 int device_info(int dev, DeviceInfo** out) {
     auto it = g_dev.find(dev);
@@ -2387,11 +2190,7 @@ int device_info(int dev, DeviceInfo** out) {
         for (int v = 0; v < kNumVariants; ++v) {
             int nb = 0;
             if (kVariants[v].occupancy(&nb, kVariants[v].block) != (int)hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            // WGs that are certainly co-resident: what the occupancy query
-            // allows, but at most two per CU, and one for 1024-thread WGs
-            // (measured with a bounded-wait probe on MI355X)
-            const int cap = kVariants[v].block >= 1024 ? 1 : 2;
-            d.capacity[v] = (nb < cap ? nb : cap) * d.cus;
+            d.resident[v] = (nb > 0 ? nb : 1) * d.cus;
         }
         it = g_dev.emplace(dev, d).first;
     }
@@ -2409,78 +2208,78 @@ int64_t max_row_chunks(const float* logits, int32_t n) {
     return (3 + (int64_t)n + 3) / 4;
 }
 
-int idx_bits_for(int32_t n) {
-    uint32_t top = (uint32_t)(n - 1);
-    int bits = 0;
-    while (top) { ++bits; top >>= 1; }
-    bits = (bits + 7) / 8 * 8;
-    return bits < 8 ? 8 : bits;
-}
-
 struct Launch {
     int variant;
     int G;
     int chunks_per_wg;
+    int region;         // entries per WG region (split kernel)
+    int sample_chunks;  // split kernel
 };
 
-// Check an explicit shape: resident variants must cover the row in G slices;
-// G > 1 needs every WG of the launch co-resident.
-int check_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, int v, int G, Launch* L) {
+// Sample of a row for the split kernel's bound (chunks, a multiple of 16):
+// 1024 chunks, 4096 for rows of 512K logits or more (the candidate count
+// above the bound grows with sqrt(k n / sample)); at most what the variant's
+// registers hold.
+int sample_chunks_for(int64_t maxc, int block) {
+    const int want = maxc >= 131072 ? 4096 : 1024;
+    const int spt = kSampleMax / block > 4 ? 4 : kSampleMax / block;
+    const int cap = spt * block;
+    return want < cap ? want : cap;
+}
+
+// Check an explicit shape: resident variants must cover the row in G
+// slices, the one-WG-per-row kernel takes G == 1, the split kernel at most
+// min(block, kMaxSplit) WGs per row.
+int check_shape(int64_t rows, int64_t maxc, int v, int G, Launch* L) {
     if (v < 0 || v >= kNumVariants || G < 1) return TOPK_SELECT_ERROR_INVALID_VALUE;
     const Variant& var = kVariants[v];
     const int64_t tile_chunks = (int64_t)var.block * (var.items / 4);
     int64_t cpw = (maxc + G - 1) / G;
+    if (cpw < 1) cpw = 1;
     if (var.resident && cpw > tile_chunks) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (var.rows_kernel && G != 1) return TOPK_SELECT_ERROR_INVALID_VALUE;
-    if (cpw < 1) cpw = 1;
-    if (G > 1 && rows * (int64_t)G > (int64_t)d.capacity[v]) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (!var.rows_kernel && (G > kMaxSplit || G > var.block)) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows * (int64_t)G > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
     L->variant = v;
     L->G = G;
     L->chunks_per_wg = (int)cpw;
+    const int64_t slice = 4 * cpw;
+    L->region = (int)(slice < kBufCap ? slice : kBufCap);
+    L->sample_chunks = sample_chunks_for(maxc, var.block);
     return TOPK_SELECT_SUCCESS;
 }
 
-// Default shape (measured on MI355X).  A cross-workgroup merge round costs
-// about the same for any split, while the per-pass time falls with the
-// slice, so few rows are spread over many WGs of about 2K-8K logits each
-// (1024 threads once a row uses more than 16 WGs).  Many rows: the fewest
-// resident WGs per row that can all be co-resident, else streaming WGs.
+// Default shape (measured on MI355X).  Few rows are spread over many WGs of
+// about 2K-8K logits each (1024 threads once a row uses more than 16 WGs);
+// a moderate number of rows over WGs of about 32K (fewer regions for each
+// row's finishing WG to gather: 64 ragged rows of 131,072 take 19.5 us with
+// 4 WGs per row against 31.9 with 8); many rows take the one-WG-per-row
+// kernel; rows too long for resident slices stream.
 int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
     auto tile_chunks = [](int v) { return (int64_t)kVariants[v].block * (kVariants[v].items / 4); };
-    if (rows * 8 <= d.cus) {
-        int64_t G = (maxc + 511) / 512;  // about 2K logits per WG
-        if (G > 128) G = 128;
-        if (G > d.cus / rows) G = d.cus / rows;
-        if (G < 1) G = 1;
-        const int64_t per = (maxc + G - 1) / G;
-        const int v512[] = {0, 1, 4, 6, 7}, v1024[] = {2, 3, 5, 7};
-        if (G <= 16) {
-            for (int v : v512)
-                if (per <= tile_chunks(v)) return check_shape(d, rows, maxc, v, (int)G, L);
-        } else {
-            for (int v : v1024)
-                if (per <= tile_chunks(v)) return check_shape(d, rows, maxc, v, (int)G, L);
-        }
-    }
-    const int order_many[] = {7, 5, 3, 1, 0};
-    for (int v : order_many) {
-        const int64_t G = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
-        if (G == 1 || rows * G <= (int64_t)d.capacity[v]) return check_shape(d, rows, maxc, v, (int)G, L);
-    }
-    // many rows: one streaming WG per row
-    if (rows >= d.cus) return check_shape(d, rows, maxc, 10, 1, L);
-    // few long rows: as many streaming WGs per row as can be co-resident
-    const int v = (maxc >= 16384) ? 8 : 9;
-    int64_t G = d.capacity[v] / (rows > 0 ? rows : 1);
-    const int64_t gmax = (maxc + tile_chunks(v) - 1) / tile_chunks(v);
-    if (G > gmax) G = gmax;
+    if (rows >= d.cus) return check_shape(rows, maxc, 9, 1, L);
+    int64_t target = rows * 8 <= d.cus ? 512 : 8192;  // chunks per WG
+    int64_t G = (maxc + target - 1) / target;
+    if (rows * 8 <= d.cus && G > 128) G = 128;
+    if (G > kMaxSplit) G = kMaxSplit;
     if (G < 1) G = 1;
-    return check_shape(d, rows, maxc, v, (int)G, L);
+    const int64_t per = (maxc + G - 1) / G;
+    const int v512[] = {0, 1, 2}, v1024[] = {3, 4, 5, 6};
+    if (G <= 16) {
+        for (int v : v512)
+            if (per <= tile_chunks(v)) return check_shape(rows, maxc, v, (int)G, L);
+    }
+    for (int v : v1024)
+        if (per <= tile_chunks(v)) return check_shape(rows, maxc, v, (int)G, L);
+    // rows too long for resident slices: streaming WGs
+    G = kMaxSplit;
+    const int64_t gmin = (maxc + tile_chunks(7) - 1) / tile_chunks(7);
+    if (gmin < G) G = gmin < 1 ? 1 : gmin;
+    return check_shape(rows, maxc, 7, (int)G, L);
 }
 
 int validate(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k, const int32_t* out) {
-    if (rows < 0 || n < 1 || k < 1 || k > n) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (rows < 0 || n < 1 || n > kMaxN || k < 1 || k > n) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows == 0) return TOPK_SELECT_SUCCESS;
     if (!logits || !out) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (((uintptr_t)logits & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3))
@@ -2495,54 +2294,35 @@ int validate(const float* logits, int32_t rows, int32_t n, const int32_t* length
     return TOPK_SELECT_SUCCESS;
 }
 
-int get_workspace(int dev, hipStream_t stream, size_t need, Workspace** out) {
-    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
-    if (w.bytes < need) {
-        if (w.base) {
-            // the old workspace may still be in use by enqueued work
-            if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            (void)hipFree(w.base);
-            w.base = nullptr;
-            w.bytes = 0;
-        }
-        void* p = nullptr;
-        if (hipMalloc(&p, need) != hipSuccess) {
-            (void)hipGetLastError();
-            return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
-        }
-        if (hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
-            (void)hipFree(p);
-            return TOPK_SELECT_ERROR_LAUNCH;
-        }
-        w.base = p;
-        w.bytes = need;
-    }
-    *out = &w;
-    return TOPK_SELECT_SUCCESS;
+// Is work being captured into a graph on `stream`?  Allocations and clears
+// must not happen then: they would not be replayed, or would break the
+// capture.
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+    return st != hipStreamCaptureStatusNone;
 }
 
-// Grow-only scratch that needs no clearing (the old one is freed once the
-// stream has finished with it).
-int grow_scratch(hipStream_t stream, void** ptr, size_t* bytes, size_t need) {
-    if (*bytes < need) {
-        if (*ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            (void)hipFree(*ptr);
-            *ptr = nullptr;
-            *bytes = 0;
-        }
-        void* p = nullptr;
-        if (hipMalloc(&p, need) != hipSuccess) {
-            (void)hipGetLastError();
-            return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
-        }
-        *ptr = p;
-        *bytes = need;
+// Grow-only scratch buffer of a workspace: a larger need allocates a new
+// buffer (cleared when `zero`) and retires the old one (kept until the
+// workspace is released: enqueued work and captured graphs may use it).
+int grow(Workspace& w, hipStream_t stream, void** ptr, size_t* bytes, size_t need, bool zero) {
+    if (*bytes >= need) return TOPK_SELECT_SUCCESS;
+    if (capturing(stream)) return TOPK_SELECT_ERROR_CAPTURE;
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess) {
+        (void)hipGetLastError();
+        return TOPK_SELECT_ERROR_OUT_OF_MEMORY;
     }
+    if (zero && hipMemsetAsync(p, 0, need, stream) != hipSuccess) {
+        (void)hipFree(p);
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+    if (*ptr) w.retired.push_back(*ptr);
+    *ptr = p;
+    *bytes = need;
     return TOPK_SELECT_SUCCESS;
 }
-
-int get_aux(hipStream_t stream, Workspace* w, size_t need) { return grow_scratch(stream, &w->aux, &w->aux_bytes, need); }
 
 bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -2605,14 +2385,19 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     const int64_t maxc = max_row_chunks(logits, n);
     Launch L;
-    rc = forced ? check_shape(*d, rows, maxc, forced->variant, forced->wgs_per_row, &L)
+    rc = forced ? check_shape(rows, maxc, forced->variant, forced->wgs_per_row, &L)
                 : choose_shape(*d, rows, maxc, &L);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     const Variant& var = kVariants[L.variant];
-    const size_t rows_bytes = L.G > 1 ? (size_t)rows * sizeof(RowWorkspace) : 0;
-    Workspace* w = nullptr;
-    rc = get_workspace(dev, stream, kStatusBytes + rows_bytes, &w);
+    const bool split = !var.rows_kernel && L.G > 1;
+    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+    const size_t rows_bytes = split ? (size_t)rows * sizeof(SplitRow) : 0;
+    rc = grow(w, stream, &w.base, &w.bytes, kStatusBytes + rows_bytes, true);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
+    if (split) {
+        rc = grow(w, stream, &w.stage, &w.stage_bytes, (size_t)rows * (size_t)L.G * (size_t)L.region * 8u, true);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+    }
     SortShape sh{};
     size_t keys_bytes = 0;
     if (ordered) {
@@ -2622,28 +2407,29 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
         if ((int64_t)rows * sh.nruns > 0x7FFFFFFFll || (int64_t)rows * sh.rank_wgs > 0x7FFFFFFFll ||
             (int64_t)rows * (sh.kp / (kMergeBlock * kMergeItems)) > 0x7FFFFFFFll)
             return TOPK_SELECT_ERROR_INVALID_VALUE;
-        rc = get_aux(stream, w, 2u * keys_bytes + run_bytes);
+        rc = grow(w, stream, &w.aux, &w.aux_bytes, 2u * keys_bytes + run_bytes, false);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
     }
-    char* base = reinterpret_cast<char*>(w->base);
+    char* base = reinterpret_cast<char*>(w.base);
     KParams P;
     P.logits = logits;
     P.lengths = lengths;
     // ordered output: the selection writes its indices and their keys to
     // scratch, the sort writes out_idx
-    char* const aux = reinterpret_cast<char*>(w->aux);
+    char* const aux = reinterpret_cast<char*>(w.aux);
     P.out = ordered ? reinterpret_cast<int32_t*>(aux + keys_bytes) : out;
     P.keys = ordered ? reinterpret_cast<uint32_t*>(aux) : nullptr;
     P.status = reinterpret_cast<uint32_t*>(base);
-    P.ws = L.G > 1 ? reinterpret_cast<RowWorkspace*>(base + kStatusBytes) : nullptr;
+    P.rws = split ? reinterpret_cast<SplitRow*>(base + kStatusBytes) : nullptr;
+    P.stage = split ? reinterpret_cast<uint64_t*>(w.stage) : nullptr;
     P.rows = rows;
     P.n = n;
     P.k = k;
     P.G = L.G;
     P.chunks_per_wg = L.chunks_per_wg;
-    P.idx_bits = idx_bits_for(n);
-    P.mcopies = L.G <= 16 ? 1 : (L.G <= 32 ? 2 : kMergeCopies);
-    P.ahead = var.rows_kernel ? d->capacity[L.variant] : 0;
+    P.region = L.region;
+    P.sample_chunks = L.sample_chunks;
+    P.ahead = var.rows_kernel ? d->resident[L.variant] : 0;
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
@@ -2686,12 +2472,12 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     }
     return TOPK_SELECT_SUCCESS;
 }
-
 // ---- indexer logits and the selection on them
 
 int validate_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
                      int32_t dim, int64_t kstride, const int32_t* lengths, const float* logits) {
-    if (rows < 0 || n < 1 || heads < 1 || heads > 64 || kstride < 0) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    if (rows < 0 || n < 1 || n > kMaxN || heads < 1 || heads > 64 || kstride < 0)
+        return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (dim != 32 && dim != 64 && dim != 128) return TOPK_SELECT_ERROR_INVALID_VALUE;
     if (rows == 0) return TOPK_SELECT_SUCCESS;
     if (!q || !kc || !w) return TOPK_SELECT_ERROR_INVALID_VALUE;
@@ -2779,7 +2565,7 @@ int run_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t r
     float* lg = logits;
     if (!lg) {
         Workspace& ws = g_ws[{dev, (uintptr_t)stream}];
-        rc = grow_scratch(stream, &ws.lg, &ws.lg_bytes, (size_t)rows * (size_t)n * 4u);
+        rc = grow(ws, stream, &ws.lg, &ws.lg_bytes, (size_t)rows * (size_t)n * 4u, false);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
         lg = reinterpret_cast<float*>(ws.lg);
     }
@@ -2815,7 +2601,7 @@ int run_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, con
     if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
     std::lock_guard<std::recursive_mutex> lock(g_mu);
     Workspace& ws = g_ws[{dev, (uintptr_t)stream}];
-    int rc = grow_scratch(stream, &ws.at, &ws.at_bytes, (size_t)rows * (size_t)S * heads * (dim + 2) * 4u);
+    int rc = grow(ws, stream, &ws.at, &ws.at_bytes, (size_t)rows * (size_t)S * heads * (dim + 2) * 4u, false);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     AttnParams p;
     p.q = q;
@@ -2976,12 +2762,18 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
         std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
         auto it = tks::g_ws.find({dev, (uintptr_t)stream});
         if (it == tks::g_ws.end() || !it->second.base) return TOPK_SELECT_SUCCESS;
+        tks::Workspace& w = it->second;
         uint32_t v = 0;
-        if (hipMemcpy(&v, it->second.base, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
-            return TOPK_SELECT_ERROR_LAUNCH;
-        if (v) {
+        if (hipMemcpy(&v, w.base, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        if (v & tks::kFlagTimeout) {
+            // a WG gave up waiting for another: counts or candidates it did
+            // not see may have been written after the row was finished, so
+            // the whole coordination state is cleared (the stream is idle)
+            if (hipMemset(w.base, 0, w.bytes) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+            if (w.stage && hipMemset(w.stage, 0, w.stage_bytes) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        } else if (v) {
             const uint32_t zero = 0;
-            if (hipMemcpy(it->second.base, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            if (hipMemcpy(w.base, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
                 return TOPK_SELECT_ERROR_LAUNCH;
         }
         *flags = (int32_t)v;
@@ -2995,17 +2787,20 @@ int topk_select_release_workspace(void) {
     try {
         std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
         int rc = TOPK_SELECT_SUCCESS;
+        int cur = 0;
+        (void)hipGetDevice(&cur);
         for (auto& kv : tks::g_ws) {
-            if (kv.second.base || kv.second.aux || kv.second.lg || kv.second.at) {
-                int cur = 0;
-                (void)hipGetDevice(&cur);
-                (void)hipSetDevice(kv.first.first);
-                if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                for (void* p : {kv.second.base, kv.second.aux, kv.second.lg, kv.second.at})
-                    if (p && hipFree(p) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
-                (void)hipSetDevice(cur);
-            }
+            tks::Workspace& w = kv.second;
+            std::vector<void*> bufs = w.retired;
+            for (void* p : {w.base, w.stage, w.aux, w.lg, w.at})
+                if (p) bufs.push_back(p);
+            if (bufs.empty()) continue;
+            (void)hipSetDevice(kv.first.first);
+            if (hipDeviceSynchronize() != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
+            for (void* p : bufs)
+                if (hipFree(p) != hipSuccess) rc = TOPK_SELECT_ERROR_LAUNCH;
         }
+        (void)hipSetDevice(cur);
         tks::g_ws.clear();
         return rc;
     } catch (...) {
@@ -3021,6 +2816,8 @@ const char* topk_select_error_string(int status) {
         case TOPK_SELECT_ERROR_LAUNCH: return "HIP call or kernel launch failed";
         case TOPK_SELECT_ERROR_NO_DEVICE: return "no usable HIP device is current";
         case TOPK_SELECT_ERROR_DEVICE_FLAG: return "a kernel raised a device-side error flag";
+        case TOPK_SELECT_ERROR_CAPTURE:
+            return "scratch would have to be allocated during graph capture (call once on the stream first)";
         default: return "unknown status";
     }
 }

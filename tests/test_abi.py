@@ -46,7 +46,7 @@ def test_version_and_error_strings(lib):
     from sparse_attention_topk_fp32_amd import _native
 
     assert lib.topk_select_version() == 1
-    for code in range(6):
+    for code in range(7):
         s = _native.error_string(code)
         assert s and s != "unknown status"
     assert _native.error_string(99) == "unknown status"
@@ -73,6 +73,9 @@ def test_argument_checks_answer_before_any_hip_call(lib):
     assert _call(lib, a, 1, 16, None, 4, o + 1) == INV
     assert _call(lib, a, 2, 16, None, 4, a + 64) == INV  # out overlaps logits
     assert _call(lib, a, 2, 16, o, 4, o + 4) == INV  # out overlaps lengths
+    # rows longer than 2^30 logits are refused (offsets stay far from 32-bit limits)
+    assert _call(lib, a, 1, (1 << 30) + 1, None, 4, o) == INV
+    assert _call(lib, a, 1, 0x7FFFFFFF, None, 4, o) == INV
 
 
 def test_sorted_argument_checks_answer_before_any_hip_call(lib):
