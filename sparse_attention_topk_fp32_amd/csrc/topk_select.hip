@@ -2084,16 +2084,20 @@ using OccFn = int (*)(int*, int);
 // The sample's chunks per thread are a template parameter: 1 for the usual
 // 1024-chunk sample of 1024-thread WGs (code for unused sample slots still
 // costs issue cycles), else what the sample needs.
-constexpr int split_spt(int block, int sample_chunks) { return sample_chunks <= block ? 1 : 4; }
+constexpr int split_spt(int block, int sample_chunks) {
+    return sample_chunks <= block ? 1 : (sample_chunks <= 2 * block ? 2 : 4);
+}
 
 template <int B, int I, bool R>
 void launch_split(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
     const int spt = split_spt(B, p.sample_chunks);
     if (p.keys) {
         if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 1>), grid, block, 0, s, p);
+        else if (spt == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 2>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 4>), grid, block, 0, s, p);
     } else {
         if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 1>), grid, block, 0, s, p);
+        else if (spt == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 2>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 4>), grid, block, 0, s, p);
     }
 }
@@ -2258,9 +2262,17 @@ int check_shape(int64_t rows, int64_t maxc, int v, int G, Launch* L) {
 int choose_shape(const DeviceInfo& d, int64_t rows, int64_t maxc, Launch* L) {
     auto tile_chunks = [](int v) { return (int64_t)kVariants[v].block * (kVariants[v].items / 4); };
     if (rows >= d.cus) return check_shape(rows, maxc, 9, 1, L);
-    int64_t target = rows * 8 <= d.cus ? 512 : 8192;  // chunks per WG
-    int64_t G = (maxc + target - 1) / target;
-    if (rows * 8 <= d.cus && G > 128) G = 128;
+    // Few rows: slices of up to 2048 chunks (8192 logits), at least 8 WGs
+    // per row while slices stay >= 512 chunks.  The finishing WG's gather
+    // grows with the number of regions, so fewer, longer slices beat many
+    // short ones once a row has 8 or more.  Many rows: long slices.
+    const bool few = rows * 8 <= d.cus;
+    int64_t G = few ? (maxc + 2047) / 2048 : (maxc + 8191) / 8192;
+    if (few) {
+        const int64_t g8 = (maxc + 511) / 512;
+        if (G < 8) G = g8 < 8 ? g8 : 8;
+        if (G > 128) G = 128;
+    }
     if (G > kMaxSplit) G = kMaxSplit;
     if (G < 1) G = 1;
     const int64_t per = (maxc + G - 1) / G;
