@@ -52,8 +52,10 @@ enum {
     TOPK_SELECT_ERROR_LAUNCH = 3,        /* a HIP call or the kernel launch failed */
     TOPK_SELECT_ERROR_NO_DEVICE = 4,     /* no usable HIP device is current */
     TOPK_SELECT_ERROR_DEVICE_FLAG = 5,   /* a kernel raised a device-side error flag */
-    TOPK_SELECT_ERROR_CAPTURE = 6        /* scratch would have to be allocated while the stream is
+    TOPK_SELECT_ERROR_CAPTURE = 6,       /* scratch would have to be allocated while the stream is
                                             being captured into a graph; nothing was enqueued */
+    TOPK_SELECT_ERROR_SCRATCH_LIMIT = 7  /* topk_select_no_alloc: the input needs more than its fixed
+                                            scratch; nothing was enqueued */
 };
 
 /* hipStream_t, passed as an opaque pointer so this header needs no HIP headers.
@@ -96,6 +98,38 @@ typedef void* topk_select_stream_t;
  */
 int topk_select(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                 int32_t* out_idx, topk_select_stream_t stream);
+
+/*
+ * topk_select_no_alloc - topk_select for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * topk_select, with the same launch shapes, so the same output bytes.
+ *
+ * Scratch: a static device array of TOPK_SELECT_NO_ALLOC_SCRATCH_BYTES
+ * (32 MiB) per device, held until the process ends; the call allocates
+ * nothing (no hipMalloc/hipFree, no allocating library routine).  The first
+ * call on a device looks the array up and clears it with a kernel on
+ * `stream`, waiting for that kernel (returns TOPK_SELECT_ERROR_CAPTURE if
+ * the stream is being captured then: make one call before capturing).
+ * Shapes with one workgroup per row (rows >= the device's CU count) need
+ * only 256 bytes of it; shapes that split a row over G workgroups need
+ * rows * G * region * 8 bytes of candidate stage (region = the candidate
+ * capacity of one workgroup, at most 7168) plus a row table, and are limited
+ * to 256 rows.  An input beyond the limit returns
+ * TOPK_SELECT_ERROR_SCRATCH_LIMIT and enqueues nothing (for example, one
+ * row of n = 2^30, or 64 rows of n = 2^20; the configurations up to 64 rows
+ * of n = 131072 and any row count >= the CU count fit).
+ *
+ * Every call on a device shares that device's array, and each call leaves
+ * it cleared for the next: calls that overlap in time on one device (on
+ * different streams, or from different host threads without ordering) race
+ * on it and give wrong results.  Serialise them, e.g. on one stream.
+ * topk_select_device_status reports (and clears) flags raised by these calls
+ * as well, on the device current when it is called.
+ */
+#define TOPK_SELECT_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+int topk_select_no_alloc(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                         int32_t* out_idx, topk_select_stream_t stream);
 
 /*
  * topk_select_sorted - the same selection, each row in order: values
@@ -250,7 +284,9 @@ int topk_select_variant_info(int32_t v, topk_select_plan_t* plan);
  * counts or candidates written after their row was finished; this call
  * clears the whole workspace then, and a later call on the stream is exact
  * only after it.  Returns DEVICE_FLAG when any flag was set, SUCCESS
- * otherwise.
+ * otherwise.  The flags of topk_select_no_alloc calls on the current device
+ * are read and cleared as well (wait for those calls first when they ran on
+ * other streams).
  */
 int topk_select_device_status(topk_select_stream_t stream, int32_t* flags);
 

@@ -29,6 +29,7 @@ __all__ = [
     "select",
     "topk_select",
     "topk_select_ex",
+    "topk_select_no_alloc",
     "select_sorted",
     "indexer_logits",
     "indexer_select",
@@ -65,6 +66,13 @@ def topk_select_ex(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int
     p = _native.PlanT(variant, wgs_per_row, 0, 0, 0, 0)
     return _native.load().topk_select_ex(logits_ptr or None, rows, n, lengths_ptr or None, k, out_ptr or None,
                                          stream or None, ctypes.byref(p))
+
+
+def topk_select_no_alloc(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                         stream: int = 0) -> int:
+    """Raw C-ABI call of the allocation-free entry point; returns the status code."""
+    return _native.load().topk_select_no_alloc(logits_ptr or None, rows, n, lengths_ptr or None, k,
+                                               out_ptr or None, stream or None)
 
 
 def topk_select_sorted(logits_ptr: int, rows: int, n: int, lengths_ptr: Optional[int], k: int, out_ptr: int,

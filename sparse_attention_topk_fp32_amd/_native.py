@@ -21,11 +21,13 @@ ERROR_LAUNCH = 3
 ERROR_NO_DEVICE = 4
 ERROR_DEVICE_FLAG = 5
 ERROR_CAPTURE = 6
+ERROR_SCRATCH_LIMIT = 7
 
 # Names declared in include/topk_select.h.
 EXPORTS = (
     "topk_select",
     "topk_select_ex",
+    "topk_select_no_alloc",
     "topk_select_sorted",
     "topk_select_sorted_ex",
     "topk_indexer_logits",
@@ -78,6 +80,8 @@ def load() -> ctypes.CDLL:
         lib.topk_select.restype = ctypes.c_int
         lib.topk_select_ex.argtypes = [P, I, I, P, I, P, P, ctypes.POINTER(PlanT)]
         lib.topk_select_ex.restype = ctypes.c_int
+        lib.topk_select_no_alloc.argtypes = [P, I, I, P, I, P, P]
+        lib.topk_select_no_alloc.restype = ctypes.c_int
         lib.topk_select_sorted.argtypes = [P, I, I, P, I, P, P, P]
         lib.topk_select_sorted.restype = ctypes.c_int
         lib.topk_select_sorted_ex.argtypes = [P, I, I, P, I, P, P, P, ctypes.POINTER(PlanT)]

@@ -2185,6 +2185,19 @@ std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 constexpr size_t kStatusBytes = 256;
 constexpr int32_t kMaxN = 1 << 30;  // longest row accepted (element offsets stay far from 32-bit limits)
 
+// Fixed scratch of topk_select_no_alloc: the status word, a SplitRow for
+// each of up to kScratchRows rows (row r always at the same address), then
+// the stage of candidate regions.  One copy per device, for the life of the
+// process.  Host code never passes `scratch` itself (on the host the name is
+// only a stand-in): the device address comes from hipGetSymbolAddress, once
+// per device, and is kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)TOPK_SELECT_NO_ALLOC_SCRATCH_BYTES;
+constexpr int kScratchRows = 256;
+constexpr size_t kScratchStage = (kStatusBytes + (size_t)kScratchRows * sizeof(SplitRow) + 255u) / 256u * 256u;
+static_assert(kScratchStage < kScratchBytes, "scratch too small for its row table");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::map<int, void*> g_scratch;  // device -> device address of `scratch`
+
 int device_info(int dev, DeviceInfo** out) {
     auto it = g_dev.find(dev);
     if (it == g_dev.end()) {
@@ -2306,6 +2319,33 @@ int validate(const float* logits, int32_t rows, int32_t n, const int32_t* length
     return TOPK_SELECT_SUCCESS;
 }
 
+__global__ void __launch_bounds__(256) topk_clear_kernel(uint4* p, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * 256u;
+    for (size_t i = (size_t)blockIdx.x * 256u + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+bool capturing(hipStream_t stream);
+
+// Device address of `scratch` on `dev` (the current device).  The first
+// call on a device looks it up, clears the array with a kernel on `stream`
+// and waits for it, so every later call on any stream finds it zeroed.
+int scratch_address(int dev, hipStream_t stream, char** out) {
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        if (capturing(stream)) return TOPK_SELECT_ERROR_CAPTURE;
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return TOPK_SELECT_ERROR_LAUNCH;
+        }
+        topk_clear_kernel<<<dim3(1024), dim3(256), 0, stream>>>(reinterpret_cast<uint4*>(ptr), kScratchBytes / 16u);
+        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        it = g_scratch.emplace(dev, ptr).first;
+    }
+    *out = reinterpret_cast<char*>(it->second);
+    return TOPK_SELECT_SUCCESS;
+}
+
 // Is work being captured into a graph on `stream`?  Allocations and clears
 // must not happen then: they would not be replayed, or would break the
 // capture.
@@ -2380,7 +2420,7 @@ void launch_sort(const SortShape& sh, int32_t rows, hipStream_t stream, const So
 }
 
 int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k, int32_t* out,
-        bool ordered, float* vals, hipStream_t stream, const topk_select_plan_t* forced) {
+        bool ordered, float* vals, hipStream_t stream, const topk_select_plan_t* forced, bool no_alloc = false) {
     int rc = validate(logits, rows, n, lengths, k, out);
     if (rc != TOPK_SELECT_SUCCESS || rows == 0) return rc;
     if (ordered && vals) {
@@ -2402,13 +2442,28 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     const Variant& var = kVariants[L.variant];
     const bool split = !var.rows_kernel && L.G > 1;
-    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
-    const size_t rows_bytes = split ? (size_t)rows * sizeof(SplitRow) : 0;
-    rc = grow(w, stream, &w.base, &w.bytes, kStatusBytes + rows_bytes, true);
-    if (rc != TOPK_SELECT_SUCCESS) return rc;
-    if (split) {
-        rc = grow(w, stream, &w.stage, &w.stage_bytes, (size_t)rows * (size_t)L.G * (size_t)L.region * 8u, true);
+    const size_t stage_bytes = split ? (size_t)rows * (size_t)L.G * (size_t)L.region * 8u : 0;
+    char* base = nullptr;
+    void* stage = nullptr;
+    if (no_alloc) {
+        if (ordered) return TOPK_SELECT_ERROR_INVALID_VALUE;
+        if (split && (rows > kScratchRows || stage_bytes > kScratchBytes - kScratchStage))
+            return TOPK_SELECT_ERROR_SCRATCH_LIMIT;
+        rc = scratch_address(dev, stream, &base);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
+        stage = base + kScratchStage;
+    }
+    Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+    if (!no_alloc) {
+        const size_t rows_bytes = split ? (size_t)rows * sizeof(SplitRow) : 0;
+        rc = grow(w, stream, &w.base, &w.bytes, kStatusBytes + rows_bytes, true);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+        if (split) {
+            rc = grow(w, stream, &w.stage, &w.stage_bytes, stage_bytes, true);
+            if (rc != TOPK_SELECT_SUCCESS) return rc;
+        }
+        base = reinterpret_cast<char*>(w.base);
+        stage = w.stage;
     }
     SortShape sh{};
     size_t keys_bytes = 0;
@@ -2422,7 +2477,6 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
         rc = grow(w, stream, &w.aux, &w.aux_bytes, 2u * keys_bytes + run_bytes, false);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
     }
-    char* base = reinterpret_cast<char*>(w.base);
     KParams P;
     P.logits = logits;
     P.lengths = lengths;
@@ -2433,7 +2487,7 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.keys = ordered ? reinterpret_cast<uint32_t*>(aux) : nullptr;
     P.status = reinterpret_cast<uint32_t*>(base);
     P.rws = split ? reinterpret_cast<SplitRow*>(base + kStatusBytes) : nullptr;
-    P.stage = split ? reinterpret_cast<uint64_t*>(w.stage) : nullptr;
+    P.stage = split ? reinterpret_cast<uint64_t*>(stage) : nullptr;
     P.rows = rows;
     P.n = n;
     P.k = k;
@@ -2706,6 +2760,15 @@ int topk_select_ex(const float* logits, int32_t rows, int32_t n, const int32_t* 
     }
 }
 
+int topk_select_no_alloc(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
+                         int32_t* out_idx, topk_select_stream_t stream) {
+    try {
+        return tks::run(logits, rows, n, lengths, k, out_idx, false, nullptr, (hipStream_t)stream, nullptr, true);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
 int topk_select_sorted(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                        int32_t* out_idx, float* out_val, topk_select_stream_t stream) {
     try {
@@ -2772,21 +2835,32 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
         if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
         if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
         std::lock_guard<std::recursive_mutex> lock(tks::g_mu);
+        // Reads the status word at the start of `base` and clears it; after
+        // a timeout (a WG gave up waiting for another, so counts or
+        // candidates it did not see may have been written after the row was
+        // finished) the whole coordination state is cleared instead.
+        auto take = [](void* base, size_t bytes, void* stage, size_t stage_bytes, uint32_t* v) -> bool {
+            if (hipMemcpy(v, base, sizeof(*v), hipMemcpyDeviceToHost) != hipSuccess) return false;
+            if (*v & tks::kFlagTimeout) {
+                if (hipMemset(base, 0, bytes) != hipSuccess) return false;
+                if (stage && hipMemset(stage, 0, stage_bytes) != hipSuccess) return false;
+            } else if (*v) {
+                const uint32_t zero = 0;
+                if (hipMemcpy(base, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return false;
+            }
+            return true;
+        };
+        uint32_t v = 0, u = 0;
         auto it = tks::g_ws.find({dev, (uintptr_t)stream});
-        if (it == tks::g_ws.end() || !it->second.base) return TOPK_SELECT_SUCCESS;
-        tks::Workspace& w = it->second;
-        uint32_t v = 0;
-        if (hipMemcpy(&v, w.base, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-        if (v & tks::kFlagTimeout) {
-            // a WG gave up waiting for another: counts or candidates it did
-            // not see may have been written after the row was finished, so
-            // the whole coordination state is cleared (the stream is idle)
-            if (hipMemset(w.base, 0, w.bytes) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-            if (w.stage && hipMemset(w.stage, 0, w.stage_bytes) != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-        } else if (v) {
-            const uint32_t zero = 0;
-            if (hipMemcpy(w.base, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
-                return TOPK_SELECT_ERROR_LAUNCH;
+        if (it != tks::g_ws.end() && it->second.base) {
+            tks::Workspace& w = it->second;
+            if (!take(w.base, w.bytes, w.stage, w.stage_bytes, &u)) return TOPK_SELECT_ERROR_LAUNCH;
+            v |= u;
+        }
+        auto sc = tks::g_scratch.find(dev);
+        if (sc != tks::g_scratch.end()) {
+            if (!take(sc->second, tks::kScratchBytes, nullptr, 0, &u)) return TOPK_SELECT_ERROR_LAUNCH;
+            v |= u;
         }
         *flags = (int32_t)v;
         return v ? TOPK_SELECT_ERROR_DEVICE_FLAG : TOPK_SELECT_SUCCESS;
@@ -2830,6 +2904,8 @@ const char* topk_select_error_string(int status) {
         case TOPK_SELECT_ERROR_DEVICE_FLAG: return "a kernel raised a device-side error flag";
         case TOPK_SELECT_ERROR_CAPTURE:
             return "scratch would have to be allocated during graph capture (call once on the stream first)";
+        case TOPK_SELECT_ERROR_SCRATCH_LIMIT:
+            return "the input needs more scratch than the fixed array of topk_select_no_alloc (nothing was enqueued)";
         default: return "unknown status";
     }
 }

@@ -46,7 +46,7 @@ def test_version_and_error_strings(lib):
     from sparse_attention_topk_fp32_amd import _native
 
     assert lib.topk_select_version() == 1
-    for code in range(7):
+    for code in range(8):
         s = _native.error_string(code)
         assert s and s != "unknown status"
     assert _native.error_string(99) == "unknown status"
