@@ -55,8 +55,11 @@
 namespace tks {
 
 constexpr int kSmall = 256;       // bucket ranked exactly by comparisons
-constexpr int kCopies = 16;       // LDS copies of a 256-bin histogram (against atomic conflicts)
+constexpr int kCopies = 8;        // LDS copies of a 256-bin histogram (against atomic conflicts)
 constexpr int kStride = 260;      // words per copy: 256 bins, a spare slot, 16-byte aligned
+// a histogram area: kCopies 256-bin copies, or one 4096-bin copy (the first
+// pass over a row in global memory)
+constexpr int kHistWords = kCopies * kStride > 4096 ? kCopies * kStride : 4096;
 constexpr int kBufCap = 7168;     // candidate buffer of the split kernel's finishing WG (entries)
 constexpr int kMaxSplit = 256;    // WGs per row of the split kernel
 constexpr int kSampleMax = 4096;  // chunks in a row's sample (split kernel)
@@ -372,7 +375,9 @@ __device__ __forceinline__ uint32_t window_bin(uint64_t c, uint32_t lo) {
 // gathered (in any order) and ranked exactly.  Every position follows from
 // the buffer's order and the values alone, so the output order is
 // determined by them.  The loops are rolled: the cost of a pass is the
-// instructions its waves issue, so it scales with the entries.  Uses hist
+// instructions its waves issue, so it scales with the entries, and the
+// code stays short (it runs once per launch, often from a cold
+// instruction cache).  Uses hist
 // (kCopies x kStride words; zero on entry unless prebuilt), small (kSmall
 // entries), scan and sel.  Every thread of the WG calls it, after a barrier
 // that follows the buffer's (and the histogram's) last write.
@@ -434,7 +439,19 @@ __device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, 
         // count winners (high half) and gathered entries (low half), one
         // block scan numbers both in buffer order, then place them
         uint32_t cnt = 0;
-        if (any | gath) {
+        const uint32_t bk = lo + (b << 16);
+        const uint64_t wk64 = all ? (uint64_t)bk : (b < 255u ? (uint64_t)bk + 0x10000u : (1ull << 32));
+        const bool anyk = wk64 <= 0xFFFFFFFFull;
+        const uint32_t wk = (uint32_t)wk64;
+        if (round == 0) {
+            const uint32_t* const ch = reinterpret_cast<const uint32_t*>(cand) + 1;  // keys: high words
+#pragma unroll 2
+            for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
+                const uint32_t key = ch[2u * i];
+                const bool w = anyk & (key >= wk);
+                cnt += (w ? (1u << 16) : 0u) + ((gath & (key >= bk) & !w) ? 1u : 0u);
+            }
+        } else if (any | gath) {
 #pragma unroll 2
             for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
                 const uint64_t c = cand[i];
@@ -444,7 +461,20 @@ __device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, 
         uint32_t tot;
         const uint32_t pos = block_scan_total<BLOCK>(cnt, scan, tot);
         uint32_t p = W + (pos >> 16), g = pos & 0xFFFFu;
-        if (any | gath) {
+        if (round == 0) {
+#pragma unroll 2
+            for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
+                const uint64_t c = cand[i];
+                const uint32_t key = (uint32_t)(c >> 32);
+                const bool w = anyk & (key >= wk);
+                if (w) {
+                    put_out(out, okey, p++, c, k, status);
+                } else if (gath & (key >= bk)) {
+                    if (g < (uint32_t)kSmall) small[g] = c;
+                    ++g;
+                }
+            }
+        } else if (any | gath) {
 #pragma unroll 2
             for (uint32_t i = (uint32_t)tid; i < m; i += BLOCK) {
                 const uint64_t c = cand[i];
@@ -472,12 +502,14 @@ __device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, 
         }
         lds_sync();  // the histogram is cleared next
     }
-    // exact rank of the gathered few: P lanes per candidate (as many as the
-    // block holds, at most 64), each comparing a strided share four at a
-    // time, their counts added by lane shuffles
+    // exact rank of the gathered few: P consecutive lanes per candidate (P a
+    // power of two up to 16 with P * ms within the block: one pass), each
+    // comparing a strided share four at a time; the counts of a group are
+    // summed into its first lane by DPP row shifts (a group never crosses a
+    // row of 16 lanes)
     lds_sync();
     uint32_t P = 1;
-    while (P < 64u && 2u * P * ms <= 2u * (uint32_t)BLOCK) P *= 2u;
+    while (P < 16u && 2u * P * ms <= (uint32_t)BLOCK) P *= 2u;
     for (uint32_t i0 = 0; i0 < ms; i0 += (uint32_t)BLOCK / P) {
         const uint32_t i = i0 + (uint32_t)tid / P, qq = (uint32_t)tid % P;
         if (i0 + (uint32_t)(tid & ~63) / P >= ms) break;  // whole waves past the end
@@ -488,9 +520,10 @@ __device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, 
             rank += (uint32_t)(small[j] > c) + (uint32_t)(small[j + P] > c) + (uint32_t)(small[j + 2u * P] > c) +
                     (uint32_t)(small[j + 3u * P] > c);
         for (; j < ms; j += P) rank += small[j] > c;
-        for (uint32_t sft = 32u; sft >= 1u; sft >>= 1) {
-            if (sft < P) rank += (uint32_t)__shfl_xor((int)rank, (int)sft);
-        }
+        if (P > 1u) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x101, 0xF, 0xF, false);  // row_shl:1
+        if (P > 2u) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x102, 0xF, 0xF, false);  // row_shl:2
+        if (P > 4u) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x104, 0xF, 0xF, false);  // row_shl:4
+        if (P > 8u) rank += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)rank, 0x108, 0xF, 0xF, false);  // row_shl:8
         if (i < ms && qq == 0u && rank < need) put_out(out, okey, W + rank, c, k, status);
     }
 }
@@ -502,7 +535,8 @@ __device__ __forceinline__ void select_buffer(const uint64_t* cand, uint32_t m, 
 // largest, until it holds at most `cap`; a last pass sends the composites
 // above the range to the output and the range's to the buffer, in a fixed
 // order (block scans), and select_buffer finishes.  Passes are rolled loops
-// of U chunks per lane (small code beside the hot paths).
+// of U chunks per lane (small code beside the hot paths).  hist holds
+// kHistWords words.
 template <int BLOCK, int CAP>
 __device__ __forceinline__ void select_by_passes(const char* base, int off, int L, int nchunks, int k, int32_t* out,
                                                  uint32_t* okey, uint64_t* cand, uint32_t* hist, uint64_t* small,
@@ -547,7 +581,7 @@ __device__ __forceinline__ void select_by_passes(const char* base, int off, int 
         const uint64_t range = mx - mn;
         const int q = range ? 64 - __builtin_clzll(range) : 0;
         const int s = q > nbits ? q - nbits : 0;
-        clear_words(hist, kCopies * kStride, tid, BLOCK);
+        clear_words(hist, first ? 4096 : kCopies * kStride, tid, BLOCK);
         lds_sync();
         uint32_t* const hc = first ? hist : hist + (tid % kCopies) * kStride;
         const uint64_t lo = mn, hi = mx;
@@ -657,7 +691,7 @@ __device__ __forceinline__ uint32_t bound_select(const uint32_t (&ks)[NK], uint3
 
 template <int BLOCK>
 struct SplitSmem {
-    alignas(16) uint32_t hist[kCopies * kStride];  // 256-bin histograms, kCopies copies
+    alignas(16) uint32_t hist[kHistWords];  // 256-bin histograms, kCopies copies (or 4096 bins)
     alignas(16) uint64_t cand[kBufCap];       // candidates (finishing WG); the bound's second histogram before
     uint64_t small[kSmall];                   // the last few, ranked exactly
     uint32_t cnt[kMaxSplit];                  // the other WGs' candidate counts (finishing WG)
@@ -824,21 +858,32 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     int par = 0;
     auto place_tile = [&](int c_tile, uint32_t first) {
         uint32_t p = first;
+        if (to_region) {
 #pragma unroll
-        for (int j = 0; j < CHUNKS; ++j) {
-            const int ib = 4 * (c_tile + j * BLOCK + tid) - off;
+            for (int j = 0; j < CHUNKS; ++j) {
+                const int ib = 4 * (c_tile + j * BLOCK + tid) - off;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t key = keys[4 * j + e];
-                if (key >= lo) {
-                    const uint64_t c = composite(key, (uint32_t)(ib + e));
-                    if (to_region) {
-                        if (p < R) st_dev(&region[p], c);
-                    } else if (p < (uint32_t)kBufCap) {
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = keys[4 * j + e];
+                    const bool t = key >= lo;
+                    if (t & (p < R)) st_dev(&region[p], composite(key, (uint32_t)(ib + e)));
+                    p += t ? 1u : 0u;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CHUNKS; ++j) {
+                const int ib = 4 * (c_tile + j * BLOCK + tid) - off;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = keys[4 * j + e];
+                    const bool t = key >= lo;
+                    if (t & (p < (uint32_t)kBufCap)) {
+                        const uint64_t c = composite(key, (uint32_t)(ib + e));
                         sm.cand[p] = c;
                         atomicAdd(&hc[window_bin(c, lo)], 1u);
                     }
-                    ++p;
+                    p += t ? 1u : 0u;
                 }
             }
         }
@@ -944,7 +989,8 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
         // for; all missing ones polled again together), moved to the buffer
         // and cleared for the next launch
         {
-            const uint32_t cw = mine ? min(sm.cnt[wr], (uint32_t)R) : 0u, pw = mine ? sm.pre[wr] : 0u;
+            const uint32_t cn = sm.cnt[mine ? wr : 0], pn = sm.pre[mine ? wr : 0];
+            const uint32_t cw = mine ? min(cn, (uint32_t)R) : 0u, pw = mine ? pn : 0u;
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
                 bool miss = false;
@@ -1066,7 +1112,7 @@ template <int BLOCK>
 struct RowsSmem {
     union {
         uint32_t h12[2 * 4097];                  // first digit: 2 copies of 4096 bins (stride 4097)
-        alignas(16) uint32_t h8[kCopies * kStride];  // 256-bin rounds
+        alignas(16) uint32_t h8[kHistWords];     // 256-bin rounds (4096 bins in a pass over the row)
     } h;
     alignas(16) uint64_t cand[kRowsCap];  // candidates at or above the running bound
     uint64_t small[kSmall];               // the last few, ranked exactly
@@ -1189,7 +1235,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
             for (int u = 0; u < RC; ++u) {
                 const uint32_t i = i0 + (uint32_t)(u * BLOCK + tid);
-                e[u] = i < used ? sm.cand[i] : 0ull;
+                e[u] = sm.cand[i < used ? i : used - 1u];  // clamped: an unpredicated load
                 const uint32_t kd = i < used ? pred(e[u]) : 0u;
                 keepm |= kd << u;
                 cnt += kd;
@@ -2237,9 +2283,12 @@ struct Launch {
 // 1024 chunks, 4096 for rows of 512K logits or more (the candidate count
 // above the bound grows with sqrt(k n / sample)); at most what the variant's
 // registers hold.
-int sample_chunks_for(int64_t maxc, int block) {
+int sample_chunks_for(int64_t maxc, int block, int items) {
     const int want = maxc >= 131072 ? 4096 : 1024;
-    const int spt = kSampleMax / block > 4 ? 4 : kSampleMax / block;
+    // at most four sampled chunks per thread, two beside 32 logits per
+    // thread (registers)
+    const int most = items >= 32 ? 2 : 4;
+    const int spt = kSampleMax / block > most ? most : kSampleMax / block;
     const int cap = spt * block;
     return want < cap ? want : cap;
 }
@@ -2262,7 +2311,7 @@ int check_shape(int64_t rows, int64_t maxc, int v, int G, Launch* L) {
     L->chunks_per_wg = (int)cpw;
     const int64_t slice = 4 * cpw;
     L->region = (int)(slice < kBufCap ? slice : kBufCap);
-    L->sample_chunks = sample_chunks_for(maxc, var.block);
+    L->sample_chunks = sample_chunks_for(maxc, var.block, var.items);
     return TOPK_SELECT_SUCCESS;
 }
 
