@@ -9,11 +9,18 @@ device memory.  The headline workload is one row of 131,072 bf16-valued fp32
 logits with k = 2048 (the batch-1 decode case); the batch-64 case (64 rows of
 131,072 with ragged valid lengths) is timed the same way and reported beside it.
 
-Timing: the K timed launches are captured into a HIP graph (torch.cuda.CUDAGraph)
-and replayed, so the per-step time is the GPU time of back-to-back launches, not
-Python's call overhead; HIP events on the launch stream bracket the timed
-region.  The per-call time of plain eager calls from Python is reported too.
-The oracle (CPU) is timed on a bounded sample for the `cpu_baseline` field.
+Timing: exactly K = --steps launches are timed (`steps` in the output).  They
+are captured into one HIP graph (torch.cuda.CUDAGraph), launch i reading input
+copy i mod C, where the C copies total at least 512 MiB; W = --warmup untimed
+launches (graph replays) come first, then a 512 MiB device write flushes the
+caches, and HIP events on the launch stream bracket one replay.  So the
+per-step time is the GPU time of back-to-back launches on cold inputs, not
+Python's call overhead.  Warm-cache and eager per-call times are reported
+beside it (with their own launch counts).  A plain streaming read
+(topk_stream_read) measures the read bandwidth the HBM achieves, and each
+bandwidth figure is also given as a fraction of it.  The oracle (CPU) is
+timed on bounded samples: the headline row on one core (`cpu_baseline`), and
+the batched workloads over all usable host cores (`cpu_baseline_batched`).
 """
 
 from __future__ import annotations
@@ -72,6 +79,36 @@ def time_graph(torch, fn_list, steps: int, warmup: int, stream):
     return e0.elapsed_time(e1) * 1e-3 / (reps * len(fn_list)), reps * len(fn_list)
 
 
+def time_cold_exact(torch, fn_for_copy, copies: int, steps: int, warmup: int, stream, flush):
+    """Exactly `steps` launches timed: launch i reads input copy i % copies
+    (a copy is read again only after every other copy, over 512 MiB apart),
+    captured into one graph; `warmup` untimed launches first (graph
+    replays), then the caches are flushed by writing the `flush` tensor, and
+    HIP events on the launch stream bracket one replay.  Returns seconds per
+    launch."""
+    fns = [fn_for_copy(i % copies) for i in range(steps)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for f in fns[:copies]:  # allocates the library workspace outside the capture
+            f()
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for f in fns:
+                f()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, (warmup + steps - 1) // steps)):
+            g.replay()
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
 def time_eager(torch, fn, steps: int, warmup: int, stream):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -88,9 +125,11 @@ def time_eager(torch, fn, steps: int, warmup: int, stream):
 
 
 def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: int, eager_only: bool = False,
-                   ordered: bool = False):
+                   ordered: bool = False, flush=None):
     """Per-launch seconds (graph, warm), (graph, cold: rotating copies), eager.
-    With `ordered`, the ordered selection with values (topk_select_sorted)."""
+    With `ordered`, the ordered selection with values (topk_select_sorted).
+    With `flush` (a device tensor of 512 MiB or more), the cold time is
+    exactly `steps` launches after a cache flush (time_cold_exact)."""
     w = W.generate(name)
     rows, n = w.x.shape
     stream = torch.cuda.Stream()
@@ -111,10 +150,14 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
     cold_fns = [(lambda i: (lambda: call(i, i % 2)))(i) for i in range(copies)]
     if eager_only:
         t_eager = time_eager(torch, warm_fns[0], steps, warmup, stream)
-        t_warm, n_warm, t_cold = t_eager, steps, t_eager
+        t_warm, n_warm, t_cold, n_cold = t_eager, steps, t_eager, steps
     else:
         t_warm, n_warm = time_graph(torch, warm_fns * 32, steps, warmup, stream)
-        t_cold, n_cold = time_graph(torch, cold_fns, steps, warmup, stream) if copies > 1 else (t_warm, n_warm)
+        if flush is not None:
+            t_cold = time_cold_exact(torch, lambda i: cold_fns[i], copies, steps, warmup, stream, flush)
+            n_cold = steps
+        else:
+            t_cold, n_cold = time_graph(torch, cold_fns, steps, warmup, stream) if copies > 1 else (t_warm, n_warm)
         t_eager = time_eager(torch, warm_fns[0], max(20, steps // 4), warmup, stream)
     flags = tks.device_status(stream)
     if flags:
@@ -123,7 +166,7 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
         "workload": w.config.name, "rows": rows, "n": n, "k": w.k,
         "lengths": None if w.lengths is None else "per-row",
         "bytes": algorithmic_bytes(rows, n, w.k, w.lengths),
-        "t_warm": t_warm, "t_cold": t_cold, "t_eager": t_eager, "launches_timed": n_warm,
+        "t_warm": t_warm, "t_cold": t_cold, "t_eager": t_eager, "launches_timed": n_cold, "launches_warm": n_warm,
         "plan": tks.plan(rows, n, w.k), "x": w.x, "lengths_arr": w.lengths,
     }
 
@@ -230,6 +273,60 @@ def calibrate_copy(torch, mib: int):
     torch.cuda.synchronize()
 
 
+def host_info() -> dict:
+    """nproc, the CPU model and the compiler the oracle is built with
+    (read before the GPU is touched)."""
+    import subprocess
+
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        cc = subprocess.run(["gcc", "--version"], capture_output=True, text=True, timeout=20).stdout.splitlines()[0]
+    except Exception:
+        cc = "unknown"
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model, "compiler": cc}
+
+
+def cpu_rows_baseline(x, k, lengths, threads: int, runs: int = 3):
+    """The oracle as it stands over all rows of a batch, rows split in
+    contiguous blocks over `threads` host threads (the oracle's C loop runs
+    outside the GIL); median of `runs` passes.  Also the single-thread
+    per-row time on the first few rows."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    rows = x.shape[0]
+    bounds = np.linspace(0, rows, threads + 1).astype(int)
+    parts = [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+
+    def run(ab):
+        a, b = ab
+        oracle.topk(x[a:b], k, None if lengths is None else lengths[a:b])
+
+    times = []
+    with ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            list(ex.map(run, parts))
+            times.append(time.perf_counter() - t0)
+    few = min(rows, 8)
+    t0 = time.perf_counter()
+    oracle.topk(x[:few], k, None if lengths is None else lengths[:few])
+    single = (time.perf_counter() - t0) / few
+    return float(np.median(times)), len(parts), single
+
+
 def cpu_baseline(w_x, k, budget_s: float = 10.0):
     """The oracle as it stands on one host core, on the headline row, repeated
     for about `budget_s` seconds; returns the median seconds per row."""
@@ -269,12 +366,16 @@ def main() -> int:
                     help="time plain eager launches only (no graph capture; for counter collection)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--stream-read-mib", type=int, default=2048,
+                    help="size of the streaming read that measures achievable read bandwidth (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selector runs on a single GPU "
               "(a batch shards by rows across GPUs with no communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    host = None if args.no_cpu else host_info()  # before the GPU is touched
 
     import torch
 
@@ -291,10 +392,11 @@ def main() -> int:
             return args.cold_copies
         return int(max(2, min(1024, (512 << 20) // (c.rows * c.n * 4) + 1)))
 
+    flush = None if args.eager_only else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     head = bench_workload(torch, tks, W, args.workload, args.steps, args.warmup,
-                          1 if args.eager_only else copies_for(args.workload), args.eager_only)
+                          1 if args.eager_only else copies_for(args.workload), args.eager_only, flush=flush)
     batch = bench_workload(torch, tks, W, args.batch_workload, max(200, args.steps // 10), args.warmup,
-                           1 if args.eager_only else copies_for(args.batch_workload), args.eager_only)
+                           1 if args.eager_only else copies_for(args.batch_workload), args.eager_only, flush=flush)
 
     others = []
     for name in [x for x in args.other_workloads.split(",") if x]:
@@ -324,6 +426,18 @@ def main() -> int:
 
     if args.calibrate_copy_mib:
         calibrate_copy(torch, args.calibrate_copy_mib)
+
+    stream_bw = None
+    if args.stream_read_mib and not args.eager_only:
+        nbytes = args.stream_read_mib << 20
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        st = torch.cuda.Stream()
+        t_rd, n_rd = time_graph(torch, [lambda: tks.stream_read(buf, sink, st)] * 4, 20, 4, st)
+        stream_bw = {"bytes_per_launch": nbytes, "launches_timed": n_rd, "us_per_launch": round(t_rd * 1e6, 3),
+                     "GBps": round(nbytes / t_rd / 1e9, 1),
+                     "kernel": "topk_stream_read (16-byte loads, every CU, nothing else)"}
+        del buf
 
     t = head["t_cold"]
     us_per_row = t * 1e6 / head["rows"]
@@ -357,7 +471,10 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBPS, 6),
             "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
             "algorithmic_bytes_per_launch": head["bytes"],
+            "achievable_read_GBps": None if stream_bw is None else stream_bw["GBps"],
+            "frac_of_achievable": None if stream_bw is None else round(achieved / stream_bw["GBps"], 6),
         },
+        "stream_read": stream_bw,
         "batch64": {
             "workload": batch["workload"], "rows": batch["rows"], "n": batch["n"], "k": batch["k"],
             "rows_per_s": round(batch["rows"] / bt, 1),
@@ -367,9 +484,13 @@ def main() -> int:
             "achieved_GBps": round(batch["bytes"] / bt / 1e9, 3),
             "hbm_frac": round(batch["bytes"] / bt / 1e9 / HBM_PEAK_GBPS, 6),
             "algorithmic_bytes_per_launch": batch["bytes"],
+            "frac_of_achievable": None if stream_bw is None else round(batch["bytes"] / bt / 1e9 / stream_bw["GBps"], 6),
+            "launches_timed": batch["launches_timed"],
             "plan": batch["plan"],
         },
         "latency_detail": {
+            "value_launches": head["launches_timed"],
+            "warm_launches": head["launches_warm"],
             "us_per_launch_warm": round(head["t_warm"] * 1e6, 3),
             "us_per_launch_cold": round(head["t_cold"] * 1e6, 3),
             "us_per_call_eager_python": round(head["t_eager"] * 1e6, 3),
@@ -404,7 +525,21 @@ def main() -> int:
             "sample": "the headline row (1 x %d, k=%d), %d repeated oracle calls, median; "
                       "single-threaded C oracle (stable sort by value desc, index asc)"
                       % (head["n"], head["k"], reps),
+            **host,
         }
+        # the batched workloads over all usable host cores (at most 16)
+        threads = max(1, min(16, host["usable_cpus"]))
+        rows_base = []
+        for o in [batch] + [o for o in others if o["rows"] >= 64]:
+            sec, used, single = cpu_rows_baseline(o["x"], o["k"], o["lengths_arr"], threads)
+            rows_base.append({
+                "workload": o["workload"], "rows": o["rows"], "n": o["n"], "k": o["k"],
+                "rows_per_s": round(o["rows"] / sec, 1), "us_per_row": round(sec * 1e6 / o["rows"], 3),
+                "threads": used, "single_thread_us_per_row": round(single * 1e6, 2),
+                "sample": "all %d rows, rows split in contiguous blocks over %d threads, median of 3 passes; "
+                          "single-thread figure from the first 8 rows" % (o["rows"], used),
+            })
+        res["cpu_baseline_batched"] = rows_base
     print(json.dumps(res), flush=True)
     return 0
 

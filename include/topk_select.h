@@ -36,6 +36,7 @@
 #ifndef TOPK_SELECT_H_
 #define TOPK_SELECT_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -299,6 +300,24 @@ const char* topk_select_error_string(int status);
 
 /* TOPK_SELECT_VERSION of the built library. */
 int topk_select_version(void);
+
+/*
+ * topk_stream_read - the yardstick for the selection's memory traffic (the
+ * article's roofline view: the selection is bound by reading the logits
+ * once): reads `bytes` of device memory at `p` once with 16-byte loads
+ * spread over every CU, and nothing else, so its rate is the read bandwidth
+ * the HBM achieves for a plain stream.
+ *
+ *   p       device, 16-byte aligned, `bytes` readable.  Read only.
+ *   bytes   a positive multiple of 16.
+ *   sink    device, uint32_t[1]: written only in the (practically never
+ *           taken) case that keeps the loads live; its value means nothing.
+ *   stream  stream the launch is enqueued on (returns without waiting).
+ *
+ * Returns INVALID_VALUE (nothing enqueued) for a null or misaligned pointer
+ * or a size that is zero or not a multiple of 16.
+ */
+int topk_stream_read(const void* p, size_t bytes, uint32_t* sink, topk_select_stream_t stream);
 
 #ifdef __cplusplus
 }

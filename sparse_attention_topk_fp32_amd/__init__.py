@@ -44,6 +44,7 @@ __all__ = [
     "device_status",
     "release_workspace",
     "version",
+    "stream_read",
     "TopkSelectError",
 ]
 
@@ -365,3 +366,12 @@ def release_workspace() -> None:
 
 def version() -> int:
     return int(_native.load().topk_select_version())
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """One streaming read of the device tensor `buf` (16-byte aligned, a
+    multiple of 16 bytes) on `stream`; `sink` is a device int32/uint32
+    tensor of at least one element.  For measuring achievable read bandwidth."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_native.load().topk_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream_handle(stream)),
+           "topk_stream_read")

@@ -40,6 +40,7 @@ EXPORTS = (
     "topk_select_release_workspace",
     "topk_select_error_string",
     "topk_select_version",
+    "topk_stream_read",
 )
 
 
@@ -107,6 +108,8 @@ def load() -> ctypes.CDLL:
         lib.topk_select_error_string.restype = ctypes.c_char_p
         lib.topk_select_version.argtypes = []
         lib.topk_select_version.restype = ctypes.c_int
+        lib.topk_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+        lib.topk_stream_read.restype = ctypes.c_int
         _lib = lib
         return lib
 

@@ -2373,6 +2373,31 @@ __global__ void __launch_bounds__(256) topk_clear_kernel(uint4* p, size_t n16) {
     for (size_t i = (size_t)blockIdx.x * 256u + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Streaming read of n16 16-byte words: WG b reads the contiguous span
+// [b * per, (b + 1) * per), eight loads in flight per thread, folded into
+// one word per thread; a word is stored only when the fold hits a value no
+// input of interest produces, so the loads stay live and the kernel writes
+// (almost) nothing.  Many short spans (128 WGs per CU) keep every channel
+// busy to the end.
+__global__ void __launch_bounds__(256) topk_stream_read_kernel(const uint4* __restrict__ p, size_t n16, size_t per,
+                                                               uint32_t* sink) {
+    size_t i = (size_t)blockIdx.x * per + threadIdx.x;
+    const size_t end = min(n16, (size_t)(blockIdx.x + 1) * per);
+    uint32_t acc = 0;
+    for (; i + 7u * 256u < end; i += 8u * 256u) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[i + (size_t)u * 256u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < end; i += 256u) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 bool capturing(hipStream_t stream);
 
 // Device address of `scratch` on `dev` (the current device).  The first
@@ -2960,5 +2985,26 @@ const char* topk_select_error_string(int status) {
 }
 
 int topk_select_version(void) { return TOPK_SELECT_VERSION; }
+
+int topk_stream_read(const void* p, size_t bytes, uint32_t* sink, topk_select_stream_t stream) {
+    if (!p || !sink || ((uintptr_t)p & 15u) || (bytes & 15u) || bytes == 0) return TOPK_SELECT_ERROR_INVALID_VALUE;
+    try {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return TOPK_SELECT_ERROR_NO_DEVICE;
+        const size_t n16 = bytes / 16u;
+        size_t grid = (size_t)cus * 128u;  // spans of at least 256 words
+        if (grid > (n16 + 255u) / 256u) grid = (n16 + 255u) / 256u;
+        const size_t per = (n16 + grid - 1u) / grid;
+        (void)hipGetLastError();
+        tks::topk_stream_read_kernel<<<dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream>>>(
+            reinterpret_cast<const uint4*>(p), n16, per, sink);
+        return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
 
 }  // extern "C"

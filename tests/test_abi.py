@@ -175,3 +175,16 @@ def test_select_rejects_non_gpu_tensors():
         tks.select(np.zeros((4, 8), np.float32), 2)
     with pytest.raises(TypeError):
         tks.select_sorted(torch.zeros(4, 8), 2)
+
+
+def test_stream_read_argument_checks_answer_before_any_hip_call(lib):
+    """Null, misaligned or mis-sized arguments are refused on the host (no
+    HIP call is made, so this runs without a GPU)."""
+    from sparse_attention_topk_fp32_amd import _native
+
+    lib2 = _native.load()
+    assert lib2.topk_stream_read(None, 16, 16, None) == _native.ERROR_INVALID_VALUE
+    assert lib2.topk_stream_read(16, 16, None, None) == _native.ERROR_INVALID_VALUE
+    assert lib2.topk_stream_read(17, 16, 16, None) == _native.ERROR_INVALID_VALUE
+    assert lib2.topk_stream_read(16, 0, 16, None) == _native.ERROR_INVALID_VALUE
+    assert lib2.topk_stream_read(16, 24, 16, None) == _native.ERROR_INVALID_VALUE

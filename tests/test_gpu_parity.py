@@ -462,3 +462,16 @@ def test_workspace_reuse_across_row_counts(torch_gpu):
     for x, k in ((one, 2048), (eight, 1000), (one, 9000), (eight, 1000), (eight[:3], 16)):
         got = run_gpu(torch_gpu, x, k)
         assert_parity(x, k, None, got)
+
+
+def test_stream_read_runs(torch_gpu):
+    """The bandwidth yardstick: a plain streaming read launches and leaves
+    the sink alone on ordinary data."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    _say("stream_read 64 MiB")
+    buf = torch_gpu.ones(16 << 20, dtype=torch_gpu.float32, device="cuda")
+    sink = torch_gpu.full((1,), 7, dtype=torch_gpu.int32, device="cuda")
+    tks.stream_read(buf, sink)
+    torch_gpu.cuda.synchronize()
+    assert int(sink.item()) == 7
