@@ -460,8 +460,9 @@ def main() -> int:
         "config": {
             "workload": head["workload"], "rows": head["rows"], "n": head["n"], "k": head["k"],
             "batch": head["rows"], "plan": head["plan"],
-            "timing": "HIP-graph replay of back-to-back launches on one stream, rotating input "
-                      "copies totalling >= 512 MiB (cold caches)",
+            "timing": "exactly `steps` back-to-back launches in one HIP-graph replay on one stream, "
+                      "launch i reading input copy i mod C (copies totalling >= 512 MiB), after `warmup` "
+                      "untimed launches and a 512 MiB cache-flushing write (cold caches)",
         },
         "roofline": {
             "bound": "hbm",
@@ -540,6 +541,13 @@ def main() -> int:
                           "single-thread figure from the first 8 rows" % (o["rows"], used),
             })
         res["cpu_baseline_batched"] = rows_base
+        # the other one-row workloads on one core
+        singles = []
+        for o in [o for o in others if o["rows"] == 1]:
+            spr, reps1 = cpu_baseline(o["x"], o["k"], budget_s=3.0)
+            singles.append({"workload": o["workload"], "n": o["n"], "k": o["k"], "us_per_row": round(spr * 1e6, 2),
+                            "cores": 1, "sample": "%d repeated oracle calls on the row, median" % reps1})
+        res["cpu_baseline_single_rows"] = singles
     print(json.dumps(res), flush=True)
     return 0
 

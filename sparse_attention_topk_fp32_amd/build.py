@@ -19,6 +19,10 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "topk_select.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopk_select.so")
+# test build: the same source with TKS_TEST_HOOKS (the wait bound settable
+# from the host, for exercising the give-up path); never loaded by the
+# product binding
+HOOKS_LIB = os.path.join(PKG, "libtopk_select_hooks.so")
 ARCH = os.environ.get("TOPK_SELECT_ARCH", "gfx950")
 
 
@@ -38,16 +42,26 @@ def command(out: str = LIB, extra=()):
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; callers decide when to rebuild)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+def build(verbose: bool = False, hooks: bool = True) -> str:
+    """Compile the library, and the test-hook build beside it (always;
+    callers decide when to rebuild).  The two compilations run in parallel."""
+    jobs = [(LIB, ())]
+    if hooks:
+        jobs.append((HOOKS_LIB, ("-DTKS_TEST_HOOKS",)))
+    procs = []
+    for out, extra in jobs:
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = command(tmp, extra)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, tmp, cmd, subprocess.Popen(cmd)))
+    failed = [cmd for _, _, cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    for out, tmp, _, _ in procs:
+        os.replace(tmp, out)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    print(build(verbose="-q" not in sys.argv, hooks="--no-hooks" not in sys.argv))

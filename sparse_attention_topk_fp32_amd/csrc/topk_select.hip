@@ -51,6 +51,7 @@
 #include <vector>
 
 #include "topk_select.h"
+#include "key_map.h"
 
 namespace tks {
 
@@ -112,16 +113,8 @@ __device__ __forceinline__ uint32_t make_tag(uint32_t epoch) { return 0x80000000
 // placed in scratch memory when they are passed around)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Mapping step: float -> unsigned key with key(a) < key(b) iff a < b for
-// non-NaN values.  Adding +0.0 turns -0.0 into +0.0 (IEEE round to nearest)
-// and leaves every other value, subnormals included, unchanged, so -0.0 and
-// +0.0 get the same key and tie.  Negative values have all bits flipped,
-// non-negative ones only the sign bit.  Key 0 marks "no element": only the
-// NaN pattern 0xFFFFFFFF also maps there (NaN is outside the contract).
-__device__ __forceinline__ uint32_t key_of(float x) {
-    const uint32_t u = __float_as_uint(x + 0.0f);
-    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
+// Mapping step (key_map.h, checked on the host over every bit pattern).
+__device__ __forceinline__ uint32_t key_of(float x) { return tks_key_of(x); }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
     return ((uint64_t)key << 32) | (uint64_t)~idx;
@@ -2985,6 +2978,18 @@ const char* topk_select_error_string(int status) {
 }
 
 int topk_select_version(void) { return TOPK_SELECT_VERSION; }
+
+#ifdef TKS_TEST_HOOKS
+// Test builds only (not part of the ABI): the bound on a wait for another
+// workgroup, in ticks of the 100 MHz constant clock, on the current device
+// (0: every wait gives up before its first poll).
+int topk_select_test_set_spin_limit(uint64_t ticks) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(tks::g_spin_limit), &ticks, sizeof(ticks), 0, hipMemcpyHostToDevice) ==
+                   hipSuccess
+               ? TOPK_SELECT_SUCCESS
+               : TOPK_SELECT_ERROR_LAUNCH;
+}
+#endif
 
 int topk_stream_read(const void* p, size_t bytes, uint32_t* sink, topk_select_stream_t stream) {
     if (!p || !sink || ((uintptr_t)p & 15u) || (bytes & 15u) || bytes == 0) return TOPK_SELECT_ERROR_INVALID_VALUE;
