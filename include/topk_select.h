@@ -222,9 +222,10 @@ int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, i
  *   kvstride 0 (shared keys and values) or at least n*dim, a multiple of 8.
  *
  * Precision: bf16 products are exact in float and the scores are summed in
- * float; the softmax weights are rounded to bf16 for the P.V product on the
- * matrix cores.  Each output lies within
- *   (2 (dim + 2) 2^-24 smax + 2^-8 + (k + 64) 2^-24 + 2^-20) * sum_j p_j |V[idx_j][c]|
+ * float; each softmax weight p is split into two bf16 terms, hi = bf16(p)
+ * and lo = bf16(p - hi) (|p - hi - lo| <= 2^-16 p), for two P.V products on
+ * the matrix cores summed in float.  Each output lies within
+ *   (2 (dim + 2) 2^-24 smax + 2^-16 + (k + 64) 2^-24 + 2^-20) * sum_j p_j |V[idx_j][c]|
  * of the exact value, smax = max_j scale * sum_i |q_i K[idx_j]_i|.
  * Two kernels are enqueued (per chunk of 64 slots, then the combination);
  * scratch of rows * ceil(k/64) * heads * (dim + 2) * 4 bytes per (device,

@@ -1860,8 +1860,9 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
 // none).  Split over the slots: a WG takes 64 slots of one row, computes
 // the scores on the matrix cores (A = 16 heads x 32 dims of the queries,
 // B = 32 dims x 16 gathered keys), a softmax over its slots (maximum m,
-// sum l) and P.V on the matrix cores (A = 16 heads x 32 slots of P in bf16,
-// B = 32 slots x 16 dims of the gathered values, held transposed in LDS so
+// sum l) and P.V on the matrix cores (A = 16 heads x 32 slots of P, as the
+// sum of two bf16 terms, one product each; B = 32 slots x 16 dims of the
+// gathered values, held transposed in LDS so
 // that a lane's 8 slots of one dim are 16 contiguous bytes), and writes
 // (m, l, partial output); a second kernel combines a row's chunks.
 
@@ -1888,7 +1889,8 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParam
     __shared__ u32x4_t qs[NH * CPR];          // queries, chunk c of head h in slot c ^ (h % CPR)
     __shared__ u32x4_t ks[kAttnSlots * CPR];  // gathered keys, same swizzle by slot
     __shared__ u32x4_t vt[D * 8];             // values transposed: dim row of 64 slots, chunk c in c ^ vsw(dim)
-    __shared__ u32x4_t ps[NH * 8];            // P in bf16: head row of 64 slots, chunk c in c ^ (head % 8)
+    __shared__ u32x4_t ps[NH * 8];            // P's high bf16 term: head row of 64 slots, chunk c in c ^ (head % 8)
+    __shared__ u32x4_t pl[NH * 8];            // P's low bf16 term (P - high), same layout
     __shared__ float red[2][kAttnBlock / 64][NH];
     const int row = blockIdx.x / P.S;
     const int sp = blockIdx.x - row * P.S;
@@ -1996,10 +1998,18 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParam
             for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft);
             sum[hb][i] = x;
             if (m == 0) red[1][wave][h] = x;
-            // P in bf16 (round to nearest even), head row h, slot j
-            const uint32_t u = __float_as_uint(p);
-            const uint16_t pb = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-            reinterpret_cast<uint16_t*>(ps)[(h * 8 + ((j >> 3) ^ (h % 8))) * 8 + (j & 7)] = pb;
+            // P as two bf16 terms (each rounded to nearest even): hi, and lo
+            // for the remainder p - hi (exact in float), so hi + lo is within
+            // 2^-16 p of p; head row h, slot j
+            auto bf16_rne = [](float x) {
+                const uint32_t u = __float_as_uint(x);
+                return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            };
+            const uint16_t ph = bf16_rne(p);
+            const uint16_t plo = bf16_rne(p - __uint_as_float((uint32_t)ph << 16));
+            const int pidx = (h * 8 + ((j >> 3) ^ (h % 8))) * 8 + (j & 7);
+            reinterpret_cast<uint16_t*>(ps)[pidx] = ph;
+            reinterpret_cast<uint16_t*>(pl)[pidx] = plo;
         }
     __syncthreads();
     float* const prow = P.part + ((size_t)row * P.S + sp) * (size_t)H * (D + 2);
@@ -2017,7 +2027,8 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParam
         }
     }
     // P.V: output tiles of 16 heads x 16 dims, HB * D/16 of them over the
-    // four waves; two 32-slot steps each
+    // four waves; two 32-slot steps each, each step a matrix-core product
+    // for P's low term and one for its high term into the same float sums
     for (int tile = wave; tile < HB * (D / 16); tile += kAttnBlock / 64) {
         const int hb = tile / (D / 16), db = tile % (D / 16);
         floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -2025,9 +2036,11 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParam
         for (int ts = 0; ts < kAttnSlots / 32; ++ts) {
             const int c = ts * 4 + g;  // slots 8c .. 8c+7
             const int h = hb * 16 + m, dim = db * 16 + m;
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ps[h * 8 + (c ^ (h % 8))]);
+            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, pl[h * 8 + (c ^ (h % 8))]);
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, ps[h * 8 + (c ^ (h % 8))]);
             const bf16x8_t b = __builtin_bit_cast(bf16x8_t, vt[dim * 8 + (c ^ vsw(dim))]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
         }
         // lane holds heads 4g+i of dim db*16 + m
 #pragma unroll
