@@ -103,6 +103,8 @@ struct KParams {
     int32_t region;         // entries of one WG's region in the stage
     int32_t sample_chunks;  // split kernel: chunks in a row's sample (a multiple of 16)
     int32_t ahead;          // one WG per row: rows from a row to the one whose first tile it touches (0: none)
+    int32_t* oout;          // one WG per row, keys recorded: the ordered output's indices [rows, k] (null: none)
+    float* ovals;           // and its values (null: none)
 };
 
 __device__ __forceinline__ uint32_t make_tag(uint32_t epoch) { return 0x80000000u | (epoch & 0x7FFFFFFFu); }
@@ -115,6 +117,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Mapping step (key_map.h, checked on the host over every bit pattern).
 __device__ __forceinline__ uint32_t key_of(float x) { return tks_key_of(x); }
+
+// The logit a key came from; -0.0 and +0.0 share a key, so a zero key reads
+// the logit itself to return its sign.
+__device__ __forceinline__ float value_of(uint32_t key, const float* prow, uint32_t L, uint32_t idx) {
+    if (key == 0x80000000u) return idx < L ? prow[idx] : 0.0f;
+    return __uint_as_float(key & 0x80000000u ? key ^ 0x80000000u : ~key);
+}
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
     return ((uint64_t)key << 32) | (uint64_t)~idx;
@@ -1101,6 +1110,137 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
 constexpr int kRowsCap = 5376;
 constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered entries is refined
 
+// The ordered form of one row, produced by the WG that selected it (the
+// need_sorted option of section 02's radix_topk: descending order; equal
+// values by index ascending, the rule that selects them).  The row's cnt
+// selected composites (recorded keys and indices, or keys of the logits
+// when the whole valid row is selected) are binned by key into at most
+// kOrdBins bins over their key range, counted, scattered into T bin by bin
+// (descending bins), and each is written at its exact rank: the entries of
+// the bins above its own plus the larger ones of its own bin (bins hold a
+// few entries, or equal keys).  Positions follow from the values alone;
+// slots past cnt get -1 and -inf.  sidx/skey may point to LDS or global
+// memory.  T: CAP composites of LDS (cnt <= CAP); hist: 2 * kOrdBins words;
+// scan: BLOCK / 64 words.
+constexpr int kOrdBins = 2048;
+constexpr int kOrdLds = 2048;  // one WG per row: k up to this keeps the unordered output in LDS
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void ordered_finish(const int32_t* sidx, const uint32_t* skey, bool from_logits,
+                                               const float* prow, uint32_t L, uint32_t cnt, int k, int32_t* oout,
+                                               float* ovals, uint64_t* T, uint32_t* hist, uint32_t* scan) {
+    constexpr int NU = (CAP + BLOCK - 1) / BLOCK;
+    constexpr int NW = BLOCK / 64;
+    constexpr int BPT = kOrdBins / BLOCK;  // bins per thread for the starts
+    static_assert(kOrdBins % BLOCK == 0 && kOrdBins >= BLOCK, "whole bins per thread");
+    constexpr uint32_t BITS = 11;          // log2(kOrdBins)
+    static_assert((1 << BITS) == kOrdBins, "kOrdBins is 2^BITS");
+    const int tid = threadIdx.x;
+    const uint32_t wid = (uint32_t)tid / 64u;
+    uint32_t* const cur = hist + kOrdBins;
+    clear_words(hist, kOrdBins, tid, BLOCK);
+    uint64_t e[NU];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const uint32_t i = (uint32_t)(tid + u * BLOCK);
+        e[u] = 0ull;
+        if (i < cnt) {
+            const uint32_t idx = from_logits ? i : (uint32_t)sidx[i];
+            const uint32_t key = from_logits ? key_of(prow[i]) : skey[i];
+            e[u] = composite(key, idx);
+            kmin = min(kmin, key);
+            kmax = max(kmax, key);
+        }
+    }
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, sft));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, sft));
+    }
+    uint32_t* const red = cur;  // the cursors are written only after this is read
+    if (lane_id() == 0) {
+        red[wid] = kmin;
+        red[NW + wid] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        kmin = min(kmin, red[w]);
+        kmax = max(kmax, red[NW + w]);
+    }
+    const uint32_t range = kmax - kmin;  // cnt >= 1
+    const uint32_t q = range ? 32u - (uint32_t)__builtin_clz(range) : 0u;
+    const uint32_t sh = q > BITS ? q - BITS : 0u;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+        if ((uint32_t)(tid + u * BLOCK) < cnt) atomicAdd(&hist[((uint32_t)(e[u] >> 32) - kmin) >> sh], 1u);
+    __syncthreads();
+    // bin starts, bins descending: thread t owns bins top .. top - BPT + 1
+    {
+        const uint32_t top = (uint32_t)kOrdBins - 1u - (uint32_t)(tid * BPT);
+        uint32_t c[BPT], t = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            c[i] = hist[top - (uint32_t)i];
+            t += c[i];
+        }
+        uint32_t tot;
+        uint32_t ex = block_scan_total<BLOCK>(t, scan, tot);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            cur[top - (uint32_t)i] = ex;
+            ex += c[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        if ((uint32_t)(tid + u * BLOCK) < cnt) {
+            const uint32_t b = ((uint32_t)(e[u] >> 32) - kmin) >> sh;
+            T[atomicAdd(&cur[b], 1u)] = e[u];
+        }
+    }
+    __syncthreads();
+    // cur[b] is now the end of bin b in T.  The ranked entries are staged in
+    // LDS after T when they fit (then written in order), else stored at
+    // their ranks directly
+    const bool staged = 2u * cnt <= (uint32_t)CAP;
+    uint2* const O = reinterpret_cast<uint2*>(T + cnt);
+    for (uint32_t qi = (uint32_t)tid; qi < cnt; qi += BLOCK) {
+        const uint64_t c = T[qi];
+        const uint32_t key = (uint32_t)(c >> 32);
+        const uint32_t b = (key - kmin) >> sh;
+        const uint32_t end = cur[b], st = end - hist[b];
+        uint32_t r = st;
+        for (uint32_t j = st; j < end; j += 8u) {
+            uint64_t t[8];  // clamped loads, the slots past the bin not counted
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t[u] = T[min(j + (uint32_t)u, end - 1u)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) r += (uint32_t)((j + (uint32_t)u < end) & (t[u] > c));
+        }
+        const uint32_t idx = ~(uint32_t)c;
+        const float v = value_of(key, prow, L, idx);
+        if (staged) {
+            O[r] = make_uint2(idx, __float_as_uint(v));
+        } else {
+            oout[r] = (int32_t)idx;
+            if (ovals) ovals[r] = v;
+        }
+    }
+    if (staged) {  // in order: coalesced stores
+        __syncthreads();
+        for (uint32_t j = (uint32_t)tid; j < cnt; j += BLOCK) {
+            const uint2 o = O[j];
+            oout[j] = (int32_t)o.x;
+            if (ovals) ovals[j] = __uint_as_float(o.y);
+        }
+    }
+    for (uint32_t j = cnt + (uint32_t)tid; j < (uint32_t)k; j += BLOCK) {
+        oout[j] = -1;
+        if (ovals) ovals[j] = -__builtin_huge_valf();
+    }
+}
+
 template <int BLOCK>
 struct RowsSmem {
     union {
@@ -1108,6 +1248,8 @@ struct RowsSmem {
         alignas(16) uint32_t h8[kHistWords];     // 256-bin rounds (4096 bins in a pass over the row)
     } h;
     alignas(16) uint64_t cand[kRowsCap];  // candidates at or above the running bound
+    static_assert(kHistWords >= 2 * kOrdBins, "the ordered form's bins fit the histogram area");
+    static_assert(kHistWords + 2 * kOrdLds <= 2 * 4097, "the selection's output fits above the histograms");
     uint64_t small[kSmall];               // the last few, ranked exactly
     uint32_t scan[BLOCK / 64];
     uint32_t scan2[2][BLOCK / 64];
@@ -1128,10 +1270,30 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     const int n = P.n;
     const int k = P.k;
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
-    int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
-    uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;  // recorded keys (ordered output)
     const int L = valid_length(P.lengths, row, n);
+    // ordered form made here (KEYS and oout): for k <= kOrdLds the
+    // selection's unordered output and keys go to the upper half of the
+    // histogram area, unused by the selection's rounds; else to global
+    // scratch (P.out / P.keys), read back after a workgroup barrier
+    int32_t* const oout = KEYS && P.oout ? P.oout + (size_t)row * (size_t)k : nullptr;
+    float* const ovals = KEYS && P.ovals ? P.ovals + (size_t)row * (size_t)k : nullptr;
+    const bool in_lds = KEYS && oout && k <= kOrdLds;
+    int32_t* __restrict__ out =
+        in_lds ? reinterpret_cast<int32_t*>(sm.h.h12 + kHistWords) : P.out + (size_t)row * (size_t)k;
+    uint32_t* const okey =
+        !KEYS ? nullptr : (in_lds ? sm.h.h12 + kHistWords + kOrdLds : P.keys + (size_t)row * (size_t)k);
     if (L <= k) {  // everything valid is selected; pad with -1
+        if (KEYS && oout) {
+            if (L > 0)
+                ordered_finish<BLOCK, kRowsCap>(out, okey, true, prow, (uint32_t)L, (uint32_t)L, k, oout, ovals,
+                                                sm.cand, sm.h.h8, sm.scan);
+            else
+                for (int i = tid; i < k; i += BLOCK) {
+                    oout[i] = -1;
+                    if (ovals) ovals[i] = -__builtin_huge_valf();
+                }
+            return;
+        }
         for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
         return;
     }
@@ -1407,6 +1569,16 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                                           sm.sel, P.status);
     }
     __asm__ volatile("" ::"v"(sink));
+    if constexpr (KEYS) {
+        if (oout) {
+            // the WG's own writes of the unordered form are read back
+            // (workgroup-scope barrier: they are complete and visible, in
+            // LDS or global memory)
+            __syncthreads();
+            ordered_finish<BLOCK, kRowsCap>(out, okey, false, prow, (uint32_t)L, (uint32_t)k, k, oout, ovals, sm.cand,
+                                            sm.h.h8, sm.scan);
+        }
+    }
 }
 // ----------------------------------------------------------------- ordered output
 // The ordered form of the selection: section 02 of the TopK article gives
@@ -1454,12 +1626,6 @@ __device__ __forceinline__ uint64_t sort_input(const SortParams& P, int row, int
     return ((uint64_t)key << 32) | (uint64_t)~idx;
 }
 
-// The logit a key came from; -0.0 and +0.0 share a key, so a zero key reads
-// the logit itself to return its sign.
-__device__ __forceinline__ float value_of(uint32_t key, const float* prow, uint32_t L, uint32_t idx) {
-    if (key == 0x80000000u) return idx < L ? prow[idx] : 0.0f;
-    return __uint_as_float(key & 0x80000000u ? key ^ 0x80000000u : ~key);
-}
 
 // Write output slot j of a row from a composite (0 = no element: -1, -inf).
 __device__ __forceinline__ void put_sorted(uint64_t c, int32_t* orow, float* vrow, const float* prow, uint32_t L,
@@ -2576,10 +2742,15 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.region = L.region;
     P.sample_chunks = L.sample_chunks;
     P.ahead = var.rows_kernel ? d->resident[L.variant] : 0;
+    // ordered output from the one-WG-per-row kernel: its WGs order their
+    // rows themselves (no sort kernel)
+    const bool ordered_in_rows = ordered && var.rows_kernel && k <= kRowsCap;
+    P.oout = ordered_in_rows ? out : nullptr;
+    P.ovals = ordered_in_rows ? vals : nullptr;
     (void)hipGetLastError();
     var.launch(dim3((unsigned)(rows * L.G)), dim3((unsigned)var.block), stream, P);
     if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
-    if (!ordered) return TOPK_SELECT_SUCCESS;
+    if (!ordered || ordered_in_rows) return TOPK_SELECT_SUCCESS;
 
     SortParams S;
     S.logits = logits;
