@@ -788,9 +788,11 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     // the row reads the same sample, blocks of 16 chunks spread evenly from
     // the row's first chunk to its last (all of it when the row is no
     // longer), and takes the prefix of the sample's element of rank
-    // r = m + 5 sqrt(m) + 8, m = k S / L the expected count of the row's k
+    // r = m + 4 sqrt(m) + 6, m = k S / L the expected count of the row's k
     // largest among its S sampled logits: a rank that the sample's count
-    // above the row's k-th largest exceeds with a probability below 1e-6.
+    // above the row's k-th largest exceeds with a probability below 1e-5
+    // (binomial tail, for logits drawn alike along the row), so a miss, and
+    // the slow path below, comes about once in 10^5 calls or less.
     // The bound is a lower bound on the k-th largest key when it holds; the
     // finishing WG checks that at least k candidates came out, else the row
     // is finished by passes over it.
@@ -839,7 +841,7 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
         uint32_t r = (uint32_t)k;
         if (!whole_sample) {
             const float mexp = (float)k * (float)S / (float)L;
-            const float rf = ceilf(mexp + 5.0f * sqrtf(mexp) + 8.0f);
+            const float rf = ceilf(mexp + 4.0f * sqrtf(mexp) + 6.0f);
             r = rf >= (float)S ? S : (uint32_t)rf;
         }
         lo = bound_select<BLOCK, 4 * SPT>(sk, r, sm.hist, h2, sm.sel);
@@ -848,10 +850,13 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     if (tid == 0) sm.tag = tag;
 
     // ---- candidates: the slice's composites at or above the bound, in a
-    // fixed order (tile, thread, slot).  A WG that does not finish writes
-    // them to its region and publishes their number; the finishing WG keeps
-    // its own in LDS.
+    // fixed order (tile, thread, slot), staged in LDS.  A WG that does not
+    // finish publishes their number and copies them to its region; the
+    // finishing WG keeps its own in LDS.
     const bool to_region = multi && !fin;
+    // long slices stage their candidates in LDS for line-sized region
+    // stores; short ones (few candidates per thread) store directly
+    constexpr bool kStaged = ITEMS >= 16 || !RESIDENT;
     uint64_t* const region = to_region ? P.stage + ((size_t)row * (size_t)G + (size_t)w) * R : nullptr;
     // the finishing WG counts its candidates into the first round's window
     // histogram as they are placed (sm.hist is zero after the bound)
@@ -860,7 +865,7 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     int par = 0;
     auto place_tile = [&](int c_tile, uint32_t first) {
         uint32_t p = first;
-        if (to_region) {
+        if (to_region) {  // staged in LDS and copied to the region afterwards (long slices), or direct
 #pragma unroll
             for (int j = 0; j < CHUNKS; ++j) {
                 const int ib = 4 * (c_tile + j * BLOCK + tid) - off;
@@ -868,7 +873,11 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t key = keys[4 * j + e];
                     const bool t = key >= lo;
-                    if (t & (p < R)) st_dev(&region[p], composite(key, (uint32_t)(ib + e)));
+                    if constexpr (kStaged) {
+                        if (t & (p < (uint32_t)kBufCap)) sm.cand[p] = composite(key, (uint32_t)(ib + e));
+                    } else {
+                        if (t & (p < R)) st_dev(&region[p], composite(key, (uint32_t)(ib + e)));
+                    }
                     p += t ? 1u : 0u;
                 }
             }
@@ -911,7 +920,15 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
         }
         if (to_region && tid == 0) st_dev(&rw->cnt[w], ((uint64_t)tag << 32) | (uint64_t)total);
     }
-    if (to_region) return;
+    if (to_region) {
+        if constexpr (!kStaged) return;
+        // the staged candidates to the region in consecutive order: each
+        // wave's stores cover whole lines
+        lds_sync();
+        const uint32_t nw = min(total, (uint32_t)(R < (size_t)kBufCap ? R : (size_t)kBufCap));
+        for (uint32_t i = (uint32_t)tid; i < nw; i += BLOCK) st_dev(&region[i], sm.cand[i]);
+        return;
+    }
 
     // ---- the finishing WG: its own candidates are cand[0 .. total); the
     // other WGs' follow in WG order
