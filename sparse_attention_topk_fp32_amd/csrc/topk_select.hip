@@ -1136,16 +1136,17 @@ constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered en
 // (descending bins), and each is written at its exact rank: the entries of
 // the bins above its own plus the larger ones of its own bin (bins hold a
 // few entries, or equal keys).  Positions follow from the values alone;
-// slots past cnt get -1 and -inf.  sidx/skey may point to LDS or global
-// memory.  T: CAP composites of LDS (cnt <= CAP); hist: 2 * kOrdBins words;
-// scan: BLOCK / 64 words.
+// slots past cnt get -1 and -inf.  T: CAP composites of LDS (cnt <= MAXC
+// <= CAP; the ranked entries are staged after them when 2 cnt <= CAP);
+// hist: 2 * kOrdBins words; scan: BLOCK / 64 words.
 constexpr int kOrdBins = 2048;
 constexpr int kOrdLds = 2048;  // one WG per row: k up to this keeps the unordered output in LDS
-template <int BLOCK, int CAP>
+template <int BLOCK, int MAXC, int CAP>
 __device__ __forceinline__ void ordered_finish(const int32_t* sidx, const uint32_t* skey, bool from_logits,
                                                const float* prow, uint32_t L, uint32_t cnt, int k, int32_t* oout,
                                                float* ovals, uint64_t* T, uint32_t* hist, uint32_t* scan) {
-    constexpr int NU = (CAP + BLOCK - 1) / BLOCK;
+    static_assert(MAXC <= CAP, "the entries fit T");
+    constexpr int NU = (MAXC + BLOCK - 1) / BLOCK;  // cnt <= MAXC
     constexpr int NW = BLOCK / 64;
     constexpr int BPT = kOrdBins / BLOCK;  // bins per thread for the starts
     static_assert(kOrdBins % BLOCK == 0 && kOrdBins >= BLOCK, "whole bins per thread");
@@ -1244,12 +1245,12 @@ __device__ __forceinline__ void ordered_finish(const int32_t* sidx, const uint32
             if (ovals) ovals[r] = v;
         }
     }
-    if (staged) {  // in order: coalesced stores
+    if (staged) {  // in order: coalesced stores, marked non-temporal (written once, not read here)
         __syncthreads();
         for (uint32_t j = (uint32_t)tid; j < cnt; j += BLOCK) {
             const uint2 o = O[j];
-            oout[j] = (int32_t)o.x;
-            if (ovals) ovals[j] = __uint_as_float(o.y);
+            __builtin_nontemporal_store((int32_t)o.x, oout + j);
+            if (ovals) __builtin_nontemporal_store(__uint_as_float(o.y), ovals + j);
         }
     }
     for (uint32_t j = cnt + (uint32_t)tid; j < (uint32_t)k; j += BLOCK) {
@@ -1273,9 +1274,14 @@ struct RowsSmem {
     uint32_t sel[4];
 };
 
-template <int BLOCK, int ITEMS, int PD, bool KEYS>
+// MODE 0: unordered output; 1: unordered output with its keys recorded to
+// global scratch (ordered by a second launch); 2: the ordered output made
+// here (k <= kOrdLds), the unordered form kept in LDS.
+template <int BLOCK, int ITEMS, int PD, int MODE>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void topk_rows_kernel(const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
+    constexpr bool KEYS = MODE != 0;
+    constexpr bool ORD = MODE == 2;
     constexpr int F = 12;
     constexpr int NB0 = 1 << F;
     constexpr int CHUNKS = ITEMS / 4;
@@ -1288,21 +1294,20 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     const int k = P.k;
     const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
     const int L = valid_length(P.lengths, row, n);
-    // ordered form made here (KEYS and oout): for k <= kOrdLds the
-    // selection's unordered output and keys go to the upper half of the
-    // histogram area, unused by the selection's rounds; else to global
-    // scratch (P.out / P.keys), read back after a workgroup barrier
-    int32_t* const oout = KEYS && P.oout ? P.oout + (size_t)row * (size_t)k : nullptr;
-    float* const ovals = KEYS && P.ovals ? P.ovals + (size_t)row * (size_t)k : nullptr;
-    const bool in_lds = KEYS && oout && k <= kOrdLds;
+    // ordered form made here (ORD): the selection's unordered output and
+    // keys go to the upper half of the histogram area, unused by the
+    // selection's rounds (LDS addresses known at compile time: LDS
+    // instructions); else to out_idx, or to global scratch with the keys
+    int32_t* const oout = ORD ? P.oout + (size_t)row * (size_t)k : nullptr;
+    float* const ovals = ORD && P.ovals ? P.ovals + (size_t)row * (size_t)k : nullptr;
     int32_t* __restrict__ out =
-        in_lds ? reinterpret_cast<int32_t*>(sm.h.h12 + kHistWords) : P.out + (size_t)row * (size_t)k;
+        ORD ? reinterpret_cast<int32_t*>(sm.h.h12 + kHistWords) : P.out + (size_t)row * (size_t)k;
     uint32_t* const okey =
-        !KEYS ? nullptr : (in_lds ? sm.h.h12 + kHistWords + kOrdLds : P.keys + (size_t)row * (size_t)k);
+        !KEYS ? nullptr : (ORD ? sm.h.h12 + kHistWords + kOrdLds : P.keys + (size_t)row * (size_t)k);
     if (L <= k) {  // everything valid is selected; pad with -1
-        if (KEYS && oout) {
+        if constexpr (ORD) {
             if (L > 0)
-                ordered_finish<BLOCK, kRowsCap>(out, okey, true, prow, (uint32_t)L, (uint32_t)L, k, oout, ovals,
+                ordered_finish<BLOCK, kOrdLds, kRowsCap>(out, okey, true, prow, (uint32_t)L, (uint32_t)L, k, oout, ovals,
                                                 sm.cand, sm.h.h8, sm.scan);
             else
                 for (int i = tid; i < k; i += BLOCK) {
@@ -1586,15 +1591,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                                           sm.sel, P.status);
     }
     __asm__ volatile("" ::"v"(sink));
-    if constexpr (KEYS) {
-        if (oout) {
-            // the WG's own writes of the unordered form are read back
-            // (workgroup-scope barrier: they are complete and visible, in
-            // LDS or global memory)
-            __syncthreads();
-            ordered_finish<BLOCK, kRowsCap>(out, okey, false, prow, (uint32_t)L, (uint32_t)k, k, oout, ovals, sm.cand,
-                                            sm.h.h8, sm.scan);
-        }
+    if constexpr (ORD) {
+        lds_sync();  // the unordered form is complete in LDS
+        ordered_finish<BLOCK, kOrdLds, kRowsCap>(out, okey, false, prow, (uint32_t)L, (uint32_t)k, k, oout, ovals,
+                                                 sm.cand, sm.h.h8, sm.scan);
     }
 }
 // ----------------------------------------------------------------- ordered output
@@ -2348,17 +2348,19 @@ int occupancy_split(int* nb, int block) {
 
 template <int B, int I, int D>
 void launch_rows(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-    if (p.keys) hipLaunchKernelGGL((topk_rows_kernel<B, I, D, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((topk_rows_kernel<B, I, D, false>), grid, block, 0, s, p);
+    if (p.oout) hipLaunchKernelGGL((topk_rows_kernel<B, I, D, 2>), grid, block, 0, s, p);
+    else if (p.keys) hipLaunchKernelGGL((topk_rows_kernel<B, I, D, 1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((topk_rows_kernel<B, I, D, 0>), grid, block, 0, s, p);
 }
 
 template <int B, int I, int D>
 int occupancy_rows(int* nb, int block) {
-    int a = 0, b = 0;
-    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_rows_kernel<B, I, D, false>, block, 0);
-    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_rows_kernel<B, I, D, true>, block, 0);
-    *nb = a < b ? a : b;
-    return r1 != 0 ? r1 : r2;
+    int a = 0, b = 0, c = 0;
+    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_rows_kernel<B, I, D, 0>, block, 0);
+    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_rows_kernel<B, I, D, 1>, block, 0);
+    const int r3 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, topk_rows_kernel<B, I, D, 2>, block, 0);
+    *nb = min(a, min(b, c));
+    return r1 != 0 ? r1 : (r2 != 0 ? r2 : r3);
 }
 
 struct Variant {
@@ -2759,9 +2761,9 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.region = L.region;
     P.sample_chunks = L.sample_chunks;
     P.ahead = var.rows_kernel ? d->resident[L.variant] : 0;
-    // ordered output from the one-WG-per-row kernel: its WGs order their
-    // rows themselves (no sort kernel)
-    const bool ordered_in_rows = ordered && var.rows_kernel && k <= kRowsCap;
+    // ordered output from the one-WG-per-row kernel for k <= kOrdLds: its
+    // WGs order their rows themselves (no sort kernel)
+    const bool ordered_in_rows = ordered && var.rows_kernel && k <= kOrdLds;
     P.oout = ordered_in_rows ? out : nullptr;
     P.ovals = ordered_in_rows ? vals : nullptr;
     (void)hipGetLastError();
