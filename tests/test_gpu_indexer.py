@@ -125,3 +125,75 @@ def test_indexer_batched_ragged_workload(torch_gpu):
     assert_logits_close(wl, lg[sample], rows=sample)
     want = oracle.topk(lg, wl.k, wl.lengths)
     assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(want, 1))
+
+
+def _sample_groups(n):
+    """Groups of 64 tokens that the indexer with the selection's first pass
+    samples for its bound: every F-th group (F the smallest power of two from 2 that
+    keeps 64 or fewer), group j F + F - 1 for j < ng // F."""
+    ng = (n + 63) // 64
+    F = 2
+    while ng // F > 64:
+        F *= 2
+    return [j * F + F - 1 for j in range(ng // F)]
+
+
+def _select_and_check(torch_gpu, wl, label):
+    import sparse_attention_topk_fp32_amd as tks
+
+    _say(label)
+    q, kc, w, L = _dev(torch_gpu, wl)
+    idx, lg = tks.indexer_select(q, kc, w, wl.k, lengths=L, return_logits=True)
+    assert tks.device_status() == 0
+    lg = lg.cpu().numpy()
+    want = oracle.topk(lg, wl.k, wl.lengths)
+    assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(want, 1))
+    return idx.cpu().numpy(), lg
+
+
+@pytest.mark.parametrize("rows,n,heads,dim,k,lengths", [
+    (5, 12345, 20, 64, 1000, "uniform"),  # ragged rows, n not a multiple of 64
+    (1, 16384, 64, 128, 5000, None),      # large k, candidates still on chip
+    (1, 16384, 64, 128, 7000, None),      # too many for the buffer: logits kernel, then the selection
+    (2, 65, 8, 32, 64, None),              # two groups, one sampled
+    (3, 200000, 16, 32, 2048, None),      # n not a multiple of 64, sample stride 64
+    (8, 65536, 64, 128, 4096, "uniform"),
+])
+def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths):
+    wl = W.draw(rows, n, heads, dim, k=k, seed=rows * 7 + n % 1000 + k, lengths=lengths)
+    if lengths == "uniform":
+        # some rows short of k (every valid token selected), one empty
+        wl.lengths[0] = min(k, n)
+        if rows > 2:
+            wl.lengths[1] = 0
+    _select_and_check(torch_gpu, wl, "indexer shape rows=%d n=%d heads=%d dim=%d k=%d %s" % (
+        rows, n, heads, dim, k, lengths or "full"))
+
+
+@pytest.mark.parametrize("scale,label", [(8.0, "sample above the row"), (0.125, "sample below the row")])
+def test_indexer_selection_misleading_sample(torch_gpu, scale, label):
+    """The sampled groups' keys scaled (exactly, by a power of two) so that
+    the sample's bound lies far above the row's k-th largest (fewer than k
+    candidates) or far below it (more than the on-chip buffer): the row is
+    then selected by passes over its logits, still exactly."""
+    n, k = 65536, 2048
+    wl = W.draw(1, n, 16, 64, k=k, seed=5 + int(scale * 8))
+    for g in _sample_groups(n):
+        wl.kc[0, 64 * g:64 * g + 64] *= np.float32(scale)
+    _select_and_check(torch_gpu, wl, "indexer %s n=%d k=%d" % (label, n, k))
+
+
+def test_indexer_selection_is_repeatable(torch_gpu):
+    """The indexer selection writes the same bytes on every call (positions
+    follow from block scans and exact ranks, not from timing)."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    for name in ("idx_b1_n128k_h64_d128", "idx_b64_n16k_h64_d128_ragged"):
+        wl = W.generate_indexer(name)
+        _say("indexer repeatability %s" % name)
+        q, kc, w, L = _dev(torch_gpu, wl)
+        first = tks.indexer_select(q, kc, w, wl.k, lengths=L).cpu().numpy()
+        for _ in range(3):
+            again = tks.indexer_select(q, kc, w, wl.k, lengths=L).cpu().numpy()
+            assert np.array_equal(first, again)
+        assert tks.device_status() == 0
