@@ -193,12 +193,7 @@ int topk_indexer_logits(const uint16_t* q, const uint16_t* kc, const float* w, i
  *   out_logits  device, float [rows, n], receives the logits; or NULL, and
  *               they go to a scratch area of the (device, stream) of
  *               rows*n*4 bytes (grown with hipMalloc when needed).
- * Two kernels are enqueued.  When the candidates of a sampled bound fit
- * the finishing WG's buffer (k up to about 6,000 for rows up to 2^20), the
- * first computes the logits and, in the same pass, the candidates at or
- * above a bound taken from a sample of the row's groups, and the second
- * selects from those candidates (reading the logits only when the sample
- * misled); else the logits kernel and topk_select run.
+ * Two kernels are enqueued (the logits, then the selection).
  */
 int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
                         int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k,

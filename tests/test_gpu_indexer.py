@@ -127,15 +127,9 @@ def test_indexer_batched_ragged_workload(torch_gpu):
     assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(want, 1))
 
 
-def _sample_groups(n):
-    """Groups of 64 tokens that the indexer with the selection's first pass
-    samples for its bound: every F-th group (F the smallest power of two from 2 that
-    keeps 64 or fewer), group j F + F - 1 for j < ng // F."""
-    ng = (n + 63) // 64
-    F = 2
-    while ng // F > 64:
-        F *= 2
-    return [j * F + F - 1 for j in range(ng // F)]
+def _periodic_groups(n, per):
+    """Every per-th group of 64 tokens (group j per + per - 1)."""
+    return [j * per + per - 1 for j in range((n + 63) // 64 // per)]
 
 
 def _select_and_check(torch_gpu, wl, label):
@@ -153,10 +147,10 @@ def _select_and_check(torch_gpu, wl, label):
 
 @pytest.mark.parametrize("rows,n,heads,dim,k,lengths", [
     (5, 12345, 20, 64, 1000, "uniform"),  # ragged rows, n not a multiple of 64
-    (1, 16384, 64, 128, 5000, None),      # large k, candidates still on chip
-    (1, 16384, 64, 128, 7000, None),      # too many for the buffer: logits kernel, then the selection
-    (2, 65, 8, 32, 64, None),              # two groups, one sampled
-    (3, 200000, 16, 32, 2048, None),      # n not a multiple of 64, sample stride 64
+    (1, 16384, 64, 128, 5000, None),      # large k
+    (1, 16384, 64, 128, 7000, None),
+    (2, 65, 8, 32, 64, None),              # one token past a group of 64
+    (3, 200000, 16, 32, 2048, None),      # n not a multiple of 64
     (8, 65536, 64, 128, 4096, "uniform"),
 ])
 def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths):
@@ -170,15 +164,16 @@ def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths):
         rows, n, heads, dim, k, lengths or "full"))
 
 
-@pytest.mark.parametrize("scale,label", [(8.0, "sample above the row"), (0.125, "sample below the row")])
-def test_indexer_selection_misleading_sample(torch_gpu, scale, label):
-    """The sampled groups' keys scaled (exactly, by a power of two) so that
-    the sample's bound lies far above the row's k-th largest (fewer than k
-    candidates) or far below it (more than the on-chip buffer): the row is
-    then selected by passes over its logits, still exactly."""
+@pytest.mark.parametrize("scale,label", [(8.0, "periodic groups above the row"),
+                                         (0.125, "periodic groups below the row")])
+def test_indexer_selection_periodic_rows(torch_gpu, scale, label):
+    """Rows with a period: the keys of every 16th group of 64 tokens scaled
+    (exactly, by a power of two), so that their logits lie far above or far
+    below the rest; selection still exact against the oracle on the
+    emitted logits."""
     n, k = 65536, 2048
     wl = W.draw(1, n, 16, 64, k=k, seed=5 + int(scale * 8))
-    for g in _sample_groups(n):
+    for g in _periodic_groups(n, 16):
         wl.kc[0, 64 * g:64 * g + 64] *= np.float32(scale)
     _select_and_check(torch_gpu, wl, "indexer %s n=%d k=%d" % (label, n, k))
 
