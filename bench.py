@@ -172,7 +172,8 @@ def bench_workload(torch, tks, W, name: str, steps: int, warmup: int, copies: in
 
 
 def bench_indexer(torch, tks, W, name: str, steps: int, warmup: int):
-    """The indexer producer (DSA step 1) and producer + selection, cold: key
+    """The indexer producer (DSA step 1), producer + selection, and the
+    fused form (the selection's first pass in the logits kernel), cold: key
     copies rotated (>= 512 MiB).  Seconds per launch."""
     wl = W.generate_indexer(name)
     rows, H, d = wl.q.shape
@@ -193,6 +194,9 @@ def bench_indexer(torch, tks, W, name: str, steps: int, warmup: int):
     t_select, _ = time_graph(torch, [(lambda kc: (lambda: tks.indexer_select(q, kc, w, wl.k, lengths=L, out=out,
                                                                              out_logits=lg)))(kc)
                                      for kc in kcs], steps, warmup, stream)
+    t_fused, _ = time_graph(torch, [(lambda kc: (lambda: tks.indexer_select(q, kc, w, wl.k, lengths=L, out=out,
+                                                                            out_logits=lg, fused=True)))(kc)
+                                    for kc in kcs], steps, warmup, stream)
     if tks.device_status(stream):
         raise RuntimeError("device-side error flags raised during the indexer benchmark")
     valid = n * rows if wl.lengths is None else int(np.minimum(wl.lengths.astype(np.int64), n).sum())
@@ -202,6 +206,7 @@ def bench_indexer(torch, tks, W, name: str, steps: int, warmup: int):
     flops = 2 * valid * H * d
     return {"workload": name, "rows": rows, "n": n, "heads": H, "dim": d, "k": wl.k,
             "us_logits": round(t_logits * 1e6, 3), "us_logits_and_select": round(t_select * 1e6, 3),
+            "us_logits_and_select_fused": round(t_fused * 1e6, 3),
             "algorithmic_bytes_logits": nbytes, "achieved_GBps": round(nbytes / t_logits / 1e9, 3),
             "hbm_frac": round(nbytes / t_logits / 1e9 / HBM_PEAK_GBPS, 6),
             "mfma_TFLOPs": round(flops / t_logits / 1e12, 3),

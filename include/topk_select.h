@@ -200,6 +200,38 @@ int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, i
                         int32_t* out_idx, float* out_logits, topk_select_stream_t stream);
 
 /*
+ * topk_indexer_select_fused - the same result as topk_indexer_select (the
+ * same index set; the order within a row is fixed, by the values and the
+ * launch shape, but may differ from topk_indexer_select's), with the
+ * selection's pass over the row moved into the logits kernel (the article's
+ * section 01: step 1 producing step 2's input), so that the selection
+ * afterwards reads candidates only:
+ *   1. one kernel computes the logits (written to out_logits or scratch, as
+ *      above); WGs holding every F-th group of 64 tokens (F a power of two,
+ *      at most 64 groups per row) publish their keys and the row's bound,
+ *      the sample's element of rank m + 4 sqrt(m) + 6, m = k * S / L for S
+ *      sampled valid tokens; the other WGs wait for it and write their
+ *      logits at or above it to per-WG regions;
+ *   2. one WG per row gathers those candidates and selects the k largest
+ *      on chip; when fewer than k or too many came out (the sample misled)
+ *      it selects by passes over the logits row.
+ * Taken when the candidates fit the finishing WG (about
+ * k + 4 sqrt(k F) + 6 F + 256 <= 7168) and a row needs at most 512 WGs;
+ * else this is topk_indexer_select.  Measured on MI355X it is slower than
+ * topk_indexer_select (the bound exists only once the logits pass is done,
+ * and the chain after it outlasts the selection on fresh logits); it is the
+ * fused form of the producer, kept for comparison.
+ * Scratch of the (device, stream), grown with hipMalloc: 4160 + 32768 bytes
+ * per row (zeroed when allocated) and 8 bytes per logit of the row's
+ * regions.  Waits are bounded as in topk_select (flag 1); a WG that gives
+ * up makes its row be selected by passes over the logits, so the output
+ * stays exact.  Errors as for topk_indexer_select.
+ */
+int topk_indexer_select_fused(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                              int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k,
+                              int32_t* out_idx, float* out_logits, topk_select_stream_t stream);
+
+/*
  * topk_sparse_attention - attention over the selected positions: the TopK
  * article, section 01, step 3 of DSA-style decoding (attention computed only
  * on the keys and values of the k selected positions).  The article gives

@@ -37,6 +37,7 @@ __all__ = [
     "topk_select_sorted",
     "topk_indexer_logits",
     "topk_indexer_select",
+    "topk_indexer_select_fused",
     "topk_select_sorted_ex",
     "plan",
     "num_variants",
@@ -105,6 +106,16 @@ def topk_indexer_select(q_ptr: int, kc_ptr: int, w_ptr: int, rows: int, n: int, 
     return _native.load().topk_indexer_select(q_ptr or None, kc_ptr or None, w_ptr or None, rows, n, heads, dim,
                                               kstride, lengths_ptr or None, k, out_ptr or None,
                                               logits_ptr or None, stream or None)
+
+
+def topk_indexer_select_fused(q_ptr: int, kc_ptr: int, w_ptr: int, rows: int, n: int, heads: int, dim: int,
+                              kstride: int, lengths_ptr: Optional[int], k: int, out_ptr: int,
+                              logits_ptr: Optional[int], stream: int = 0) -> int:
+    """Raw C-ABI call of the indexer with the selection's first pass in the
+    logits kernel."""
+    return _native.load().topk_indexer_select_fused(q_ptr or None, kc_ptr or None, w_ptr or None, rows, n, heads,
+                                                    dim, kstride, lengths_ptr or None, k, out_ptr or None,
+                                                    logits_ptr or None, stream or None)
 
 
 def _stream_handle(stream) -> int:
@@ -270,10 +281,12 @@ def indexer_logits(q, kc, w, lengths=None, out=None, stream=None):
 
 
 def indexer_select(q, kc, w, k: int, lengths=None, out=None, out_logits=None, return_logits: bool = False,
-                   stream=None):
+                   stream=None, fused: bool = False):
     """The indexer logits, then the selection of the k largest per row
     (unordered, as ``select``).  Returns the indices, or (indices, logits)
-    with ``return_logits`` (or ``out_logits`` given)."""
+    with ``return_logits`` (or ``out_logits`` given).  ``fused`` calls
+    topk_indexer_select_fused (the selection's first pass in the logits
+    kernel) instead of topk_indexer_select."""
     import torch
 
     rows, heads, dim, n, kstride, lp = _indexer_args(q, kc, w, lengths)
@@ -286,10 +299,11 @@ def indexer_select(q, kc, w, k: int, lengths=None, out=None, out_logits=None, re
         out_logits = torch.empty((rows, n), dtype=torch.float32, device=q.device)
     elif want:
         _check_out(out_logits, torch.float32, rows, n, q, "out_logits")
+    fn = topk_indexer_select_fused if fused else topk_indexer_select
     with torch.cuda.device(q.device):
-        rc = topk_indexer_select(q.data_ptr(), kc.data_ptr(), w.data_ptr(), rows, n, heads, dim, kstride, lp, k,
-                                 out.data_ptr(), out_logits.data_ptr() if want else None, _stream_handle(stream))
-    _check(rc, "topk_indexer_select")
+        rc = fn(q.data_ptr(), kc.data_ptr(), w.data_ptr(), rows, n, heads, dim, kstride, lp, k, out.data_ptr(),
+                out_logits.data_ptr() if want else None, _stream_handle(stream))
+    _check(rc, "topk_indexer_select_fused" if fused else "topk_indexer_select")
     return (out, out_logits) if want else out
 
 

@@ -32,6 +32,7 @@ EXPORTS = (
     "topk_select_sorted_ex",
     "topk_indexer_logits",
     "topk_indexer_select",
+    "topk_indexer_select_fused",
     "topk_sparse_attention",
     "topk_select_plan",
     "topk_select_num_variants",
@@ -92,6 +93,8 @@ def load() -> ctypes.CDLL:
         lib.topk_indexer_logits.restype = ctypes.c_int
         lib.topk_indexer_select.argtypes = [P, P, P, I, I, I, I, I64, P, I, P, P, P]
         lib.topk_indexer_select.restype = ctypes.c_int
+        lib.topk_indexer_select_fused.argtypes = [P, P, P, I, I, I, I, I64, P, I, P, P, P]
+        lib.topk_indexer_select_fused.restype = ctypes.c_int
         lib.topk_sparse_attention.argtypes = [P, P, P, P, I, I, I, I, I64, I, ctypes.c_float, P, P]
         lib.topk_sparse_attention.restype = ctypes.c_int
         lib.topk_select_plan.argtypes = [I, I, I, ctypes.POINTER(PlanT)]

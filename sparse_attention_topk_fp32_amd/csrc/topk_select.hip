@@ -683,6 +683,60 @@ __device__ __forceinline__ uint32_t bound_select(const uint32_t (&ks)[NK], uint3
     return lo > 1u ? lo : 1u;
 }
 
+// The key of rank r (1-based, from the top) among the keys the WG's threads
+// hold (NK each, 0 = empty), located to within 1/4096 of their range in one
+// pass: the range [min, max] of the keys split into 4096 bins; returns the
+// lower edge of the bin holding rank r (at least 1), a lower bound on that
+// key.  Bins follow the keys' own range, so keys that share their top bits
+// (logits of one magnitude) still spread over many bins (few LDS atomics
+// on one word).  hist: 4096 words, zero on entry, behind a barrier; scan:
+// BLOCK / 64 words; red: 2 BLOCK / 64 words; sel: 4 words.
+template <int BLOCK, int NK>
+__device__ __forceinline__ uint32_t bound_select_range(const uint32_t (&ks)[NK], uint32_t r, uint32_t* hist,
+                                                       uint32_t* scan, uint32_t* sel, uint32_t* red,
+                                                       uint32_t* status) {
+    constexpr int NW = BLOCK / 64;
+    const int tid = threadIdx.x;
+    uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        if (ks[i] != 0u) {
+            mn = min(mn, ks[i]);
+            mx = max(mx, ks[i]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    }
+    if ((tid & 63) == 0) {
+        red[2 * (tid >> 6)] = mn;
+        red[2 * (tid >> 6) + 1] = mx;
+    }
+    lds_sync();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        mn = min(mn, red[2 * i]);
+        mx = max(mx, red[2 * i + 1]);
+    }
+    mn = uniform(mn);
+    mx = uniform(mx);
+    if (mx == 0u) return 1u;  // no keys
+    const uint32_t range = mx - mn;
+    const int q = range ? 32 - __builtin_clz(range) : 0;
+    const int s = q > 12 ? q - 12 : 0;  // (key - mn) >> s < 4096
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+        if (ks[i] != 0u) atomicAdd(&hist[(ks[i] - mn) >> s], 1u);
+    lds_sync();
+    uint32_t b, above, hb;
+    local_select<BLOCK, 4096, 1, 4096, false>(hist, r, scan, sel, status, b, above, hb);
+    if (hb == 0u) return 1u;
+    const uint32_t lo = mn + (b << s);
+    return lo > 1u ? lo : 1u;
+}
+
 // ----------------------------------------------------------------- split kernel (few rows)
 //
 // BLOCK threads per WG, ITEMS logits per thread per tile; RESIDENT: the
@@ -2050,6 +2104,401 @@ __global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P)
     }
 }
 
+// ----------------------------------------------------------------- indexer with the selection's first pass
+//
+// Steps 1 and 2 of DSA-style decoding (the TopK article, section 01) where
+// the logits kernel also does the selection's pass over the row, so that
+// the selection afterwards reads candidates only, never the logits row.  A
+// row's groups of 64 tokens are split between sample WGs, which take every
+// F-th group (sample group j is group j F + F - 1), and tile WGs, which
+// take the others in order.  Both write the logits (the output, or
+// scratch) as the logits kernel does and keep their keys in registers.
+//  * Sample WGs publish their keys, tagged with the row's epoch; the row's
+//    last sample WG reads them all and publishes the bound, a lower bound on
+//    the sample's element of rank r = m + 4 sqrt(m) + 6, m = k S / L for S
+//    sampled valid tokens (the split selection's rule).
+//  * Tile WGs wait for the bound, then write how many of their keys reach
+//    it and those composites, in a fixed order, to their region.
+// Then one WG per row (topk_indexer_finish_kernel) gathers the sample's keys
+// at or above the bound and every region into LDS and selects the row's k
+// largest there (select_buffer, which needs every key at or above the
+// bound and at least k of them).  When fewer than k or more than its
+// buffer holds came out (the sample misled) it selects by passes over the
+// logits row instead.
+// The only wait is a tile WG's for its row's bound, which WGs placed before
+// it in the grid publish (dispatched before it, so it never waits on a WG
+// without a slot); it is bounded (spin_limit; flag kFlagTimeout), and a WG
+// that gives up marks its count so that the row is selected by passes.
+
+constexpr int kFusedMaxT = 512;        // tile WGs per row
+constexpr int kFusedSample = 4096;     // sampled tokens per row at most (64 groups)
+constexpr int kFinBlock = 1024;        // threads of the finishing WG
+constexpr uint32_t kFusedGaveUp = 0xFFFFFFFFu;  // a tile WG's count when its wait for the bound gave up
+
+// Per-row state; the rows' sample keys follow the array of these
+// (kFusedSample tagged entries per row, row r always at the same place, so
+// that a stale entry only ever carries an older epoch of its own row).
+struct alignas(64) FusedRow {
+    uint64_t bound;            // (tag << 32) | the row's bound
+    uint32_t epoch;            // advanced by the finishing WG
+    uint32_t pad[13];
+    uint64_t cnt[kFusedMaxT];  // (tag << 32) | candidates of tile WG t
+};
+
+struct FusedParams {
+    const uint16_t* q;       // [rows, H, D] bf16
+    const uint16_t* kc;      // keys of row r at kc + r * kstride: [n, D] bf16
+    const float* w;          // [rows, H]
+    const int32_t* lengths;  // [rows] or null
+    float* logits;           // [rows, n]
+    int32_t* out;            // [rows, k]
+    uint32_t* status;
+    FusedRow* frs;           // [rows]
+    uint64_t* samp;          // [rows][kFusedSample] tagged sample keys
+    uint64_t* stage;         // [rows][NT][256 gpw] candidate composites
+    int64_t kstride;
+    int32_t rows, n, H, k;
+    int32_t gpw;             // groups of 64 tokens per wave
+    int32_t F;               // sample stride in groups (>= 2)
+    int32_t ns;              // sample groups per row (<= 64)
+    int32_t NS, NT;          // sample and tile WGs per row
+};
+
+template <int D, int HB>
+__global__ void __launch_bounds__(kLogitBlock) topk_indexer_cand_kernel(FusedParams P) {
+    constexpr int BLOCK = kLogitBlock;
+    constexpr int CPR = D / 8;
+    constexpr int GB = 64 * D * 2;   // bytes of one group's keys
+    constexpr int NL = GB / 1024;    // 16-byte loads per lane per group
+    constexpr int kStageBytes = (BLOCK / 64) * GB;
+    constexpr int kLds = kStageBytes + HB * 16 * CPR * 16;
+    static_assert((4096 + 4 + 3 * BLOCK / 64) * 4 <= kLds, "the bound's histogram fits");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+    const int per_row = P.NS + P.NT;
+    const int row = (int)blockIdx.x / per_row;
+    const int wi = (int)blockIdx.x - row * per_row;
+    const bool sampler = wi < P.NS;
+    const int widx = sampler ? wi : wi - P.NS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = P.n, H = P.H, k = P.k;
+    const int L = valid_length(P.lengths, row, n);
+    const int F = P.F, ns = P.ns, gpw = P.gpw;
+    const int ng = (n + 63) >> 6;
+    const int gbase = (widx * (BLOCK / 64) + wave) * gpw;  // the wave's first group number in its role
+    const int cntw = max(0, min(gpw, (sampler ? ns : ng - ns) - gbase));
+    auto group_of = [&](int i) -> int {
+        const int u = gbase + i;
+        return sampler ? u * F + F - 1 : u + min(u / (F - 1), ns);
+    };
+    int nvw = 0;  // the wave's groups holding valid tokens (a prefix: groups ascend)
+    for (int i = 0; i < cntw; ++i)
+        if (64 * group_of(i) < L) nvw = i + 1;
+    u32x4_t* const st = reinterpret_cast<u32x4_t*>(smem) + wave * (GB / 16);
+    u32x4_t* const qs = reinterpret_cast<u32x4_t*>(smem + kStageBytes);
+    const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kstride);
+    u32x4_t r[NL];
+    const bool early = gpw > 1 && nvw > 0;
+    if (early) {
+        const int tw = 64 * group_of(0);
+        logits_load<D, NL>(r, K, tw, L - 1 - tw, lane);
+    }
+    logits_stage_queries<D>(qs, P.q, row, H);
+    FusedRow* const fr = P.frs + row;
+    // a sample WG's epoch (tags of its keys) is loaded now, before its key
+    // loads, and is there when they are; tile WGs load it once their keys
+    // are done (the many WGs of a row then do not load it all at once)
+    uint32_t ep = 0;
+    if (sampler && L > k) ep = ld_dev(&fr->epoch);
+    __syncthreads();
+    float* const lrow = P.logits + (size_t)row * (size_t)n;
+    const float ninf = -__builtin_huge_valf();
+    uint32_t kk[8];  // key of token 64 group_of(i) + lane (0: none)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kk[i] = 0u;
+    if (nvw > 0) {
+        bf16x8_t a[HB][D / 32];
+        float wt[HB][4];
+        logits_operands<D, HB>(qs, P.w + (size_t)row * H, H, lane, a, wt);
+        if (!early) {
+            const int tw = 64 * group_of(0);
+            logits_load<D, NL>(r, K, tw, L - 1 - tw, lane);
+        }
+        for (int i = 0; i < nvw; ++i) {
+            const int tw = 64 * group_of(i);
+            logits_stage<D, NL>(st, r, lane);
+            if (i + 1 < nvw) {
+                const int tn = 64 * group_of(i + 1);
+                logits_load<D, NL>(r, K, tn, L - 1 - tn, lane);
+            }
+            const float mine = logits_group<D, HB>(st, a, wt, tw, L, lane);
+            const int t = tw + lane;
+            const bool valid = t < L;
+            if (t < n) lrow[t] = valid ? mine : ninf;
+            const uint32_t key = valid ? key_of(mine) : 0u;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                if (s2 == i) kk[s2] = key;
+        }
+    }
+    for (int i = nvw; i < cntw; ++i) {
+        const int t = 64 * group_of(i) + lane;
+        if (t < n) lrow[t] = ninf;
+    }
+    if (L <= k) return;  // every valid token is selected: nothing to publish
+    const uint64_t lim = spin_limit();
+    uint64_t* const sp = P.samp + (size_t)row * (size_t)kFusedSample;
+    if (sampler) {
+        const uint32_t tag = make_tag(uniform(ep));
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+            if (s2 < cntw) st_dev(&sp[(gbase + s2) * 64 + lane], ((uint64_t)tag << 32) | kk[s2]);
+        if (widx != P.NS - 1) return;
+        // the row's last sample WG: every sample key (waited for), then the bound
+        __syncthreads();  // the key stage and the queries are done with
+        uint32_t* const hist = reinterpret_cast<uint32_t*>(smem);
+        uint32_t* const sel = hist + 4096;
+        uint32_t* const scan = sel + 4;
+        uint32_t* const red = scan + BLOCK / 64;
+        clear_words(hist, 4096, tid, BLOCK);
+        const int SN = ns * 64;
+        uint64_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int j = tid + u * BLOCK;
+            v[u] = j < SN ? ld_dev(&sp[j]) : ((uint64_t)tag << 32);
+        }
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            bool miss = false;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) miss |= (uint32_t)(v[u] >> 32) != tag;
+            if (!miss) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 >= lim) {
+                raise_flag(P.status, kFlagTimeout);  // the bound then comes from the keys seen
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int j = tid + u * BLOCK;
+                if ((uint32_t)(v[u] >> 32) != tag) v[u] = ld_dev(&sp[j]);
+            }
+        }
+        uint32_t ks[16], cnt = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            ks[u] = (uint32_t)(v[u] >> 32) == tag ? (uint32_t)v[u] : 0u;
+            cnt += ks[u] != 0u;
+        }
+        uint32_t S;
+        (void)block_scan_total<BLOCK>(cnt, scan, S);
+        uint32_t lo = 1u;
+        if (S > 0u) {
+            const float mexp = (float)k * (float)S / (float)L;
+            const float rf = ceilf(mexp + 4.0f * sqrtf(mexp) + 6.0f);
+            lo = bound_select_range<BLOCK, 16>(ks, rf >= (float)S ? S : (uint32_t)rf, hist, scan, sel, red, P.status);
+        }
+        if (tid == 0) st_dev(&fr->bound, ((uint64_t)tag << 32) | lo);
+        return;
+    }
+    // a tile WG: wave 0 waits for the bound (published by a sample WG placed
+    // before), polling with a pause so that a row's many waiting WGs load
+    // the memory system little; the bound reaches the other waves through
+    // LDS (wave 0's key stage, which it no longer uses)
+    uint32_t* const scan = reinterpret_cast<uint32_t*>(smem);
+    uint32_t* const lo_w = scan + BLOCK / 64;
+    uint32_t tag = 0;  // wave 0's
+    if (wave == 0) {
+        tag = make_tag(uniform(ld_dev(&fr->epoch)));
+        uint32_t v = 1u;
+        if (ns > 0) {
+            uint64_t bv = ld_dev(&fr->bound);
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while ((uint32_t)(bv >> 32) != tag) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= lim) {
+                    bv = 0ull;  // gave up: 0, never a bound
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                bv = ld_dev(&fr->bound);
+            }
+            v = (uint32_t)bv;
+        }
+        if (lane == 0) *lo_w = v;
+    }
+    lds_sync();  // every wave is past its key stage; the bound is in LDS
+    const uint32_t lo = *lo_w;
+    const bool g = lo == 0u;  // the wait gave up: the WG writes no candidates
+    uint32_t c = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) c += (s2 < nvw) & (kk[s2] >= lo) & !g;
+    uint32_t total;
+    uint32_t p = block_scan_total<BLOCK>(c, scan, total);
+    if (tid == 0) {
+        if (g) raise_flag(P.status, kFlagTimeout);
+        fr->cnt[widx] = ((uint64_t)tag << 32) | (g ? kFusedGaveUp : total);
+    }
+    uint64_t* const region = P.stage + ((size_t)row * (size_t)P.NT + (size_t)widx) * (size_t)(256 * gpw);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+        if ((s2 < nvw) & (kk[s2] >= lo) & !g) {
+            const uint32_t t = (uint32_t)(64 * group_of(s2) + lane);
+            region[p++] = composite(kk[s2], t);
+        }
+    }
+}
+
+struct FusedFinSmem {
+    alignas(16) uint32_t hist[kHistWords];
+    alignas(16) uint64_t cand[kBufCap];
+    uint64_t small[kSmall];
+    uint32_t cnt[kFusedMaxT];  // the tile WGs' counts
+    uint32_t pre[kFusedMaxT];  // their exclusive prefix
+    uint32_t scan[kFinBlock / 64];
+    uint32_t sel[4];
+    uint32_t bad;
+};
+
+// The finishing WG of a row: everything the candidate kernel wrote is
+// complete (the kernel before it on the stream), so it reads its counts,
+// sample keys and regions directly.
+__global__ void __launch_bounds__(kFinBlock) topk_indexer_finish_kernel(FusedParams P) {
+    constexpr int BLOCK = kFinBlock;
+    static_assert(BLOCK >= kFusedMaxT, "one count per thread");
+    static_assert(4 * BLOCK >= kFusedSample, "four sample entries per thread");
+    __shared__ FusedFinSmem sm;
+    const int row = (int)blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = P.n, k = P.k;
+    const int L = valid_length(P.lengths, row, n);
+    int32_t* const out = P.out + (size_t)row * (size_t)k;
+    if (L <= k) {  // every valid token is selected; pad with -1
+        for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
+        return;
+    }
+    FusedRow* const fr = P.frs + row;
+    const uint32_t epoch = fr->epoch;
+    const uint32_t tag = make_tag(epoch);
+    const int NT = P.NT, F = P.F;
+    const int SN = P.ns * 64;  // sample entries
+    const uint32_t R = 256u * (uint32_t)P.gpw;
+    const uint64_t* const sp = P.samp + (size_t)row * (size_t)kFusedSample;
+    uint64_t sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = tid + u * BLOCK;
+        sv[u] = j < SN ? sp[j] : 0ull;
+    }
+    bool bad = false;
+    uint32_t lo = 1u;
+    if (SN > 0) {
+        const uint64_t bv = fr->bound;
+        bad = (uint32_t)(bv >> 32) != tag;
+        lo = bad ? 1u : (uint32_t)bv;
+    }
+    clear_words(sm.hist, kCopies * kStride, tid, BLOCK);
+    if (tid == 0) sm.bad = 0u;
+    if (tid < NT) {
+        const uint64_t cv = fr->cnt[tid];
+        uint32_t c = (uint32_t)cv;
+        if ((uint32_t)(cv >> 32) != tag || c > R) {  // the tile WG gave up waiting for the bound
+            bad = true;
+            c = 0u;
+        }
+        sm.cnt[tid] = c;
+    }
+    uint32_t cs = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = tid + u * BLOCK;
+        if (j < SN && (uint32_t)(sv[u] >> 32) != tag) bad = true;
+        cs += (j < SN) & ((uint32_t)sv[u] >= lo);
+    }
+    if (bad) sm.bad = 1u;
+    lds_sync();  // counts, cleared histogram
+    // the sample's candidates first, in (thread, entry) order, counted into
+    // the first round's window histogram as they are placed
+    uint32_t* const hc = sm.hist + (tid % kCopies) * kStride;
+    uint32_t nsc;
+    uint32_t ps = block_scan_total<BLOCK>(cs, sm.scan, nsc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = tid + u * BLOCK;
+        const uint32_t key = (uint32_t)sv[u];
+        if ((j < SN) & (key >= lo)) {
+            const uint32_t t = (uint32_t)(((j >> 6) * F + F - 1) * 64 + (j & 63));
+            if (ps < (uint32_t)kBufCap) {
+                const uint64_t c = composite(key, t);
+                sm.cand[ps] = c;
+                atomicAdd(&hc[window_bin(c, lo)], 1u);
+            }
+            ++ps;
+        }
+    }
+    // then the regions in WG order
+    const uint32_t cmine = tid < NT ? sm.cnt[tid] : 0u;
+    uint32_t X;
+    const uint32_t pr = block_scan_total<BLOCK>(cmine, sm.scan, X);
+    if (tid < NT) sm.pre[tid] = pr;
+    lds_sync();
+    const uint32_t C = nsc + X;
+    const bool ok = sm.bad == 0u && C >= (uint32_t)k && C <= (uint32_t)kBufCap;
+    if (__builtin_expect(ok, 1)) {
+        // thread t takes entries [t E, t E + E) of the regions' sequence,
+        // locating the first by a binary search over the prefixes and
+        // walking from there
+        const uint32_t E = (X + BLOCK - 1) / BLOCK;
+        const uint32_t ib = (uint32_t)tid * E, ie = min(X, ib + E);
+        if (ib < ie) {
+            int a = 0, b = NT;  // the last region whose prefix is at most ib (it holds entry ib)
+            while (b - a > 1) {
+                const int mid = (a + b) >> 1;
+                if (sm.pre[mid] <= ib) a = mid;
+                else b = mid;
+            }
+            uint32_t j = ib - sm.pre[a];
+            // addresses of eight entries first, then their loads together
+            for (uint32_t i0 = ib; i0 < ie; i0 += 8u) {
+                const uint64_t* ad[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    ad[u] = nullptr;
+                    if (i0 + (uint32_t)u < ie) {
+                        while (j >= sm.cnt[a]) {  // past region a: the next non-empty one
+                            ++a;
+                            j = 0;
+                        }
+                        ad[u] = P.stage + ((size_t)row * (size_t)NT + (size_t)a) * (size_t)R + j;
+                        ++j;
+                    }
+                }
+                uint64_t v8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v8[u] = ad[u] ? *ad[u] : 0ull;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (ad[u]) {
+                        sm.cand[nsc + i0 + (uint32_t)u] = v8[u];
+                        atomicAdd(&hc[window_bin(v8[u], lo)], 1u);
+                    }
+                }
+            }
+        }
+    }
+    if (tid == 0) fr->epoch = epoch + 1u;
+    lds_sync();
+    if (__builtin_expect(ok, 1)) {
+        select_buffer<BLOCK>(sm.cand, C, (uint32_t)k, 0u, lo, true, sm.hist, sm.small, sm.scan, sm.sel, out, nullptr,
+                             k, P.status);
+    } else {
+        const float* const prow = P.logits + (size_t)row * (size_t)n;
+        const int off = (int)(((uintptr_t)prow >> 2) & 3);
+        const int nchunks = (off + L + 3) >> 2;
+        select_by_passes<BLOCK, kBufCap>(reinterpret_cast<const char*>(prow - off), off, L, nchunks, k, out, nullptr,
+                                         sm.cand, sm.hist, sm.small, sm.scan, sm.sel, P.status);
+    }
+}
+
 // ----------------------------------------------------------------- attention over the selected positions
 // The step after the selection (the TopK article, section 01, step 3 of
 // DSA: attention computed only on the keys and values of the k selected
@@ -2430,6 +2879,10 @@ struct Workspace {
     size_t lg_bytes = 0;
     void* at = nullptr;       // attention over the selected positions: per-chunk partials
     size_t at_bytes = 0;
+    void* fu = nullptr;       // indexer with the selection's first pass: FusedRow per row, then the sample keys
+    size_t fu_bytes = 0;
+    void* fst = nullptr;      // indexer with the selection's first pass: candidate regions
+    size_t fst_bytes = 0;
     std::vector<void*> retired;
 };
 
@@ -2901,9 +3354,48 @@ int launch_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t
     return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
 }
 
+// Shape of the indexer with the selection's first pass: groups per wave as
+// for the logits kernel; the sample stride F the smallest power of two from
+// 2 that keeps the sample within 64 groups.  Taken when the tile WGs of a
+// row stay within kFusedMaxT and the candidates a bound lets through (about
+// k + 4 sqrt(k F) + 6 F, see the sample rank) fit the finishing WG's buffer
+// with room to spare; else the logits kernel and topk_select run.
+struct FusedShape {
+    int gpw, F, ns, NS, NT;
+    int64_t grid;
+};
+
+bool fused_shape(int cus, int32_t rows, int32_t n, int32_t k, FusedShape* f) {
+    const int64_t ng = ((int64_t)n + 63) / 64;
+    const int64_t resident_waves = (int64_t)cus * 2 * (kLogitBlock / 64);
+    int64_t gpw = ((int64_t)rows * ng + resident_waves - 1) / resident_waves;
+    gpw = gpw < 1 ? 1 : (gpw > 8 ? 8 : gpw);
+    int64_t F = 2;
+    while (ng / F > kFusedSample / 64) F *= 2;
+    const int64_t ns = ng / F, nr = ng - ns, gw = (kLogitBlock / 64) * gpw;
+    const int64_t NS = (ns + gw - 1) / gw, NT = (nr + gw - 1) / gw;
+    if (NT < 1 || NT > kFusedMaxT) return false;
+    const double est = (double)k + 4.0 * __builtin_sqrt((double)k * (double)F) + 6.0 * (double)F + 256.0;
+    if (est > (double)kBufCap) return false;
+    const int64_t grid = (int64_t)rows * (NS + NT);
+    if (grid > 0x7FFFFFFFll) return false;
+    f->gpw = (int)gpw;
+    f->F = (int)F;
+    f->ns = (int)ns;
+    f->NS = (int)NS;
+    f->NT = (int)NT;
+    f->grid = grid;
+    return true;
+}
+
+template <int D, int HB>
+void launch_fused_t(unsigned grid, hipStream_t stream, const FusedParams& p) {
+    topk_indexer_cand_kernel<D, HB><<<grid, kLogitBlock, 0, stream>>>(p);
+}
+
 int run_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
                 int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k, int32_t* out_idx, float* logits,
-                hipStream_t stream) {
+                hipStream_t stream, bool fused) {
     int rc = validate_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, logits);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
     if (k < 1 || k > n) return TOPK_SELECT_ERROR_INVALID_VALUE;
@@ -2923,6 +3415,65 @@ int run_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int32_t r
         rc = grow(ws, stream, &ws.lg, &ws.lg_bytes, (size_t)rows * (size_t)n * 4u, false);
         if (rc != TOPK_SELECT_SUCCESS) return rc;
         lg = reinterpret_cast<float*>(ws.lg);
+    }
+    DeviceInfo* d = nullptr;
+    rc = device_info(dev, &d);
+    if (rc != TOPK_SELECT_SUCCESS) return rc;
+    FusedShape fs;
+    if (fused && fused_shape(d->cus, rows, n, k, &fs)) {
+        Workspace& ws = g_ws[{dev, (uintptr_t)stream}];
+        rc = grow(ws, stream, &ws.base, &ws.bytes, kStatusBytes, true);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+        const size_t row_bytes = sizeof(FusedRow) + (size_t)kFusedSample * 8u;
+        rc = grow(ws, stream, &ws.fu, &ws.fu_bytes, (size_t)rows * row_bytes, true);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+        // regions sized for the rows of this call (read only up to the counts written in the same call)
+        const size_t stage_bytes = (size_t)rows * (size_t)fs.NT * (size_t)(256 * fs.gpw) * 8u;
+        rc = grow(ws, stream, &ws.fst, &ws.fst_bytes, stage_bytes, true);
+        if (rc != TOPK_SELECT_SUCCESS) return rc;
+        // the row table and the sample keys keep one fixed layout per
+        // buffer: sized for the buffer's capacity, not this call's rows
+        const size_t cap_rows = ws.fu_bytes / row_bytes;
+        FusedParams p;
+        p.q = q;
+        p.kc = kc;
+        p.w = w;
+        p.lengths = lengths;
+        p.logits = lg;
+        p.out = out_idx;
+        p.status = reinterpret_cast<uint32_t*>(ws.base);
+        p.frs = reinterpret_cast<FusedRow*>(ws.fu);
+        p.samp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.fu) + cap_rows * sizeof(FusedRow));
+        p.stage = reinterpret_cast<uint64_t*>(ws.fst);
+        p.kstride = kstride;
+        p.rows = rows;
+        p.n = n;
+        p.H = heads;
+        p.k = k;
+        p.gpw = fs.gpw;
+        p.F = fs.F;
+        p.ns = fs.ns;
+        p.NS = fs.NS;
+        p.NT = fs.NT;
+        const int hb = heads <= 16 ? 1 : (heads <= 32 ? 2 : 4);
+        const unsigned g = (unsigned)fs.grid;
+        (void)hipGetLastError();
+        if (dim == 32) {
+            if (hb == 1) launch_fused_t<32, 1>(g, stream, p);
+            else if (hb == 2) launch_fused_t<32, 2>(g, stream, p);
+            else launch_fused_t<32, 4>(g, stream, p);
+        } else if (dim == 64) {
+            if (hb == 1) launch_fused_t<64, 1>(g, stream, p);
+            else if (hb == 2) launch_fused_t<64, 2>(g, stream, p);
+            else launch_fused_t<64, 4>(g, stream, p);
+        } else {
+            if (hb == 1) launch_fused_t<128, 1>(g, stream, p);
+            else if (hb == 2) launch_fused_t<128, 2>(g, stream, p);
+            else launch_fused_t<128, 4>(g, stream, p);
+        }
+        if (hipGetLastError() != hipSuccess) return TOPK_SELECT_ERROR_LAUNCH;
+        topk_indexer_finish_kernel<<<dim3((unsigned)rows), kFinBlock, 0, stream>>>(p);
+        return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
     }
     rc = launch_logits(q, kc, w, rows, n, heads, dim, kstride, lengths, lg, stream);
     if (rc != TOPK_SELECT_SUCCESS) return rc;
@@ -3023,7 +3574,18 @@ int topk_indexer_select(const uint16_t* q, const uint16_t* kc, const float* w, i
                         int32_t* out_idx, float* out_logits, topk_select_stream_t stream) {
     try {
         return tks::run_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, k, out_idx, out_logits,
-                                (hipStream_t)stream);
+                                (hipStream_t)stream, false);
+    } catch (...) {
+        return TOPK_SELECT_ERROR_LAUNCH;
+    }
+}
+
+int topk_indexer_select_fused(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n,
+                              int32_t heads, int32_t dim, int64_t kstride, const int32_t* lengths, int32_t k,
+                              int32_t* out_idx, float* out_logits, topk_select_stream_t stream) {
+    try {
+        return tks::run_indexer(q, kc, w, rows, n, heads, dim, kstride, lengths, k, out_idx, out_logits,
+                                (hipStream_t)stream, true);
     } catch (...) {
         return TOPK_SELECT_ERROR_LAUNCH;
     }
@@ -3128,11 +3690,13 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
         // a timeout (a WG gave up waiting for another, so counts or
         // candidates it did not see may have been written after the row was
         // finished) the whole coordination state is cleared instead.
-        auto take = [](void* base, size_t bytes, void* stage, size_t stage_bytes, uint32_t* v) -> bool {
+        auto take = [](void* base, size_t bytes, std::initializer_list<std::pair<void*, size_t>> more,
+                       uint32_t* v) -> bool {
             if (hipMemcpy(v, base, sizeof(*v), hipMemcpyDeviceToHost) != hipSuccess) return false;
             if (*v & tks::kFlagTimeout) {
                 if (hipMemset(base, 0, bytes) != hipSuccess) return false;
-                if (stage && hipMemset(stage, 0, stage_bytes) != hipSuccess) return false;
+                for (const auto& m : more)
+                    if (m.first && hipMemset(m.first, 0, m.second) != hipSuccess) return false;
             } else if (*v) {
                 const uint32_t zero = 0;
                 if (hipMemcpy(base, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return false;
@@ -3143,12 +3707,13 @@ int topk_select_device_status(topk_select_stream_t stream, int32_t* flags) {
         auto it = tks::g_ws.find({dev, (uintptr_t)stream});
         if (it != tks::g_ws.end() && it->second.base) {
             tks::Workspace& w = it->second;
-            if (!take(w.base, w.bytes, w.stage, w.stage_bytes, &u)) return TOPK_SELECT_ERROR_LAUNCH;
+            if (!take(w.base, w.bytes, {{w.stage, w.stage_bytes}, {w.fu, w.fu_bytes}, {w.fst, w.fst_bytes}}, &u))
+                return TOPK_SELECT_ERROR_LAUNCH;
             v |= u;
         }
         auto sc = tks::g_scratch.find(dev);
         if (sc != tks::g_scratch.end()) {
-            if (!take(sc->second, tks::kScratchBytes, nullptr, 0, &u)) return TOPK_SELECT_ERROR_LAUNCH;
+            if (!take(sc->second, tks::kScratchBytes, {}, &u)) return TOPK_SELECT_ERROR_LAUNCH;
             v |= u;
         }
         *flags = (int32_t)v;
@@ -3167,7 +3732,7 @@ int topk_select_release_workspace(void) {
         for (auto& kv : tks::g_ws) {
             tks::Workspace& w = kv.second;
             std::vector<void*> bufs = w.retired;
-            for (void* p : {w.base, w.stage, w.aux, w.lg, w.at})
+            for (void* p : {w.base, w.stage, w.aux, w.lg, w.at, w.fu, w.fst})
                 if (p) bufs.push_back(p);
             if (bufs.empty()) continue;
             (void)hipSetDevice(kv.first.first);

@@ -107,11 +107,11 @@ def test_indexer_argument_checks_answer_before_any_hip_call(lib):
     def logits(q_=q, kc_=kc, w_=w, rows=2, n=64, heads=16, dim=64, kstride=0, lengths=None, out=lg):
         return lib.topk_indexer_logits(q_, kc_, w_, rows, n, heads, dim, kstride, lengths, out, None)
 
-    def select(k=8, out=o, logits_out=None, **kw):
+    def select(k=8, out=o, logits_out=None, fn="topk_indexer_select", **kw):
         a = dict(q_=q, kc_=kc, w_=w, rows=2, n=64, heads=16, dim=64, kstride=0, lengths=None)
         a.update(kw)
-        return lib.topk_indexer_select(a["q_"], a["kc_"], a["w_"], a["rows"], a["n"], a["heads"], a["dim"],
-                                       a["kstride"], a["lengths"], k, out, logits_out, None)
+        return getattr(lib, fn)(a["q_"], a["kc_"], a["w_"], a["rows"], a["n"], a["heads"], a["dim"],
+                                a["kstride"], a["lengths"], k, out, logits_out, None)
 
     assert logits(rows=0) == _native.SUCCESS
     assert logits(heads=0) == INV and logits(heads=65) == INV
@@ -121,10 +121,13 @@ def test_indexer_argument_checks_answer_before_any_hip_call(lib):
     assert logits(q_=q + 8) == INV and logits(kc_=kc + 4) == INV  # 16-byte alignment
     assert logits(out=None) == INV
     assert logits(out=q + 16) == INV  # logits overlap the queries
-    assert select(k=65) == INV and select(k=0) == INV
-    assert select(out=None) == INV
-    assert select(out=q) == INV  # indices overlap the queries
-    assert select(rows=0) == _native.SUCCESS
+    for fn in ("topk_indexer_select", "topk_indexer_select_fused"):
+        assert select(k=65, fn=fn) == INV and select(k=0, fn=fn) == INV
+        assert select(out=None, fn=fn) == INV
+        assert select(out=q, fn=fn) == INV  # indices overlap the queries
+        assert select(out=lg, logits_out=lg, fn=fn) == INV  # indices overlap the logits output
+        assert select(dim=48, fn=fn) == INV
+        assert select(rows=0, fn=fn) == _native.SUCCESS
 
 
 def test_sparse_attention_argument_checks_answer_before_any_hip_call(lib):

@@ -86,3 +86,48 @@ def test_waits_that_give_up_still_select_exactly(hooks, name):
         assert st == 0 and flags == 0, (st, flags)
         _exact(w, got)
 
+
+def test_indexer_candidates_give_up_still_select_exactly(hooks):
+    """topk_indexer_select_fused with the wait bound at 0: its
+    tile workgroups give up waiting for the row's bound and mark their
+    counts, every kernel still ends, flag 1 is raised, and the finishing
+    workgroup selects the row by passes over the logits, exactly.  After
+    device_status, calls with the normal bound are exact."""
+    torch, lib = hooks
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    lib.topk_indexer_select_fused.argtypes = [P, P, P, I, I, I, I, ctypes.c_int64, P, I, P, P, P]
+    lib.topk_indexer_select_fused.restype = ctypes.c_int
+    wl = W.generate_indexer("idx_b1_n128k_h64_d128")
+    rows, H, d = wl.q.shape
+    n = wl.kc.shape[-2]
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    kc = torch.from_numpy(wl.kc).cuda().to(torch.bfloat16)
+    w = torch.from_numpy(wl.w).cuda()
+    stream = torch.cuda.Stream()
+
+    def call():
+        out = torch.full((rows, wl.k), -7, dtype=torch.int32, device="cuda")
+        lg = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+        rc = lib.topk_indexer_select_fused(q.data_ptr(), kc.data_ptr(), w.data_ptr(), rows, n, H, d, n * d, None, wl.k,
+                                     out.data_ptr(), lg.data_ptr(), stream.cuda_stream)
+        assert rc == 0
+        flags = ctypes.c_int32(-1)
+        st = lib.topk_select_device_status(stream.cuda_stream, ctypes.byref(flags))
+        return out.cpu().numpy(), lg.cpu().numpy(), st, flags.value
+
+    _say("give-up indexer %s: normal bound" % wl.config.name)
+    _, lg_ref, st, flags = call()
+    assert st == 0 and flags == 0, (st, flags)
+    _say("give-up indexer: wait bound 0")
+    assert lib.topk_select_test_set_spin_limit(0) == 0
+    got, lg, st, flags = call()
+    assert st == 5 and flags == 1, (st, flags)
+    assert np.array_equal(lg.view(np.uint32), lg_ref.view(np.uint32)), "logits differ after the give-up"
+    want = oracle.topk(lg_ref, wl.k, None)
+    assert np.array_equal(np.sort(got, 1), np.sort(want, 1)), "output differs from the oracle"
+    _say("give-up indexer: normal bound again after device_status cleared the workspace")
+    assert lib.topk_select_test_set_spin_limit(DEFAULT_LIMIT) == 0
+    for _ in range(3):
+        got, lg, st, flags = call()
+        assert st == 0 and flags == 0, (st, flags)
+        assert np.array_equal(np.sort(got, 1), np.sort(want, 1)), "output differs from the oracle"

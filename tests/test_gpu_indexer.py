@@ -93,6 +93,10 @@ def test_indexer_logits_and_selection(torch_gpu, rows, n, heads, dim, shared, le
     assert np.array_equal(lg2.view(np.uint32), lg.view(np.uint32)), "the two entry points computed different logits"
     want = oracle.topk(lg2, k, wl.lengths)
     assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(want, 1))
+    idx3, lg3 = tks.indexer_select(q, kc, w, k, lengths=L, return_logits=True, fused=True)
+    assert tks.device_status() == 0
+    assert np.array_equal(lg3.cpu().numpy().view(np.uint32), lg.view(np.uint32)), "the fused form's logits differ"
+    assert np.array_equal(np.sort(idx3.cpu().numpy(), 1), np.sort(want, 1))
 
 
 def test_indexer_batch1_decode_workload(torch_gpu):
@@ -127,17 +131,23 @@ def test_indexer_batched_ragged_workload(torch_gpu):
     assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(want, 1))
 
 
-def _periodic_groups(n, per):
-    """Every per-th group of 64 tokens (group j per + per - 1)."""
-    return [j * per + per - 1 for j in range((n + 63) // 64 // per)]
+def _sample_groups(n):
+    """The groups of 64 tokens that topk_indexer_select_fused samples for
+    its bound: every F-th group (F the smallest power of two from 2 that
+    keeps 64 or fewer), group j F + F - 1 for j < ng // F."""
+    ng = (n + 63) // 64
+    F = 2
+    while ng // F > 64:
+        F *= 2
+    return [j * F + F - 1 for j in range(ng // F)]
 
 
-def _select_and_check(torch_gpu, wl, label):
+def _select_and_check(torch_gpu, wl, label, fused=False):
     import sparse_attention_topk_fp32_amd as tks
 
-    _say(label)
+    _say(label + (" (fused)" if fused else ""))
     q, kc, w, L = _dev(torch_gpu, wl)
-    idx, lg = tks.indexer_select(q, kc, w, wl.k, lengths=L, return_logits=True)
+    idx, lg = tks.indexer_select(q, kc, w, wl.k, lengths=L, return_logits=True, fused=fused)
     assert tks.device_status() == 0
     lg = lg.cpu().numpy()
     want = oracle.topk(lg, wl.k, wl.lengths)
@@ -145,6 +155,7 @@ def _select_and_check(torch_gpu, wl, label):
     return idx.cpu().numpy(), lg
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launch", "fused"])
 @pytest.mark.parametrize("rows,n,heads,dim,k,lengths", [
     (5, 12345, 20, 64, 1000, "uniform"),  # ragged rows, n not a multiple of 64
     (1, 16384, 64, 128, 5000, None),      # large k
@@ -153,7 +164,7 @@ def _select_and_check(torch_gpu, wl, label):
     (3, 200000, 16, 32, 2048, None),      # n not a multiple of 64
     (8, 65536, 64, 128, 4096, "uniform"),
 ])
-def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths):
+def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths, fused):
     wl = W.draw(rows, n, heads, dim, k=k, seed=rows * 7 + n % 1000 + k, lengths=lengths)
     if lengths == "uniform":
         # some rows short of k (every valid token selected), one empty
@@ -161,25 +172,28 @@ def test_indexer_selection_shapes(torch_gpu, rows, n, heads, dim, k, lengths):
         if rows > 2:
             wl.lengths[1] = 0
     _select_and_check(torch_gpu, wl, "indexer shape rows=%d n=%d heads=%d dim=%d k=%d %s" % (
-        rows, n, heads, dim, k, lengths or "full"))
+        rows, n, heads, dim, k, lengths or "full"), fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launch", "fused"])
 @pytest.mark.parametrize("scale,label", [(8.0, "periodic groups above the row"),
                                          (0.125, "periodic groups below the row")])
-def test_indexer_selection_periodic_rows(torch_gpu, scale, label):
-    """Rows with a period: the keys of every 16th group of 64 tokens scaled
-    (exactly, by a power of two), so that their logits lie far above or far
-    below the rest; selection still exact against the oracle on the
-    emitted logits."""
+def test_indexer_selection_periodic_rows(torch_gpu, scale, label, fused):
+    """Rows with a period: the keys of every F-th group of 64 tokens scaled
+    (exactly, by a power of two) so that their logits lie far above or far
+    below the rest.  The groups are the fused form's sample, so its bound
+    lies far above the row's k-th largest (fewer than k candidates) or far
+    below it (more than its buffer): it selects by passes over the logits.
+    Exact against the oracle on the emitted logits either way."""
     n, k = 65536, 2048
     wl = W.draw(1, n, 16, 64, k=k, seed=5 + int(scale * 8))
-    for g in _periodic_groups(n, 16):
+    for g in _sample_groups(n):
         wl.kc[0, 64 * g:64 * g + 64] *= np.float32(scale)
-    _select_and_check(torch_gpu, wl, "indexer %s n=%d k=%d" % (label, n, k))
+    _select_and_check(torch_gpu, wl, "indexer %s n=%d k=%d" % (label, n, k), fused)
 
 
 def test_indexer_selection_is_repeatable(torch_gpu):
-    """The indexer selection writes the same bytes on every call (positions
+    """Both indexer selections write the same bytes on every call (positions
     follow from block scans and exact ranks, not from timing)."""
     import sparse_attention_topk_fp32_amd as tks
 
@@ -187,8 +201,9 @@ def test_indexer_selection_is_repeatable(torch_gpu):
         wl = W.generate_indexer(name)
         _say("indexer repeatability %s" % name)
         q, kc, w, L = _dev(torch_gpu, wl)
-        first = tks.indexer_select(q, kc, w, wl.k, lengths=L).cpu().numpy()
-        for _ in range(3):
-            again = tks.indexer_select(q, kc, w, wl.k, lengths=L).cpu().numpy()
-            assert np.array_equal(first, again)
-        assert tks.device_status() == 0
+        for fused in (False, True):
+            first = tks.indexer_select(q, kc, w, wl.k, lengths=L, fused=fused).cpu().numpy()
+            for _ in range(3):
+                again = tks.indexer_select(q, kc, w, wl.k, lengths=L, fused=fused).cpu().numpy()
+                assert np.array_equal(first, again), fused
+            assert tks.device_status() == 0

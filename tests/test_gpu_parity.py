@@ -448,6 +448,50 @@ def test_graph_replay_matches_eager(torch_gpu):
         assert_parity(w.x, w.k, w.lengths, out.cpu().numpy())
 
 
+def test_graph_survives_workspace_growth(torch_gpu):
+    """A graph keeps the buffers it was captured with: a first call inside a
+    capture (no workspace yet) is refused with the capture error and
+    enqueues nothing; after an eager warm-up, a captured call keeps giving
+    the eager result even after a larger eager call on the same stream has
+    grown the workspace (the old buffers are retired, not freed)."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    torch = torch_gpu
+    _say("graph capture: refused first call, growth between replays")
+    tks.release_workspace()
+    w1, w4 = W.generate("c2"), W.generate("c4")
+    x1 = torch.from_numpy(w1.x).cuda()
+    x4 = torch.from_numpy(w4.x).cuda()
+    L4 = torch.from_numpy(w4.lengths).cuda()
+    out1 = torch.full((1, w1.k), -7, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with pytest.raises(tks.TopkSelectError):
+            with torch.cuda.graph(g0, stream=s):
+                tks.select(x1, w1.k, out=out1)
+    torch.cuda.synchronize()
+    assert int((out1 != -7).sum()) == 0
+    with torch.cuda.stream(s):
+        eager = tks.select(x1, w1.k).clone()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            tks.select(x1, w1.k, out=out1)
+        big = tks.select(x4, w4.k, lengths=L4)  # 64 rows: the row table and the stage grow
+    torch.cuda.synchronize()
+    assert_parity(w4.x, w4.k, w4.lengths, big.cpu().numpy())
+    for rep in range(3):
+        out1.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out1, eager), rep
+    assert tks.device_status(s) == 0
+    assert_parity(w1.x, w1.k, None, out1.cpu().numpy())
+
+
 def test_workspace_reuse_across_row_counts(torch_gpu):
     """Calls with different row counts reuse one workspace: per-row scratch
     must never be overlapped by another call's staging area (a one-row split
