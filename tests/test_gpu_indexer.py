@@ -207,3 +207,17 @@ def test_indexer_selection_is_repeatable(torch_gpu):
                 again = tks.indexer_select(q, kc, w, wl.k, lengths=L, fused=fused).cpu().numpy()
                 assert np.array_equal(first, again), fused
             assert tks.device_status() == 0
+
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launch", "fused"])
+def test_indexer_selection_drifting_rows(torch_gpu, fused):
+    """Rows whose logits grow along the row (keys of the third quarter
+    scaled by 2, of the last by 4, exactly): the k largest all sit in the
+    last quarter, away from most of the rows' sampled groups.  Exact
+    against the oracle on the emitted logits."""
+    rows, n, k = 32, 16384, 2048
+    wl = W.draw(rows, n, 16, 64, k=k, seed=91)
+    wl.kc[:, n // 2:3 * n // 4] *= np.float32(2.0)
+    wl.kc[:, 3 * n // 4:] *= np.float32(4.0)
+    _select_and_check(torch_gpu, wl, "indexer drifting rows=%d n=%d k=%d" % (rows, n, k), fused)
