@@ -221,3 +221,50 @@ def test_indexer_selection_drifting_rows(torch_gpu, fused):
     wl.kc[:, n // 2:3 * n // 4] *= np.float32(2.0)
     wl.kc[:, 3 * n // 4:] *= np.float32(4.0)
     _select_and_check(torch_gpu, wl, "indexer drifting rows=%d n=%d k=%d" % (rows, n, k), fused)
+
+
+def test_indexer_fused_graph_replay_and_streams(torch_gpu):
+    """The fused form's per-row state (epochs, tags) lives in device memory:
+    captured in a graph, every replay (with eager calls between) writes the
+    eager call's bytes; calls on two streams at once (each with its own
+    workspace) both match it."""
+    import sparse_attention_topk_fp32_amd as tks
+
+    torch = torch_gpu
+    wl = W.generate_indexer("idx_b64_n16k_h64_d128_ragged")
+    _say("indexer fused: graph replay x3 and two streams")
+    q, kc, w, L = _dev(torch, wl)
+    rows = wl.q.shape[0]
+    s = torch.cuda.Stream()
+    out = torch.full((rows, wl.k), -7, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(s):
+        eager = tks.indexer_select(q, kc, w, wl.k, lengths=L, fused=True).clone()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            tks.indexer_select(q, kc, w, wl.k, lengths=L, out=out, fused=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        _ = tks.indexer_select(q, kc, w, wl.k, lengths=L, fused=True)  # eager work between replays
+        torch.cuda.synchronize()
+    assert tks.device_status(s) == 0
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    o1 = torch.empty_like(out)
+    o2 = torch.empty_like(out)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            tks.indexer_select(q, kc, w, wl.k, lengths=L, out=o1, fused=True)
+        with torch.cuda.stream(s2):
+            tks.indexer_select(q, kc, w, wl.k, lengths=L, out=o2, fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, eager) and torch.equal(o2, eager)
+    assert tks.device_status(s1) == 0 and tks.device_status(s2) == 0
+    lg = tks.indexer_logits(q, kc, w, lengths=L).cpu().numpy()
+    want = oracle.topk(lg, wl.k, wl.lengths)
+    assert np.array_equal(np.sort(eager.cpu().numpy(), 1), np.sort(want, 1))
