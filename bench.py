@@ -246,10 +246,17 @@ def bench_attention(torch, tks, W, name: str, steps: int, warmup: int):
 
 
 def kernel_source_sha256() -> str:
+    """SHA-256 over the library's kernel sources (every file of csrc/, by
+    name, each as its name and its bytes)."""
     import hashlib
 
-    src = os.path.join(ROOT, "sparse_attention_topk_fp32_amd", "csrc", "topk_select.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    d = os.path.join(ROOT, "sparse_attention_topk_fp32_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):

@@ -1,0 +1,288 @@
+// attention.h - attention over the selected positions on the matrix cores.
+// Part of the topk_select library: included once, in order, by topk_select.hip.
+
+#pragma once
+
+#include "indexer.h"
+
+namespace tks {
+
+// ----------------------------------------------------------------- attention over the selected positions
+// The step after the selection (the TopK article, section 01, step 3 of
+// DSA: attention computed only on the keys and values of the k selected
+// positions).  The article gives no formula; computed here is plain scaled
+// dot-product attention of each query head over the selected positions,
+// keys and values shared by the heads:
+//     out[r][h] = sum_j softmax_j(scale * q[r][h] . K[idx_j]) V[idx_j],
+// over the slots holding a position (-1, or a value outside [0, n), holds
+// none).  Split over the slots: a WG takes 64 slots of one row, computes
+// the scores on the matrix cores (A = 16 heads x 32 dims of the queries,
+// B = 32 dims x 16 gathered keys), a softmax over its slots (maximum m,
+// sum l) and P.V on the matrix cores (A = 16 heads x 32 slots of P, as the
+// sum of two bf16 terms, one product each; B = 32 slots x 16 dims of the
+// gathered values, held transposed in LDS so
+// that a lane's 8 slots of one dim are 16 contiguous bytes), and writes
+// (m, l, partial output); a second kernel combines a row's chunks.
+
+constexpr int kAttnBlock = 256;  // 4 waves, 16 slots each
+constexpr int kAttnSlots = 64;   // slots per WG
+
+struct AttnParams {
+    const uint16_t* q;     // [rows, H, D] bf16
+    const uint16_t* kc;    // keys of row r at kc + r * kvstride: [n, D] bf16
+    const uint16_t* vc;    // values, same layout
+    const int32_t* idx;    // [rows, k]
+    float* out;            // [rows, H, D]
+    float* part;           // [rows, S, H, D + 2]: partial output, then m and l
+    int64_t kvstride;
+    int32_t rows, n, H, k, S;
+    float scale;
+};
+
+template <int D, int HB>
+__global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParams P) {
+    constexpr int KB = D / 32;     // 32-dim steps of a score
+    constexpr int CPR = D / 8;     // 16-byte chunks per key / value row
+    constexpr int NH = HB * 16;    // padded heads
+    __shared__ u32x4_t qs[NH * CPR];          // queries, chunk c of head h in slot c ^ (h % CPR)
+    __shared__ u32x4_t ks[kAttnSlots * CPR];  // gathered keys, same swizzle by slot
+    __shared__ u32x4_t vt[D * 8];             // values transposed: dim row of 64 slots, chunk c in c ^ vsw(dim)
+    __shared__ u32x4_t ps[NH * 8];            // P's high bf16 term: head row of 64 slots, chunk c in c ^ (head % 8)
+    __shared__ u32x4_t pl[NH * 8];            // P's low bf16 term (P - high), same layout
+    __shared__ float red[2][kAttnBlock / 64][NH];
+    const int row = blockIdx.x / P.S;
+    const int sp = blockIdx.x - row * P.S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int n = P.n, H = P.H, k = P.k;
+    const int s0 = sp * kAttnSlots;
+    const int32_t* const irow = P.idx + (size_t)row * (size_t)k;
+    const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kvstride);
+    const char* const V = reinterpret_cast<const char*>(P.vc + (size_t)row * (size_t)P.kvstride);
+    // queries (contiguous loads)
+    {
+        const u32x4_t* const qrow = reinterpret_cast<const u32x4_t*>(P.q + (size_t)row * H * D);
+        const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < NH * CPR; i += kAttnBlock) {
+            const int h = i / CPR, c = i % CPR;
+            qs[h * CPR + (c ^ (h % CPR))] = h < H ? qrow[i] : zero4;
+        }
+    }
+    // gathered keys and values: 16-byte pieces, a row of D bf16 per slot;
+    // empty slots read row 0 (their scores are discarded).  All positions
+    // are read first, then all rows, then the LDS writes, so that the
+    // dependent loads overlap.  Transposed value chunks are swizzled by
+    // (dim ^ dim/8) mod 8: the MFMA-layout reads (16 dims, one chunk) and
+    // the writes (16 dims c*8+e of one slot) both spread over the banks.
+    auto vsw = [](int dim) { return (dim ^ (dim >> 3)) & 7; };
+    constexpr int PIECES = kAttnSlots * CPR / kAttnBlock;
+    int toks[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+        const int sl = s0 + (tid + u * kAttnBlock) / CPR;
+        const int t = sl < k ? irow[sl] : -1;
+        toks[u] = (t >= 0 && t < n) ? t : 0;
+    }
+    u32x4_t kr[PIECES], vr[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+        const int c = (tid + u * kAttnBlock) % CPR;
+        const size_t off = (size_t)toks[u] * D * 2 + (size_t)c * 16;
+        kr[u] = *reinterpret_cast<const u32x4_t*>(K + off);
+        vr[u] = *reinterpret_cast<const u32x4_t*>(V + off);
+    }
+    uint16_t* const vt16 = reinterpret_cast<uint16_t*>(vt);
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+        const int i = tid + u * kAttnBlock;
+        const int j = i / CPR, c = i % CPR;
+        ks[j * CPR + (c ^ (j % CPR))] = kr[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int dim = c * 8 + e;
+            const uint32_t w = vr[u][e >> 1];
+            vt16[(dim * 8 + ((j >> 3) ^ vsw(dim))) * 8 + (j & 7)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        }
+    }
+    __syncthreads();
+    // scores of this wave's 16 slots: lane holds heads 4g+i (+16 hb) of slot 16 wave + m
+    const int j = wave * 16 + m;
+    const int sl = s0 + j;
+    const int tj = sl < k ? irow[sl] : -1;
+    const bool valid = tj >= 0 && tj < n;
+    float sc[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int c = kb * 4 + g;
+            const int h = hb * 16 + m;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, qs[h * CPR + (c ^ (h % CPR))]);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ks[j * CPR + (c ^ (j % CPR))]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[hb][i] = valid ? acc[i] * P.scale : -__builtin_huge_valf();
+    }
+    // softmax over the WG's 64 slots, per head: the maximum and the sum,
+    // over the 16 lanes of a head group, then over the 4 waves
+    float mx[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = sc[hb][i];
+#pragma unroll
+            for (int sft = 1; sft < 16; sft <<= 1) x = fmaxf(x, __shfl_xor(x, sft));
+            mx[hb][i] = x;
+            if (m == 0) red[0][wave][hb * 16 + 4 * g + i] = x;
+        }
+    __syncthreads();
+    float sum[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = hb * 16 + 4 * g + i;
+            float M = red[0][0][h];
+#pragma unroll
+            for (int w = 1; w < kAttnBlock / 64; ++w) M = fmaxf(M, red[0][w][h]);
+            mx[hb][i] = M;
+            const float p = valid ? __expf(sc[hb][i] - M) : 0.0f;  // M is finite when a slot is valid
+            sc[hb][i] = p;
+            float x = p;
+#pragma unroll
+            for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft);
+            sum[hb][i] = x;
+            if (m == 0) red[1][wave][h] = x;
+            // P as two bf16 terms (each rounded to nearest even): hi, and lo
+            // for the remainder p - hi (exact in float), so hi + lo is within
+            // 2^-16 p of p; head row h, slot j
+            auto bf16_rne = [](float x) {
+                const uint32_t u = __float_as_uint(x);
+                return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            };
+            const uint16_t ph = bf16_rne(p);
+            const uint16_t plo = bf16_rne(p - __uint_as_float((uint32_t)ph << 16));
+            const int pidx = (h * 8 + ((j >> 3) ^ (h % 8))) * 8 + (j & 7);
+            reinterpret_cast<uint16_t*>(ps)[pidx] = ph;
+            reinterpret_cast<uint16_t*>(pl)[pidx] = plo;
+        }
+    __syncthreads();
+    float* const prow = P.part + ((size_t)row * P.S + sp) * (size_t)H * (D + 2);
+    if (wave == 0) {
+        // m and l of each head of this chunk
+        for (int h = lane; h < H; h += 64) {
+            float M = red[0][0][h], Lsum = red[1][0][h];
+#pragma unroll
+            for (int w = 1; w < kAttnBlock / 64; ++w) {
+                M = fmaxf(M, red[0][w][h]);
+                Lsum += red[1][w][h];
+            }
+            prow[(size_t)h * (D + 2) + D] = M;
+            prow[(size_t)h * (D + 2) + D + 1] = Lsum;
+        }
+    }
+    // P.V: output tiles of 16 heads x 16 dims, HB * D/16 of them over the
+    // four waves; two 32-slot steps each, each step a matrix-core product
+    // for P's low term and one for its high term into the same float sums
+    for (int tile = wave; tile < HB * (D / 16); tile += kAttnBlock / 64) {
+        const int hb = tile / (D / 16), db = tile % (D / 16);
+        floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ts = 0; ts < kAttnSlots / 32; ++ts) {
+            const int c = ts * 4 + g;  // slots 8c .. 8c+7
+            const int h = hb * 16 + m, dim = db * 16 + m;
+            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, pl[h * 8 + (c ^ (h % 8))]);
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, ps[h * 8 + (c ^ (h % 8))]);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, vt[dim * 8 + (c ^ vsw(dim))]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+        }
+        // lane holds heads 4g+i of dim db*16 + m
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = hb * 16 + 4 * g + i;
+            if (h < H) prow[(size_t)h * (D + 2) + db * 16 + m] = acc[i];
+        }
+    }
+}
+
+// Combine a row's chunks: out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s
+// with M the largest m_s over the chunks holding a position; zeros when no
+// slot of the row holds one.  One WG of D threads per (row, head): the
+// chunks' (m, l) are read in parallel and their factors kept in LDS, then
+// each thread adds up its dim with eight loads in flight.
+constexpr int kAttnCombineMax = 1024;  // chunks per pass of the factor table
+template <int D>
+__global__ void __launch_bounds__(D) topk_attn_combine_kernel(AttnParams P) {
+    __shared__ float fac[kAttnCombineMax];
+    __shared__ float red[D / 64 > 0 ? D / 64 : 1];
+    __shared__ float bcast[2];
+    const int rh = blockIdx.x;  // row * H + head
+    const int row = rh / P.H, h = rh - row * P.H;
+    const int c = threadIdx.x;
+    const float* const base = P.part + (size_t)row * P.S * (size_t)P.H * (D + 2) + (size_t)h * (D + 2);
+    const size_t stride = (size_t)P.H * (D + 2);
+    const float ninf = -__builtin_huge_valf();
+    // the largest m over chunks with l > 0
+    float M = ninf;
+    for (int s = c; s < P.S; s += D) {
+        const float l = base[s * stride + D + 1];
+        if (l > 0.0f) M = fmaxf(M, base[s * stride + D]);
+    }
+    constexpr int SFT0 = D >= 64 ? 32 : D / 2;  // lanes of the (partial) wave
+    for (int sft = SFT0; sft >= 1; sft >>= 1) M = fmaxf(M, __shfl_xor(M, sft));
+    if (D > 64) {
+        if ((c & 63) == 0) red[c >> 6] = M;
+        __syncthreads();
+        if (c == 0) {
+            float x = red[0];
+            for (int w = 1; w < D / 64; ++w) x = fmaxf(x, red[w]);
+            bcast[0] = x;
+        }
+        __syncthreads();
+        M = bcast[0];
+    }
+    float num = 0.0f, den = 0.0f;
+    for (int s0 = 0; s0 < P.S; s0 += kAttnCombineMax) {
+        const int cnt = min(P.S - s0, kAttnCombineMax);
+        __syncthreads();  // the previous pass's factors are used up
+        float dpart = 0.0f;
+        for (int s = c; s < cnt; s += D) {
+            const float l = base[(s0 + s) * stride + D + 1];
+            const float f = l > 0.0f ? __expf(base[(s0 + s) * stride + D] - M) : 0.0f;
+            fac[s] = f;
+            dpart += f * l;
+        }
+        den += dpart;
+        __syncthreads();
+        int s = 0;
+        for (; s + 8 <= cnt; s += 8) {
+            float o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = base[(s0 + s + u) * stride + c];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) num += fac[s + u] * o[u];
+        }
+        for (; s < cnt; ++s) num += fac[s] * base[(s0 + s) * stride + c];
+    }
+    // the denominator: each thread added a share of the chunks
+    for (int sft = SFT0; sft >= 1; sft >>= 1) den += __shfl_xor(den, sft);
+    if (D > 64) {
+        __syncthreads();
+        if ((c & 63) == 0) red[c >> 6] = den;
+        __syncthreads();
+        if (c == 0) {
+            float x = 0.0f;
+            for (int w = 0; w < D / 64; ++w) x += red[w];
+            bcast[1] = x;
+        }
+        __syncthreads();
+        den = bcast[1];
+    }
+    P.out[(size_t)rh * D + c] = den > 0.0f ? num / den : 0.0f;
+}
+
+}  // namespace tks
