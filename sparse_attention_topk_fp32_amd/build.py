@@ -37,6 +37,8 @@ def command(out: str = LIB, extra=()):
     return [
         hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # leading scalar kernel arguments preloaded into SGPRs at wave launch
+        "-mllvm", "-amdgpu-kernarg-preload-count=9",
         "-Wall", "-Wno-unused-command-line-argument",
         "-I", INCLUDE, SRC, "-o", out, *extra,
     ]

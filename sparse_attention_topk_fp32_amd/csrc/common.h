@@ -55,6 +55,7 @@ struct KParams {
     uint64_t* stage;        // split kernel: [rows][G][region] candidate composites, 0 where unused
     int32_t rows, n, k;
     int32_t G;              // workgroups per row
+    int32_t xcds;           // split kernel: > 1 groups each row's WGs on one XCD (block b runs on XCD b mod xcds)
     int32_t chunks_per_wg;  // 16-byte chunks in one WG's slice
     int32_t region;         // entries of one WG's region in the stage
     int32_t sample_chunks;  // split kernel: chunks in a row's sample (a multiple of 16)

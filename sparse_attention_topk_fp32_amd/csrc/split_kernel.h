@@ -32,8 +32,14 @@ struct SplitSmem {
     uint32_t bad;
 };
 
+// The arguments that the first loads depend on come first, one by one: the
+// dispatcher can then place them in scalar registers as the waves start
+// (kernel-argument preloading), and the row's loads need not wait for the
+// argument fetch.  P holds the rest (its copies of these are not read).
 template <int BLOCK, int ITEMS, bool RESIDENT, bool KEYS, int SPT>
-__global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
+__global__ __launch_bounds__(BLOCK) void topk_split_kernel(const float* logits, const int32_t* lengths, int32_t rows,
+                                                           int32_t n, int32_t k, int32_t G, int32_t xcds, int32_t cpw,
+                                                           int32_t sample_chunks, const KParams P) {
     static_assert(ITEMS % 4 == 0, "ITEMS counts whole 16-byte chunks");
     static_assert(BLOCK % 64 == 0 && BLOCK >= 256, "whole waves, 256 histogram owners");
     static_assert(kCopies * kStride * 4 <= kBufCap * 8, "the bound's second histogram fits in the buffer");
@@ -44,15 +50,28 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     __shared__ SplitSmem<BLOCK> sm;
 
     const int tid = threadIdx.x;
-    const int G = P.G;
-    const int row = blockIdx.x / G;
-    const int w = blockIdx.x - row * G;
-    const int n = P.n;
-    const int k = P.k;
-    const float* __restrict__ prow = P.logits + (size_t)row * (size_t)n;
+    // Block b runs on XCD b mod X (the dispatcher deals blocks out in turn).
+    // Grouped: row r's WG w is block (r mod X) + X (w + G floor(r / X)), so
+    // a row's WGs share one XCD's L2 and meet sooner there; blocks past the
+    // last row exit.  WG w of a row still comes after WGs 0..w-1 in block
+    // order, and nothing else depends on where a WG runs.
+    int row, w;
+    if (xcds > 1) {
+        const int X = xcds;
+        const int x = (int)(blockIdx.x % (unsigned)X);
+        const int s = (int)(blockIdx.x / (unsigned)X);
+        const int rg = s / G;
+        row = x + X * rg;
+        w = s - rg * G;
+        if (row >= rows) return;
+    } else {
+        row = blockIdx.x / G;
+        w = blockIdx.x - row * G;
+    }
+    const float* __restrict__ prow = logits + (size_t)row * (size_t)n;
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
     uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;
-    const int L = valid_length(P.lengths, row, n);
+    const int L = valid_length(lengths, row, n);
     if (L <= k) {  // everything valid is selected; pad with -1
         if (w == 0)
             for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
@@ -60,7 +79,6 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     }
     const int off = (int)(((uintptr_t)prow >> 2) & 3);  // elements before the first 16-byte boundary
     const int nchunks = (off + L + 3) >> 2;
-    const int cpw = P.chunks_per_wg;
     const int Geff = (nchunks + cpw - 1) / cpw;  // WGs with a non-empty slice
     if (w >= Geff) return;
     const bool multi = Geff > 1;
@@ -122,8 +140,8 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const KParams P) {
     // finishing WG checks that at least k candidates came out, else the row
     // is finished by passes over it.
     const bool own_sample = !multi && RESIDENT;
-    const int Sc = own_sample ? 0 : min(nchunks, P.sample_chunks);
-    const bool whole_sample = nchunks <= P.sample_chunks;
+    const int Sc = own_sample ? 0 : min(nchunks, sample_chunks);
+    const bool whole_sample = nchunks <= sample_chunks;
     uint4 sraw[SPT];
     int sc[SPT];  // the sampled chunks (-1: none)
     if (!own_sample) {
