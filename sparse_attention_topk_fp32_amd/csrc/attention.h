@@ -40,7 +40,15 @@ struct AttnParams {
 };
 
 template <int D, int HB>
-__global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParams P) {
+// The arguments that the first loads depend on come first, one by one (the
+// dispatcher places them in scalar registers as the waves start: kernel-
+// argument preloading); they stand in for the parameter block's copies.
+__global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int32_t* idx_, const uint16_t* kc_,
+                                                                       const uint16_t* vc_, const uint16_t* q_,
+                                                                       int64_t kvstride_, int32_t S_, int32_t H_, int32_t k_,
+                                                                       int32_t n_, const AttnParams P0) {
+    AttnParams P = P0;
+    P.idx = idx_, P.kc = kc_, P.vc = vc_, P.q = q_, P.kvstride = kvstride_, P.S = S_, P.H = H_, P.k = k_, P.n = n_;
     constexpr int KB = D / 32;     // 32-dim steps of a score
     constexpr int CPR = D / 8;     // 16-byte chunks per key / value row
     constexpr int NH = HB * 16;    // padded heads
@@ -216,7 +224,10 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(AttnParam
 // each thread adds up its dim with eight loads in flight.
 constexpr int kAttnCombineMax = 1024;  // chunks per pass of the factor table
 template <int D>
-__global__ void __launch_bounds__(D) topk_attn_combine_kernel(AttnParams P) {
+__global__ void __launch_bounds__(D) topk_attn_combine_kernel(float* part_, float* out_, int32_t S_, int32_t H_,
+                                                              const AttnParams P0) {
+    AttnParams P = P0;  // the leading arguments are preloaded, as for the partial kernel
+    P.part = part_, P.out = out_, P.S = S_, P.H = H_;
     __shared__ float fac[kAttnCombineMax];
     __shared__ float red[D / 64 > 0 ? D / 64 : 1];
     __shared__ float bcast[2];

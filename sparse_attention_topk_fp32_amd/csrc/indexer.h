@@ -149,7 +149,15 @@ __device__ __forceinline__ float logits_group(const u32x4_t* st, const bf16x8_t 
 }
 
 template <int D, int HB>
-__global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(LogitParams P) {
+// The arguments that the first loads depend on come first, one by one (the
+// dispatcher places them in scalar registers as the waves start: kernel-
+// argument preloading); they stand in for the parameter block's copies.
+__global__ void __launch_bounds__(kLogitBlock) topk_logits_kernel(const uint16_t* q_, const uint16_t* kc_,
+                                                                 const int32_t* lengths_, int64_t kstride_, int32_t n_,
+                                                                 int32_t H_, int32_t gpw_, int32_t tiles_,
+                                                                 const LogitParams P0) {
+    LogitParams P = P0;
+    P.q = q_, P.kc = kc_, P.lengths = lengths_, P.kstride = kstride_, P.n = n_, P.H = H_, P.gpw = gpw_, P.tiles = tiles_;
     constexpr int CPR = D / 8;         // 16-byte chunks per key
     constexpr int GB = 64 * D * 2;     // bytes of one group's keys (64 tokens)
     constexpr int NL = GB / 1024;      // 16-byte loads per lane per group

@@ -148,7 +148,14 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&c)[E], uint32_t Sp, uint
 // or from the logits when the whole valid row is selected), sort them, and
 // write them to the output (one run per row) or to dst.
 template <int BLOCK, int E>
-__global__ void __launch_bounds__(BLOCK) topk_sort_kernel(SortParams P) {
+// The arguments that the first loads depend on come first, one by one (the
+// dispatcher places them in scalar registers as the waves start: kernel-
+// argument preloading); they stand in for the parameter block's copies.
+__global__ void __launch_bounds__(BLOCK) topk_sort_kernel(const int32_t* idx_, const uint32_t* keys_, const int32_t* lengths_,
+                                                           const float* logits_, int32_t n_, int32_t k_, int32_t nruns_,
+                                                           const SortParams P0) {
+    SortParams P = P0;
+    P.idx = idx_, P.keys = keys_, P.lengths = lengths_, P.logits = logits_, P.n = n_, P.k = k_, P.nruns = nruns_;
     __shared__ uint64_t buf[2 * BLOCK * E];
     const int row = blockIdx.x / P.nruns;
     const int run = blockIdx.x - row * P.nruns;
@@ -234,7 +241,14 @@ __global__ void __launch_bounds__(kMergeBlock) topk_merge_kernel(SortParams P) {
 constexpr int kRankMax = 4096;
 constexpr int kRankBlock = 256;
 
-__global__ void __launch_bounds__(kRankBlock) topk_rank_kernel(SortParams P) {
+// The arguments that the first loads depend on come first, one by one (the
+// dispatcher places them in scalar registers as the waves start: kernel-
+// argument preloading); they stand in for the parameter block's copies.
+__global__ void __launch_bounds__(kRankBlock) topk_rank_kernel(const int32_t* idx_, const uint32_t* keys_,
+                                                              const int32_t* lengths_, const float* logits_, int32_t n_,
+                                                              int32_t k_, int32_t nruns_, const SortParams P0) {
+    SortParams P = P0;
+    P.idx = idx_, P.keys = keys_, P.lengths = lengths_, P.logits = logits_, P.n = n_, P.k = k_, P.nruns = nruns_;
     __shared__ uint64_t all[kRankMax];
     const int RG = P.nruns;
     const int row = blockIdx.x / RG;

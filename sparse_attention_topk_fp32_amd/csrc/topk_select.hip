@@ -439,14 +439,17 @@ SortShape sort_shape(int32_t rows, int32_t k) {
     return s;
 }
 
+// the sort and rank kernels' leading scalar arguments, from S
+#define SORT_HEAD(S) (S).idx, (S).keys, (S).lengths, (S).logits, (S).n, (S).k, (S).nruns
+
 void launch_sort(const SortShape& sh, int32_t rows, hipStream_t stream, const SortParams& p) {
     const dim3 grid((unsigned)((int64_t)rows * sh.nruns));
-    if (sh.block == 256) topk_sort_kernel<256, 4><<<grid, 256, 0, stream>>>(p);
-    else if (sh.block == 512) topk_sort_kernel<512, 4><<<grid, 512, 0, stream>>>(p);
-    else if (sh.items == 1) topk_sort_kernel<1024, 1><<<grid, 1024, 0, stream>>>(p);
-    else if (sh.items == 2) topk_sort_kernel<1024, 2><<<grid, 1024, 0, stream>>>(p);
-    else if (sh.items == 4) topk_sort_kernel<1024, 4><<<grid, 1024, 0, stream>>>(p);
-    else topk_sort_kernel<1024, 8><<<grid, 1024, 0, stream>>>(p);
+    if (sh.block == 256) topk_sort_kernel<256, 4><<<grid, 256, 0, stream>>>(SORT_HEAD(p), p);
+    else if (sh.block == 512) topk_sort_kernel<512, 4><<<grid, 512, 0, stream>>>(SORT_HEAD(p), p);
+    else if (sh.items == 1) topk_sort_kernel<1024, 1><<<grid, 1024, 0, stream>>>(SORT_HEAD(p), p);
+    else if (sh.items == 2) topk_sort_kernel<1024, 2><<<grid, 1024, 0, stream>>>(SORT_HEAD(p), p);
+    else if (sh.items == 4) topk_sort_kernel<1024, 4><<<grid, 1024, 0, stream>>>(SORT_HEAD(p), p);
+    else topk_sort_kernel<1024, 8><<<grid, 1024, 0, stream>>>(SORT_HEAD(p), p);
 }
 
 int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k, int32_t* out,
@@ -557,7 +560,7 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     S.width = 0;
     if (sh.rank) {
         S.nruns = sh.rank_wgs;
-        topk_rank_kernel<<<dim3((unsigned)((int64_t)rows * sh.rank_wgs)), kRankBlock, 0, stream>>>(S);
+        topk_rank_kernel<<<dim3((unsigned)((int64_t)rows * sh.rank_wgs)), kRankBlock, 0, stream>>>(SORT_HEAD(S), S);
         return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
     }
     uint64_t* const run0 = reinterpret_cast<uint64_t*>(aux + 2u * keys_bytes);
@@ -605,7 +608,8 @@ int validate_indexer(const uint16_t* q, const uint16_t* kc, const float* w, int3
 
 template <int D, int HB>
 void launch_logits_t(unsigned grid, hipStream_t stream, const LogitParams& p) {
-    topk_logits_kernel<D, HB><<<grid, kLogitBlock, 0, stream>>>(p);
+    topk_logits_kernel<D, HB><<<grid, kLogitBlock, 0, stream>>>(p.q, p.kc, p.lengths, p.kstride, p.n, p.H, p.gpw,
+                                                                 p.tiles, p);
 }
 
 int launch_logits(const uint16_t* q, const uint16_t* kc, const float* w, int32_t rows, int32_t n, int32_t heads,
@@ -826,16 +830,18 @@ int run_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, con
     const int hb = heads <= 16 ? 1 : (heads <= 32 ? 2 : 4);
     const dim3 g1((unsigned)((int64_t)rows * S)), g2((unsigned)((int64_t)rows * heads));
     (void)hipGetLastError();
-#define TKS_ATTN(D_, HB_) topk_attn_partial_kernel<D_, HB_><<<g1, kAttnBlock, 0, stream>>>(p)
+#define TKS_ATTN(D_, HB_)                                                                                   \
+    topk_attn_partial_kernel<D_, HB_><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, p.S, p.H, \
+                                                                     p.k, p.n, p)
     if (dim == 32) {
         if (hb == 1) TKS_ATTN(32, 1); else if (hb == 2) TKS_ATTN(32, 2); else TKS_ATTN(32, 4);
-        topk_attn_combine_kernel<32><<<g2, 32, 0, stream>>>(p);
+        topk_attn_combine_kernel<32><<<g2, 32, 0, stream>>>(p.part, p.out, p.S, p.H, p);
     } else if (dim == 64) {
         if (hb == 1) TKS_ATTN(64, 1); else if (hb == 2) TKS_ATTN(64, 2); else TKS_ATTN(64, 4);
-        topk_attn_combine_kernel<64><<<g2, 64, 0, stream>>>(p);
+        topk_attn_combine_kernel<64><<<g2, 64, 0, stream>>>(p.part, p.out, p.S, p.H, p);
     } else {
         if (hb == 1) TKS_ATTN(128, 1); else if (hb == 2) TKS_ATTN(128, 2); else TKS_ATTN(128, 4);
-        topk_attn_combine_kernel<128><<<g2, 128, 0, stream>>>(p);
+        topk_attn_combine_kernel<128><<<g2, 128, 0, stream>>>(p.part, p.out, p.S, p.H, p);
     }
 #undef TKS_ATTN
     return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
