@@ -313,45 +313,68 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const float* logits, 
             sm.cnt[wr] = (uint32_t)cv;
         }
         lds_sync();
-        // prefixes over the regions (wave 0): of the counts, and of the
-        // counts past the speculative reads
-        if (tid < 64) {
-            const int npl = (others + 63) / 64;  // regions per lane
-            uint32_t a = 0, x = 0;
-            for (int i = 0; i < npl; ++i) {
-                const int r2 = tid * npl + i;
-                if (r2 < others) {
-                    const uint32_t c = sm.cnt[r2];
-                    a += c;
-                    x += c > E ? c - E : 0u;
+        // prefixes over the regions: of the counts, and of the counts past
+        // the speculative reads.  Up to 64 regions every wave scans them
+        // itself (no barrier; the arrays, which only the reads past the
+        // speculative ones use, are written when there are such); more
+        // regions: wave 0 writes the arrays, then a barrier.
+        uint32_t c_others, X, pn;
+        if (others <= 64) {
+            const int l = tid & 63;
+            const uint32_t c = l < others ? sm.cnt[l] : 0u;
+            const uint32_t x = c > E ? c - E : 0u;
+            const uint32_t ia = wave_inclusive_scan(c), ix = wave_inclusive_scan(x);
+            c_others = (uint32_t)__builtin_amdgcn_readlane((int)ia, 63);
+            X = (uint32_t)__builtin_amdgcn_readlane((int)ix, 63);
+            pn = (uint32_t)__shfl((int)(ia - c), mine ? wr : 0);
+            if (X != 0u) {
+                if (tid < others) {
+                    sm.pre[tid] = ia - c;
+                    sm.prex[tid] = ix - x;
+                }
+                lds_sync();
+            }
+        } else {
+            if (tid < 64) {
+                const int npl = (others + 63) / 64;  // regions per lane
+                uint32_t a = 0, x = 0;
+                for (int i = 0; i < npl; ++i) {
+                    const int r2 = tid * npl + i;
+                    if (r2 < others) {
+                        const uint32_t c = sm.cnt[r2];
+                        a += c;
+                        x += c > E ? c - E : 0u;
+                    }
+                }
+                const uint32_t ia = wave_inclusive_scan(a), ix = wave_inclusive_scan(x);
+                uint32_t pa = ia - a, px = ix - x;
+                for (int i = 0; i < npl; ++i) {
+                    const int r2 = tid * npl + i;
+                    if (r2 < others) {
+                        const uint32_t c = sm.cnt[r2];
+                        sm.pre[r2] = pa;
+                        sm.prex[r2] = px;
+                        pa += c;
+                        px += c > E ? c - E : 0u;
+                    }
+                }
+                if (tid == 63) {
+                    sm.tot[0] = ia;
+                    sm.tot[1] = ix;
                 }
             }
-            const uint32_t ia = wave_inclusive_scan(a), ix = wave_inclusive_scan(x);
-            uint32_t pa = ia - a, px = ix - x;
-            for (int i = 0; i < npl; ++i) {
-                const int r2 = tid * npl + i;
-                if (r2 < others) {
-                    const uint32_t c = sm.cnt[r2];
-                    sm.pre[r2] = pa;
-                    sm.prex[r2] = px;
-                    pa += c;
-                    px += c > E ? c - E : 0u;
-                }
-            }
-            if (tid == 63) {
-                sm.tot[0] = ia;
-                sm.tot[1] = ix;
-            }
+            lds_sync();
+            c_others = uniform(sm.tot[0]);
+            X = uniform(sm.tot[1]);
+            pn = sm.pre[mine ? wr : 0];
         }
-        lds_sync();
-        const uint32_t c_others = uniform(sm.tot[0]), X = uniform(sm.tot[1]);
         C = total + c_others;
         ok = sm.bad == 0u && C >= (uint32_t)k && C <= (uint32_t)kBufCap;
         // every entry is read (when the row is finished otherwise, waited
         // for; all missing ones polled again together), moved to the buffer
         // and cleared for the next launch
         {
-            const uint32_t cn = sm.cnt[mine ? wr : 0], pn = sm.pre[mine ? wr : 0];
+            const uint32_t cn = sm.cnt[mine ? wr : 0];
             const uint32_t cw = mine ? min(cn, (uint32_t)R) : 0u, pw = mine ? pn : 0u;
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
