@@ -150,12 +150,12 @@ int topk_select_no_alloc(const float* logits, int32_t rows, int32_t n, const int
  * Besides the workspace of topk_select, the (device, stream) keeps a second
  * scratch area (grown as needed with hipMalloc; no clearing): rows*k*4 bytes
  * of keys, plus 2*rows*kp*8 bytes when k > 8192 (kp = k rounded up to a
- * multiple of 8192).  The work: when the shape takes the one-WG-per-row
- * kernel (many rows) and k <= 2048, that kernel orders its rows itself (one
- * launch); otherwise the selection kernel records the key of every index it
- * writes and a second launch orders them: the rank kernel for few rows
- * (rows * k^2 <= 2^25, k <= 4096), else one sort kernel (k <= 8192) or a
- * sort kernel and ceil(log2(kp/8192)) merge passes.
+ * multiple of 8192).  The work: for k <= 2048 the workgroup that finishes a
+ * row orders it itself (one launch; the split kernel from the keys it
+ * records in that scratch); for larger k the selection kernel records the
+ * key of every index it writes and a second launch orders them: the rank
+ * kernel for few rows (rows * k^2 <= 2^25, k <= 4096), else one sort kernel
+ * (k <= 8192) or a sort kernel and ceil(log2(kp/8192)) merge passes.
  */
 int topk_select_sorted(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, int32_t k,
                        int32_t* out_idx, float* out_val, topk_select_stream_t stream);

@@ -26,138 +26,6 @@ namespace tks {
 constexpr int kRowsCap = 5376;
 constexpr uint32_t kRowsDenseBin = 512;  // a bound bin holding more buffered entries is refined
 
-// The ordered form of one row, produced by the WG that selected it (the
-// need_sorted option of section 02's radix_topk: descending order; equal
-// values by index ascending, the rule that selects them).  The row's cnt
-// selected composites (recorded keys and indices, or keys of the logits
-// when the whole valid row is selected) are binned by key into at most
-// kOrdBins bins over their key range, counted, scattered into T bin by bin
-// (descending bins), and each is written at its exact rank: the entries of
-// the bins above its own plus the larger ones of its own bin (bins hold a
-// few entries, or equal keys).  Positions follow from the values alone;
-// slots past cnt get -1 and -inf.  T: CAP composites of LDS (cnt <= MAXC
-// <= CAP; the ranked entries are staged after them when 2 cnt <= CAP);
-// hist: 2 * kOrdBins words; scan: BLOCK / 64 words.
-constexpr int kOrdBins = 2048;
-constexpr int kOrdLds = 2048;  // one WG per row: k up to this keeps the unordered output in LDS
-template <int BLOCK, int MAXC, int CAP>
-__device__ __forceinline__ void ordered_finish(const int32_t* sidx, const uint32_t* skey, bool from_logits,
-                                               const float* prow, uint32_t L, uint32_t cnt, int k, int32_t* oout,
-                                               float* ovals, uint64_t* T, uint32_t* hist, uint32_t* scan) {
-    static_assert(MAXC <= CAP, "the entries fit T");
-    constexpr int NU = (MAXC + BLOCK - 1) / BLOCK;  // cnt <= MAXC
-    constexpr int NW = BLOCK / 64;
-    constexpr int BPT = kOrdBins / BLOCK;  // bins per thread for the starts
-    static_assert(kOrdBins % BLOCK == 0 && kOrdBins >= BLOCK, "whole bins per thread");
-    constexpr uint32_t BITS = 11;          // log2(kOrdBins)
-    static_assert((1 << BITS) == kOrdBins, "kOrdBins is 2^BITS");
-    const int tid = threadIdx.x;
-    const uint32_t wid = (uint32_t)tid / 64u;
-    uint32_t* const cur = hist + kOrdBins;
-    clear_words(hist, kOrdBins, tid, BLOCK);
-    uint64_t e[NU];
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const uint32_t i = (uint32_t)(tid + u * BLOCK);
-        e[u] = 0ull;
-        if (i < cnt) {
-            const uint32_t idx = from_logits ? i : (uint32_t)sidx[i];
-            const uint32_t key = from_logits ? key_of(prow[i]) : skey[i];
-            e[u] = composite(key, idx);
-            kmin = min(kmin, key);
-            kmax = max(kmax, key);
-        }
-    }
-    for (int sft = 32; sft >= 1; sft >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, sft));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, sft));
-    }
-    uint32_t* const red = cur;  // the cursors are written only after this is read
-    if (lane_id() == 0) {
-        red[wid] = kmin;
-        red[NW + wid] = kmax;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        kmin = min(kmin, red[w]);
-        kmax = max(kmax, red[NW + w]);
-    }
-    const uint32_t range = kmax - kmin;  // cnt >= 1
-    const uint32_t q = range ? 32u - (uint32_t)__builtin_clz(range) : 0u;
-    const uint32_t sh = q > BITS ? q - BITS : 0u;
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-        if ((uint32_t)(tid + u * BLOCK) < cnt) atomicAdd(&hist[((uint32_t)(e[u] >> 32) - kmin) >> sh], 1u);
-    __syncthreads();
-    // bin starts, bins descending: thread t owns bins top .. top - BPT + 1
-    {
-        const uint32_t top = (uint32_t)kOrdBins - 1u - (uint32_t)(tid * BPT);
-        uint32_t c[BPT], t = 0;
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            c[i] = hist[top - (uint32_t)i];
-            t += c[i];
-        }
-        uint32_t tot;
-        uint32_t ex = block_scan_total<BLOCK>(t, scan, tot);
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            cur[top - (uint32_t)i] = ex;
-            ex += c[i];
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        if ((uint32_t)(tid + u * BLOCK) < cnt) {
-            const uint32_t b = ((uint32_t)(e[u] >> 32) - kmin) >> sh;
-            T[atomicAdd(&cur[b], 1u)] = e[u];
-        }
-    }
-    __syncthreads();
-    // cur[b] is now the end of bin b in T.  The ranked entries are staged in
-    // LDS after T when they fit (then written in order), else stored at
-    // their ranks directly
-    const bool staged = 2u * cnt <= (uint32_t)CAP;
-    uint2* const O = reinterpret_cast<uint2*>(T + cnt);
-    for (uint32_t qi = (uint32_t)tid; qi < cnt; qi += BLOCK) {
-        const uint64_t c = T[qi];
-        const uint32_t key = (uint32_t)(c >> 32);
-        const uint32_t b = (key - kmin) >> sh;
-        const uint32_t end = cur[b], st = end - hist[b];
-        uint32_t r = st;
-        for (uint32_t j = st; j < end; j += 8u) {
-            uint64_t t[8];  // clamped loads, the slots past the bin not counted
-#pragma unroll
-            for (int u = 0; u < 8; ++u) t[u] = T[min(j + (uint32_t)u, end - 1u)];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) r += (uint32_t)((j + (uint32_t)u < end) & (t[u] > c));
-        }
-        const uint32_t idx = ~(uint32_t)c;
-        const float v = value_of(key, prow, L, idx);
-        if (staged) {
-            O[r] = make_uint2(idx, __float_as_uint(v));
-        } else {
-            oout[r] = (int32_t)idx;
-            if (ovals) ovals[r] = v;
-        }
-    }
-    if (staged) {  // in order: coalesced stores, marked non-temporal (written once, not read here)
-        __syncthreads();
-        for (uint32_t j = (uint32_t)tid; j < cnt; j += BLOCK) {
-            const uint2 o = O[j];
-            __builtin_nontemporal_store((int32_t)o.x, oout + j);
-            if (ovals) __builtin_nontemporal_store(__uint_as_float(o.y), ovals + j);
-        }
-    }
-    for (uint32_t j = cnt + (uint32_t)tid; j < (uint32_t)k; j += BLOCK) {
-        oout[j] = -1;
-        if (ovals) ovals[j] = -__builtin_huge_valf();
-    }
-}
-
 template <int BLOCK>
 struct RowsSmem {
     union {

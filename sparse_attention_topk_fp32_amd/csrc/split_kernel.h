@@ -72,9 +72,29 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const float* logits, 
     int32_t* __restrict__ out = P.out + (size_t)row * (size_t)k;
     uint32_t* const okey = KEYS ? P.keys + (size_t)row * (size_t)k : nullptr;
     const int L = valid_length(lengths, row, n);
+    // ordered output made by the finishing WG itself (k <= kOrdLds): from
+    // the unordered indices and keys it records, read back after a barrier
+    int32_t* const oout = KEYS && P.oout ? P.oout + (size_t)row * (size_t)k : nullptr;
+    float* const ovals = KEYS && P.oout && P.ovals ? P.ovals + (size_t)row * (size_t)k : nullptr;
     if (L <= k) {  // everything valid is selected; pad with -1
-        if (w == 0)
-            for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
+        if (w == 0) {
+            bool done = false;
+            if constexpr (KEYS) {
+                if (oout && L > 0) {
+                    ordered_finish<BLOCK, kOrdLds, kBufCap, true>(out, okey, true, prow, (uint32_t)L, (uint32_t)L, k, oout,
+                                                            ovals, sm.cand, sm.hist, sm.scan);
+                    done = true;
+                } else if (oout) {
+                    for (int i = tid; i < k; i += BLOCK) {
+                        oout[i] = -1;
+                        if (ovals) ovals[i] = -__builtin_huge_valf();
+                    }
+                    done = true;
+                }
+            }
+            if (!done)
+                for (int i = tid; i < k; i += BLOCK) out[i] = i < L ? i : -1;
+        }
         return;
     }
     const int off = (int)(((uintptr_t)prow >> 2) & 3);  // elements before the first 16-byte boundary
@@ -474,6 +494,13 @@ __global__ __launch_bounds__(BLOCK) void topk_split_kernel(const float* logits, 
         lds_sync();
         select_by_passes<BLOCK, kBufCap>(base, off, L, nchunks, k, out, okey, sm.cand, sm.hist, sm.small, sm.scan,
                                          sm.sel, P.status);
+    }
+    if constexpr (KEYS) {
+        if (oout) {
+            __syncthreads();  // the recorded unordered form (global scratch) is complete and visible to the WG
+            ordered_finish<BLOCK, kOrdLds, kBufCap, true>(out, okey, false, prow, (uint32_t)L, (uint32_t)k, k, oout, ovals,
+                                                    sm.cand, sm.hist, sm.scan);
+        }
     }
 }
 

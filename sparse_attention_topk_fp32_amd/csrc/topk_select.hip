@@ -78,25 +78,32 @@ constexpr int split_spt(int block, int sample_chunks) {
 // the split kernel's leading scalar arguments, from P
 #define SPLIT_HEAD(p) (p).logits, (p).lengths, (p).rows, (p).n, (p).k, (p).G, (p).xcds, (p).chunks_per_wg, (p).sample_chunks
 
+// (32 logits per thread hold at most two sampled chunks per thread: see
+// sample_chunks_for; no variant with four is compiled for them)
+template <int I>
+constexpr int split_spt_max() { return I >= 32 ? 2 : 4; }
+
 template <int B, int I, bool R>
 void launch_split(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
+    constexpr int SM = split_spt_max<I>();
     const int spt = split_spt(B, p.sample_chunks);
     if (p.keys) {
         if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 1>), grid, block, 0, s, SPLIT_HEAD(p), p);
-        else if (spt == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 2>), grid, block, 0, s, SPLIT_HEAD(p), p);
-        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 4>), grid, block, 0, s, SPLIT_HEAD(p), p);
+        else if (spt == 2 || SM == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, 2>), grid, block, 0, s, SPLIT_HEAD(p), p);
+        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, true, SM>), grid, block, 0, s, SPLIT_HEAD(p), p);
     } else {
         if (spt == 1) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 1>), grid, block, 0, s, SPLIT_HEAD(p), p);
-        else if (spt == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 2>), grid, block, 0, s, SPLIT_HEAD(p), p);
-        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 4>), grid, block, 0, s, SPLIT_HEAD(p), p);
+        else if (spt == 2 || SM == 2) hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, 2>), grid, block, 0, s, SPLIT_HEAD(p), p);
+        else hipLaunchKernelGGL((topk_split_kernel<B, I, R, false, SM>), grid, block, 0, s, SPLIT_HEAD(p), p);
     }
 }
 
 template <int B, int I, bool R>
 int occupancy_split(int* nb, int block) {
+    constexpr int SM = split_spt_max<I>();
     int a = 0, b = 0;
-    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_split_kernel<B, I, R, false, 4>, block, 0);
-    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_split_kernel<B, I, R, true, 4>, block, 0);
+    const int r1 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, topk_split_kernel<B, I, R, false, SM>, block, 0);
+    const int r2 = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, topk_split_kernel<B, I, R, true, SM>, block, 0);
     *nb = a < b ? a : b;
     return r1 != 0 ? r1 : r2;
 }
@@ -546,9 +553,10 @@ int run(const float* logits, int32_t rows, int32_t n, const int32_t* lengths, in
     P.region = L.region;
     P.sample_chunks = L.sample_chunks;
     P.ahead = var.rows_kernel ? d->resident[L.variant] : 0;
-    // ordered output from the one-WG-per-row kernel for k <= kOrdLds: its
-    // WGs order their rows themselves (no sort kernel)
-    const bool ordered_in_rows = ordered && var.rows_kernel && k <= kOrdLds;
+    // ordered output for k <= kOrdLds: the WG that finishes a row orders it
+    // itself (one-WG-per-row kernel: from LDS; split kernel: from the
+    // recorded scratch), no second launch
+    const bool ordered_in_rows = ordered && k <= kOrdLds;
     P.oout = ordered_in_rows ? out : nullptr;
     P.ovals = ordered_in_rows ? vals : nullptr;
     (void)hipGetLastError();
