@@ -219,79 +219,57 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int
 
 // Combine a row's chunks: out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s
 // with M the largest m_s over the chunks holding a position; zeros when no
-// slot of the row holds one.  One WG of D threads per (row, head): the
-// chunks' (m, l) are read in parallel and their factors kept in LDS, then
-// each thread adds up its dim with eight loads in flight.
-constexpr int kAttnCombineMax = 1024;  // chunks per pass of the factor table
-template <int D>
+// slot of the row holds one.  One WG of D threads per (row, head), thread c
+// owning dim c.  The chunks go in batches of SB: a batch's SB partial
+// outputs of dim c and, in lane s of every wave, chunk s's (m, l) are all
+// loaded at once (one memory round trip per batch), M and the denominator
+// are reduced within each wave by shuffles, and lane s's factor is read by
+// every lane with a lane read, so no LDS or barrier is used.  Across
+// batches the sums are rescaled to the running maximum.  SB chunks per
+// batch: 32 (one batch for k <= 2048) when the grid is small and each WG's
+// latency is the time; 16 for many (row, head) pairs, where the
+// fewer loads in flight per thread measured faster.
+constexpr int kAttnCombineFewMax = 256;  // (row, head) pairs up to which SB = 32
+template <int D, int SB>
 __global__ void __launch_bounds__(D) topk_attn_combine_kernel(float* part_, float* out_, int32_t S_, int32_t H_,
                                                               const AttnParams P0) {
     AttnParams P = P0;  // the leading arguments are preloaded, as for the partial kernel
     P.part = part_, P.out = out_, P.S = S_, P.H = H_;
-    __shared__ float fac[kAttnCombineMax];
-    __shared__ float red[D / 64 > 0 ? D / 64 : 1];
-    __shared__ float bcast[2];
+    static_assert(SB == 16 || SB == 32, "chunks per batch");
+    constexpr int RW = D < 64 ? D : 64;  // lanes of a wave in the reductions (lanes past the batch hold nothing)
     const int rh = blockIdx.x;  // row * H + head
     const int row = rh / P.H, h = rh - row * P.H;
-    const int c = threadIdx.x;
+    const int c = threadIdx.x, cs = c & 63;
     const float* const base = P.part + (size_t)row * P.S * (size_t)P.H * (D + 2) + (size_t)h * (D + 2);
     const size_t stride = (size_t)P.H * (D + 2);
     const float ninf = -__builtin_huge_valf();
-    // the largest m over chunks with l > 0
-    float M = ninf;
-    for (int s = c; s < P.S; s += D) {
-        const float l = base[s * stride + D + 1];
-        if (l > 0.0f) M = fmaxf(M, base[s * stride + D]);
-    }
-    constexpr int SFT0 = D >= 64 ? 32 : D / 2;  // lanes of the (partial) wave
-    for (int sft = SFT0; sft >= 1; sft >>= 1) M = fmaxf(M, __shfl_xor(M, sft));
-    if (D > 64) {
-        if ((c & 63) == 0) red[c >> 6] = M;
-        __syncthreads();
-        if (c == 0) {
-            float x = red[0];
-            for (int w = 1; w < D / 64; ++w) x = fmaxf(x, red[w]);
-            bcast[0] = x;
-        }
-        __syncthreads();
-        M = bcast[0];
-    }
-    float num = 0.0f, den = 0.0f;
-    for (int s0 = 0; s0 < P.S; s0 += kAttnCombineMax) {
-        const int cnt = min(P.S - s0, kAttnCombineMax);
-        __syncthreads();  // the previous pass's factors are used up
-        float dpart = 0.0f;
-        for (int s = c; s < cnt; s += D) {
-            const float l = base[(s0 + s) * stride + D + 1];
-            const float f = l > 0.0f ? __expf(base[(s0 + s) * stride + D] - M) : 0.0f;
-            fac[s] = f;
-            dpart += f * l;
-        }
-        den += dpart;
-        __syncthreads();
-        int s = 0;
-        for (; s + 8 <= cnt; s += 8) {
-            float o[8];
+    float Mrun = ninf, num = 0.0f, den = 0.0f;
+    for (int s0 = 0; s0 < P.S; s0 += SB) {
+        const int cnt = min(P.S - s0, SB);
+        const float* const b0 = base + (size_t)s0 * stride;
+        float o[SB];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) o[u] = base[(s0 + s + u) * stride + c];
+        for (int u = 0; u < SB; ++u) o[u] = u < cnt ? b0[u * stride + c] : 0.0f;
+        float m = ninf, l = 0.0f;
+        if (cs < cnt) {
+            const float2 ml = *reinterpret_cast<const float2*>(b0 + cs * stride + D);
+            m = ml.x, l = ml.y;
+        }
+        float mb = l > 0.0f ? m : ninf;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) num += fac[s + u] * o[u];
-        }
-        for (; s < cnt; ++s) num += fac[s] * base[(s0 + s) * stride + c];
-    }
-    // the denominator: each thread added a share of the chunks
-    for (int sft = SFT0; sft >= 1; sft >>= 1) den += __shfl_xor(den, sft);
-    if (D > 64) {
-        __syncthreads();
-        if ((c & 63) == 0) red[c >> 6] = den;
-        __syncthreads();
-        if (c == 0) {
-            float x = 0.0f;
-            for (int w = 0; w < D / 64; ++w) x += red[w];
-            bcast[1] = x;
-        }
-        __syncthreads();
-        den = bcast[1];
+        for (int sft = RW / 2; sft >= 1; sft >>= 1) mb = fmaxf(mb, __shfl_xor(mb, sft));
+        const float Mnew = fmaxf(Mrun, mb);
+        const float f = l > 0.0f ? __expf(m - Mnew) : 0.0f;
+        float dl = f * l;
+#pragma unroll
+        for (int sft = RW / 2; sft >= 1; sft >>= 1) dl += __shfl_xor(dl, sft);
+        const float r = Mrun == ninf ? 0.0f : __expf(Mrun - Mnew);
+        num *= r;
+        den = den * r + dl;
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)) * o[u];
+        Mrun = Mnew;
     }
     P.out[(size_t)rh * D + c] = den > 0.0f ? num / den : 0.0f;
 }

@@ -849,20 +849,30 @@ int run_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, con
     const int hb = heads <= 16 ? 1 : (heads <= 32 ? 2 : 4);
     const dim3 g1((unsigned)((int64_t)rows * S)), g2((unsigned)((int64_t)rows * heads));
     (void)hipGetLastError();
+    // the combine's chunks per batch: 32 for a small grid, 16 for a large one
+    const bool few = (int64_t)rows * heads <= kAttnCombineFewMax;
+#define TKS_COMBINE(D_)                                                                              \
+    do {                                                                                           \
+        if (few)                                                                                   \
+            topk_attn_combine_kernel<D_, 32><<<g2, D_, 0, stream>>>(p.part, p.out, p.S, p.H, p);   \
+        else                                                                                       \
+            topk_attn_combine_kernel<D_, 16><<<g2, D_, 0, stream>>>(p.part, p.out, p.S, p.H, p);   \
+    } while (0)
 #define TKS_ATTN(D_, HB_)                                                                                   \
     topk_attn_partial_kernel<D_, HB_><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, p.S, p.H, \
                                                                      p.k, p.n, p)
     if (dim == 32) {
         if (hb == 1) TKS_ATTN(32, 1); else if (hb == 2) TKS_ATTN(32, 2); else TKS_ATTN(32, 4);
-        topk_attn_combine_kernel<32><<<g2, 32, 0, stream>>>(p.part, p.out, p.S, p.H, p);
+        TKS_COMBINE(32);
     } else if (dim == 64) {
         if (hb == 1) TKS_ATTN(64, 1); else if (hb == 2) TKS_ATTN(64, 2); else TKS_ATTN(64, 4);
-        topk_attn_combine_kernel<64><<<g2, 64, 0, stream>>>(p.part, p.out, p.S, p.H, p);
+        TKS_COMBINE(64);
     } else {
         if (hb == 1) TKS_ATTN(128, 1); else if (hb == 2) TKS_ATTN(128, 2); else TKS_ATTN(128, 4);
-        topk_attn_combine_kernel<128><<<g2, 128, 0, stream>>>(p.part, p.out, p.S, p.H, p);
+        TKS_COMBINE(128);
     }
 #undef TKS_ATTN
+#undef TKS_COMBINE
     return hipGetLastError() == hipSuccess ? TOPK_SELECT_SUCCESS : TOPK_SELECT_ERROR_LAUNCH;
 }
 

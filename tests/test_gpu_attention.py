@@ -62,6 +62,10 @@ def _cases():
         (2, 3000, 40, 64, 700, False, None),
         (4, 2500, 64, 128, 300, True, "uniform"),
         (2, 100, 17, 32, 130, False, None),
+        # several combine batches of 32 chunks (79 chunks: a ragged last one)
+        (1, 9000, 8, 64, 5000, False, None),
+        # more than 256 (row, head) pairs: batches of 16 chunks (24 chunks)
+        (20, 3000, 16, 32, 1500, False, "uniform"),
     ]:
         out.append(pytest.param(rows, n, heads, dim, k, shared, lengths,
                                 id="r%d_n%d_h%d_d%d_k%d_%s_%s" % (rows, n, heads, dim, k,
