@@ -25,7 +25,8 @@ namespace tks {
 // (m, l, partial output); a second kernel combines a row's chunks.
 
 constexpr int kAttnBlock = 256;  // 4 waves, 16 slots each
-constexpr int kAttnSlots = 64;   // slots per WG
+constexpr int kAttnSlots = 64;   // slots per sub-chunk (one or two per WG)
+constexpr int kAttnWideMinWgs = 512;  // WGs of 2 (or 4) sub-chunks from which a launch takes them
 
 struct AttnParams {
     const uint16_t* q;     // [rows, H, D] bf16
@@ -39,31 +40,40 @@ struct AttnParams {
     float scale;
 };
 
-template <int D, int HB>
+template <int D, int HB, int SUB>
 // The arguments that the first loads depend on come first, one by one (the
 // dispatcher places them in scalar registers as the waves start: kernel-
 // argument preloading); they stand in for the parameter block's copies.
+// SUB sub-chunks of 64 slots per WG: all of their positions, keys and
+// values are loaded at once; the scores of each sub-chunk are taken in turn
+// from the one key tile in LDS, the softmax runs over all of the WG's slots,
+// and P.V adds up the sub-chunks in turn into the same sums (no rescaling).
+// SUB = 2 halves the partial outputs a row writes and the combine reads,
+// SUB = 4 quarters them.
 __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int32_t* idx_, const uint16_t* kc_,
                                                                        const uint16_t* vc_, const uint16_t* q_,
                                                                        int64_t kvstride_, int32_t S_, int32_t H_, int32_t k_,
                                                                        int32_t n_, const AttnParams P0) {
     AttnParams P = P0;
     P.idx = idx_, P.kc = kc_, P.vc = vc_, P.q = q_, P.kvstride = kvstride_, P.S = S_, P.H = H_, P.k = k_, P.n = n_;
+    static_assert(SUB == 1 || SUB == 2 || SUB == 4, "sub-chunks per WG");
     constexpr int KB = D / 32;     // 32-dim steps of a score
     constexpr int CPR = D / 8;     // 16-byte chunks per key / value row
     constexpr int NH = HB * 16;    // padded heads
+    constexpr int TILES = HB * (D / 16);                        // P.V output tiles of 16 heads x 16 dims
+    constexpr int NT = (TILES + kAttnBlock / 64 - 1) / (kAttnBlock / 64);  // tiles per wave
     __shared__ u32x4_t qs[NH * CPR];          // queries, chunk c of head h in slot c ^ (h % CPR)
     __shared__ u32x4_t ks[kAttnSlots * CPR];  // gathered keys, same swizzle by slot
     __shared__ u32x4_t vt[D * 8];             // values transposed: dim row of 64 slots, chunk c in c ^ vsw(dim)
-    __shared__ u32x4_t ps[NH * 8];            // P's high bf16 term: head row of 64 slots, chunk c in c ^ (head % 8)
-    __shared__ u32x4_t pl[NH * 8];            // P's low bf16 term (P - high), same layout
+    __shared__ u32x4_t ps[SUB][NH * 8];       // P's high bf16 term: head row of 64 slots, chunk c in c ^ (head % 8)
+    __shared__ u32x4_t pl[SUB][NH * 8];       // P's low bf16 term (P - high), same layout
     __shared__ float red[2][kAttnBlock / 64][NH];
     const int row = blockIdx.x / P.S;
     const int sp = blockIdx.x - row * P.S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int n = P.n, H = P.H, k = P.k;
-    const int s0 = sp * kAttnSlots;
+    const int s0 = sp * (kAttnSlots * SUB);
     const int32_t* const irow = P.idx + (size_t)row * (size_t)k;
     const char* const K = reinterpret_cast<const char*>(P.kc + (size_t)row * (size_t)P.kvstride);
     const char* const V = reinterpret_cast<const char*>(P.vc + (size_t)row * (size_t)P.kvstride);
@@ -84,70 +94,95 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int
     // the writes (16 dims c*8+e of one slot) both spread over the banks.
     auto vsw = [](int dim) { return (dim ^ (dim >> 3)) & 7; };
     constexpr int PIECES = kAttnSlots * CPR / kAttnBlock;
-    int toks[PIECES];
+    int toks[SUB][PIECES];
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-        const int sl = s0 + (tid + u * kAttnBlock) / CPR;
-        const int t = sl < k ? irow[sl] : -1;
-        toks[u] = (t >= 0 && t < n) ? t : 0;
-    }
-    u32x4_t kr[PIECES], vr[PIECES];
+    for (int t = 0; t < SUB; ++t)
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-        const int c = (tid + u * kAttnBlock) % CPR;
-        const size_t off = (size_t)toks[u] * D * 2 + (size_t)c * 16;
-        kr[u] = *reinterpret_cast<const u32x4_t*>(K + off);
-        vr[u] = *reinterpret_cast<const u32x4_t*>(V + off);
-    }
+        for (int u = 0; u < PIECES; ++u) {
+            const int sl = s0 + t * kAttnSlots + (tid + u * kAttnBlock) / CPR;
+            const int tk = sl < k ? irow[sl] : -1;
+            toks[t][u] = (tk >= 0 && tk < n) ? tk : 0;
+        }
+    u32x4_t kr[SUB][PIECES], vr[SUB][PIECES];
+#pragma unroll
+    for (int t = 0; t < SUB; ++t)
+#pragma unroll
+        for (int u = 0; u < PIECES; ++u) {
+            const int c = (tid + u * kAttnBlock) % CPR;
+            const size_t off = (size_t)toks[t][u] * D * 2 + (size_t)c * 16;
+            kr[t][u] = *reinterpret_cast<const u32x4_t*>(K + off);
+            vr[t][u] = *reinterpret_cast<const u32x4_t*>(V + off);
+        }
     uint16_t* const vt16 = reinterpret_cast<uint16_t*>(vt);
+    auto put_keys = [&](const u32x4_t (&r)[PIECES]) {
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-        const int i = tid + u * kAttnBlock;
-        const int j = i / CPR, c = i % CPR;
-        ks[j * CPR + (c ^ (j % CPR))] = kr[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dim = c * 8 + e;
-            const uint32_t w = vr[u][e >> 1];
-            vt16[(dim * 8 + ((j >> 3) ^ vsw(dim))) * 8 + (j & 7)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        for (int u = 0; u < PIECES; ++u) {
+            const int i = tid + u * kAttnBlock;
+            const int j = i / CPR, c = i % CPR;
+            ks[j * CPR + (c ^ (j % CPR))] = r[u];
         }
-    }
-    __syncthreads();
-    // scores of this wave's 16 slots: lane holds heads 4g+i (+16 hb) of slot 16 wave + m
+    };
+    auto put_values = [&](const u32x4_t (&r)[PIECES]) {
+#pragma unroll
+        for (int u = 0; u < PIECES; ++u) {
+            const int i = tid + u * kAttnBlock;
+            const int j = i / CPR, c = i % CPR;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int dim = c * 8 + e;
+                const uint32_t w = r[u][e >> 1];
+                vt16[(dim * 8 + ((j >> 3) ^ vsw(dim))) * 8 + (j & 7)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+            }
+        }
+    };
+    put_values(vr[0]);
+    // scores: lane holds heads 4g+i (+16 hb) of slot 16 wave + m of each sub-chunk
     const int j = wave * 16 + m;
-    const int sl = s0 + j;
-    const int tj = sl < k ? irow[sl] : -1;
-    const bool valid = tj >= 0 && tj < n;
-    float sc[HB][4];
+    float sc[SUB][HB][4];
+    bool valid[SUB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < SUB; ++t) {
+        if (t > 0) __syncthreads();  // the previous sub-chunk's scores have read the key tile
+        put_keys(kr[t]);
+        __syncthreads();
+        const int sl = s0 + t * kAttnSlots + j;
+        const int tj = sl < k ? irow[sl] : -1;
+        valid[t] = tj >= 0 && tj < n;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int c = kb * 4 + g;
-            const int h = hb * 16 + m;
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, qs[h * CPR + (c ^ (h % CPR))]);
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ks[j * CPR + (c ^ (j % CPR))]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        for (int hb = 0; hb < HB; ++hb) {
+            floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int c = kb * 4 + g;
+                const int h = hb * 16 + m;
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, qs[h * CPR + (c ^ (h % CPR))]);
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ks[j * CPR + (c ^ (j % CPR))]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[t][hb][i] = valid[t] ? acc[i] * P.scale : -__builtin_huge_valf();
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[hb][i] = valid ? acc[i] * P.scale : -__builtin_huge_valf();
     }
-    // softmax over the WG's 64 slots, per head: the maximum and the sum,
-    // over the 16 lanes of a head group, then over the 4 waves
-    float mx[HB][4];
+    // softmax over the WG's slots, per head: the maximum and the sum, over
+    // the sub-chunks, the 16 lanes of a head group, then the 4 waves
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float x = sc[hb][i];
+            float x = sc[0][hb][i];
+#pragma unroll
+            for (int t = 1; t < SUB; ++t) x = fmaxf(x, sc[t][hb][i]);
 #pragma unroll
             for (int sft = 1; sft < 16; sft <<= 1) x = fmaxf(x, __shfl_xor(x, sft));
-            mx[hb][i] = x;
             if (m == 0) red[0][wave][hb * 16 + 4 * g + i] = x;
         }
     __syncthreads();
-    float sum[HB][4];
+    // P as two bf16 terms (each rounded to nearest even): hi, and lo for the
+    // remainder p - hi (exact in float), so hi + lo is within 2^-16 p of p
+    auto bf16_rne = [](float x) {
+        const uint32_t u = __float_as_uint(x);
+        return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    };
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -156,26 +191,20 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int
             float M = red[0][0][h];
 #pragma unroll
             for (int w = 1; w < kAttnBlock / 64; ++w) M = fmaxf(M, red[0][w][h]);
-            mx[hb][i] = M;
-            const float p = valid ? __expf(sc[hb][i] - M) : 0.0f;  // M is finite when a slot is valid
-            sc[hb][i] = p;
-            float x = p;
+            float x = 0.0f;
+#pragma unroll
+            for (int t = 0; t < SUB; ++t) {
+                const float p = valid[t] ? __expf(sc[t][hb][i] - M) : 0.0f;  // M is finite when a slot is valid
+                x += p;
+                const uint16_t ph = bf16_rne(p);
+                const uint16_t plo = bf16_rne(p - __uint_as_float((uint32_t)ph << 16));
+                const int pidx = (h * 8 + ((j >> 3) ^ (h % 8))) * 8 + (j & 7);  // head row h, slot j
+                reinterpret_cast<uint16_t*>(ps[t])[pidx] = ph;
+                reinterpret_cast<uint16_t*>(pl[t])[pidx] = plo;
+            }
 #pragma unroll
             for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft);
-            sum[hb][i] = x;
             if (m == 0) red[1][wave][h] = x;
-            // P as two bf16 terms (each rounded to nearest even): hi, and lo
-            // for the remainder p - hi (exact in float), so hi + lo is within
-            // 2^-16 p of p; head row h, slot j
-            auto bf16_rne = [](float x) {
-                const uint32_t u = __float_as_uint(x);
-                return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-            };
-            const uint16_t ph = bf16_rne(p);
-            const uint16_t plo = bf16_rne(p - __uint_as_float((uint32_t)ph << 16));
-            const int pidx = (h * 8 + ((j >> 3) ^ (h % 8))) * 8 + (j & 7);
-            reinterpret_cast<uint16_t*>(ps)[pidx] = ph;
-            reinterpret_cast<uint16_t*>(pl)[pidx] = plo;
         }
     __syncthreads();
     float* const prow = P.part + ((size_t)row * P.S + sp) * (size_t)H * (D + 2);
@@ -192,27 +221,47 @@ __global__ void __launch_bounds__(kAttnBlock) topk_attn_partial_kernel(const int
             prow[(size_t)h * (D + 2) + D + 1] = Lsum;
         }
     }
-    // P.V: output tiles of 16 heads x 16 dims, HB * D/16 of them over the
-    // four waves; two 32-slot steps each, each step a matrix-core product
-    // for P's low term and one for its high term into the same float sums
-    for (int tile = wave; tile < HB * (D / 16); tile += kAttnBlock / 64) {
-        const int hb = tile / (D / 16), db = tile % (D / 16);
-        floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // P.V: output tiles of 16 heads x 16 dims, TILES of them over the four
+    // waves; per sub-chunk two 32-slot steps each, each step a matrix-core
+    // product for P's low term and one for its high term into the same
+    // float sums
+    floatx4_t acc[NT];
 #pragma unroll
-        for (int ts = 0; ts < kAttnSlots / 32; ++ts) {
-            const int c = ts * 4 + g;  // slots 8c .. 8c+7
-            const int h = hb * 16 + m, dim = db * 16 + m;
-            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, pl[h * 8 + (c ^ (h % 8))]);
-            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, ps[h * 8 + (c ^ (h % 8))]);
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, vt[dim * 8 + (c ^ vsw(dim))]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+    for (int it = 0; it < NT; ++it) acc[it] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+        if (t > 0) {
+            __syncthreads();  // the previous sub-chunk's products have read the value tile
+            put_values(vr[t]);
+            __syncthreads();
         }
-        // lane holds heads 4g+i of dim db*16 + m
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+            const int tile = wave + it * (kAttnBlock / 64);
+            if (TILES % (kAttnBlock / 64) != 0 && tile >= TILES) break;
+            const int hb = tile / (D / 16), db = tile % (D / 16);
+#pragma unroll
+            for (int ts = 0; ts < kAttnSlots / 32; ++ts) {
+                const int c = ts * 4 + g;  // slots 8c .. 8c+7
+                const int h = hb * 16 + m, dim = db * 16 + m;
+                const bf16x8_t al = __builtin_bit_cast(bf16x8_t, pl[t][h * 8 + (c ^ (h % 8))]);
+                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, ps[t][h * 8 + (c ^ (h % 8))]);
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, vt[dim * 8 + (c ^ vsw(dim))]);
+                acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[it], 0, 0, 0);
+                acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[it], 0, 0, 0);
+            }
+        }
+    }
+    // lane holds heads 4g+i of dim db*16 + m
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+        const int tile = wave + it * (kAttnBlock / 64);
+        if (TILES % (kAttnBlock / 64) != 0 && tile >= TILES) break;
+        const int hb = tile / (D / 16), db = tile % (D / 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = hb * 16 + 4 * g + i;
-            if (h < H) prow[(size_t)h * (D + 2) + db * 16 + m] = acc[i];
+            if (h < H) prow[(size_t)h * (D + 2) + db * 16 + m] = acc[it][i];
         }
     }
 }

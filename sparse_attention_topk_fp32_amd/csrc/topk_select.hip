@@ -824,7 +824,15 @@ int run_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, con
     if (overlaps(out, ob, q, (size_t)rows * heads * dim * 2u) || overlaps(out, ob, kc, kvb) ||
         overlaps(out, ob, vc, kvb) || overlaps(out, ob, idx, (size_t)rows * k * 4u))
         return TOPK_SELECT_ERROR_INVALID_VALUE;
-    const int64_t S = (k + kAttnSlots - 1) / kAttnSlots;
+    // four (256 slots) or two (128 slots) sub-chunks per WG when that still
+    // gives kAttnWideMinWgs WGs: a quarter or half of the partial outputs to
+    // write and combine
+    const int64_t S2 = (k + 2 * kAttnSlots - 1) / (2 * kAttnSlots);
+    const int64_t S4 = (k + 4 * kAttnSlots - 1) / (4 * kAttnSlots);
+    const int sub = (k > 3 * kAttnSlots && (int64_t)rows * S4 >= kAttnWideMinWgs)   ? 4
+                    : (k > kAttnSlots && (int64_t)rows * S2 >= kAttnWideMinWgs) ? 2
+                                                                                  : 1;
+    const int64_t S = (k + sub * kAttnSlots - 1) / (sub * kAttnSlots);
     if ((int64_t)rows * S > 0x7FFFFFFFll || (int64_t)rows * heads > 0x7FFFFFFFll) return TOPK_SELECT_ERROR_INVALID_VALUE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TOPK_SELECT_ERROR_NO_DEVICE;
@@ -858,9 +866,18 @@ int run_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, con
         else                                                                                       \
             topk_attn_combine_kernel<D_, 16><<<g2, D_, 0, stream>>>(p.part, p.out, p.S, p.H, p);   \
     } while (0)
-#define TKS_ATTN(D_, HB_)                                                                                   \
-    topk_attn_partial_kernel<D_, HB_><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, p.S, p.H, \
-                                                                     p.k, p.n, p)
+#define TKS_ATTN(D_, HB_)                                                                                  \
+    do {                                                                                                   \
+        if (sub == 4)                                                                                      \
+            topk_attn_partial_kernel<D_, HB_, 4><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, \
+                                                                                p.S, p.H, p.k, p.n, p);   \
+        else if (sub == 2)                                                                                 \
+            topk_attn_partial_kernel<D_, HB_, 2><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, \
+                                                                                p.S, p.H, p.k, p.n, p);   \
+        else                                                                                               \
+            topk_attn_partial_kernel<D_, HB_, 1><<<g1, kAttnBlock, 0, stream>>>(p.idx, p.kc, p.vc, p.q, p.kvstride, \
+                                                                                p.S, p.H, p.k, p.n, p);   \
+    } while (0)
     if (dim == 32) {
         if (hb == 1) TKS_ATTN(32, 1); else if (hb == 2) TKS_ATTN(32, 2); else TKS_ATTN(32, 4);
         TKS_COMBINE(32);

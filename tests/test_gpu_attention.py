@@ -66,6 +66,14 @@ def _cases():
         (1, 9000, 8, 64, 5000, False, None),
         # more than 256 (row, head) pairs: batches of 16 chunks (24 chunks)
         (20, 3000, 16, 32, 1500, False, "uniform"),
+        # at least 512 WGs of two 64-slot sub-chunks: 128 slots per WG (a
+        # ragged last WG; empty slots past each row's length)
+        (48, 3000, 16, 64, 1500, False, "uniform"),
+        (520, 200, 4, 32, 100, True, None),
+        # at least 512 WGs of four sub-chunks: 256 slots per WG (the last
+        # WG of a row ragged in its fourth sub-chunk), 16 and 40 heads
+        (130, 2000, 16, 128, 1000, False, "uniform"),
+        (260, 1500, 40, 64, 500, True, None),
     ]:
         out.append(pytest.param(rows, n, heads, dim, k, shared, lengths,
                                 id="r%d_n%d_h%d_d%d_k%d_%s_%s" % (rows, n, heads, dim, k,
