@@ -263,9 +263,11 @@ int topk_indexer_select_fused(const uint16_t* q, const uint16_t* kc, const float
  * the matrix cores summed in float.  Each output lies within
  *   (2 (dim + 2) 2^-24 smax + 2^-16 + (k + 64) 2^-24 + 2^-20) * sum_j p_j |V[idx_j][c]|
  * of the exact value, smax = max_j scale * sum_i |q_i K[idx_j]_i|.
- * Two kernels are enqueued (per chunk of 64 slots, then the combination);
- * scratch of rows * ceil(k/64) * heads * (dim + 2) * 4 bytes per (device,
- * stream), grown with hipMalloc when needed.  Errors as for topk_select.
+ * Two kernels are enqueued (per chunk of C slots, then the combination): C
+ * is 256 when that still makes at least 512 chunks in all, else 128 when
+ * that does, else 64.  Scratch of rows * ceil(k/C) * heads * (dim + 2) * 4
+ * bytes per (device, stream), grown with hipMalloc when needed.  Errors as
+ * for topk_select.
  */
 int topk_sparse_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
                           int32_t rows, int32_t n, int32_t heads, int32_t dim, int64_t kvstride, int32_t k,
