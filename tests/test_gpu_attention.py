@@ -71,9 +71,10 @@ def _cases():
         (48, 3000, 16, 64, 1500, False, "uniform"),
         (520, 200, 4, 32, 100, True, None),
         # at least 512 WGs of four sub-chunks: 256 slots per WG (the last
-        # WG of a row ragged in its fourth sub-chunk), 16 and 40 heads
+        # WG of a row ragged in its fourth sub-chunk), 16, 40 and 64 heads
         (130, 2000, 16, 128, 1000, False, "uniform"),
         (260, 1500, 40, 64, 500, True, None),
+        (520, 800, 64, 32, 300, False, "uniform"),
     ]:
         out.append(pytest.param(rows, n, heads, dim, k, shared, lengths,
                                 id="r%d_n%d_h%d_d%d_k%d_%s_%s" % (rows, n, heads, dim, k,
